@@ -1,0 +1,116 @@
+"""Paged decode attention, written as its plain definition — test infrastructure.
+
+Source: "PagedAttention" (shubhamtatvamasi.com), section "How attention reads
+paged memory" and the figure beside it.  A decode query of one sequence sees
+that sequence's tokens 0..L-1; logical block i of the sequence lives in
+physical block ``block_table[i]`` of a per-layer pool shaped
+``[num_blocks, block_size, kv_heads, head_dim]``, and token j sits at
+offset ``j % block_size`` of logical block ``j // block_size``.  Paging only
+changes where the rows live, so paged attention equals ordinary softmax
+attention over the sequence's keys and values gathered back into logical
+order — that is what this module computes, in float64, with two passes
+(maximum first, then exponentials and sums) rather than the kernel's online
+update.
+
+Readings of points the pages leave open (each also listed in the design
+notes):
+
+* the softmax scale is an explicit argument (the workloads use 1/sqrt(D));
+* with ``Hq`` query heads over ``Hkv`` cache heads, query head ``h`` reads
+  cache head ``h // (Hq // Hkv)`` (contiguous groups);
+* ``seq_lens`` counts the token written in the same step, and no other
+  mask applies; a sequence of length 0 yields zeros;
+* fp8 caches hold codes of ``x / scale``; the stored value is
+  ``decode(code) * scale`` (the scale is applied exactly in float64);
+* the output is returned in float64 (the GPU path writes float32).
+"""
+
+import numpy as np
+
+from .storage import to_float64
+
+
+def gather_sequence(pool, table_row, seq_len, block_size, head):
+    """Rows 0..seq_len-1 of one sequence for cache head ``head``: [L, D].
+
+    Walks the block table: logical block i -> physical block table_row[i],
+    concatenated in logical order, cut to the first ``seq_len`` tokens.
+    """
+    n_blocks = -(-int(seq_len) // int(block_size))
+    phys = np.asarray(table_row[:n_blocks], dtype=np.int64)
+    blocks = pool[phys, :, head, :]                 # [n, bs, D]
+    rows = blocks.reshape(n_blocks * block_size, pool.shape[3])
+    return rows[:seq_len]
+
+
+def attention_one_head(q, k, v, scale):
+    """softmax(scale * q k^T) v for a block of query rows, in float64.
+
+    q: [G, D], k: [L, D], v: [L, D]  ->  [G, D].
+    Pass 1 takes the row maximum of the scores; pass 2 forms
+    exp(score - max), its sum, and the weighted sum of value rows.
+    """
+    scores = scale * (q @ k.T)                      # [G, L]
+    m = scores.max(axis=1, keepdims=True)
+    p = np.exp(scores - m)
+    denom = p.sum(axis=1, keepdims=True)
+    return (p @ v) / denom
+
+
+def paged_attention(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
+                    seq_lens, block_size, scale, k_scale=1.0, v_scale=1.0):
+    """Decode attention for every sequence and query head -> float64 [S, Hq, D].
+
+    query: [S, Hq, D] storage array of kind ``q_kind``.
+    k_pool, v_pool: [num_blocks, block_size, Hkv, D] of kind ``kv_kind``.
+    block_tables: int32 [S, max_blocks]; only the first ceil(L/bs) columns
+    of a row are read.  seq_lens: int32 [S].
+    k_scale, v_scale: per-tensor scales, used only for ``"fp8_e4m3"``.
+    """
+    S, Hq, D = query.shape
+    Hkv = k_pool.shape[2]
+    assert Hq % Hkv == 0
+    assert k_pool.shape[1] == block_size
+    G = Hq // Hkv
+    q64 = to_float64(query, q_kind)
+    ks = float(np.float32(k_scale)) if kv_kind == "fp8_e4m3" else 1.0
+    vs = float(np.float32(v_scale)) if kv_kind == "fp8_e4m3" else 1.0
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    for s in range(S):
+        L = int(seq_lens[s])
+        if L == 0:
+            continue
+        for h in range(Hkv):
+            k = to_float64(gather_sequence(k_pool, block_tables[s], L,
+                                           block_size, h), kv_kind) * ks
+            v = to_float64(gather_sequence(v_pool, block_tables[s], L,
+                                           block_size, h), kv_kind) * vs
+            out[s, h * G:(h + 1) * G] = attention_one_head(
+                q64[s, h * G:(h + 1) * G], k, v, scale)
+    return out
+
+
+def paged_attention_rows(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
+                         seq_lens, block_size, scale, rows, k_scale=1.0,
+                         v_scale=1.0):
+    """Same as :func:`paged_attention`, but only for the (seq, q_head) pairs
+    in ``rows``; returns float64 [len(rows), D].  Used to check sampled
+    outputs of full-size workloads one by one."""
+    S, Hq, D = query.shape
+    Hkv = k_pool.shape[2]
+    G = Hq // Hkv
+    ks = float(np.float32(k_scale)) if kv_kind == "fp8_e4m3" else 1.0
+    vs = float(np.float32(v_scale)) if kv_kind == "fp8_e4m3" else 1.0
+    out = np.zeros((len(rows), D), dtype=np.float64)
+    for i, (s, hq) in enumerate(rows):
+        L = int(seq_lens[s])
+        if L == 0:
+            continue
+        h = hq // G
+        k = to_float64(gather_sequence(k_pool, block_tables[s], L,
+                                       block_size, h), kv_kind) * ks
+        v = to_float64(gather_sequence(v_pool, block_tables[s], L,
+                                       block_size, h), kv_kind) * vs
+        q = to_float64(query[s, hq:hq + 1], q_kind)
+        out[i] = attention_one_head(q, k, v, scale)[0]
+    return out

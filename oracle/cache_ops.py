@@ -1,0 +1,64 @@
+"""Slot-mapped cache write and copy-on-write block copy — test infrastructure.
+
+Both functions return new arrays and leave their inputs untouched.
+
+cache_write — "How PagedAttention Works in vLLM ..." (instagit.com), section
+"write_to_paged_cache: Direct In-Place Updates" and the code example: new
+key/value rows ``[T, kv_heads, head_dim]`` go, in place, to the flat slots
+given by an int32 slot mapping, where slot = physical_block * block_size +
+offset (the slot numbering follows the block/offset addressing of
+"PagedAttention" (shubhamtatvamasi.com), "How attention reads paged memory").
+Readings: a negative slot means "skip this token" (padding); when the cache
+dtype equals the source dtype the row is copied bit for bit; for an fp8
+cache each element becomes ``e4m3(float32(x) / float32(scale))`` with an
+IEEE float32 division and the saturating round-to-nearest-even encoder of
+:mod:`oracle.fp8_e4m3`.
+
+copy_blocks — "PagedAttention" (shubhamtatvamasi.com), "Sharing and
+copy-on-write" and the FAQ entry on copy-on-write for parallel sampling:
+before a sequence appends to a shared, partially filled block, the engine
+copies that block into a fresh one.  The library's part is the copy: for
+each (src, dst) pair, every slot of block ``dst`` in both pools takes the
+contents of block ``src``.  Reading: the whole block is copied (the pairs
+carry no token counts).
+"""
+
+import numpy as np
+
+from .fp8_e4m3 import e4m3_encode
+from .storage import to_float64
+
+
+def _encode_row(row, src_kind, cache_kind, scale):
+    if cache_kind == src_kind:
+        return row.copy()
+    if cache_kind == "fp8_e4m3":
+        x32 = to_float64(row, src_kind).astype(np.float32)   # exact widening
+        y = x32 / np.float32(scale)                           # IEEE fp32 div
+        return e4m3_encode(y.astype(np.float64))
+    raise ValueError(f"unsupported write {src_kind} -> {cache_kind}")
+
+
+def cache_write(k_pool, v_pool, cache_kind, key, value, src_kind,
+                slot_mapping, block_size, k_scale=1.0, v_scale=1.0):
+    """Scatter new rows into copies of the pools; returns (k_pool, v_pool)."""
+    kp = k_pool.copy()
+    vp = v_pool.copy()
+    for t in range(len(slot_mapping)):
+        slot = int(slot_mapping[t])
+        if slot < 0:
+            continue
+        b, o = divmod(slot, int(block_size))
+        kp[b, o] = _encode_row(key[t], src_kind, cache_kind, k_scale)
+        vp[b, o] = _encode_row(value[t], src_kind, cache_kind, v_scale)
+    return kp, vp
+
+
+def copy_blocks(k_pool, v_pool, pairs):
+    """Whole-block copies src -> dst in both pools; returns (k_pool, v_pool)."""
+    kp = k_pool.copy()
+    vp = v_pool.copy()
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        kp[dst] = kp[src]
+        vp[dst] = vp[src]
+    return kp, vp

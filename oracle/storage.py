@@ -1,0 +1,31 @@
+"""Exact widening of stored cache/query values to float64 — test infrastructure.
+
+Storage kinds: ``"f32"`` (float32), ``"f16"`` (float16), ``"bf16"`` (uint16
+holding the upper half of a float32 bit pattern), ``"fp8_e4m3"`` (uint8 OCP
+E4M3 codes, decoded by :mod:`oracle.fp8_e4m3`).  Every conversion here is
+exact: each stored value is representable in float64.
+"""
+
+import numpy as np
+
+from .fp8_e4m3 import e4m3_decode
+
+KINDS = ("f32", "f16", "bf16", "fp8_e4m3")
+
+
+def to_float64(arr, kind):
+    a = np.asarray(arr)
+    if kind == "f32":
+        assert a.dtype == np.float32, a.dtype
+        return a.astype(np.float64)
+    if kind == "f16":
+        assert a.dtype == np.float16, a.dtype
+        return a.astype(np.float64)
+    if kind == "bf16":
+        assert a.dtype == np.uint16, a.dtype
+        bits32 = a.astype(np.uint32) << np.uint32(16)
+        return bits32.view(np.float32).astype(np.float64)
+    if kind == "fp8_e4m3":
+        assert a.dtype == np.uint8, a.dtype
+        return e4m3_decode(a)
+    raise ValueError(f"unknown storage kind {kind!r}")
