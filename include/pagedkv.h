@@ -1,0 +1,188 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV-cache hot path.
+ *
+ * Three operations, all asynchronous on the caller's HIP stream:
+ *
+ *   cache_write_slots  slot-mapped scatter of new key/value rows into the
+ *                      paged pools ("How PagedAttention Works in vLLM ...",
+ *                      instagit.com, section "write_to_paged_cache: Direct
+ *                      In-Place Updates", and its code example);
+ *   copy_blocks        whole-block copies for copy-on-write ("PagedAttention",
+ *                      shubhamtatvamasi.com, section "Sharing and
+ *                      copy-on-write" and the FAQ entry on copy-on-write for
+ *                      parallel sampling);
+ *   paged_attn_decode  one decode query per sequence attends over its tokens
+ *                      by walking its block table over the shared pool
+ *                      ("PagedAttention", section "How attention reads paged
+ *                      memory"), with an online softmax per partition of the
+ *                      sequence and a log-sum-exp merge across partitions.
+ *
+ * Memory layout (all buffers are device memory owned by the caller):
+ *   k_cache, v_cache   [num_blocks, block_size, num_kv_heads, head_dim],
+ *                      contiguous, one pool per tensor (the "flash" layout's
+ *                      kv[0] and kv[1] are exactly this);
+ *   block_tables       int32 [num_seqs, max_blocks_per_seq], row-major;
+ *                      entry i of row s is the physical block of logical
+ *                      block i; only the first ceil(seq_len/block_size)
+ *                      entries of a row are read;
+ *   seq_lens           int32 [num_seqs]: tokens of the sequence, including
+ *                      the one written this step;
+ *   slot_mapping       int32 [num_tokens]: slot = block * block_size + offset;
+ *                      a negative slot skips the token;
+ *   query, out         [num_seqs, num_q_heads, head_dim]; out is float32;
+ *                      query head q reads cache head q / (num_q_heads /
+ *                      num_kv_heads);
+ *   k_scale, v_scale   float32 scalars in device memory, read only for an
+ *                      fp8 cache (stored value = decode(code) * scale).
+ *
+ * Errors: every host-checkable precondition is checked before any HIP call;
+ * a failed check returns a non-zero pkv_status and launches nothing.  The
+ * contents of device buffers (table entries in range, slots in range, no
+ * duplicate slots, copy pairs with distinct destinations that are not also
+ * sources) are the caller's contract and are not checked.  A failed launch
+ * returns PKV_ERR_HIP.  The library allocates no memory, never synchronises
+ * and keeps no state: calls are thread-safe, and two calls that share an
+ * attention workspace must not overlap in time.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  PKV_FP8_E4M3 is the OCP E4M3 "fn" format (bias 7, no
+ * infinities, S.1111.111 = NaN, largest magnitude 448). */
+typedef enum pkv_dtype {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3
+} pkv_dtype;
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL                   */
+  PKV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent       */
+  PKV_ERR_DTYPE = 3,       /* unknown dtype or unsupported dtype pairing   */
+  PKV_ERR_UNSUPPORTED = 4, /* valid request this build does not implement  */
+  PKV_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned             */
+  PKV_ERR_WORKSPACE = 6,   /* attention workspace missing or too small     */
+  PKV_ERR_HIP = 8          /* the HIP runtime reported an error            */
+} pkv_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pkv_status_string(int status);
+
+/*
+ * cache_write_slots -- write new K/V rows into the pools in place.
+ *
+ * key, value   [num_tokens, num_kv_heads, head_dim] of src_dtype, contiguous.
+ * k_cache,
+ * v_cache      pools of cache_dtype (layout above), updated in place.
+ * slot_mapping device int32 [num_tokens]; token t goes to block
+ *              slot/block_size, offset slot%block_size; slot < 0 skips it.
+ * k_scale,
+ * v_scale      device float32 scalars, required when cache_dtype is
+ *              PKV_FP8_E4M3, ignored otherwise.
+ *
+ * Element conversion: with src_dtype == cache_dtype the row is copied bit for
+ * bit.  With an fp8 cache (src_dtype F32, F16 or BF16) each element is
+ * encoded as e4m3(float32(x) / scale): IEEE float32 division, round to
+ * nearest even, finite values beyond 448 saturate to +-448, NaN stays NaN.
+ * No other pairing is accepted (PKV_ERR_DTYPE).  num_tokens == 0 is a valid
+ * no-op.  head_dim must be 64 or 128; pointers 16-byte aligned.
+ */
+int cache_write_slots(const void* key, const void* value, int src_dtype,
+                      void* k_cache, void* v_cache, int cache_dtype,
+                      const int32_t* slot_mapping, int64_t num_tokens,
+                      int64_t num_blocks, int32_t block_size,
+                      int32_t num_kv_heads, int32_t head_dim,
+                      const float* k_scale, const float* v_scale,
+                      hipStream_t stream);
+
+/*
+ * copy_blocks -- for each pair (src, dst), every slot of block dst in both
+ * pools takes the bytes of block src.
+ *
+ * block_pairs  device int32 [num_pairs][2] = {src, dst}.  Destinations must be
+ *              distinct and no destination may also be a source (otherwise
+ *              the result depends on scheduling).  num_pairs == 0 is a valid
+ *              no-op (nothing is launched).
+ */
+int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
+                const int32_t* block_pairs, int64_t num_pairs,
+                int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                int32_t head_dim, hipStream_t stream);
+
+/*
+ * paged_attn_partition_size -- the partition length (tokens) that
+ * paged_attn_decode uses for these arguments: partition_size itself when it
+ * is non-zero, else a choice made from the other arguments only.  Returns a
+ * positive multiple of 32, or a negative pkv_status for invalid arguments.
+ */
+int32_t paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t max_seq_len,
+                                  int32_t partition_size);
+
+/*
+ * paged_attn_workspace_size -- bytes of device workspace paged_attn_decode
+ * needs for these arguments (0 when every sequence fits one partition), or
+ * (size_t)-1 for invalid arguments.
+ *
+ * Workspace contract: the first 256 KiB are merge counters that must be zero
+ * before the first call that uses the buffer (zero the whole buffer once
+ * after allocating it).  Every completed call leaves them zero again, so a
+ * buffer may be reused by later calls of any shape that fit its size.
+ */
+size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t partition_size);
+
+/*
+ * paged_attn_decode -- out[s, q, :] = softmax(scale * q . K_s^T) V_s over
+ * tokens 0 .. seq_lens[s]-1 of sequence s, gathered through its block table.
+ *
+ * query        [num_seqs, num_q_heads, head_dim] of q_dtype, contiguous.
+ * out          float32 [num_seqs, num_q_heads, head_dim].
+ * k_cache,
+ * v_cache      pools of cache_dtype; (q_dtype, cache_dtype) is one of
+ *              (F32,F32) (F16,F16) (BF16,BF16) or (F32|F16|BF16, FP8_E4M3).
+ * k_scale,
+ * v_scale      device float32 scalars, required for an fp8 cache.
+ * max_seq_len  host-side upper bound of seq_lens (sizes the launch; a
+ *              sequence longer than it is the caller's error).
+ * scale        softmax scale applied to q . k.
+ * partition_size  tokens per partition, a positive multiple of 32, or 0 to
+ *              let the library choose (see paged_attn_partition_size).
+ *              Sequences longer than one partition are split; partitions
+ *              are merged by log-sum-exp into the same result.
+ * workspace    device buffer of workspace_bytes >= paged_attn_workspace_size
+ *              (may be NULL when that is 0); see the workspace contract.
+ *
+ * A sequence of length 0 yields zeros.  num_q_heads must be a multiple of
+ * num_kv_heads; head_dim 64 or 128; max_blocks_per_seq * block_size >=
+ * max_seq_len.  Pointers 16-byte aligned (seq_lens, block_tables: 4-byte).
+ */
+int paged_attn_decode(float* out, const void* query, int q_dtype,
+                      const void* k_cache, const void* v_cache,
+                      int cache_dtype, const float* k_scale,
+                      const float* v_scale, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                      int32_t max_seq_len, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int64_t num_blocks,
+                      int32_t block_size, float scale,
+                      int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,136 @@
+// pkv_device.h -- element types, gfx950 MFMA steps and fp8 conversions shared
+// by the HIP kernels of libpagedkv.  Device-side only; no host API here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+// Storage element tags (the byte layout of one cache or query element).
+struct F32 { typedef float scalar; static constexpr int bytes = 4; };
+struct F16 { typedef _Float16 scalar; static constexpr int bytes = 2; };
+struct BF16 { typedef __bf16 scalar; static constexpr int bytes = 2; };
+struct FP8 { typedef uint8_t scalar; static constexpr int bytes = 1; };
+
+template <typename T> struct is_fp8 { static constexpr bool value = false; };
+template <> struct is_fp8<FP8> { static constexpr bool value = true; };
+
+template <typename A, typename B> struct same { static constexpr bool value = false; };
+template <typename A> struct same<A, A> { static constexpr bool value = true; };
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& f) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  return __builtin_bit_cast(To, f);
+}
+
+// ---------------------------------------------------------------------------
+// One "k32 step" of a 16x16 output tile: acc[m][n] += sum over (group, e) of
+// A_lane(m, group)[e] * B_lane(n, group)[e], where lane = row + 16 * group and
+// each lane supplies 8 operand elements.  For 16-bit types this is one
+// v_mfma_f32_16x16x32_{bf16,f16}; for float32 it is eight 16x16x4 steps, step
+// e taking element e of every lane.  Either way A and B pair the same
+// (group, element) slots, so callers only need to give matching slots to both
+// operands.  Accumulator layout: lane (n + 16 * (m / 4)) holds row m % 4 of
+// its 4-float vector.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+template <> struct Mma<BF16> {
+  typedef uint32_t operand[4];   // 8 bf16 packed two per register
+  __device__ __forceinline__ static f32x4_t step(const operand& a,
+                                                 const operand& b, f32x4_t c) {
+    u32x4_t av = {a[0], a[1], a[2], a[3]};
+    u32x4_t bv = {b[0], b[1], b[2], b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av),
+                                                   bitcast<bf16x8_t>(bv), c,
+                                                   0, 0, 0);
+  }
+};
+
+template <> struct Mma<F16> {
+  typedef uint32_t operand[4];
+  __device__ __forceinline__ static f32x4_t step(const operand& a,
+                                                 const operand& b, f32x4_t c) {
+    u32x4_t av = {a[0], a[1], a[2], a[3]};
+    u32x4_t bv = {b[0], b[1], b[2], b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(av),
+                                                  bitcast<f16x8_t>(bv), c,
+                                                  0, 0, 0);
+  }
+};
+
+template <> struct Mma<F32> {
+  typedef float operand[8];
+  __device__ __forceinline__ static f32x4_t step(const operand& a,
+                                                 const operand& b, f32x4_t c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Conversions.  fp8 -> wider types use gfx950's scaled converts with scale 1,
+// which decode OCP E4M3 exactly (every E4M3 value is representable in f16,
+// bf16 and f32).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t word, bool hi) {
+  f16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true)
+                 : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
+  return bitcast<uint32_t>(v);
+}
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word, bool hi) {
+  bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true)
+                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+  return bitcast<uint32_t>(v);
+}
+__device__ __forceinline__ f32x2_t fp8x2_to_f32x2(uint32_t word, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);
+}
+
+// float -> 16-bit storage, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bits(float x, BF16) {
+  return bitcast<uint16_t>(static_cast<__bf16>(x));
+}
+__device__ __forceinline__ uint16_t f32_to_bits(float x, F16) {
+  return bitcast<uint16_t>(static_cast<_Float16>(x));
+}
+__device__ __forceinline__ float bits_to_f32(uint16_t b, BF16) {
+  return bitcast<float>(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float bits_to_f32(uint16_t b, F16) {
+  return static_cast<float>(bitcast<_Float16>(b));
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide helpers (wave64).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float xor_sum(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = xor_max(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+}  // namespace pkv

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Cache writes and block copies must match bit for bit over
+the whole pool; attention must be within max-abs error 1e-5 (fp32 inputs),
+2e-3 (fp16/bf16) and 2e-2 (fp8 cache) of the float64 oracle.
+
+Cases run from small to large; each prints its name before touching the GPU.
+"""
+
+from dataclasses import replace
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_336_amd import workloads as W
+from paged_kv_cache_336_amd.step import DeviceStep
+
+from parity_helpers import (TOL, assert_pools_bitwise, check_attention,
+                            oracle_out, oracle_pools, say, max_abs_err)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from paged_kv_cache_336_amd import ops
+    ops.load_library()
+
+
+def run_full(w, rows=None, partition_size=None):
+    say(f"{w.name}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"D={w.head_dim} bs={w.block_size} kv={w.kv_kind} "
+        f"maxL={w.max_seq_len} P={w.partition_size}")
+    dev = DeviceStep(w, replicas=False)
+    pools = oracle_pools(w)
+    dev.copy()
+    dev.write()
+    assert_pools_bitwise(dev, pools)
+    err, out = check_attention(dev, w, pools, rows=rows,
+                               partition_size=partition_size)
+    say(f"{w.name}: max abs err {err:.3g}")
+    return dev, pools, out
+
+
+# ---------------------------------------------------------------------------
+# cache write and copy on their own
+# ---------------------------------------------------------------------------
+
+def test_page_one_write_example():
+    import torch
+    say("page-1 write example: 64 blocks, bs 32, 8 heads, D 128, fp16")
+    rng = np.random.default_rng(11)
+    kp = rng.standard_normal((64, 32, 8, 128)).astype(np.float16)
+    vp = rng.standard_normal((64, 32, 8, 128)).astype(np.float16)
+    key = rng.standard_normal((4, 8, 128)).astype(np.float16)
+    val = rng.standard_normal((4, 8, 128)).astype(np.float16)
+    slots = np.arange(4, dtype=np.int32)
+    from paged_kv_cache_336_amd import ops
+    kc, vc = torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda()
+    ops.cache_write_slots(torch.from_numpy(key).cuda(),
+                          torch.from_numpy(val).cuda(), kc, vc,
+                          torch.from_numpy(slots).cuda())
+    ek, ev = oracle.cache_write(kp, vp, "f16", key, val, "f16", slots, 32)
+    assert kc.cpu().numpy().tobytes() == ek.tobytes()
+    assert vc.cpu().numpy().tobytes() == ev.tobytes()
+
+
+@pytest.mark.parametrize("kind,src", [("f32", "f32"), ("bf16", "bf16"),
+                                      ("f16", "f16"), ("fp8_e4m3", "bf16"),
+                                      ("fp8_e4m3", "f16"),
+                                      ("fp8_e4m3", "f32")])
+def test_cache_write_and_copy_bitwise(kind, src):
+    import torch
+    from paged_kv_cache_336_amd import ops
+    from paged_kv_cache_336_amd.step import _to_torch, to_host_storage
+    say(f"write+copy {src}->{kind}")
+    w = W.custom_decode(seed=40 + len(kind) + len(src), num_seqs=5,
+                        lens=[1, 17, 40, 100, 3], hq=8, hkv=4, d=64, bs=8,
+                        q_kind=src if kind == "fp8_e4m3" else kind,
+                        kv_kind=kind, src_kind=src, num_new_per_seq=3)
+    # negative slots are skipped; scales are non-powers-of-two
+    slots = w.slot_mapping.copy()
+    slots[1] = -1
+    w = replace(w, slot_mapping=slots, k_scale=0.0173, v_scale=0.0291)
+    kc = _to_torch(w.k_pool, kind, "cuda")
+    vc = _to_torch(w.v_pool, kind, "cuda")
+    ks = torch.tensor([w.k_scale], dtype=torch.float32, device="cuda")
+    vs = torch.tensor([w.v_scale], dtype=torch.float32, device="cuda")
+    ck = "fp8_e4m3" if kind == "fp8_e4m3" else None
+    ops.cache_write_slots(_to_torch(w.key, src, "cuda"),
+                          _to_torch(w.value, src, "cuda"), kc, vc,
+                          torch.from_numpy(slots).cuda(), k_scale=ks,
+                          v_scale=vs, cache_kind=ck)
+    ek, ev = oracle.cache_write(w.k_pool, w.v_pool, kind, w.key, w.value, src,
+                                slots, w.block_size, w.k_scale, w.v_scale)
+    torch.cuda.synchronize()
+    assert to_host_storage(kc, kind).tobytes() == ek.tobytes()
+    assert to_host_storage(vc, kind).tobytes() == ev.tobytes()
+    # copy: the first block of each sequence into free blocks
+    used = set(int(b) for s, L in enumerate(w.seq_lens)
+               for b in w.block_tables[s, :W.blocks_for(L, 8)])
+    free = [b for b in range(w.num_blocks) if b not in used]
+    pairs = np.array([[w.block_tables[s, 0], free[s]] for s in range(2)],
+                     dtype=np.int32)
+    ops.copy_blocks(kc, vc, torch.from_numpy(pairs).cuda(), cache_kind=ck)
+    ek, ev = oracle.copy_blocks(ek, ev, pairs)
+    # an empty pair list is a no-op
+    ops.copy_blocks(kc, vc, torch.zeros((0, 2), dtype=torch.int32,
+                                        device="cuda"), cache_kind=ck)
+    torch.cuda.synchronize()
+    assert to_host_storage(kc, kind).tobytes() == ek.tobytes()
+    assert to_host_storage(vc, kind).tobytes() == ev.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# attention on small cases
+# ---------------------------------------------------------------------------
+
+def test_worked_example():
+    run_full(W.worked_example())
+
+
+SMALL = [
+    # (q, kv, D, bs, hq, hkv, lens, P)
+    ("f32", "f32", 64, 4, 1, 1, [22], 32),
+    ("f32", "f32", 128, 16, 4, 2, [1, 31, 32, 33, 200], 64),
+    ("f32", "f32", 64, 3, 8, 8, [5, 97], 32),
+    ("bf16", "bf16", 128, 16, 32, 8, [1, 2, 15, 16, 17, 300, 1000], 0),
+    ("bf16", "bf16", 128, 1, 4, 4, [1, 40, 70], 32),
+    ("bf16", "bf16", 64, 48, 12, 2, [47, 48, 49, 500], 96),
+    ("bf16", "bf16", 128, 544, 8, 1, [543, 544, 545, 2000], 512),
+    ("f16", "f16", 128, 16, 64, 8, [1, 100, 1023, 1025], 0),
+    ("f16", "f16", 64, 5, 20, 2, [9, 64, 130], 32),
+    ("f16", "f16", 128, 32, 48, 1, [33, 700], 128),
+    ("bf16", "fp8_e4m3", 128, 64, 32, 8, [1, 63, 64, 65, 1500], 512),
+    ("bf16", "fp8_e4m3", 64, 4, 4, 2, [3, 90], 32),
+    ("f16", "fp8_e4m3", 128, 16, 8, 8, [17, 600], 64),
+    ("f32", "fp8_e4m3", 64, 16, 2, 1, [1, 33, 300], 64),
+    ("bf16", "bf16", 128, 16, 8, 8, [0, 5, 0, 40], 32),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[
+    f"{c[0]}-{c[1]}-D{c[2]}-bs{c[3]}-G{c[4] // c[5]}-P{c[7]}" for c in SMALL])
+def test_small_cases(case):
+    q, kv, d, bs, hq, hkv, lens, P = case
+    w = W.custom_decode(seed=zlib.crc32(str(case).encode()) % 10000,
+                        num_seqs=len(lens),
+                        lens=lens, hq=hq, hkv=hkv, d=d, bs=bs, q_kind=q,
+                        kv_kind=kv, partition_size=P)
+    if kv == "fp8_e4m3":
+        w = replace(w, k_scale=0.0123, v_scale=0.0217)
+    run_full(w)
+
+
+def test_single_token_returns_its_value_exactly():
+    import torch
+    w = W.custom_decode(seed=77, num_seqs=6, lens=[1] * 6, hq=16, hkv=4,
+                        d=128, bs=16, q_kind="bf16", kv_kind="bf16")
+    dev, pools, out = run_full(w)
+    kp, vp = pools
+    for s in range(6):
+        b = int(w.block_tables[s, 0])
+        for hq in range(16):
+            v = oracle.to_float64(vp[b, 0, hq // 4], "bf16")
+            assert np.array_equal(out[s, hq].astype(np.float64), v)
+
+
+def test_fp8_value_decode_all_codes():
+    """L = 1 makes the output the stored value times v_scale: with the
+    value rows holding every finite E4M3 code the kernel's decode is checked
+    code by code (float32 product, rounded once)."""
+    import torch
+    say("fp8 decode of all codes through attention")
+    w = W.custom_decode(seed=5, num_seqs=2, lens=[1, 1], hq=1, hkv=1, d=128,
+                        bs=16, q_kind="bf16", kv_kind="fp8_e4m3")
+    w = replace(w, k_scale=0.5, v_scale=0.0371)
+    dev = DeviceStep(w, replicas=False)
+    dev.copy()
+    dev.write()
+    codes = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    codes[codes & 0x7F == 0x7F] = 0
+    for s in range(2):
+        b, o = divmod(int(w.slot_mapping[s]), 16)
+        dev.v_cache[b, o, 0] = torch.from_numpy(codes[s]).cuda()
+    dev.attend()
+    torch.cuda.synchronize()
+    got = dev.out.cpu().numpy()[:, 0, :]
+    exp = (oracle.e4m3_decode(codes) * float(np.float32(w.v_scale))).astype(
+        np.float32)
+    assert np.array_equal(got, exp)
+
+
+def test_block_relabelling_is_bitwise_invariant():
+    import torch
+    w = W.custom_decode(seed=31, num_seqs=4, lens=[5, 77, 300, 1200], hq=32,
+                        hkv=8, d=128, bs=16, q_kind="bf16", kv_kind="bf16",
+                        partition_size=128)
+    dev, _, out1 = run_full(w)
+    perm = np.random.default_rng(3).permutation(w.num_blocks)
+    w2 = W.permute_physical(w, perm)
+    dev2, _, out2 = run_full(w2)
+    assert out1.tobytes() == out2.tobytes()
+
+
+def test_partition_sizes_agree():
+    import torch
+    w = W.custom_decode(seed=12, num_seqs=3, lens=[100, 1000, 3000], hq=32,
+                        hkv=8, d=128, bs=16, q_kind="bf16", kv_kind="bf16")
+    dev, pools, _ = run_full(w)
+    outs = []
+    for P in (32, 96, 512, 3008):
+        err, out = check_attention(dev, w, pools, partition_size=P)
+        say(f"partition {P}: err {err:.3g}")
+        outs.append(out.astype(np.float64))
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 1e-5
+
+
+def test_workspace_reuse_across_shapes():
+    import torch
+    from paged_kv_cache_336_amd import ops
+    ws = ops.Workspace("cuda")
+    for seed, lens, P in ((1, [900, 3000], 64), (2, [100] * 12, 32),
+                          (3, [4000, 10, 2500], 96)):
+        w = W.custom_decode(seed=seed, num_seqs=len(lens), lens=lens, hq=16,
+                            hkv=4, d=128, bs=16, q_kind="f16", kv_kind="f16",
+                            partition_size=P)
+        say(f"workspace reuse: lens {lens} P {P}")
+        dev = DeviceStep(w, replicas=False)
+        dev.workspace = ws
+        pools = oracle_pools(w)
+        dev.copy()
+        dev.write()
+        check_attention(dev, w, pools)
+        torch.cuda.synchronize()
+        assert int(ws.buf[:256 * 1024].view(torch.int32).abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# the headline workload shapes at full size
+# ---------------------------------------------------------------------------
+
+def test_llama8b_decode_full():
+    w = W.llama8b_decode()
+    dev, pools, _ = run_full(w)
+    # the same result through a single partition per sequence
+    check_attention(dev, w, pools, partition_size=4096)
+
+
+def test_llama70b_decode_full():
+    run_full(W.llama70b_decode())
+
+
+@pytest.mark.parametrize("phase", ["fork", "divergent"])
+@pytest.mark.parametrize("bs", [32, 544])
+def test_prefix_sharing_full(phase, bs):
+    w, prompt_tables = W.prefix_sharing(block_size=bs, phase=phase)
+    dev, pools, _ = run_full(w)
+    # full shared prompt blocks are untouched by the step
+    kp, vp = dev.pools_host()
+    full = 2048 // bs
+    for ptab in prompt_tables:
+        for b in ptab[:full]:
+            assert kp[b].tobytes() == w.k_pool[b].tobytes()
+            assert vp[b].tobytes() == w.v_pool[b].tobytes()
+
+
+def test_long_context_fp8_full():
+    w = W.long_context_fp8()
+    rows = [(0, 0), (1, 5), (3, 13), (4, 31), (6, 16), (7, 2)]
+    run_full(w, rows=rows)
