@@ -124,7 +124,8 @@ int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
  * paged_attn_partition_size -- the partition length (tokens) that
  * paged_attn_decode uses for these arguments: partition_size itself when it
  * is non-zero, else a choice made from the other arguments only.  Returns a
- * positive multiple of 32, or a negative pkv_status for invalid arguments.
+ * positive multiple of 32 (at most 4096), or a negative pkv_status for
+ * invalid arguments (including a partition_size above 4096).
  */
 int32_t paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t max_seq_len,
@@ -135,10 +136,10 @@ int32_t paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
  * needs for these arguments (0 when every sequence fits one partition), or
  * (size_t)-1 for invalid arguments.
  *
- * Workspace contract: the first 256 KiB are merge counters that must be zero
- * before the first call that uses the buffer (zero the whole buffer once
- * after allocating it).  Every completed call leaves them zero again, so a
- * buffer may be reused by later calls of any shape that fit its size.
+ * The workspace holds the per-partition partial results (running max, running
+ * sum and unnormalised output of every query head) between the partition pass
+ * and the merge pass of one call; it needs no initialisation and may be
+ * reused by later calls of any shape that fit its size.
  */
 size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
@@ -158,12 +159,13 @@ size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * max_seq_len  host-side upper bound of seq_lens (sizes the launch; a
  *              sequence longer than it is the caller's error).
  * scale        softmax scale applied to q . k.
- * partition_size  tokens per partition, a positive multiple of 32, or 0 to
- *              let the library choose (see paged_attn_partition_size).
+ * partition_size  tokens per partition, a positive multiple of 32 no larger
+ *              than 4096, or 0 to let the library choose (see
+ *              paged_attn_partition_size).
  *              Sequences longer than one partition are split; partitions
  *              are merged by log-sum-exp into the same result.
  * workspace    device buffer of workspace_bytes >= paged_attn_workspace_size
- *              (may be NULL when that is 0); see the workspace contract.
+ *              (may be NULL when that is 0); see paged_attn_workspace_size.
  *
  * A sequence of length 0 yields zeros.  num_q_heads must be a multiple of
  * num_kv_heads; head_dim 64 or 128; max_blocks_per_seq * block_size >=

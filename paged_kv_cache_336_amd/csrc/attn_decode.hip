@@ -9,10 +9,19 @@
 // running maximum / running sum ("online softmax") per query head.
 //
 // Work unit: (sequence s, kv head h, chunk of <= 16 query heads of the group
-// reading h, partition p of the sequence).  One 64-lane wave per unit, so each
-// K/V row of a kv head is read once for all query heads that share it.
+// reading h, partition p of the sequence), one 256-thread workgroup (4 waves)
+// per unit, so each K/V row of a kv head is read once for all query heads
+// that share it.  The partition's 32-token tiles are dealt round-robin to the
+// 4 waves; each wave keeps its own online-softmax state and the waves combine
+// theirs through LDS at the end.
 //
-// Per 32-token tile:
+// Per 32-token tile (one wave):
+//   * Block-table entries are read with wave-uniform (scalar) loads, one per
+//     16-token half-tile when bs % 16 == 0.  The half-tile's base address then
+//     lives in SGPRs as a buffer resource whose size covers exactly the live
+//     rows, so rows past the end of the sequence are neither fetched nor need
+//     a branch, and the next tile's rows are requested before the current one
+//     is computed.
 //   * K rows go straight from HBM into MFMA A-operand registers as 16-byte
 //     loads (lane = token row + 16 * piece group), Q sits in the B operand;
 //     S = K . Q^T on v_mfma_f32_16x16x32 (bf16/f16; fp8 keys are decoded to
@@ -20,25 +29,31 @@
 //   * Scores are scaled into the log2 domain; the running max uses xor
 //     shuffles across the 4 lanes that hold one query head's column.
 //   * V rows are loaded as 16-byte pieces, converted to the PV operand type
-//     and staged in LDS (XOR-swizzled 16-byte chunks), then read back
-//     transposed as the A operand of O^T += V^T . P^T, so P never leaves the
-//     registers the QK product left it in.  For bf16/f16 caches P is split
-//     into a high and a low part (two MFMAs), which keeps the weights exact
-//     to ~2^-16 relative.
+//     and staged in the wave's own LDS slice (XOR-swizzled 16-byte chunks),
+//     then read back transposed as the A operand of O^T += V^T . P^T, so P
+//     never leaves the registers the QK product left it in.  For bf16/f16
+//     caches P is split into a high and a low part (two MFMAs), which keeps
+//     the weights exact to ~2^-16 relative.
 //
 // Partitions: a sequence longer than one partition writes an unnormalised
-// partial (o, running max m, running sum l) per query head to the workspace;
-// the wave that completes the last partition of an (s, h, chunk) -- found with
-// a device-scope counter -- merges all of them:
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
-// then resets the counter to zero for the next call.  Reduction order depends
-// only on logical token positions, so relabelling physical blocks leaves the
-// output bit-identical.
+// partial (o, running max m, running sum l) per query head to the workspace,
+// and a second kernel, one workgroup per (sequence, query head), merges them:
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// The kernel boundary is what makes one partition's writes visible to the
+// merging workgroup; an in-kernel hand-off would need a device-scope fence in
+// every partition's workgroup, which on this part writes back a whole L2 and
+// costs far more than the second launch.  Reduction order depends only on
+// logical token positions, so relabelling physical blocks leaves the output
+// bit-identical.
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
+
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr uint32_t kRawBufferFlags = 0x00020000;  // dword3: 32-bit data format
 
 template <typename QT, typename CT> struct PvOperand { typedef CT type; };
 template <> struct PvOperand<BF16, FP8> { typedef F16 type; };
@@ -52,57 +67,418 @@ __device__ __forceinline__ int slot_token(int j, int e) {
   return e < 4 ? 4 * j + e : 12 + 4 * j + e;
 }
 
-template <int D>
-__device__ void merge_partials(const AttnArgs& a, int s, int h, int gc,
-                               int gcount, int nparts, float vscale) {
-  const int lane = threadIdx.x;
-  constexpr int DPL = D / 64;
-  for (int g = 0; g < gcount; ++g) {
-    const int hq = h * a.group + gc * 16 + g;
-    const int64_t base = ((int64_t)s * a.num_q_heads + hq) * a.max_parts;
-    float M = -INFINITY;
-    for (int q = lane; q < nparts; q += 64) M = fmaxf(M, a.part_m[base + q]);
-    M = wave_max(M);
-    float den = 0.f;
-    float acc[DPL];
+// Compile-time shape of one (query type, cache type, head_dim) instance.
+template <typename QT, typename CT, int D> struct Shape {
+  typedef typename PvOperand<QT, CT>::type PVT;
+  static constexpr bool PSPLIT = !is_fp8<CT>::value && CT::bytes == 2;
+  static constexpr int EP = 16 / CT::bytes;           // elements per piece
+  static constexpr int KPIECES = D * CT::bytes / 64;  // K pieces/lane/half
+  static constexpr int KWORDS = KPIECES * 4;
+  static constexpr int QSTEPS = D / 32;               // k32 steps over D
+  static constexpr int ROW_BYTES = D * CT::bytes;     // one token, one head
+  static constexpr int PPR = ROW_BYTES / 16;          // pieces per row
+  static constexpr int NV = PPR / 2;                  // V pieces/lane/tile
+  static constexpr int TOK_PER_V = 64 / PPR;
+  static constexpr int PVB = PVT::bytes;
+  static constexpr int LDS_ROW = D * PVB;
+  static constexpr int VCH = EP * PVB / 16;           // LDS chunks per piece
+  static constexpr int QWORDS = D / 4 * QT::bytes / 4;
+  static constexpr int NBLK = D / 16;                 // 16-wide output blocks
+  static constexpr int STAGE_BYTES = 32 * LDS_ROW;    // V tile, one wave
+  static constexpr int ORow = D + 4;                  // padded LDS row (floats)
+  static constexpr int COMBINE_BYTES = kWaves * 16 * ORow * 4;
+  static constexpr int SMEM_BYTES = kWaves * STAGE_BYTES > COMBINE_BYTES
+                                        ? kWaves * STAGE_BYTES
+                                        : COMBINE_BYTES;
+  static_assert(NV >= 1 && KPIECES >= 1, "head_dim too small");
+  static_assert(LDS_ROW / 16 >= 4 * PVB, "swizzle needs 4 distinct spans");
+  static_assert(16 % TOK_PER_V == 0, "a V load must not straddle halves");
+};
+
+// One tile's raw K and V bytes as loaded from the pool.
+template <typename QT, typename CT, int D> struct TileRegs {
+  typedef Shape<QT, CT, D> S;
+  uint32_t kw[2][S::KWORDS];
+  u32x4_t vraw[S::NV];
+};
+
+// Online-softmax state of one wave: running max (log2 domain) and this
+// lane's share of the running sum for query head column c, and O^T blocks.
+template <int NBLK> struct WaveState {
+  float m;
+  float l;
+  f32x4_t o[NBLK];
+};
+
+// ---------------------------------------------------------------------------
+// Tile loads, block_size % 16 == 0: one table entry per 16-token half, rows
+// addressed through a buffer resource spanning the half's live rows only
+// (rows past the sequence end read as zero and are never fetched).  tab is
+// the partition's window of the block table, staged in LDS, whose entry 0 is
+// logical block lb_first; reading it there keeps the table lookups off the
+// vector-memory counter, so waiting for one never drains the prefetch.
+// ---------------------------------------------------------------------------
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void load_tile_uniform(
+    TileRegs<QT, CT, D>& tr, const AttnArgs& a, const int32_t* tab,
+    int lb_first, const uint8_t* kbase, const uint8_t* vbase, int64_t stride,
+    int t0, int t_end, int lane) {
+  typedef Shape<QT, CT, D> S;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+  const int bs = a.block_size;
+  // Everything addressing the half-tile is wave-uniform; readfirstlane says
+  // so to the compiler, which keeps it in SGPRs (scalar table loads, buffer
+  // resources in SGPRs) instead of looping over lanes.
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  __amdgpu_buffer_rsrc_t kr[2], vr[2];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
-    for (int q = 0; q < nparts; ++q) {
-      const float w = fast_exp2(a.part_m[base + q] - M);
-      den = fmaf(w, a.part_l[base + q], den);
-      const float* src = a.part_o + (base + q) * D + lane * DPL;
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w, src[k], acc[k]);
+  for (int hh = 0; hh < 2; ++hh) {
+    const int tb = t0 + 16 * hh;
+    int nvalid = t_end - tb;
+    nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
+    int64_t row0 = 0;
+    if (nvalid > 0) {
+      const int lb = tb / bs;
+      const int phys = __builtin_amdgcn_readfirstlane(tab[lb - lb_first]);
+      row0 = (int64_t)phys * bs + (tb - lb * bs);
     }
-    float* dst = a.out + ((int64_t)s * a.num_q_heads + hq) * D + lane * DPL;
+    // (the clamp above may be selected as a vector min/max)
+    const int nrec = __builtin_amdgcn_readfirstlane(nvalid * (int)stride);
+    kr[hh] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kbase + row0 * stride), (short)0, nrec,
+        kRawBufferFlags);
+    vr[hh] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(vbase + row0 * stride), (short)0, nrec,
+        kRawBufferFlags);
+  }
+  const int kofs = c * (int)stride + j * 16;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) dst[k] = acc[k] / den * vscale;
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int r = 0; r < S::KPIECES; ++r) {
+      const u32x4_t v =
+          __builtin_amdgcn_raw_buffer_load_b128(kr[hh], kofs + r * 64, 0, 0);
+      tr.kw[hh][4 * r + 0] = v[0];
+      tr.kw[hh][4 * r + 1] = v[1];
+      tr.kw[hh][4 * r + 2] = v[2];
+      tr.kw[hh][4 * r + 3] = v[3];
+    }
+  }
+  const int vtok = lane / S::PPR;
+  const int vofs = vtok * (int)stride + (lane % S::PPR) * 16;
+#pragma unroll
+  for (int v = 0; v < S::NV; ++v) {
+    const int hh = (v * S::TOK_PER_V) >> 4;
+    const int tin = (v * S::TOK_PER_V) & 15;
+    // the whole offset goes in the per-lane operand: the range check covers it
+    tr.vraw[v] = __builtin_amdgcn_raw_buffer_load_b128(
+        vr[hh], vofs + tin * (int)stride, 0, 0);
+  }
+}
+
+// Tile loads for any block size: one table lookup per token (vector), masked
+// lanes skip the load and hold zeros.
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void load_tile_any(
+    TileRegs<QT, CT, D>& tr, const AttnArgs& a, const int32_t* trow,
+    const uint8_t* kbase, const uint8_t* vbase, int64_t stride, int t0,
+    int t_end, int lane) {
+  typedef Shape<QT, CT, D> S;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+  const int bs = a.block_size;
+  const int tok = t0 + (lane & 31);
+  int myslot = 0;
+  if (tok < t_end) {
+    const int lb = tok / bs;
+    myslot = trow[lb] * bs + (tok - lb * bs);
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int ks = __shfl(myslot, 16 * hh + c, 64);
+    const bool ok = t0 + 16 * hh + c < t_end;
+    const uint8_t* row = kbase + (int64_t)ks * stride;
+#pragma unroll
+    for (int r = 0; r < S::KPIECES; ++r) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4_t*>(row + (4 * r + j) * 16);
+      tr.kw[hh][4 * r + 0] = v[0];
+      tr.kw[hh][4 * r + 1] = v[1];
+      tr.kw[hh][4 * r + 2] = v[2];
+      tr.kw[hh][4 * r + 3] = v[3];
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < S::NV; ++v) {
+    const int tv = lane / S::PPR + v * S::TOK_PER_V;
+    const int vs = __shfl(myslot, tv, 64);
+    tr.vraw[v] = u32x4_t{0u, 0u, 0u, 0u};
+    if (t0 + tv < t_end)
+      tr.vraw[v] = *reinterpret_cast<const u32x4_t*>(
+          vbase + (int64_t)vs * stride + (lane % S::PPR) * 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One tile: S = K Q^T, online-softmax update, O^T += V^T P^T.
+// vt is this wave's LDS slice (32 rows of D PV-operand elements).
+// ---------------------------------------------------------------------------
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void compute_tile(
+    const TileRegs<QT, CT, D>& tr, const uint32_t* qw,
+    WaveState<Shape<QT, CT, D>::NBLK>& st, uint8_t* vt, int t0, int t_end,
+    float qk_mul, int lane) {
+  typedef Shape<QT, CT, D> S;
+  typedef typename S::PVT PVT;
+  constexpr int PVB = S::PVB;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+
+  // ---------------- S = K . Q^T ----------------
+  f32x4_t sacc[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    sacc[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < S::QSTEPS; ++q) {
+      typename Mma<QT>::operand ka, qb;
+      if constexpr (same<QT, CT>::value && QT::bytes == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          ka[w] = tr.kw[hh][4 * q + w];
+          qb[w] = qw[4 * q + w];
+        }
+      } else if constexpr (same<QT, CT>::value) {  // float32
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ka[e] = bitcast<float>(tr.kw[hh][8 * q + e]);
+          qb[e] = bitcast<float>(qw[8 * q + e]);
+        }
+      } else if constexpr (QT::bytes == 2) {  // fp8 keys -> bf16/f16
+        const uint32_t w0 = tr.kw[hh][2 * q], w1 = tr.kw[hh][2 * q + 1];
+        if constexpr (same<QT, BF16>::value) {
+          ka[0] = fp8x2_to_bf16x2(w0, false);
+          ka[1] = fp8x2_to_bf16x2(w0, true);
+          ka[2] = fp8x2_to_bf16x2(w1, false);
+          ka[3] = fp8x2_to_bf16x2(w1, true);
+        } else {
+          ka[0] = fp8x2_to_f16x2(w0, false);
+          ka[1] = fp8x2_to_f16x2(w0, true);
+          ka[2] = fp8x2_to_f16x2(w1, false);
+          ka[3] = fp8x2_to_f16x2(w1, true);
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qb[w] = qw[4 * q + w];
+      } else {  // fp8 keys -> f32
+        const uint32_t w0 = tr.kw[hh][2 * q], w1 = tr.kw[hh][2 * q + 1];
+        const f32x2_t p0 = fp8x2_to_f32x2(w0, false), p1 = fp8x2_to_f32x2(w0, true);
+        const f32x2_t p2 = fp8x2_to_f32x2(w1, false), p3 = fp8x2_to_f32x2(w1, true);
+        ka[0] = p0[0]; ka[1] = p0[1]; ka[2] = p1[0]; ka[3] = p1[1];
+        ka[4] = p2[0]; ka[5] = p2[1]; ka[6] = p3[0]; ka[7] = p3[1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[e] = bitcast<float>(qw[8 * q + e]);
+      }
+      sacc[hh] = Mma<QT>::step(ka, qb, sacc[hh]);
+    }
+  }
+
+  // ---------------- online softmax (log2 domain) ----------------
+  float sv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
+    sv[e] = (t0 + slot_token(j, e) < t_end) ? raw * qk_mul : -INFINITY;
+  }
+  float mx = sv[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+  mx = xor_max(mx, 16);
+  mx = xor_max(mx, 32);
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = fast_exp2(st.m - m_new);
+  float pv[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pv[e] = fast_exp2(sv[e] - m_new);
+    psum += pv[e];
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+#pragma unroll
+  for (int n = 0; n < S::NBLK; ++n) st.o[n] *= alpha;
+
+  // ---------------- V -> LDS (PV operand type, swizzled) ----------------
+#pragma unroll
+  for (int v = 0; v < S::NV; ++v) {
+    const int tv = lane / S::PPR + v * S::TOK_PER_V;
+    const int swz = ((tv >> 2) & 3) * PVB;
+    uint8_t* rowp = vt + tv * S::LDS_ROW;
+    const int ch0 = (lane % S::PPR) * S::VCH;
+    if constexpr (same<PVT, CT>::value) {
+      *reinterpret_cast<u32x4_t*>(rowp + ((ch0 ^ swz) << 4)) = tr.vraw[v];
+    } else if constexpr (PVB == 2) {  // fp8 -> f16, two chunks
+      u32x4_t lo, hi;
+      lo[0] = fp8x2_to_f16x2(tr.vraw[v][0], false);
+      lo[1] = fp8x2_to_f16x2(tr.vraw[v][0], true);
+      lo[2] = fp8x2_to_f16x2(tr.vraw[v][1], false);
+      lo[3] = fp8x2_to_f16x2(tr.vraw[v][1], true);
+      hi[0] = fp8x2_to_f16x2(tr.vraw[v][2], false);
+      hi[1] = fp8x2_to_f16x2(tr.vraw[v][2], true);
+      hi[2] = fp8x2_to_f16x2(tr.vraw[v][3], false);
+      hi[3] = fp8x2_to_f16x2(tr.vraw[v][3], true);
+      *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 0) ^ swz) << 4)) = lo;
+      *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 1) ^ swz) << 4)) = hi;
+    } else {  // fp8 -> f32, four chunks
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2_t p0 = fp8x2_to_f32x2(tr.vraw[v][w], false);
+        const f32x2_t p1 = fp8x2_to_f32x2(tr.vraw[v][w], true);
+        f32x4_t q = {p0[0], p0[1], p1[0], p1[1]};
+        *reinterpret_cast<f32x4_t*>(rowp + (((ch0 + w) ^ swz) << 4)) = q;
+      }
+    }
+  }
+  // The slice is private to this wave and one wave's LDS operations execute
+  // in issue order, so the transposed reads below see these stores with no
+  // barrier (the compiler keeps the may-alias store -> load order).
+
+  // ---------------- O^T += V^T . P^T ----------------
+  typename Mma<PVT>::operand pb_hi, pb_lo;
+  if constexpr (PVB == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t h0 = f32_to_bits(pv[2 * w], PVT{});
+      const uint32_t h1 = f32_to_bits(pv[2 * w + 1], PVT{});
+      pb_hi[w] = h0 | (h1 << 16);
+      if constexpr (S::PSPLIT) {
+        const uint32_t l0 = f32_to_bits(pv[2 * w] - bits_to_f32(h0, PVT{}), PVT{});
+        const uint32_t l1 = f32_to_bits(pv[2 * w + 1] - bits_to_f32(h1, PVT{}), PVT{});
+        pb_lo[w] = l0 | (l1 << 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb_hi[e] = pv[e];
+  }
+  const int swz_j = j * PVB;
+#pragma unroll
+  for (int n = 0; n < S::NBLK; ++n) {
+    const int byte = (16 * n + c) * PVB;
+    const int col = (((byte >> 4) ^ swz_j) << 4) + (byte & 15);
+    typename Mma<PVT>::operand va;
+    if constexpr (PVB == 2) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t e0 = *reinterpret_cast<const uint16_t*>(
+            vt + slot_token(j, 2 * w) * S::LDS_ROW + col);
+        const uint32_t e1 = *reinterpret_cast<const uint16_t*>(
+            vt + slot_token(j, 2 * w + 1) * S::LDS_ROW + col);
+        va[w] = e0 | (e1 << 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        va[e] = *reinterpret_cast<const float*>(vt + slot_token(j, e) * S::LDS_ROW + col);
+    }
+    st.o[n] = Mma<PVT>::step(va, pb_hi, st.o[n]);
+    if constexpr (S::PSPLIT) st.o[n] = Mma<PVT>::step(va, pb_lo, st.o[n]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the partitions of one (sequence, query head): one workgroup.
+// Threads take 4 output columns each and a strided subset of the partitions
+// (D/4 columns x kThreads/(D/4) subsets); subsets are summed through LDS.
+// ---------------------------------------------------------------------------
+template <int D, bool SCALED>
+__global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
+  constexpr int D4 = D / 4;
+  constexpr int NSUB = kThreads / D4;
+  __shared__ __attribute__((aligned(16))) float red[NSUB][D];
+  __shared__ float sm_red[2][kWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hq = blockIdx.x % a.num_q_heads;
+  const int s = blockIdx.x / a.num_q_heads;
+  const int L = a.seq_lens[s];
+  const int nparts = L > 0 ? (L + a.partition_size - 1) / a.partition_size : 1;
+  if (nparts <= 1) return;  // written directly by the partition kernel
+
+  const int64_t row = (int64_t)s * a.num_q_heads + hq;
+  const auto* pm = as_global(a.part_m + row * a.max_parts);
+  const auto* pl = as_global(a.part_l + row * a.max_parts);
+  const auto* po = as_global(a.part_o + row * a.max_parts * D);
+
+  // M = max_p m_p
+  float M = -INFINITY;
+  for (int q = tid; q < nparts; q += kThreads) M = fmaxf(M, pm[q]);
+  M = wave_max(M);
+  if (lane == 0) sm_red[0][wave] = M;
+  __syncthreads();
+  M = sm_red[0][0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_red[0][w]);
+
+  // den = sum_p 2^(m_p - M) l_p ; acc = sum_p 2^(m_p - M) o_p
+  float den = 0.f;
+  for (int q = tid; q < nparts; q += kThreads) den += fast_exp2(pm[q] - M) * pl[q];
+  den = wave_sum(den);
+  if (lane == 0) sm_red[1][wave] = den;
+
+  const int d4 = tid % D4;
+  const int sub = tid / D4;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  int q = sub;
+  for (; q + 3 * NSUB < nparts; q += 4 * NSUB) {
+    float w[4];
+    f32x4_t o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u] = pm[q + u * NSUB];
+      o[u] = *reinterpret_cast<const __attribute__((address_space(1))) f32x4_t*>(
+          po + (int64_t)(q + u * NSUB) * D + 4 * d4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += fast_exp2(w[u] - M) * o[u];
+  }
+  for (; q < nparts; q += NSUB)
+    acc += fast_exp2(pm[q] - M) *
+           *reinterpret_cast<const __attribute__((address_space(1))) f32x4_t*>(
+               po + (int64_t)q * D + 4 * d4);
+  *reinterpret_cast<f32x4_t*>(&red[sub][4 * d4]) = acc;
+  __syncthreads();
+
+  if (tid < D4) {
+    den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) den += sm_red[1][w];
+    f32x4_t o = *reinterpret_cast<const f32x4_t*>(&red[0][4 * tid]);
+#pragma unroll
+    for (int u = 1; u < NSUB; ++u)
+      o += *reinterpret_cast<const f32x4_t*>(&red[u][4 * tid]);
+    const float vscale = SCALED ? *a.v_scale : 1.f;
+    *reinterpret_cast<f32x4_t*>(a.out + row * D + 4 * tid) = o * (vscale / den);
   }
 }
 
 template <typename QT, typename CT, int D, bool UNIFORM>
-__global__ __launch_bounds__(64) void attn_decode_kernel(AttnArgs a) {
-  typedef typename PvOperand<QT, CT>::type PVT;
-  constexpr bool PSPLIT = !is_fp8<CT>::value && CT::bytes == 2;
-  constexpr int EP = 16 / CT::bytes;           // cache elements per 16-B piece
-  constexpr int KPIECES = D * CT::bytes / 64;  // K pieces per lane per half
-  constexpr int KWORDS = KPIECES * 4;
-  constexpr int QSTEPS = D / 32;               // k32 steps over head_dim
-  constexpr int ROW_BYTES = D * CT::bytes;     // one token's row of one head
-  constexpr int PPR = ROW_BYTES / 16;          // pieces per row
-  constexpr int NV = PPR / 2;                  // V pieces per lane per tile
-  constexpr int TOK_PER_V = 64 / PPR;
-  constexpr int PVB = PVT::bytes;
-  constexpr int LDS_ROW = D * PVB;
-  constexpr int VCH = EP * PVB / 16;           // LDS chunks per V piece
-  constexpr int QWORDS = D / 4 * QT::bytes / 4;
-  constexpr int NBLK = D / 16;                 // 16-wide output blocks
-  static_assert(NV >= 1 && KPIECES >= 1, "head_dim too small");
-  static_assert(LDS_ROW / 16 >= 4 * PVB, "swizzle needs 4 distinct spans");
+__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
+  typedef Shape<QT, CT, D> S;
+  constexpr int NBLK = S::NBLK;
+  constexpr bool PREFETCH = UNIFORM && CT::bytes <= 2;
 
-  __shared__ __attribute__((aligned(16))) uint8_t vt[32 * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM_BYTES];
+  __shared__ float sm_ml[kWaves][2][16];
+  __shared__ float sm_stat[32];
+  __shared__ int32_t sm_tab[UNIFORM ? kMaxTableWindow : 1];
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int c = lane & 15;
   const int j = lane >> 4;
 
@@ -120,6 +496,7 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(AttnArgs a) {
   if (part >= nparts) return;
   const int t_begin = part * P;
   const int t_end = min(t_begin + P, L);
+  const int ntiles = (t_end - t_begin + 31) / 32;
   const int gcount = min(16, a.group - gc * 16);
   const int hq = h * a.group + gc * 16 + c;
   const bool head_live = c < gcount;
@@ -132,14 +509,14 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(AttnArgs a) {
   const float qk_mul = a.qk_scale_log2 * kscale;
 
   // ---- query: B operand of S = K Q^T, in the same element order as K ----
-  uint32_t qw[QWORDS];
+  uint32_t qw[S::QWORDS];
   {
     const uint8_t* qrow = static_cast<const uint8_t*>(a.query) +
                           ((int64_t)s * a.num_q_heads + hq) * D * QT::bytes;
-    constexpr int QBYTES_PER_R = EP * QT::bytes;
+    constexpr int QBYTES_PER_R = S::EP * QT::bytes;
     constexpr int QLOADS = QBYTES_PER_R / 16;
 #pragma unroll
-    for (int r = 0; r < D / (4 * EP); ++r) {
+    for (int r = 0; r < D / (4 * S::EP); ++r) {
 #pragma unroll
       for (int k = 0; k < QLOADS; ++k) {
         u32x4_t v = {0u, 0u, 0u, 0u};
@@ -156,282 +533,124 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(AttnArgs a) {
   }
 
   const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int bs = a.block_size;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) +
-                         (int64_t)h * ROW_BYTES;
+                         (int64_t)h * S::ROW_BYTES;
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) +
-                         (int64_t)h * ROW_BYTES;
-  const int64_t slot_stride = (int64_t)a.num_kv_heads * ROW_BYTES;
+                         (int64_t)h * S::ROW_BYTES;
+  const int64_t stride = (int64_t)a.num_kv_heads * S::ROW_BYTES;
+  uint8_t* vt = smem + wave * S::STAGE_BYTES;
 
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4_t oacc[NBLK];
-#pragma unroll
-  for (int n = 0; n < NBLK; ++n) oacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int t0 = t_begin; t0 < t_end; t0 += 32) {
-    // ---------------- slots of the rows this lane loads ----------------
-    int kslot[2];
-    int vslot[NV];
-    if constexpr (UNIFORM) {
-      // block_size % 16 == 0: each 16-token half lies in one block, so one
-      // (wave-uniform, scalar) table lookup per half.
-      int phys[2], off[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int tb = t0 + 16 * hh;
-        phys[hh] = 0;
-        off[hh] = 0;
-        if (tb < t_end) {
-          const int lb = tb / bs;
-          phys[hh] = trow[lb];
-          off[hh] = tb - lb * bs;
-        }
-        kslot[hh] = phys[hh] * bs + off[hh] + c;
-      }
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int tv = lane / PPR + v * TOK_PER_V;
-        const int hh = (v * TOK_PER_V) >> 4;
-        vslot[v] = phys[hh] * bs + off[hh] + (tv & 15);
-      }
-    } else {
-      const int tok = t0 + (lane & 31);
-      int myslot = 0;
-      if (tok < t_end) {
-        const int lb = tok / bs;
-        myslot = trow[lb] * bs + (tok - lb * bs);
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) kslot[hh] = __shfl(myslot, 16 * hh + c, 64);
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-        vslot[v] = __shfl(myslot, lane / PPR + v * TOK_PER_V, 64);
-    }
-
-    // ---------------- loads (masked past the end) ----------------
-    uint32_t kw[2][KWORDS];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const bool ok = t0 + 16 * hh + c < t_end;
-      const uint8_t* row = kbase + (int64_t)kslot[hh] * slot_stride;
-#pragma unroll
-      for (int r = 0; r < KPIECES; ++r) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (ok) v = *reinterpret_cast<const u32x4_t*>(row + (4 * r + j) * 16);
-        kw[hh][4 * r + 0] = v[0];
-        kw[hh][4 * r + 1] = v[1];
-        kw[hh][4 * r + 2] = v[2];
-        kw[hh][4 * r + 3] = v[3];
-      }
-    }
-    u32x4_t vraw[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int tv = lane / PPR + v * TOK_PER_V;
-      vraw[v] = u32x4_t{0u, 0u, 0u, 0u};
-      if (t0 + tv < t_end)
-        vraw[v] = *reinterpret_cast<const u32x4_t*>(
-            vbase + (int64_t)vslot[v] * slot_stride + (lane % PPR) * 16);
-    }
-
-    // ---------------- S = K . Q^T ----------------
-    f32x4_t sacc[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      sacc[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < QSTEPS; ++st) {
-        typename Mma<QT>::operand ka, qb;
-        if constexpr (same<QT, CT>::value && QT::bytes == 2) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            ka[w] = kw[hh][4 * st + w];
-            qb[w] = qw[4 * st + w];
-          }
-        } else if constexpr (same<QT, CT>::value) {  // float32
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ka[e] = bitcast<float>(kw[hh][8 * st + e]);
-            qb[e] = bitcast<float>(qw[8 * st + e]);
-          }
-        } else if constexpr (QT::bytes == 2) {  // fp8 keys -> bf16/f16
-          const uint32_t w0 = kw[hh][2 * st], w1 = kw[hh][2 * st + 1];
-          if constexpr (same<QT, BF16>::value) {
-            ka[0] = fp8x2_to_bf16x2(w0, false);
-            ka[1] = fp8x2_to_bf16x2(w0, true);
-            ka[2] = fp8x2_to_bf16x2(w1, false);
-            ka[3] = fp8x2_to_bf16x2(w1, true);
-          } else {
-            ka[0] = fp8x2_to_f16x2(w0, false);
-            ka[1] = fp8x2_to_f16x2(w0, true);
-            ka[2] = fp8x2_to_f16x2(w1, false);
-            ka[3] = fp8x2_to_f16x2(w1, true);
-          }
-#pragma unroll
-          for (int w = 0; w < 4; ++w) qb[w] = qw[4 * st + w];
-        } else {  // fp8 keys -> f32
-          const uint32_t w0 = kw[hh][2 * st], w1 = kw[hh][2 * st + 1];
-          const f32x2_t p0 = fp8x2_to_f32x2(w0, false), p1 = fp8x2_to_f32x2(w0, true);
-          const f32x2_t p2 = fp8x2_to_f32x2(w1, false), p3 = fp8x2_to_f32x2(w1, true);
-          ka[0] = p0[0]; ka[1] = p0[1]; ka[2] = p1[0]; ka[3] = p1[1];
-          ka[4] = p2[0]; ka[5] = p2[1]; ka[6] = p3[0]; ka[7] = p3[1];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qb[e] = bitcast<float>(qw[8 * st + e]);
-        }
-        sacc[hh] = Mma<QT>::step(ka, qb, sacc[hh]);
-      }
-    }
-
-    // ---------------- online softmax (log2 domain) ----------------
-    float sv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
-      sv[e] = (t0 + slot_token(j, e) < t_end) ? raw * qk_mul : -INFINITY;
-    }
-    float mx = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    float pv[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = fast_exp2(sv[e] - m_new);
-      psum += pv[e];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int n = 0; n < NBLK; ++n) oacc[n] *= alpha;
-
-    // ---------------- V -> LDS (PV operand type, swizzled) ----------------
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int tv = lane / PPR + v * TOK_PER_V;
-      const int swz = ((tv >> 2) & 3) * PVB;
-      uint8_t* rowp = vt + tv * LDS_ROW;
-      const int ch0 = (lane % PPR) * VCH;
-      if constexpr (same<PVT, CT>::value) {
-        *reinterpret_cast<u32x4_t*>(rowp + ((ch0 ^ swz) << 4)) = vraw[v];
-      } else if constexpr (PVB == 2) {  // fp8 -> f16, two chunks
-        u32x4_t lo, hi;
-        lo[0] = fp8x2_to_f16x2(vraw[v][0], false);
-        lo[1] = fp8x2_to_f16x2(vraw[v][0], true);
-        lo[2] = fp8x2_to_f16x2(vraw[v][1], false);
-        lo[3] = fp8x2_to_f16x2(vraw[v][1], true);
-        hi[0] = fp8x2_to_f16x2(vraw[v][2], false);
-        hi[1] = fp8x2_to_f16x2(vraw[v][2], true);
-        hi[2] = fp8x2_to_f16x2(vraw[v][3], false);
-        hi[3] = fp8x2_to_f16x2(vraw[v][3], true);
-        *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 0) ^ swz) << 4)) = lo;
-        *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 1) ^ swz) << 4)) = hi;
-      } else {  // fp8 -> f32, four chunks
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const f32x2_t p0 = fp8x2_to_f32x2(vraw[v][w], false);
-          const f32x2_t p1 = fp8x2_to_f32x2(vraw[v][w], true);
-          f32x4_t q = {p0[0], p0[1], p1[0], p1[1]};
-          *reinterpret_cast<f32x4_t*>(rowp + (((ch0 + w) ^ swz) << 4)) = q;
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---------------- O^T += V^T . P^T ----------------
-    typename Mma<PVT>::operand pb_hi, pb_lo;
-    if constexpr (PVB == 2) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t h0 = f32_to_bits(pv[2 * w], PVT{});
-        const uint32_t h1 = f32_to_bits(pv[2 * w + 1], PVT{});
-        pb_hi[w] = h0 | (h1 << 16);
-        if constexpr (PSPLIT) {
-          const uint32_t l0 = f32_to_bits(pv[2 * w] - bits_to_f32(h0, PVT{}), PVT{});
-          const uint32_t l1 = f32_to_bits(pv[2 * w + 1] - bits_to_f32(h1, PVT{}), PVT{});
-          pb_lo[w] = l0 | (l1 << 16);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb_hi[e] = pv[e];
-    }
-    const int swz_j = j * PVB;
-#pragma unroll
-    for (int n = 0; n < NBLK; ++n) {
-      const int byte = (16 * n + c) * PVB;
-      const int col = (((byte >> 4) ^ swz_j) << 4) + (byte & 15);
-      typename Mma<PVT>::operand va;
-      if constexpr (PVB == 2) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t e0 = *reinterpret_cast<const uint16_t*>(
-              vt + slot_token(j, 2 * w) * LDS_ROW + col);
-          const uint32_t e1 = *reinterpret_cast<const uint16_t*>(
-              vt + slot_token(j, 2 * w + 1) * LDS_ROW + col);
-          va[w] = e0 | (e1 << 16);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          va[e] = *reinterpret_cast<const float*>(vt + slot_token(j, e) * LDS_ROW + col);
-      }
-      oacc[n] = Mma<PVT>::step(va, pb_hi, oacc[n]);
-      if constexpr (PSPLIT) oacc[n] = Mma<PVT>::step(va, pb_lo, oacc[n]);
+  int lb_first = 0;
+  if constexpr (UNIFORM) {
+    // the partition's block-table entries, once per workgroup
+    if (t_end > t_begin) {
+      lb_first = t_begin / a.block_size;
+      const int count = (t_end - 1) / a.block_size - lb_first + 1;
+      for (int i = tid; i < count; i += kThreads)
+        sm_tab[i] = trow[lb_first + i];
     }
     __syncthreads();
   }
 
-  // ---------------- epilogue ----------------
-  float l_tot = xor_sum(l_run, 16);
-  l_tot = xor_sum(l_tot, 32);
-
-  if (nparts == 1) {
-    if (head_live) {
-      const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;
-      float* dst = a.out + ((int64_t)s * a.num_q_heads + hq) * D + 4 * j;
+  WaveState<NBLK> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
-      for (int n = 0; n < NBLK; ++n) {
-        f32x4_t o = oacc[n];
-        if (l_tot > 0.f) {
-          o[0] = o[0] / l_tot * vscale;
-          o[1] = o[1] / l_tot * vscale;
-          o[2] = o[2] / l_tot * vscale;
-          o[3] = o[3] / l_tot * vscale;
-        } else {
-          o = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        (void)inv;
-        *reinterpret_cast<f32x4_t*>(dst + 16 * n) = o;
-      }
+  for (int n = 0; n < NBLK; ++n) st.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (PREFETCH) {
+    // Loads of tile k + kWaves are in flight while tile k is computed; past
+    // the last tile the buffer ranges are empty, so those loads fetch
+    // nothing and the loop needs no branch around them.
+    TileRegs<QT, CT, D> cur, nxt;
+    load_tile_uniform<QT, CT, D>(cur, a, sm_tab, lb_first, kbase, vbase,
+                                 stride, t_begin + 32 * wave, t_end, lane);
+    for (int k = wave; k < ntiles; k += kWaves) {
+      load_tile_uniform<QT, CT, D>(nxt, a, sm_tab, lb_first, kbase, vbase,
+                                   stride, t_begin + 32 * (k + kWaves), t_end,
+                                   lane);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of compute
+      compute_tile<QT, CT, D>(cur, qw, st, vt, t_begin + 32 * k, t_end,
+                              qk_mul, lane);
+      cur = nxt;
+    }
+  } else {
+    for (int k = wave; k < ntiles; k += kWaves) {
+      TileRegs<QT, CT, D> cur;
+      if constexpr (UNIFORM)
+        load_tile_uniform<QT, CT, D>(cur, a, sm_tab, lb_first, kbase, vbase,
+                                     stride, t_begin + 32 * k, t_end, lane);
+      else
+        load_tile_any<QT, CT, D>(cur, a, trow, kbase, vbase, stride,
+                                 t_begin + 32 * k, t_end, lane);
+      compute_tile<QT, CT, D>(cur, qw, st, vt, t_begin + 32 * k, t_end,
+                              qk_mul, lane);
+    }
+  }
+
+  // ---------------- combine the waves' states ----------------
+  float l_w = xor_sum(st.l, 16);
+  l_w = xor_sum(l_w, 32);
+  if (j == 0) {
+    sm_ml[wave][0][c] = st.m;
+    sm_ml[wave][1][c] = l_w;
+  }
+  __syncthreads();  // also: every wave is done with its V slice
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][0][c]);
+  float Ltot = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      Ltot += fast_exp2(sm_ml[w][0][c] - M) * sm_ml[w][1][c];
+  }
+  const float f = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m - M);
+  float* so = reinterpret_cast<float*>(smem);
+  if (head_live) {
+    float* dst = so + (wave * 16 + c) * S::ORow + 4 * j;
+#pragma unroll
+    for (int n = 0; n < NBLK; ++n)
+      *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st.o[n] * f;
+  }
+  if (wave == 0 && j == 0) {  // per-head totals for the output pass
+    sm_stat[2 * c] = M;
+    sm_stat[2 * c + 1] = Ltot;
+  }
+  __syncthreads();
+
+  constexpr int D4 = D / 4;
+  const int items = gcount * D4;
+  const int64_t head0 = (int64_t)s * a.num_q_heads + h * a.group + gc * 16;
+  if (nparts == 1) {
+    for (int it = tid; it < items; it += kThreads) {
+      const int g = it / D4;
+      const int d4 = it - g * D4;
+      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        o += *reinterpret_cast<const f32x4_t*>(so + (w * 16 + g) * S::ORow + 4 * d4);
+      const float lt = sm_stat[2 * g + 1];
+      o = lt > 0.f ? o * (vscale / lt) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4_t*>(a.out + (head0 + g) * D + 4 * d4) = o;
     }
     return;
   }
 
-  const int64_t prow = ((int64_t)s * a.num_q_heads + hq) * a.max_parts + part;
-  if (head_live) {
-    float* dst = a.part_o + prow * D + 4 * j;
+  for (int it = tid; it < items; it += kThreads) {
+    const int g = it / D4;
+    const int d4 = it - g * D4;
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int n = 0; n < NBLK; ++n) *reinterpret_cast<f32x4_t*>(dst + 16 * n) = oacc[n];
-    if (j == 0) {
-      a.part_m[prow] = m_run;
-      a.part_l[prow] = l_tot;
+    for (int w = 0; w < kWaves; ++w)
+      o += *reinterpret_cast<const f32x4_t*>(so + (w * 16 + g) * S::ORow + 4 * d4);
+    const int64_t prow = (head0 + g) * a.max_parts + part;
+    *reinterpret_cast<f32x4_t*>(a.part_o + prow * D + 4 * d4) = o;
+    if (d4 == 0) {
+      a.part_m[prow] = sm_stat[2 * g];
+      a.part_l[prow] = sm_stat[2 * g + 1];
     }
   }
-  __threadfence();
-  uint32_t* counter =
-      a.counters + ((int64_t)s * a.num_kv_heads + h) * a.group_chunks + gc;
-  uint32_t prev = 0;
-  if (lane == 0) prev = atomicAdd(counter, 1u);
-  prev = __shfl(prev, 0, 64);
-  if (prev != (uint32_t)(nparts - 1)) return;
-  __threadfence();
-  merge_partials<D>(a, s, h, gc, gcount, nparts, vscale);
-  if (lane == 0) atomicExch(counter, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -442,10 +661,14 @@ static hipError_t launch_d(const AttnArgs& a, int grid, bool uniform,
                            hipStream_t stream) {
   if (uniform)
     hipLaunchKernelGGL((attn_decode_kernel<QT, CT, D, true>), dim3(grid),
-                       dim3(64), 0, stream, a);
+                       dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((attn_decode_kernel<QT, CT, D, false>), dim3(grid),
-                       dim3(64), 0, stream, a);
+                       dim3(kThreads), 0, stream, a);
+  if (a.max_parts > 1)
+    hipLaunchKernelGGL((attn_merge_kernel<D, is_fp8<CT>::value>),
+                       dim3(a.num_seqs * a.num_q_heads), dim3(kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

@@ -22,15 +22,17 @@ bool aligned(const void* p, uintptr_t n) {
   return (reinterpret_cast<uintptr_t>(p) % n) == 0;
 }
 
-// Partition choice when the caller passes 0: enough work units to keep a
-// few waves per SIMD busy on a 256-CU part even if every sequence were as
-// long as max_seq_len, in multiples of the 32-token tile, 64..1024 tokens.
+// Partition choice when the caller passes 0: about 4096 workgroups (16 per
+// CU of a 256-CU part) if every sequence were max_seq_len long, in multiples
+// of 128 tokens (one 32-token tile for each of a workgroup's 4 waves),
+// between 128 and 512 tokens so a partition stays a few microseconds of work
+// and the partials stay a few percent of the K/V bytes.
 int32_t auto_partition(int64_t units_per_token_range, int32_t max_seq_len) {
-  const int64_t target_slots = 16384;
-  int64_t p = (int64_t)max_seq_len * units_per_token_range / target_slots;
-  p = (p + 31) / 32 * 32;
-  if (p < 64) p = 64;
-  if (p > 1024) p = 1024;
+  const int64_t target_workgroups = 4096;
+  int64_t p = (int64_t)max_seq_len * units_per_token_range / target_workgroups;
+  p = (p + 127) / 128 * 128;
+  if (p < 128) p = 128;
+  if (p > 512) p = 512;
   return (int32_t)p;
 }
 
@@ -52,7 +54,9 @@ int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
     return PKV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
-  if (partition_size < 0 || partition_size % 32 != 0) return PKV_ERR_SHAPE;
+  if (partition_size < 0 || partition_size % 32 != 0 ||
+      partition_size > kMaxPartition)
+    return PKV_ERR_SHAPE;
   AttnShape s{};
   s.group = num_q_heads / num_kv_heads;
   s.group_chunks = (s.group + 15) / 16;
@@ -63,9 +67,8 @@ int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   if (s.max_parts < 1) s.max_parts = 1;
   if (units * s.max_parts > INT_MAX / 64) return PKV_ERR_SHAPE;
   if (s.max_parts > 1) {
-    if (units > kMaxCounters) return PKV_ERR_UNSUPPORTED;
     const size_t rows = (size_t)num_seqs * num_q_heads * s.max_parts;
-    s.off_m = kCounterRegionBytes;
+    s.off_m = 0;
     s.off_l = align_up(s.off_m + rows * 4, 256);
     s.off_o = align_up(s.off_l + rows * 4, 256);
     s.ws_bytes = s.off_o + rows * (size_t)head_dim * 4;
@@ -154,7 +157,7 @@ int32_t paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t partition_size) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 0 ||
       num_q_heads % num_kv_heads != 0 || partition_size < 0 ||
-      partition_size % 32 != 0)
+      partition_size % 32 != 0 || partition_size > kMaxPartition)
     return -PKV_ERR_SHAPE;
   if (partition_size) return partition_size;
   const int32_t g = num_q_heads / num_kv_heads;
@@ -215,10 +218,10 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.counters = s.ws_bytes ? reinterpret_cast<uint32_t*>(ws) : nullptr;
   a.part_m = s.ws_bytes ? reinterpret_cast<float*>(ws + s.off_m) : nullptr;
   a.part_l = s.ws_bytes ? reinterpret_cast<float*>(ws + s.off_l) : nullptr;
   a.part_o = s.ws_bytes ? reinterpret_cast<float*>(ws + s.off_o) : nullptr;
+  a.num_seqs = num_seqs;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;

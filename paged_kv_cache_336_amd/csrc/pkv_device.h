@@ -27,6 +27,15 @@ template <> struct is_fp8<FP8> { static constexpr bool value = true; };
 template <typename A, typename B> struct same { static constexpr bool value = false; };
 template <typename A> struct same<A, A> { static constexpr bool value = true; };
 
+// Pointers held in argument structs are generic (flat); reading through a
+// global address-space pointer tells the compiler they cannot alias LDS, so a
+// wave-uniform read of unmodified memory can become a scalar load.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T*
+as_global(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(const From& f) {
   static_assert(sizeof(To) == sizeof(From), "size mismatch");
@@ -122,6 +131,11 @@ __device__ __forceinline__ float xor_max(float v, int mask) {
 }
 __device__ __forceinline__ float xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = xor_sum(v, m);
+  return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

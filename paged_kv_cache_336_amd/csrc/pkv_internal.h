@@ -9,9 +9,11 @@
 
 namespace pkv {
 
-// Bytes at the head of the attention workspace reserved for merge counters.
-constexpr size_t kCounterRegionBytes = 256 * 1024;
-constexpr int64_t kMaxCounters = kCounterRegionBytes / 4;
+// Longest partition (tokens).  With block_size % 16 == 0 a partition of at
+// most this many tokens starting at a multiple of 32 touches at most
+// kMaxTableWindow blocks (bs 16: exactly P/16; bs >= 32: at most P/32 + 2).
+constexpr int kMaxPartition = 4096;
+constexpr int kMaxTableWindow = kMaxPartition / 16;
 
 struct AttnArgs {
   float* out;
@@ -25,7 +27,7 @@ struct AttnArgs {
   float* part_o;          // [S, Hq, max_parts, D]
   float* part_m;          // [S, Hq, max_parts]  running max (log2 domain)
   float* part_l;          // [S, Hq, max_parts]  running sum
-  uint32_t* counters;     // [S, Hkv, group_chunks]
+  int32_t num_seqs;
   int32_t max_blocks_per_seq;
   int32_t num_q_heads;
   int32_t num_kv_heads;

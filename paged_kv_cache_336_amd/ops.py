@@ -157,8 +157,8 @@ def paged_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
 
 
 class Workspace:
-    """A device workspace for paged_attn_decode that is zeroed once when it
-    is (re)allocated; the library keeps its counter region zero afterwards."""
+    """A device workspace for paged_attn_decode, grown (never shrunk) to the
+    largest size asked for; it needs no initialisation."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -169,7 +169,7 @@ class Workspace:
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(int(nbytes), dtype=torch.uint8,
+            self.buf = torch.empty(int(nbytes), dtype=torch.uint8,
                                    device=self.device)
         return self.buf
 

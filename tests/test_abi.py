@@ -134,16 +134,20 @@ def test_attention_validation(lib):
 def test_partition_choice_and_workspace_size(lib):
     # explicit sizes are taken as given
     assert ops.paged_attn_partition_size(8, 32, 8, 131072, 512) == 512
-    # automatic sizes are multiples of 32 within 64..1024
+    # automatic sizes are multiples of 128 within 128..512
     for args in [(32, 32, 8, 4096), (256, 64, 8, 8192), (1, 1, 1, 22),
                  (64, 32, 8, 2561)]:
         p = ops.paged_attn_partition_size(*args, 0)
-        assert p % 32 == 0 and 64 <= p <= 1024
-    # workspace = counter region + (m, l, o) rows for every partition slot
+        assert p % 128 == 0 and 128 <= p <= 512
+    # the largest explicit partition is 4096 tokens
+    assert ops.paged_attn_partition_size(8, 32, 8, 131072, 4096) == 4096
+    with pytest.raises(ops.PagedKVError):
+        ops.paged_attn_partition_size(8, 32, 8, 131072, 4096 + 32)
+    # workspace = (m, l, o) rows for every partition slot (+ alignment)
     S, hq, hkv, d, L, P = 8, 32, 8, 128, 131072, 512
     rows = S * hq * (L // P)
     ws = ops.paged_attn_workspace_size(S, hq, hkv, d, L, P)
-    assert ws >= 256 * 1024 + rows * (d + 2) * 4
-    assert ws <= 256 * 1024 + rows * (d + 2) * 4 + 1024
+    assert ws >= rows * (d + 2) * 4
+    assert ws <= rows * (d + 2) * 4 + 1024
     with pytest.raises(ops.PagedKVError):
         ops.paged_attn_workspace_size(S, 30, hkv, d, L, P)

