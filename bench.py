@@ -6,15 +6,20 @@ A step is one pass of the whole hot path over one batch: copy_blocks (the
 copy-on-write pairs of the batch; none for a plain decode batch), then
 cache_write_slots (one new token per sequence), then paged_attn_decode.
 Inputs are seeded synthetic tensors already resident in HBM; steps rotate
-over disjoint replicas of the block tables so the 256 MB Infinity Cache
-cannot serve one step's K/V to the next.
+over disjoint replicas of the block tables where the workload has them, so
+the 256 MB Infinity Cache cannot serve one step's K/V to the next.
 
-Prints one JSON line with the step throughput (KV-read GB/s over the whole
-step), tokens/s, the attention kernel's roofline fraction against 8 TB/s, and
-the CPU oracle's rate on a bounded sample of the same workload.
+Timing is GPU time: before each timed region the GPU is kept busy by a
+calibrated spin kernel while the host enqueues the region's work, so the
+region's events bracket back-to-back kernels and not host launch gaps.
+
+Prints one JSON line: KV-read GB/s of the whole step (value), tokens/s, the
+attention call's roofline fraction against 8 TB/s and the CPU oracle's rate
+on a bounded sample of the same workload.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,15 +27,19 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
 DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8"}
+METRIC = ("paged decode attention KV-read GB/s (% of HBM peak) + "
+          "decode tokens/s, 1 GPU")
 
 
 def algorithmic_bytes(w):
-    """Bytes the step must move, per kernel (see the design notes):
-    attention reads every live K and V row once, Q once, writes the fp32
-    output, and reads the table entries and lengths."""
+    """Bytes each call must move.  Attention reads every live K and V row
+    of every sequence once (logical bytes: a block shared by several
+    sequences counts once per sequence), the query, the block-table entries
+    and lengths, and writes the float32 output."""
     e = ELEM_BYTES[w.kv_kind]
     eq = ELEM_BYTES[w.q_kind]
     L = w.seq_lens.astype(np.int64)
@@ -45,23 +54,23 @@ def algorithmic_bytes(w):
     return {"attention": attn, "cache_write": write, "copy_blocks": copy}
 
 
-def build_workload(name, replicas, partition_size):
-    from paged_kv_cache_336_amd import workloads as W
-    kw = {}
-    if name == "llama8b_decode":
-        kw["replicas"] = replicas
-    if partition_size is not None:
-        kw["partition_size"] = partition_size
-    return W.workload_by_name(name, **kw)
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for name in ("attn_decode.hip", "pkv_device.h", "pkv_internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_336_amd", "csrc", name),
+                  "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(w, budget_s):
-    """The oracle, as it stands, on replica 0 of the same workload: repeat
-    whole steps (copy, write, attention) until the time budget is used."""
+    """The oracle, as it stands, on replica 0 of the same workload: whole
+    steps (copy, write, attention) repeated until the time budget is used."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()]
+                      or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     steps = 0
@@ -81,6 +90,43 @@ def cpu_baseline(w, budget_s):
     return steps, el, threads
 
 
+class GpuClock:
+    """Keeps the GPU busy with torch's spin kernel while the host enqueues a
+    timed region, so that region runs back to back on the GPU."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        n = 2_000_000
+        torch.cuda._sleep(n)          # warm
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(n)
+        b.record()
+        torch.cuda.synchronize()
+        self.cycles_per_ms = n / max(a.elapsed_time(b), 1e-3)
+
+    def hold(self, ms):
+        self.torch.cuda._sleep(int(self.cycles_per_ms * ms))
+
+
+def timed_region(torch, clock, enqueue, host_ms_estimate):
+    """GPU milliseconds of the work enqueue() issues, measured with events
+    recorded after a spin long enough to cover the host's enqueueing."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    clock.hold(2.0 * host_ms_estimate + 5.0)
+    start.record()
+    h0 = time.perf_counter()
+    enqueue()
+    host_ms = (time.perf_counter() - h0) * 1e3
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop), host_ms
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,13 +134,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_decode")
     ap.add_argument("--replicas", type=int, default=8)
-    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--max-waves", type=int, default=0,
+                    help="cap on the attention kernel's waves (0 = all)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(
-        os.path.dirname(os.path.abspath(__file__)), "profiles",
-        "traffic.json"))
+        ROOT, "profiles", "traffic.json"))
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -105,51 +151,62 @@ def main():
 
     import torch
     from paged_kv_cache_336_amd import ops
+    from paged_kv_cache_336_amd import workloads as W
     from paged_kv_cache_336_amd.step import DeviceStep
 
     ops.load_library()
-    w = build_workload(args.workload, args.replicas, args.partition_size)
+    kw = {"replicas": args.replicas} if args.workload == "llama8b_decode" \
+        else {}
+    w = W.workload_by_name(args.workload, **kw)
     dev = DeviceStep(w, device="cuda:0")
     R = len(dev.sets)
     nbytes = algorithmic_bytes(w)
-    stream = torch.cuda.current_stream()
+    K = args.steps
 
-    # warm-up (also grows the workspace once)
+    def step(i):
+        r = i % R
+        dev.copy(r)
+        dev.write(r)
+        dev.attend(r, max_waves=args.max_waves)
+
+    # warm-up; also estimates the host's enqueue time per step
     for i in range(args.warmup):
-        dev.run(i % R)
+        step(i)
     torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for i in range(max(args.warmup, 1)):
+        step(i)
+    host_step_ms = (time.perf_counter() - h0) * 1e3 / max(args.warmup, 1)
+    torch.cuda.synchronize()
+    clock = GpuClock(torch)
 
     # ---- timed region: K whole steps, rotating replicas ----
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        dev.run(i % R)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
+    def run_steps():
+        for i in range(K):
+            step(i)
+    step_ms_total, host_ms = timed_region(torch, clock, run_steps,
+                                          host_step_ms * K)
+    ms_step = step_ms_total / K
 
-    # ---- the attention kernel alone, one event pair per launch ----
+    # ---- the attention call alone, one event pair per call ----
     evs = [(torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        dev.attend(i % R)
-        b.record(stream)
-    torch.cuda.synchronize()
+            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+
+    def run_attn():
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            dev.attend(i % R, max_waves=args.max_waves)
+            b.record()
+    timed_region(torch, clock, run_attn, host_step_ms * K)
     attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
     attn_avg_ms = float(attn_ms.mean())
 
-    # ---- cache write alone (for the report) ----
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        dev.write(i % R)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    write_ms = start.elapsed_time(stop) / args.steps
+    # ---- the cache write alone (for the report) ----
+    def run_write():
+        for i in range(K):
+            dev.write(i % R)
+    write_total, _ = timed_region(torch, clock, run_write, host_step_ms * K)
+    write_ms = write_total / K
 
     B = nbytes["attention"]
     step_gbps = B / (ms_step * 1e-3) / 1e9
@@ -159,11 +216,10 @@ def main():
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
-            t = json.load(open(args.traffic_json))
-            rec = t.get(args.workload)
-            if rec and rec.get("kernel_source_sha") == _kernel_sha():
-                traffic = rec.get("bytes_per_launch")
-        except Exception:
+            rec = json.load(open(args.traffic_json)).get(args.workload)
+            if rec and rec.get("kernel_source_sha") == kernel_source_sha():
+                traffic = rec.get("bytes_per_call")
+        except (OSError, ValueError):
             traffic = None
 
     cpu = None
@@ -172,16 +228,16 @@ def main():
         cpu = {"value": round(B * steps / el / 1e9, 4), "unit": "GB/s",
                "cores": int(threads), "kind": "oracle",
                "sample": f"{steps} whole step(s) of {w.name} (replica 0, "
-                         f"{w.num_seqs} sequences) in {el:.1f} s",
+                         f"{w.num_seqs} sequences, the full batch) in "
+                         f"{el:.1f} s",
                "tokens_per_s": round(w.num_seqs * steps / el, 2)}
 
     line = {
-        "metric": "paged decode attention KV-read GB/s (% of HBM peak) + "
-                  "decode tokens/s, 1 GPU",
+        "metric": METRIC,
         "value": round(step_gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -200,16 +256,17 @@ def main():
             "q_dtype": w.q_kind,
             "sum_seq_len": int(w.seq_lens.sum()),
             "max_seq_len": w.max_seq_len,
-            "partition_size": dev.resolved_partition,
             "replicas": R,
+            "max_waves": args.max_waves,
         },
         "tokens_per_s": round(tokens_per_s, 1),
         "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
         "attention_us": round(attn_avg_ms * 1e3, 3),
         "cache_write_us": round(write_ms * 1e3, 3),
+        "host_enqueue_ms": round(host_ms, 3),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_decode_kernel",
+            "kernel": "paged_attn_decode (attn_decode_kernel + attn_merge_kernel)",
             "achieved": round(attn_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -220,13 +277,6 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
-
-
-def _kernel_sha():
-    import hashlib
-    p = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                     "paged_kv_cache_336_amd", "csrc", "attn_decode.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
 if __name__ == "__main__":

@@ -14,8 +14,9 @@
  *   paged_attn_decode  one decode query per sequence attends over its tokens
  *                      by walking its block table over the shared pool
  *                      ("PagedAttention", section "How attention reads paged
- *                      memory"), with an online softmax per partition of the
- *                      sequence and a log-sum-exp merge across partitions.
+ *                      memory"), with an online softmax over each wave's
+ *                      share of the sequence and a log-sum-exp merge of the
+ *                      shares of a sequence split between waves.
  *
  * Memory layout (all buffers are device memory owned by the caller):
  *   k_cache, v_cache   [num_blocks, block_size, num_kv_heads, head_dim],
@@ -121,29 +122,18 @@ int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
                 int32_t head_dim, hipStream_t stream);
 
 /*
- * paged_attn_partition_size -- the partition length (tokens) that
- * paged_attn_decode uses for these arguments: partition_size itself when it
- * is non-zero, else a choice made from the other arguments only.  Returns a
- * positive multiple of 32 (at most 4096), or a negative pkv_status for
- * invalid arguments (including a partition_size above 4096).
- */
-int32_t paged_attn_partition_size(int32_t num_seqs, int32_t num_q_heads,
-                                  int32_t num_kv_heads, int32_t max_seq_len,
-                                  int32_t partition_size);
-
-/*
  * paged_attn_workspace_size -- bytes of device workspace paged_attn_decode
- * needs for these arguments (0 when every sequence fits one partition), or
- * (size_t)-1 for invalid arguments.
+ * needs for these arguments, or (size_t)-1 for invalid arguments.
  *
- * The workspace holds the per-partition partial results (running max, running
- * sum and unnormalised output of every query head) between the partition pass
- * and the merge pass of one call; it needs no initialisation and may be
- * reused by later calls of any shape that fit its size.
+ * The workspace carries, from the first to the second kernel of one call, the
+ * per-sequence tile prefix and the partial results (running max, running sum
+ * and unnormalised output of every query head) of the rows whose tiles are
+ * split between waves.  It needs no initialisation and may be reused by later
+ * calls of any shape that fit its size (the size depends only on these
+ * arguments: about 2 * 4096 * min(16, Hq/Hkv) * (head_dim + 2) * 4 bytes).
  */
 size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t max_seq_len, int32_t partition_size);
+                                 int32_t num_kv_heads, int32_t head_dim);
 
 /*
  * paged_attn_decode -- out[s, q, :] = softmax(scale * q . K_s^T) V_s over
@@ -156,17 +146,20 @@ size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *              (F32,F32) (F16,F16) (BF16,BF16) or (F32|F16|BF16, FP8_E4M3).
  * k_scale,
  * v_scale      device float32 scalars, required for an fp8 cache.
- * max_seq_len  host-side upper bound of seq_lens (sizes the launch; a
- *              sequence longer than it is the caller's error).
+ * max_seq_len  host-side upper bound of seq_lens (a sequence longer than it
+ *              is the caller's error).
  * scale        softmax scale applied to q . k.
- * partition_size  tokens per partition, a positive multiple of 32 no larger
- *              than 4096, or 0 to let the library choose (see
- *              paged_attn_partition_size).
- *              Sequences longer than one partition are split; partitions
- *              are merged by log-sum-exp into the same result.
- * workspace    device buffer of workspace_bytes >= paged_attn_workspace_size
- *              (may be NULL when that is 0); see paged_attn_workspace_size.
+ * max_waves    0 to spread the work over every wave the GPU holds at once,
+ *              else at most this many (rounded down to a multiple of 4).
+ *              All 32-token tiles of all (sequence, kv head) rows are divided
+ *              into equal contiguous shares, one per wave; a row split
+ *              between waves is merged by log-sum-exp, giving the same result
+ *              up to float32 rounding for any split.
+ * workspace    device buffer of workspace_bytes >= paged_attn_workspace_size,
+ *              256-byte aligned.
  *
+ * Two kernels are launched on the stream (tiles, then the merge of split
+ * rows).  At most 8192 sequences per call (PKV_ERR_UNSUPPORTED beyond).
  * A sequence of length 0 yields zeros.  num_q_heads must be a multiple of
  * num_kv_heads; head_dim 64 or 128; max_blocks_per_seq * block_size >=
  * max_seq_len.  Pointers 16-byte aligned (seq_lens, block_tables: 4-byte).
@@ -179,9 +172,9 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
                       int32_t max_seq_len, int32_t num_seqs,
                       int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int64_t num_blocks,
-                      int32_t block_size, float scale,
-                      int32_t partition_size, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream);
+                      int32_t block_size, float scale, int32_t max_waves,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

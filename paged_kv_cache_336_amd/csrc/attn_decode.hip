@@ -8,20 +8,21 @@
 // kernel walks the table block by block and keeps a FlashAttention-style
 // running maximum / running sum ("online softmax") per query head.
 //
-// Work unit: (sequence s, kv head h, chunk of <= 16 query heads of the group
-// reading h, partition p of the sequence), one 256-thread workgroup (4 waves)
-// per unit, so each K/V row of a kv head is read once for all query heads
-// that share it.  The partition's 32-token tiles are dealt round-robin to the
-// 4 waves; each wave keeps its own online-softmax state and the waves combine
-// theirs through LDS at the end.
+// Work split: a row is (sequence s, kv head h, chunk of <= 16 query heads of
+// the group reading h); a row's tiles are 32 consecutive tokens.  All tiles
+// of all rows, in row-major order, are divided into equal contiguous ranges,
+// one per wave of a grid that fills the GPU once, so every wave streams the
+// same number of K/V bytes whatever the mix of sequence lengths.  Each K/V row
+// of a kv head is read once, by one wave, for all query heads that share it,
+// and waves never wait for one another while streaming.
 //
 // Per 32-token tile (one wave):
-//   * Block-table entries are read with wave-uniform (scalar) loads, one per
-//     16-token half-tile when bs % 16 == 0.  The half-tile's base address then
-//     lives in SGPRs as a buffer resource whose size covers exactly the live
-//     rows, so rows past the end of the sequence are neither fetched nor need
-//     a branch, and the next tile's rows are requested before the current one
-//     is computed.
+//   * When bs % 16 == 0 each wave holds the partition's block-table window in
+//     one VGPR and reads one entry per 16-token half-tile with a wave-uniform
+//     readlane.  The half-tile's base address then lives in SGPRs as a
+//     buffer resource whose size covers exactly the live rows, so rows past
+//     the end of the sequence are neither fetched nor need a branch, and the
+//     next tile's rows are requested before the current one is computed.
 //   * K rows go straight from HBM into MFMA A-operand registers as 16-byte
 //     loads (lane = token row + 16 * piece group), Q sits in the B operand;
 //     S = K . Q^T on v_mfma_f32_16x16x32 (bf16/f16; fp8 keys are decoded to
@@ -35,16 +36,16 @@
 //     caches P is split into a high and a low part (two MFMAs), which keeps
 //     the weights exact to ~2^-16 relative.
 //
-// Partitions: a sequence longer than one partition writes an unnormalised
-// partial (o, running max m, running sum l) per query head to the workspace,
-// and a second kernel, one workgroup per (sequence, query head), merges them:
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-// The kernel boundary is what makes one partition's writes visible to the
-// merging workgroup; an in-kernel hand-off would need a device-scope fence in
-// every partition's workgroup, which on this part writes back a whole L2 and
-// costs far more than the second launch.  Reduction order depends only on
-// logical token positions, so relabelling physical blocks leaves the output
-// bit-identical.
+// Splits: a row that one wave's range covers entirely is finished by that
+// wave.  A row cut by range boundaries gets a partial (o, running max m,
+// running sum l) per piece -- a wave holds at most two such pieces, its first
+// and its last row -- and a second kernel, one workgroup per cut row, merges
+// them:  M = max m_i,  out = sum 2^(m_i - M) o_i / sum 2^(m_i - M) l_i.
+// The kernel boundary is what makes the pieces visible to the merging
+// workgroup (an in-kernel hand-off would need a device-scope fence per wave,
+// which on this part writes back a whole L2).  Reduction order depends only
+// on logical token positions and the grid size, so relabelling physical
+// blocks leaves the output bit-identical.
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -85,11 +86,6 @@ template <typename QT, typename CT, int D> struct Shape {
   static constexpr int QWORDS = D / 4 * QT::bytes / 4;
   static constexpr int NBLK = D / 16;                 // 16-wide output blocks
   static constexpr int STAGE_BYTES = 32 * LDS_ROW;    // V tile, one wave
-  static constexpr int ORow = D + 4;                  // padded LDS row (floats)
-  static constexpr int COMBINE_BYTES = kWaves * 16 * ORow * 4;
-  static constexpr int SMEM_BYTES = kWaves * STAGE_BYTES > COMBINE_BYTES
-                                        ? kWaves * STAGE_BYTES
-                                        : COMBINE_BYTES;
   static_assert(NV >= 1 && KPIECES >= 1, "head_dim too small");
   static_assert(LDS_ROW / 16 >= 4 * PVB, "swizzle needs 4 distinct spans");
   static_assert(16 % TOK_PER_V == 0, "a V load must not straddle halves");
@@ -113,20 +109,19 @@ template <int NBLK> struct WaveState {
 // ---------------------------------------------------------------------------
 // Tile loads, block_size % 16 == 0: one table entry per 16-token half, rows
 // addressed through a buffer resource spanning the half's live rows only
-// (rows past the sequence end read as zero and are never fetched).  tab is
-// the partition's window of the block table, staged in LDS, whose entry 0 is
-// logical block lb_first; reading it there keeps the table lookups off the
-// vector-memory counter, so waiting for one never drains the prefetch.
+// (rows past the end read as zero and are never fetched, so an empty tile --
+// t0 >= t_end -- costs no memory traffic).  The wave's block-table window is
+// two VGPRs: lane i of tab_a / tab_b holds the entry of logical block
+// wb + i / wb + 64 + i, and a wave-uniform readlane turns it into a scalar.
 // ---------------------------------------------------------------------------
 template <typename QT, typename CT, int D>
 __device__ __forceinline__ void load_tile_uniform(
-    TileRegs<QT, CT, D>& tr, const AttnArgs& a, const int32_t* tab,
-    int lb_first, const uint8_t* kbase, const uint8_t* vbase, int64_t stride,
-    int t0, int t_end, int lane) {
+    TileRegs<QT, CT, D>& tr, int bs, uint32_t tab_a, uint32_t tab_b, int wb,
+    const uint8_t* kbase, const uint8_t* vbase, int64_t stride, int t0,
+    int t_end, int lane) {
   typedef Shape<QT, CT, D> S;
   const int c = lane & 15;
   const int j = lane >> 4;
-  const int bs = a.block_size;
   // Everything addressing the half-tile is wave-uniform; readfirstlane says
   // so to the compiler, which keeps it in SGPRs (scalar table loads, buffer
   // resources in SGPRs) instead of looping over lanes.
@@ -140,7 +135,12 @@ __device__ __forceinline__ void load_tile_uniform(
     int64_t row0 = 0;
     if (nvalid > 0) {
       const int lb = tb / bs;
-      const int phys = __builtin_amdgcn_readfirstlane(tab[lb - lb_first]);
+      const int idx = lb - wb;  // 0 .. 127
+      int phys;
+      if (idx < 64)  // (tab_b may still be in flight: touch it only if needed)
+        phys = __builtin_amdgcn_readlane(tab_a, idx);
+      else
+        phys = __builtin_amdgcn_readlane(tab_b, idx - 64);
       row0 = (int64_t)phys * bs + (tb - lb * bs);
     }
     // (the clamp above may be selected as a vector min/max)
@@ -181,13 +181,12 @@ __device__ __forceinline__ void load_tile_uniform(
 // lanes skip the load and hold zeros.
 template <typename QT, typename CT, int D>
 __device__ __forceinline__ void load_tile_any(
-    TileRegs<QT, CT, D>& tr, const AttnArgs& a, const int32_t* trow,
+    TileRegs<QT, CT, D>& tr, int bs, const int32_t* trow,
     const uint8_t* kbase, const uint8_t* vbase, int64_t stride, int t0,
     int t_end, int lane) {
   typedef Shape<QT, CT, D> S;
   const int c = lane & 15;
   const int j = lane >> 4;
-  const int bs = a.block_size;
   const int tok = t0 + (lane & 31);
   int myslot = 0;
   if (tok < t_end) {
@@ -221,12 +220,58 @@ __device__ __forceinline__ void load_tile_any(
 }
 
 // ---------------------------------------------------------------------------
-// One tile: S = K Q^T, online-softmax update, O^T += V^T P^T.
-// vt is this wave's LDS slice (32 rows of D PV-operand elements).
+// A tile's V rows -> the wave's LDS slice, converted to the PV operand type and
+// XOR-swizzled in 16-byte chunks so the transposed reads are conflict-free.
+// The slice is private to the wave and one wave's LDS operations execute in
+// issue order, so no barrier is needed around it.
+// ---------------------------------------------------------------------------
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void stage_v(const u32x4_t (&vraw)[Shape<QT, CT, D>::NV],
+                                        uint8_t* vt, int lane) {
+  typedef Shape<QT, CT, D> S;
+  typedef typename S::PVT PVT;
+  constexpr int PVB = S::PVB;
+#pragma unroll
+  for (int v = 0; v < S::NV; ++v) {
+    const int tv = lane / S::PPR + v * S::TOK_PER_V;
+    const int swz = ((tv >> 2) & 3) * PVB;
+    uint8_t* rowp = vt + tv * S::LDS_ROW;
+    const int ch0 = (lane % S::PPR) * S::VCH;
+    if constexpr (same<PVT, CT>::value) {
+      *reinterpret_cast<u32x4_t*>(rowp + ((ch0 ^ swz) << 4)) = vraw[v];
+    } else if constexpr (PVB == 2) {  // fp8 -> f16, two chunks
+      u32x4_t lo, hi;
+      lo[0] = fp8x2_to_f16x2(vraw[v][0], false);
+      lo[1] = fp8x2_to_f16x2(vraw[v][0], true);
+      lo[2] = fp8x2_to_f16x2(vraw[v][1], false);
+      lo[3] = fp8x2_to_f16x2(vraw[v][1], true);
+      hi[0] = fp8x2_to_f16x2(vraw[v][2], false);
+      hi[1] = fp8x2_to_f16x2(vraw[v][2], true);
+      hi[2] = fp8x2_to_f16x2(vraw[v][3], false);
+      hi[3] = fp8x2_to_f16x2(vraw[v][3], true);
+      *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 0) ^ swz) << 4)) = lo;
+      *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 1) ^ swz) << 4)) = hi;
+    } else {  // fp8 -> f32, four chunks
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2_t p0 = fp8x2_to_f32x2(vraw[v][w], false);
+        const f32x2_t p1 = fp8x2_to_f32x2(vraw[v][w], true);
+        f32x4_t q = {p0[0], p0[1], p1[0], p1[1]};
+        *reinterpret_cast<f32x4_t*>(rowp + (((ch0 + w) ^ swz) << 4)) = q;
+      }
+    }
+  }
+
+}
+
+// ---------------------------------------------------------------------------
+// One tile: S = K Q^T, online-softmax update, O^T += V^T P^T.  vt is this
+// wave's LDS slice (32 rows of D PV-operand elements), already holding the
+// tile's V rows (stage_v).
 // ---------------------------------------------------------------------------
 template <typename QT, typename CT, int D>
 __device__ __forceinline__ void compute_tile(
-    const TileRegs<QT, CT, D>& tr, const uint32_t* qw,
+    const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS], const uint32_t* qw,
     WaveState<Shape<QT, CT, D>::NBLK>& st, uint8_t* vt, int t0, int t_end,
     float qk_mul, int lane) {
   typedef Shape<QT, CT, D> S;
@@ -246,17 +291,17 @@ __device__ __forceinline__ void compute_tile(
       if constexpr (same<QT, CT>::value && QT::bytes == 2) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          ka[w] = tr.kw[hh][4 * q + w];
+          ka[w] = kw[hh][4 * q + w];
           qb[w] = qw[4 * q + w];
         }
       } else if constexpr (same<QT, CT>::value) {  // float32
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          ka[e] = bitcast<float>(tr.kw[hh][8 * q + e]);
+          ka[e] = bitcast<float>(kw[hh][8 * q + e]);
           qb[e] = bitcast<float>(qw[8 * q + e]);
         }
       } else if constexpr (QT::bytes == 2) {  // fp8 keys -> bf16/f16
-        const uint32_t w0 = tr.kw[hh][2 * q], w1 = tr.kw[hh][2 * q + 1];
+        const uint32_t w0 = kw[hh][2 * q], w1 = kw[hh][2 * q + 1];
         if constexpr (same<QT, BF16>::value) {
           ka[0] = fp8x2_to_bf16x2(w0, false);
           ka[1] = fp8x2_to_bf16x2(w0, true);
@@ -271,7 +316,7 @@ __device__ __forceinline__ void compute_tile(
 #pragma unroll
         for (int w = 0; w < 4; ++w) qb[w] = qw[4 * q + w];
       } else {  // fp8 keys -> f32
-        const uint32_t w0 = tr.kw[hh][2 * q], w1 = tr.kw[hh][2 * q + 1];
+        const uint32_t w0 = kw[hh][2 * q], w1 = kw[hh][2 * q + 1];
         const f32x2_t p0 = fp8x2_to_f32x2(w0, false), p1 = fp8x2_to_f32x2(w0, true);
         const f32x2_t p2 = fp8x2_to_f32x2(w1, false), p3 = fp8x2_to_f32x2(w1, true);
         ka[0] = p0[0]; ka[1] = p0[1]; ka[2] = p1[0]; ka[3] = p1[1];
@@ -308,41 +353,6 @@ __device__ __forceinline__ void compute_tile(
   st.m = m_new;
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) st.o[n] *= alpha;
-
-  // ---------------- V -> LDS (PV operand type, swizzled) ----------------
-#pragma unroll
-  for (int v = 0; v < S::NV; ++v) {
-    const int tv = lane / S::PPR + v * S::TOK_PER_V;
-    const int swz = ((tv >> 2) & 3) * PVB;
-    uint8_t* rowp = vt + tv * S::LDS_ROW;
-    const int ch0 = (lane % S::PPR) * S::VCH;
-    if constexpr (same<PVT, CT>::value) {
-      *reinterpret_cast<u32x4_t*>(rowp + ((ch0 ^ swz) << 4)) = tr.vraw[v];
-    } else if constexpr (PVB == 2) {  // fp8 -> f16, two chunks
-      u32x4_t lo, hi;
-      lo[0] = fp8x2_to_f16x2(tr.vraw[v][0], false);
-      lo[1] = fp8x2_to_f16x2(tr.vraw[v][0], true);
-      lo[2] = fp8x2_to_f16x2(tr.vraw[v][1], false);
-      lo[3] = fp8x2_to_f16x2(tr.vraw[v][1], true);
-      hi[0] = fp8x2_to_f16x2(tr.vraw[v][2], false);
-      hi[1] = fp8x2_to_f16x2(tr.vraw[v][2], true);
-      hi[2] = fp8x2_to_f16x2(tr.vraw[v][3], false);
-      hi[3] = fp8x2_to_f16x2(tr.vraw[v][3], true);
-      *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 0) ^ swz) << 4)) = lo;
-      *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 1) ^ swz) << 4)) = hi;
-    } else {  // fp8 -> f32, four chunks
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const f32x2_t p0 = fp8x2_to_f32x2(tr.vraw[v][w], false);
-        const f32x2_t p1 = fp8x2_to_f32x2(tr.vraw[v][w], true);
-        f32x4_t q = {p0[0], p0[1], p1[0], p1[1]};
-        *reinterpret_cast<f32x4_t*>(rowp + (((ch0 + w) ^ swz) << 4)) = q;
-      }
-    }
-  }
-  // The slice is private to this wave and one wave's LDS operations execute
-  // in issue order, so the transposed reads below see these stores with no
-  // barrier (the compiler keeps the may-alias store -> load order).
 
   // ---------------- O^T += V^T . P^T ----------------
   typename Mma<PVT>::operand pb_hi, pb_lo;
@@ -388,267 +398,487 @@ __device__ __forceinline__ void compute_tile(
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the partitions of one (sequence, query head): one workgroup.
-// Threads take 4 output columns each and a strided subset of the partitions
-// (D/4 columns x kThreads/(D/4) subsets); subsets are summed through LDS.
+// The split of the tile list.  tex[s] (s = 0 .. num_seqs) is the exclusive
+// prefix of the per-sequence tile counts ceil(L_s / 32); row (s, u), u =
+// kv_head * chunks + chunk, holds tiles [U tex[s] + u T_s, + T_s) of the
+// T = U tex[num_seqs] tiles, T_s = tex[s + 1] - tex[s].  Wave w of W owns
+// tiles [ceil(w T / W), ceil((w + 1) T / W)): tile t belongs to wave
+// floor(t W / T).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_of_tile(int64_t t, int64_t T, int W) {
+  return (int)(t * W / T);
+}
+__device__ __forceinline__ int64_t first_tile_of_wave(int w, int64_t T, int W) {
+  return ((int64_t)w * T + W - 1) / W;
+}
+
+// Partial slot of (wave w, slot q): o [gmax][D], then m [gmax], l [gmax] in
+// separate arrays.
+__device__ __forceinline__ int64_t slot_index(int w, int q) {
+  return (int64_t)w * 2 + q;
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the pieces of one cut row: one workgroup per row (s, u).  A wave
+// per query head first folds the pieces' (m, l) pairs into (M, sum 2^(m-M) l)
+// with every lane on its own pieces; then every thread takes 4 output columns
+// of one head and a strided subset of the pieces (independent loads, four at
+// a time), and the subsets are summed through LDS.  Waves of the partition
+// kernel that own no tile (more waves than tiles) wrote nothing; their slots
+// are skipped with selects, so stale values never enter the sums.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lse_fold(float& m, float& l, float m2, float l2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;  // both empty
+  l = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
+  m = M;
+}
+
 template <int D, bool SCALED>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
   constexpr int D4 = D / 4;
-  constexpr int NSUB = kThreads / D4;
-  __shared__ __attribute__((aligned(16))) float red[NSUB][D];
-  __shared__ float sm_red[2][kWaves];
+  __shared__ __attribute__((aligned(16))) float red[kThreads * 4];
+  __shared__ float sm_stat[16][2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hq = blockIdx.x % a.num_q_heads;
-  const int s = blockIdx.x / a.num_q_heads;
-  const int L = a.seq_lens[s];
-  const int nparts = L > 0 ? (L + a.partition_size - 1) / a.partition_size : 1;
-  if (nparts <= 1) return;  // written directly by the partition kernel
+  const int U = a.num_kv_heads * a.group_chunks;
+  const int s = blockIdx.x / U;
+  const int u = blockIdx.x - s * U;
+  const int* tex = a.tile_prefix;
+  const int* wfirst = a.wave_first;
+  const int ts = tex[s + 1] - tex[s];
+  if (ts == 0) return;  // zeros written by the partition kernel
+  const int64_t T = (int64_t)U * tex[a.num_seqs];
+  const int W = a.num_waves;
+  const int r0 = U * tex[s] + u * ts;
+  const int wf = wave_of_tile(r0, T, W);
+  const int wl = wave_of_tile(r0 + ts - 1, T, W);
+  if (wf == wl) return;  // finished by one wave
+  const int npieces = wl - wf + 1;
+  const int q_first = wfirst[wf] < r0 ? 1 : 0;
 
-  const int64_t row = (int64_t)s * a.num_q_heads + hq;
-  const auto* pm = as_global(a.part_m + row * a.max_parts);
-  const auto* pl = as_global(a.part_l + row * a.max_parts);
-  const auto* po = as_global(a.part_o + row * a.max_parts * D);
+  const int h = u / a.group_chunks;
+  const int gc = u - h * a.group_chunks;
+  const int gcount = min(16, a.group - gc * 16);
+  const int gmax = a.slot_heads;
+  const int64_t head0 = (int64_t)s * a.num_q_heads + h * a.group + gc * 16;
+  // piece i: slot of wave wf + i; present unless that wave owns no tile
+  auto slot_of = [&](int i) { return slot_index(wf + i, i == 0 ? q_first : 0); };
+  auto present = [&](int i) { return i == 0 || wfirst[wf + i] < wfirst[wf + i + 1]; };
 
-  // M = max_p m_p
-  float M = -INFINITY;
-  for (int q = tid; q < nparts; q += kThreads) M = fmaxf(M, pm[q]);
-  M = wave_max(M);
-  if (lane == 0) sm_red[0][wave] = M;
-  __syncthreads();
-  M = sm_red[0][0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_red[0][w]);
-
-  // den = sum_p 2^(m_p - M) l_p ; acc = sum_p 2^(m_p - M) o_p
-  float den = 0.f;
-  for (int q = tid; q < nparts; q += kThreads) den += fast_exp2(pm[q] - M) * pl[q];
-  den = wave_sum(den);
-  if (lane == 0) sm_red[1][wave] = den;
-
-  const int d4 = tid % D4;
-  const int sub = tid / D4;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  int q = sub;
-  for (; q + 3 * NSUB < nparts; q += 4 * NSUB) {
-    float w[4];
-    f32x4_t o[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      w[u] = pm[q + u * NSUB];
-      o[u] = *reinterpret_cast<const __attribute__((address_space(1))) f32x4_t*>(
-          po + (int64_t)(q + u * NSUB) * D + 4 * d4);
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int g = wave; g < gcount; g += kWaves) {
+    float m = -INFINITY, l = 0.f;
+    for (int i = lane; i < npieces; i += 64) {
+      const int64_t sl = slot_of(i) * gmax + g;
+      const float mi = a.part_m[sl], li = a.part_l[sl];
+      if (present(i)) lse_fold(m, l, mi, li);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc += fast_exp2(w[u] - M) * o[u];
+    for (int o = 32; o >= 1; o >>= 1)
+      lse_fold(m, l, __shfl_xor(m, o, 64), __shfl_xor(l, o, 64));
+    if (lane == 0) {
+      sm_stat[g][0] = m;
+      sm_stat[g][1] = l;
+    }
   }
-  for (; q < nparts; q += NSUB)
-    acc += fast_exp2(pm[q] - M) *
-           *reinterpret_cast<const __attribute__((address_space(1))) f32x4_t*>(
-               po + (int64_t)q * D + 4 * d4);
-  *reinterpret_cast<f32x4_t*>(&red[sub][4 * d4]) = acc;
   __syncthreads();
 
-  if (tid < D4) {
-    den = 0.f;
+  const int items = gcount * D4;
+  const int nsub = items >= kThreads ? 1 : kThreads / items;
+  for (int it = tid; it < items * nsub; it += kThreads) {
+    const int item = it % items;
+    const int sub = it / items;
+    const int g = item / D4;
+    const int d4 = item - g * D4;
+    const float M = sm_stat[g][0];
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    int i = sub;
+    for (; i + 3 * nsub < npieces; i += 4 * nsub) {
+      float mi[4];
+      f32x4_t oi[4];
+      bool pi[4];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) den += sm_red[1][w];
-    f32x4_t o = *reinterpret_cast<const f32x4_t*>(&red[0][4 * tid]);
+      for (int k = 0; k < 4; ++k) {
+        const int ii = i + k * nsub;
+        const int64_t sl = slot_of(ii) * gmax + g;
+        mi[k] = a.part_m[sl];
+        oi[k] = *reinterpret_cast<const f32x4_t*>(a.part_o + sl * D + 4 * d4);
+        pi[k] = present(ii);
+      }
 #pragma unroll
-    for (int u = 1; u < NSUB; ++u)
-      o += *reinterpret_cast<const f32x4_t*>(&red[u][4 * tid]);
-    const float vscale = SCALED ? *a.v_scale : 1.f;
-    *reinterpret_cast<f32x4_t*>(a.out + row * D + 4 * tid) = o * (vscale / den);
+      for (int k = 0; k < 4; ++k) {
+        const f32x4_t t = fast_exp2(mi[k] - M) * oi[k];
+        acc += pi[k] ? t : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    for (; i < npieces; i += nsub) {
+      const int64_t sl = slot_of(i) * gmax + g;
+      const f32x4_t t = fast_exp2(a.part_m[sl] - M) *
+                        *reinterpret_cast<const f32x4_t*>(a.part_o + sl * D + 4 * d4);
+      acc += present(i) ? t : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if (nsub == 1) {
+      const float f = (SCALED ? *a.v_scale : 1.f) / sm_stat[g][1];
+      *reinterpret_cast<f32x4_t*>(a.out + (head0 + g) * D + 4 * d4) = acc * f;
+    } else {
+      *reinterpret_cast<f32x4_t*>(red + 4 * (sub * items + item)) = acc;
+    }
+  }
+  if (nsub > 1) {
+    __syncthreads();
+    for (int item = tid; item < items; item += kThreads) {
+      const int g = item / D4;
+      const int d4 = item - g * D4;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int sub = 0; sub < nsub; ++sub)
+        acc += *reinterpret_cast<const f32x4_t*>(red + 4 * (sub * items + item));
+      const float f = (SCALED ? *a.v_scale : 1.f) / sm_stat[g][1];
+      *reinterpret_cast<f32x4_t*>(a.out + (head0 + g) * D + 4 * d4) = acc * f;
+    }
   }
 }
 
+// Inclusive scan of one int per thread across the workgroup.
+__device__ int block_inclusive_scan(int v, int* sm_wsum) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) sm_wsum[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += sm_wsum[w];
+  return v + add;
+}
+
+// A run of consecutive tiles of one row owned by one wave.
+struct Seg {
+  int s, h, gc;       // the row
+  int t_begin, t_end; // tokens of the sequence it covers
+  int ntiles;
+  int wb;             // first logical block of its table window
+  bool full;          // the whole row: write the final output
+  bool valid;
+};
+
+// The segment starting at tile t of the wave's range [.., te): the largest s
+// with tex[s] <= t / U (binary search in LDS; every lane runs it with the
+// same values), then the row and the tile within it.
+__device__ __forceinline__ Seg segment_at(int64_t t, int64_t te, int U,
+                                          const int* tex, const int* lens,
+                                          const AttnArgs& a) {
+  Seg g;
+  g.valid = t < te;
+  if (!g.valid) {
+    g.s = g.h = g.gc = 0;
+    g.t_begin = g.t_end = 0;
+    g.ntiles = 0;
+    g.wb = 0;
+    g.full = false;
+    return g;
+  }
+  const int q = (int)(t / U);
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(tex[mid]) <= q) lo = mid;
+    else hi = mid - 1;
+  }
+  const int base_t = __builtin_amdgcn_readfirstlane(tex[lo]);
+  const int ts = __builtin_amdgcn_readfirstlane(tex[lo + 1]) - base_t;
+  const int L = __builtin_amdgcn_readfirstlane(lens[lo]);
+  const int64_t base = (int64_t)U * base_t;
+  const int r = (int)(t - base);
+  const int u = r / ts;
+  const int k0 = r - u * ts;
+  const int64_t row_end = base + (int64_t)(u + 1) * ts;
+  const int64_t end = te < row_end ? te : row_end;
+  g.s = lo;
+  g.h = u / a.group_chunks;
+  g.gc = u - g.h * a.group_chunks;
+  g.ntiles = (int)(end - t);
+  g.t_begin = 32 * k0;
+  g.t_end = min(L, 32 * (k0 + g.ntiles));
+  g.wb = g.t_begin / a.block_size;
+  g.full = k0 == 0 && end == row_end;
+  return g;
+}
+
+// Entries wb + 64 * half + lane of the segment's table row (0 past the blocks
+// the segment can reach; such lanes fetch nothing).
+__device__ __forceinline__ uint32_t load_window(const Seg& g, int half,
+                                                const AttnArgs& a, int lane) {
+  const int nblk = g.valid ? (g.t_end + a.block_size - 1) / a.block_size : 0;
+  const int nrec = __builtin_amdgcn_readfirstlane(nblk * 4);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.block_tables +
+                           (int64_t)g.s * a.max_blocks_per_seq),
+      (short)0, nrec, kRawBufferFlags);
+  return __builtin_amdgcn_raw_buffer_load_b32(
+      r, (g.wb + 64 * half + lane) * 4, 0, 0);
+}
+
+// The query rows of a segment's row as the B operand of S = K Q^T (zeros for
+// query heads past the chunk's count and for an invalid segment).
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void load_query(uint32_t* qw, const Seg& g,
+                                           const AttnArgs& a, int lane) {
+  typedef Shape<QT, CT, D> S;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+  const int gcount = min(16, a.group - g.gc * 16);
+  const int hq0 = g.h * a.group + g.gc * 16;
+  const int nrec = __builtin_amdgcn_readfirstlane(
+      g.valid ? gcount * D * QT::bytes : 0);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(a.query) +
+                           ((int64_t)g.s * a.num_q_heads + hq0) * D * QT::bytes),
+      (short)0, nrec, kRawBufferFlags);
+  constexpr int QBYTES_PER_R = S::EP * QT::bytes;
+  constexpr int QLOADS = QBYTES_PER_R / 16;
+#pragma unroll
+  for (int rr = 0; rr < D / (4 * S::EP); ++rr) {
+#pragma unroll
+    for (int k = 0; k < QLOADS; ++k) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+          r, c * D * QT::bytes + (4 * rr + j) * QBYTES_PER_R + 16 * k, 0, 0);
+      const int w0 = (rr * QBYTES_PER_R + 16 * k) / 4;
+      qw[w0 + 0] = v[0];
+      qw[w0 + 1] = v[1];
+      qw[w0 + 2] = v[2];
+      qw[w0 + 3] = v[3];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Partition kernel: wave w streams tiles [ceil(w T / W), ceil((w+1) T / W))
+// of the row-major tile list, one segment (run of one row) after another.
+// The next segment's query rows and table window are requested when a
+// segment starts and its first tile during the current segment's last tile,
+// so a wave's loads run on across segment boundaries.
+// ---------------------------------------------------------------------------
 template <typename QT, typename CT, int D, bool UNIFORM>
-__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_decode_kernel(AttnArgs a) {
   typedef Shape<QT, CT, D> S;
   constexpr int NBLK = S::NBLK;
   constexpr bool PREFETCH = UNIFORM && CT::bytes <= 2;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM_BYTES];
-  __shared__ float sm_ml[kWaves][2][16];
-  __shared__ float sm_stat[32];
-  __shared__ int32_t sm_tab[UNIFORM ? kMaxTableWindow : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * S::STAGE_BYTES];
+  __shared__ int sm_wsum[kWaves];
+  extern __shared__ int sm_seq[];  // tex[num_seqs + 1] | lens[num_seqs]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c = lane & 15;
   const int j = lane >> 4;
+  const int nS = a.num_seqs;
+  const int U = a.num_kv_heads * a.group_chunks;
+  int* tex = sm_seq;
+  int* lens = sm_seq + nS + 1;
 
-  int u = blockIdx.x;
-  const int part = u % a.max_parts;
-  u /= a.max_parts;
-  const int gc = u % a.group_chunks;
-  u /= a.group_chunks;
-  const int h = u % a.num_kv_heads;
-  const int s = u / a.num_kv_heads;
+  // ---- tile counts of all sequences and their exclusive prefix ----
+  {
+    const int per = (nS + kThreads - 1) / kThreads;
+    const int b0 = min(tid * per, nS);
+    const int b1 = min(b0 + per, nS);
+    int sum = 0;
+    for (int i = b0; i < b1; ++i) {
+      const int L = a.seq_lens[i];
+      lens[i] = L;
+      sum += (L + 31) / 32;
+    }
+    const int incl = block_inclusive_scan(sum, sm_wsum);
+    int run = incl - sum;
+    for (int i = b0; i < b1; ++i) {
+      tex[i] = run;
+      run += (lens[i] + 31) / 32;
+    }
+    if (tid == kThreads - 1) tex[nS] = incl;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)  // the merge kernel reads the prefix from here
+    for (int i = tid; i <= nS; i += kThreads) a.tile_prefix[i] = tex[i];
 
-  const int L = a.seq_lens[s];
-  const int P = a.partition_size;
-  const int nparts = L > 0 ? (L + P - 1) / P : 1;
-  if (part >= nparts) return;
-  const int t_begin = part * P;
-  const int t_end = min(t_begin + P, L);
-  const int ntiles = (t_end - t_begin + 31) / 32;
-  const int gcount = min(16, a.group - gc * 16);
-  const int hq = h * a.group + gc * 16 + c;
-  const bool head_live = c < gcount;
+  const int W = a.num_waves;
+  const int w = blockIdx.x * kWaves + wave;
+  const int64_t T = (int64_t)U * tex[nS];
+  const int64_t tb = first_tile_of_wave(w, T, W);
+  const int64_t te = first_tile_of_wave(w + 1, T, W);
+  if (lane == 0) {  // the merge kernel reads the split from here
+    a.wave_first[w] = (int)tb;
+    if (w == W - 1) a.wave_first[W] = (int)T;
+  }
 
-  float kscale = 1.f, vscale = 1.f;
+  float vscale = 1.f, kscale = 1.f;
   if constexpr (is_fp8<CT>::value) {
     kscale = *a.k_scale;
     vscale = *a.v_scale;
   }
-  const float qk_mul = a.qk_scale_log2 * kscale;
 
-  // ---- query: B operand of S = K Q^T, in the same element order as K ----
-  uint32_t qw[S::QWORDS];
+  // ---- rows of empty sequences sit at tile position U tex[s]; the wave
+  // whose range holds that position (the last wave for position T) writes
+  // their zeros ----
   {
-    const uint8_t* qrow = static_cast<const uint8_t*>(a.query) +
-                          ((int64_t)s * a.num_q_heads + hq) * D * QT::bytes;
-    constexpr int QBYTES_PER_R = S::EP * QT::bytes;
-    constexpr int QLOADS = QBYTES_PER_R / 16;
+    int lo = 0, hi = nS;  // first s with U tex[s] >= tb
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)U * __builtin_amdgcn_readfirstlane(tex[mid]) >= tb) hi = mid;
+      else lo = mid + 1;
+    }
+    for (int s = lo; s < nS; ++s) {
+      const int64_t pos = (int64_t)U * __builtin_amdgcn_readfirstlane(tex[s]);
+      if (pos >= te && !(w == W - 1 && pos == T)) break;
+      if (__builtin_amdgcn_readfirstlane(lens[s]) != 0) continue;
+      float* dst = a.out + (int64_t)s * a.num_q_heads * D;
+      for (int i = lane; i < a.num_q_heads * D / 4; i += 64)
+        reinterpret_cast<f32x4_t*>(dst)[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  const float qk_mul = a.qk_scale_log2 * kscale;
+  const int64_t stride = (int64_t)a.num_kv_heads * S::ROW_BYTES;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_cache);
+  uint8_t* vt = smem + wave * S::STAGE_BYTES;
+  const int gmax = a.slot_heads;
+
+  Seg X = segment_at(tb, te, U, tex, lens, a);
+  int64_t pos_n = tb + X.ntiles;  // first tile of the next segment
+  Seg Xn = segment_at(pos_n, te, U, tex, lens, a);
+  bool first_seg = true;
+  uint32_t ta = 0, tbw = 0, ta_n = 0, tb_n = 0;
+  if constexpr (UNIFORM) {
+    ta = load_window(X, 0, a, lane);
+    tbw = load_window(X, 1, a, lane);
+    ta_n = load_window(Xn, 0, a, lane);
+    tb_n = load_window(Xn, 1, a, lane);
+  }
+  uint32_t qw[S::QWORDS];
+  load_query<QT, CT, D>(qw, X, a, lane);
+  TileRegs<QT, CT, D> cur;
+  if constexpr (PREFETCH)
+    load_tile_uniform<QT, CT, D>(cur, a.block_size, ta, tbw, X.wb,
+                                 kpool + (int64_t)X.h * S::ROW_BYTES,
+                                 vpool + (int64_t)X.h * S::ROW_BYTES, stride,
+                                 X.t_begin, X.t_end, lane);
+
+  while (X.valid) {
+    uint32_t qn[S::QWORDS];
+    load_query<QT, CT, D>(qn, Xn, a, lane);
+
+    WaveState<NBLK> st;
+    st.m = -INFINITY;
+    st.l = 0.f;
 #pragma unroll
-    for (int r = 0; r < D / (4 * S::EP); ++r) {
-#pragma unroll
-      for (int k = 0; k < QLOADS; ++k) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (head_live)
-          v = *reinterpret_cast<const u32x4_t*>(
-              qrow + (4 * r + j) * QBYTES_PER_R + 16 * k);
-        const int w0 = (r * QBYTES_PER_R + 16 * k) / 4;
-        qw[w0 + 0] = v[0];
-        qw[w0 + 1] = v[1];
-        qw[w0 + 2] = v[2];
-        qw[w0 + 3] = v[3];
+    for (int n = 0; n < NBLK; ++n) st.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const uint8_t* kbase = kpool + (int64_t)X.h * S::ROW_BYTES;
+    const uint8_t* vbase = vpool + (int64_t)X.h * S::ROW_BYTES;
+    if constexpr (PREFETCH) {
+      const uint8_t* kbase_n = kpool + (int64_t)Xn.h * S::ROW_BYTES;
+      const uint8_t* vbase_n = vpool + (int64_t)Xn.h * S::ROW_BYTES;
+      int wb = X.wb;
+      for (int k = 0; k < X.ntiles; ++k) {
+        stage_v<QT, CT, D>(cur.vraw, vt, lane);
+        // the next tile of this wave's stream: tile k + 1 of X, else the
+        // first tile of the next segment (an empty range past the end);
+        // requested before this tile is computed, which the scheduling
+        // barrier keeps (the compiler would otherwise sink the loads to
+        // shorten register lifetimes)
+        const bool same_seg = k + 1 < X.ntiles;
+        const int t_next = X.t_begin + 32 * (k + 1);
+        if (same_seg && t_next / a.block_size - wb >= 64) {
+          // the window moves on by 64 blocks; the new upper half is needed
+          // only 64 blocks later
+          wb += 64;
+          ta = tbw;
+          Seg shifted = X;
+          shifted.wb = wb;
+          tbw = load_window(shifted, 1, a, lane);
+        }
+        TileRegs<QT, CT, D> nxt;
+        load_tile_uniform<QT, CT, D>(
+            nxt, a.block_size, same_seg ? ta : ta_n, same_seg ? tbw : tb_n,
+            same_seg ? wb : Xn.wb, same_seg ? kbase : kbase_n,
+            same_seg ? vbase : vbase_n, stride,
+            same_seg ? t_next : Xn.t_begin, same_seg ? X.t_end : Xn.t_end,
+            lane);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile<QT, CT, D>(cur.kw, qw, st, vt, X.t_begin + 32 * k,
+                                X.t_end, qk_mul, lane);
+        cur = nxt;
+      }
+    } else {
+      const int32_t* trow = a.block_tables + (int64_t)X.s * a.max_blocks_per_seq;
+      for (int k = 0; k < X.ntiles; ++k) {
+        const int t0 = X.t_begin + 32 * k;
+        if constexpr (UNIFORM) {
+          const int wb = X.wb + (t0 / a.block_size - X.wb) / 64 * 64;
+          Seg shifted = X;
+          shifted.wb = wb;
+          const uint32_t wa = load_window(shifted, 0, a, lane);
+          const uint32_t wbb = load_window(shifted, 1, a, lane);
+          load_tile_uniform<QT, CT, D>(cur, a.block_size, wa, wbb, wb, kbase,
+                                       vbase, stride, t0, X.t_end, lane);
+        } else {
+          load_tile_any<QT, CT, D>(cur, a.block_size, trow, kbase, vbase,
+                                   stride, t0, X.t_end, lane);
+        }
+        stage_v<QT, CT, D>(cur.vraw, vt, lane);
+        compute_tile<QT, CT, D>(cur.kw, qw, st, vt, t0, X.t_end, qk_mul,
+                                lane);
       }
     }
-  }
 
-  const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) +
-                         (int64_t)h * S::ROW_BYTES;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) +
-                         (int64_t)h * S::ROW_BYTES;
-  const int64_t stride = (int64_t)a.num_kv_heads * S::ROW_BYTES;
-  uint8_t* vt = smem + wave * S::STAGE_BYTES;
-
-  int lb_first = 0;
-  if constexpr (UNIFORM) {
-    // the partition's block-table entries, once per workgroup
-    if (t_end > t_begin) {
-      lb_first = t_begin / a.block_size;
-      const int count = (t_end - 1) / a.block_size - lb_first + 1;
-      for (int i = tid; i < count; i += kThreads)
-        sm_tab[i] = trow[lb_first + i];
+    // ---------------- the segment's output (this wave alone) ----------------
+    // lane (c + 16 j) holds O^T rows 16 n + 4 j .. + 3 of query head c
+    const int gcount = min(16, a.group - X.gc * 16);
+    float l_tot = xor_sum(st.l, 16);
+    l_tot = xor_sum(l_tot, 32);
+    if (c < gcount) {
+      if (X.full) {
+        const int64_t head = (int64_t)X.s * a.num_q_heads + X.h * a.group +
+                             X.gc * 16 + c;
+        const float f = l_tot > 0.f ? vscale / l_tot : 0.f;
+        float* dst = a.out + head * D + 4 * j;
+#pragma unroll
+        for (int n = 0; n < NBLK; ++n)
+          *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st.o[n] * f;
+      } else {
+        // first segment of the wave -> slot 0, last -> slot 1
+        const int64_t sl = slot_index(w, first_seg ? 0 : 1) * gmax + c;
+        float* dst = a.part_o + sl * D + 4 * j;
+#pragma unroll
+        for (int n = 0; n < NBLK; ++n)
+          *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st.o[n];
+        if (j == 0) {
+          a.part_m[sl] = st.m;
+          a.part_l[sl] = l_tot;
+        }
+      }
     }
-    __syncthreads();
-  }
 
-  WaveState<NBLK> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int n = 0; n < NBLK; ++n) st.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  if constexpr (PREFETCH) {
-    // Loads of tile k + kWaves are in flight while tile k is computed; past
-    // the last tile the buffer ranges are empty, so those loads fetch
-    // nothing and the loop needs no branch around them.
-    TileRegs<QT, CT, D> cur, nxt;
-    load_tile_uniform<QT, CT, D>(cur, a, sm_tab, lb_first, kbase, vbase,
-                                 stride, t_begin + 32 * wave, t_end, lane);
-    for (int k = wave; k < ntiles; k += kWaves) {
-      load_tile_uniform<QT, CT, D>(nxt, a, sm_tab, lb_first, kbase, vbase,
-                                   stride, t_begin + 32 * (k + kWaves), t_end,
-                                   lane);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of compute
-      compute_tile<QT, CT, D>(cur, qw, st, vt, t_begin + 32 * k, t_end,
-                              qk_mul, lane);
-      cur = nxt;
+    // ---------------- advance to the next segment ----------------
+    first_seg = false;
+    X = Xn;
+    if constexpr (UNIFORM) {
+      ta = ta_n;
+      tbw = tb_n;
     }
-  } else {
-    for (int k = wave; k < ntiles; k += kWaves) {
-      TileRegs<QT, CT, D> cur;
-      if constexpr (UNIFORM)
-        load_tile_uniform<QT, CT, D>(cur, a, sm_tab, lb_first, kbase, vbase,
-                                     stride, t_begin + 32 * k, t_end, lane);
-      else
-        load_tile_any<QT, CT, D>(cur, a, trow, kbase, vbase, stride,
-                                 t_begin + 32 * k, t_end, lane);
-      compute_tile<QT, CT, D>(cur, qw, st, vt, t_begin + 32 * k, t_end,
-                              qk_mul, lane);
-    }
-  }
-
-  // ---------------- combine the waves' states ----------------
-  float l_w = xor_sum(st.l, 16);
-  l_w = xor_sum(l_w, 32);
-  if (j == 0) {
-    sm_ml[wave][0][c] = st.m;
-    sm_ml[wave][1][c] = l_w;
-  }
-  __syncthreads();  // also: every wave is done with its V slice
-  float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][0][c]);
-  float Ltot = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      Ltot += fast_exp2(sm_ml[w][0][c] - M) * sm_ml[w][1][c];
-  }
-  const float f = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m - M);
-  float* so = reinterpret_cast<float*>(smem);
-  if (head_live) {
-    float* dst = so + (wave * 16 + c) * S::ORow + 4 * j;
-#pragma unroll
-    for (int n = 0; n < NBLK; ++n)
-      *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st.o[n] * f;
-  }
-  if (wave == 0 && j == 0) {  // per-head totals for the output pass
-    sm_stat[2 * c] = M;
-    sm_stat[2 * c + 1] = Ltot;
-  }
-  __syncthreads();
-
-  constexpr int D4 = D / 4;
-  const int items = gcount * D4;
-  const int64_t head0 = (int64_t)s * a.num_q_heads + h * a.group + gc * 16;
-  if (nparts == 1) {
-    for (int it = tid; it < items; it += kThreads) {
-      const int g = it / D4;
-      const int d4 = it - g * D4;
-      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        o += *reinterpret_cast<const f32x4_t*>(so + (w * 16 + g) * S::ORow + 4 * d4);
-      const float lt = sm_stat[2 * g + 1];
-      o = lt > 0.f ? o * (vscale / lt) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4_t*>(a.out + (head0 + g) * D + 4 * d4) = o;
-    }
-    return;
-  }
-
-  for (int it = tid; it < items; it += kThreads) {
-    const int g = it / D4;
-    const int d4 = it - g * D4;
-    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      o += *reinterpret_cast<const f32x4_t*>(so + (w * 16 + g) * S::ORow + 4 * d4);
-    const int64_t prow = (head0 + g) * a.max_parts + part;
-    *reinterpret_cast<f32x4_t*>(a.part_o + prow * D + 4 * d4) = o;
-    if (d4 == 0) {
-      a.part_m[prow] = sm_stat[2 * g];
-      a.part_l[prow] = sm_stat[2 * g + 1];
+    for (int q = 0; q < S::QWORDS; ++q) qw[q] = qn[q];
+    pos_n += X.ntiles;
+    Xn = segment_at(pos_n, te, U, tex, lens, a);
+    if constexpr (UNIFORM) {
+      ta_n = load_window(Xn, 0, a, lane);
+      tb_n = load_window(Xn, 1, a, lane);
     }
   }
 }
@@ -656,40 +886,65 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <typename QT, typename CT, int D>
-static hipError_t launch_d(const AttnArgs& a, int grid, bool uniform,
-                           hipStream_t stream) {
-  if (uniform)
-    hipLaunchKernelGGL((attn_decode_kernel<QT, CT, D, true>), dim3(grid),
-                       dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_decode_kernel<QT, CT, D, false>), dim3(grid),
-                       dim3(kThreads), 0, stream, a);
-  if (a.max_parts > 1)
-    hipLaunchKernelGGL((attn_merge_kernel<D, is_fp8<CT>::value>),
-                       dim3(a.num_seqs * a.num_q_heads), dim3(kThreads), 0,
-                       stream, a);
+// Workgroups of the partition kernel: as many as can be resident at once
+// (occupancy x CUs), capped by the caller's wave limit and kMaxWaves.
+template <typename K>
+static int resident_grid(K kernel, size_t dyn_lds, int max_waves) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(kernel), kThreads, dyn_lds) !=
+          hipSuccess)
+    return -1;
+  int64_t g = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
+  int64_t cap = kMaxWaves / kWaves;
+  if (max_waves > 0 && max_waves / kWaves < cap) cap = max_waves / kWaves;
+  if (g > cap) g = cap;
+  return g < 1 ? 1 : (int)g;
+}
+
+template <typename QT, typename CT, int D, bool UNIFORM>
+static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
+  auto kernel = attn_decode_kernel<QT, CT, D, UNIFORM>;
+  const size_t dyn = ((size_t)2 * a.num_seqs + 1) * sizeof(int);
+  const int grid = resident_grid(kernel, dyn, max_waves);
+  if (grid < 0) return hipErrorInvalidValue;
+  a.num_waves = grid * kWaves;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
+  hipLaunchKernelGGL((attn_merge_kernel<D, is_fp8<CT>::value>),
+                     dim3(a.num_seqs * a.num_kv_heads * a.group_chunks),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
+template <typename QT, typename CT, int D>
+static hipError_t launch_d(const AttnArgs& a, int max_waves, bool uniform,
+                           hipStream_t stream) {
+  if (uniform) return launch_u<QT, CT, D, true>(a, max_waves, stream);
+  return launch_u<QT, CT, D, false>(a, max_waves, stream);
+}
+
 template <typename QT, typename CT>
-static hipError_t launch_t(const AttnArgs& a, int head_dim, int grid,
+static hipError_t launch_t(const AttnArgs& a, int head_dim, int max_waves,
                            bool uniform, hipStream_t stream) {
-  if (head_dim == 64) return launch_d<QT, CT, 64>(a, grid, uniform, stream);
-  return launch_d<QT, CT, 128>(a, grid, uniform, stream);
+  if (head_dim == 64) return launch_d<QT, CT, 64>(a, max_waves, uniform, stream);
+  return launch_d<QT, CT, 128>(a, max_waves, uniform, stream);
 }
 
 hipError_t launch_attn_decode(const AttnArgs& a, int q_dtype, int cache_dtype,
-                              int head_dim, int grid, hipStream_t stream) {
+                              int head_dim, int max_waves,
+                              hipStream_t stream) {
   const bool uniform = (a.block_size % 16) == 0;
   switch (cache_dtype) {
-    case PKV_F32: return launch_t<F32, F32>(a, head_dim, grid, uniform, stream);
-    case PKV_F16: return launch_t<F16, F16>(a, head_dim, grid, uniform, stream);
-    case PKV_BF16: return launch_t<BF16, BF16>(a, head_dim, grid, uniform, stream);
+    case PKV_F32: return launch_t<F32, F32>(a, head_dim, max_waves, uniform, stream);
+    case PKV_F16: return launch_t<F16, F16>(a, head_dim, max_waves, uniform, stream);
+    case PKV_BF16: return launch_t<BF16, BF16>(a, head_dim, max_waves, uniform, stream);
     case PKV_FP8_E4M3:
-      if (q_dtype == PKV_BF16) return launch_t<BF16, FP8>(a, head_dim, grid, uniform, stream);
-      if (q_dtype == PKV_F16) return launch_t<F16, FP8>(a, head_dim, grid, uniform, stream);
-      return launch_t<F32, FP8>(a, head_dim, grid, uniform, stream);
+      if (q_dtype == PKV_BF16) return launch_t<BF16, FP8>(a, head_dim, max_waves, uniform, stream);
+      if (q_dtype == PKV_F16) return launch_t<F16, FP8>(a, head_dim, max_waves, uniform, stream);
+      return launch_t<F32, FP8>(a, head_dim, max_waves, uniform, stream);
   }
   return hipErrorInvalidValue;
 }

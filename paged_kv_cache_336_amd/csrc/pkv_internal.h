@@ -9,11 +9,13 @@
 
 namespace pkv {
 
-// Longest partition (tokens).  With block_size % 16 == 0 a partition of at
-// most this many tokens starting at a multiple of 32 touches at most
-// kMaxTableWindow blocks (bs 16: exactly P/16; bs >= 32: at most P/32 + 2).
-constexpr int kMaxPartition = 4096;
-constexpr int kMaxTableWindow = kMaxPartition / 16;
+// Most sequences per call: the tile prefix and the lengths of all sequences
+// are held in LDS (8 bytes per sequence).
+constexpr int kMaxSeqs = 8192;
+
+// Most waves of the partition kernel (16 per CU of a 256-CU part); the
+// workspace holds two partial slots per wave.
+constexpr int kMaxWaves = 4096;
 
 struct AttnArgs {
   float* out;
@@ -24,23 +26,25 @@ struct AttnArgs {
   const float* v_scale;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* part_o;          // [S, Hq, max_parts, D]
-  float* part_m;          // [S, Hq, max_parts]  running max (log2 domain)
-  float* part_l;          // [S, Hq, max_parts]  running sum
+  float* part_o;          // [kMaxWaves][2][slot_heads][D]   partial outputs
+  float* part_m;          // [kMaxWaves][2][slot_heads]      running max (log2)
+  float* part_l;          // [kMaxWaves][2][slot_heads]      running sum
+  int32_t* tile_prefix;   // [num_seqs + 1]  tiles of the sequences before s
+  int32_t* wave_first;    // [num_waves + 1] first tile of each wave (+ total)
   int32_t num_seqs;
   int32_t max_blocks_per_seq;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;          // query heads per kv head
   int32_t group_chunks;   // ceil(group / 16)
+  int32_t slot_heads;     // min(16, group): query heads per partial slot
   int32_t block_size;
-  int32_t partition_size;
-  int32_t max_parts;
+  int32_t num_waves;      // waves of the partition kernel's grid
   float qk_scale_log2;    // softmax scale * log2(e)
 };
 
 hipError_t launch_attn_decode(const AttnArgs& a, int q_dtype, int cache_dtype,
-                              int head_dim, int grid, hipStream_t stream);
+                              int head_dim, int max_waves, hipStream_t stream);
 
 struct WriteArgs {
   const void* key;

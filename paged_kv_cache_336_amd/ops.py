@@ -7,7 +7,7 @@ first call raises.
 
 Functions keep the C names: :func:`cache_write_slots`, :func:`copy_blocks`,
 :func:`paged_attn_decode`, :func:`paged_attn_workspace_size`,
-:func:`paged_attn_partition_size`, :func:`pkv_status_string`.
+:func:`pkv_status_string`.
 """
 
 import ctypes
@@ -21,8 +21,7 @@ KIND_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
               "fp8_e4m3": PKV_FP8_E4M3}
 
 EXPORTED = ("pkv_status_string", "cache_write_slots", "copy_blocks",
-            "paged_attn_partition_size", "paged_attn_workspace_size",
-            "paged_attn_decode")
+            "paged_attn_workspace_size", "paged_attn_decode")
 
 _lib = None
 
@@ -55,10 +54,8 @@ def load_library(path=None):
                                       i32, i32, vp, vp, vp]
     lib.copy_blocks.restype = ci
     lib.copy_blocks.argtypes = [vp, vp, ci, vp, i64, i64, i32, i32, i32, vp]
-    lib.paged_attn_partition_size.restype = i32
-    lib.paged_attn_partition_size.argtypes = [i32, i32, i32, i32, i32]
     lib.paged_attn_workspace_size.restype = sz
-    lib.paged_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attn_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.paged_attn_decode.restype = ci
     lib.paged_attn_decode.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp, vp, i32,
                                       vp, i32, i32, i32, i32, i32, i64, i32,
@@ -137,20 +134,9 @@ def copy_blocks(k_cache, v_cache, block_pairs, cache_kind=None, stream=None):
         _stream(stream)))
 
 
-def paged_attn_partition_size(num_seqs, num_q_heads, num_kv_heads,
-                              max_seq_len, partition_size=0):
-    v = load_library().paged_attn_partition_size(
-        num_seqs, num_q_heads, num_kv_heads, max_seq_len, partition_size)
-    if v < 0:
-        raise PagedKVError("paged_attn_partition_size", -v)
-    return v
-
-
-def paged_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                              max_seq_len, partition_size=0):
-    v = load_library().paged_attn_workspace_size(
-        num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-        partition_size)
+def paged_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim):
+    v = load_library().paged_attn_workspace_size(num_seqs, num_q_heads,
+                                                 num_kv_heads, head_dim)
     if v == ctypes.c_size_t(-1).value:
         raise PagedKVError("paged_attn_workspace_size", 2)
     return v
@@ -179,14 +165,13 @@ _default_ws = {}
 
 def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
                       max_seq_len, scale, k_scale=None, v_scale=None,
-                      partition_size=0, workspace=None, cache_kind=None,
+                      max_waves=0, workspace=None, cache_kind=None,
                       stream=None):
     """out[S, Hq, D] (float32) = paged decode attention; see pagedkv.h."""
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
-    need = paged_attn_workspace_size(s, hq, hkv, d, max_seq_len,
-                                     partition_size)
+    need = paged_attn_workspace_size(s, hq, hkv, d)
     if workspace is None:
         key = str(query.device)
         workspace = _default_ws.setdefault(key, Workspace(query.device))
@@ -196,6 +181,6 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
         _ptr(v_cache), dtype_code(k_cache, cache_kind), _ptr(k_scale),
         _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
         _ptr(seq_lens), int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
-        int(partition_size), _ptr(buf),
+        int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
         _stream(stream)))

@@ -69,15 +69,7 @@ class DeviceStep:
         self.out = torch.empty(w.query.shape, dtype=torch.float32, device=dev)
         self.cache_kind = w.kv_kind if w.kv_kind == "fp8_e4m3" else None
         self.workspace = ops.Workspace(dev)
-        self.partition_size = w.partition_size
         self.max_seq_len = w.max_seq_len
-
-    @property
-    def resolved_partition(self):
-        w = self.w
-        return ops.paged_attn_partition_size(w.num_seqs, w.num_q_heads,
-                                             w.num_kv_heads, self.max_seq_len,
-                                             self.partition_size)
 
     def copy(self, r=0, stream=None):
         pairs = self.sets[r]["copy_pairs"]
@@ -91,13 +83,12 @@ class DeviceStep:
                               k_scale=self.k_scale, v_scale=self.v_scale,
                               cache_kind=kind, stream=stream)
 
-    def attend(self, r=0, stream=None, partition_size=None):
-        p = self.partition_size if partition_size is None else partition_size
+    def attend(self, r=0, stream=None, max_waves=0):
         ops.paged_attn_decode(self.out, self.query, self.k_cache, self.v_cache,
                               self.sets[r]["block_tables"], self.seq_lens,
                               self.max_seq_len, self.w.scale,
                               k_scale=self.k_scale, v_scale=self.v_scale,
-                              partition_size=p, workspace=self.workspace,
+                              max_waves=max_waves, workspace=self.workspace,
                               cache_kind=self.cache_kind, stream=stream)
 
     def run(self, r=0, stream=None):

@@ -106,7 +106,6 @@ class Workload:
     copy_pairs: np.ndarray   # int32 [P, 2] (src, dst)
     k_scale: float = 1.0     # float32 values; meaningful for fp8 caches
     v_scale: float = 1.0
-    partition_size: int = 0  # 0 = library's choice
     # Extra disjoint copies of (tables, slots, pairs) over the same pool,
     # for rotating benchmark steps through more memory than the caches hold.
     replicas: list = field(default_factory=list)
@@ -216,7 +215,7 @@ def _unused_column_fill(block_tables, counts, filler):
 
 def _build(name, rng, *, q_kind, kv_kind, src_kind, hq, hkv, d, bs, nb,
            block_tables, seq_lens, cached_lens, slot_mapping, copy_pairs,
-           replicas=(), partition_size=0, note="", live_extra=None):
+           replicas=(), note="", live_extra=None):
     """Draw pool values and rows for an already-laid-out step."""
     live = live_slot_mask(nb, bs, block_tables, cached_lens)
     for rep in replicas:
@@ -243,7 +242,7 @@ def _build(name, rng, *, q_kind, kv_kind, src_kind, hq, hkv, d, bs, nb,
         key=key, value=value,
         slot_mapping=np.asarray(slot_mapping, dtype=np.int32),
         copy_pairs=np.asarray(copy_pairs, dtype=np.int32).reshape(-1, 2),
-        k_scale=k_scale, v_scale=v_scale, partition_size=partition_size,
+        k_scale=k_scale, v_scale=v_scale,
         replicas=list(replicas), note=note)
 
 
@@ -300,7 +299,7 @@ def worked_example(seed_family=0):
 
 
 def llama8b_decode(num_seqs=32, median=512, cap=4096, num_blocks=16384,
-                   replicas=1, seed_family=1, partition_size=0):
+                   replicas=1, seed_family=1):
     """Llama-3-8B-shaped decode layer: 32 sequences, 32/8 heads, D 128,
     bs 16, bf16; lognormal lengths (median 512, cap 4096); block ids from a
     random permutation of a 16384-block pool; 1 new token per sequence.
@@ -325,12 +324,11 @@ def llama8b_decode(num_seqs=32, median=512, cap=4096, num_blocks=16384,
                   block_tables=sets[0]["block_tables"], seq_lens=lens,
                   cached_lens=cached, slot_mapping=sets[0]["slot_mapping"],
                   copy_pairs=sets[0]["copy_pairs"], replicas=sets[1:],
-                  partition_size=partition_size,
                   note=f"{len(sets)} disjoint replica(s)")
 
 
 def llama70b_decode(num_seqs=256, median=1024, cap=8192, occupancy=0.9,
-                    seed_family=2, partition_size=0):
+                    seed_family=2):
     """70B-shaped decode layer at high concurrency: 256 sequences, 64/8
     heads, D 128, bs 16, fp16; lognormal lengths (median 1024, cap 8192);
     scattered blocks in a pool sized to 90 % occupancy; 256 new tokens."""
@@ -350,13 +348,11 @@ def llama70b_decode(num_seqs=256, median=1024, cap=8192, occupancy=0.9,
                   src_kind="f16", hq=64, hkv=8, d=128, bs=bs, nb=nb,
                   block_tables=tables, seq_lens=lens, cached_lens=cached,
                   slot_mapping=slots, copy_pairs=np.zeros((0, 2)),
-                  partition_size=partition_size,
                   note=f"pool {nb} blocks, {used} used")
 
 
 def prefix_sharing(block_size=32, phase="fork", groups=8, samples=8,
-                   prompt_len=2048, max_tail=512, seed_family=3,
-                   partition_size=0):
+                   prompt_len=2048, max_tail=512, seed_family=3):
     """Parallel sampling with a shared prompt: ``groups`` prompts of
     ``prompt_len`` tokens, ``samples`` samples each (refcount = samples on
     the prompt's blocks), 32/8 heads, D 128, bf16.
@@ -446,17 +442,18 @@ def prefix_sharing(block_size=32, phase="fork", groups=8, samples=8,
                   hq=32, hkv=8, d=128, bs=bs, nb=nb, block_tables=tables,
                   seq_lens=lens, cached_lens=cached_for_live,
                   slot_mapping=slots, copy_pairs=pairs,
-                  live_extra=extra_live, partition_size=partition_size,
+                  live_extra=extra_live,
                   note=note), prompt_tables
 
 
 def long_context_fp8(num_seqs=8, seq_len=131072, block_size=64,
-                     partition_size=512, seed_family=4):
+                     seed_family=4):
     """Long-context split-K decode: 8 sequences of 131072 tokens, 32/8
     heads, D 128, bs 64; K/V cached as fp8 E4M3 with per-tensor scales
-    (max|live value| / 448), Q and the new rows bf16; partitions of 512
-    tokens.  Blocks are a random permutation of the used blocks plus one
-    poisoned spare for unused table columns."""
+    (max|live value| / 448), Q and the new rows bf16.  Blocks are a random
+    permutation of the used blocks plus one poisoned spare for unused table
+    columns.  (How each sequence is split for the log-sum-exp merge is the
+    kernel's choice, not part of the inputs.)"""
     rng = np.random.default_rng([SEED_BASE, seed_family])
     bs = block_size
     lens = np.full(num_seqs, seq_len, dtype=np.int64)
@@ -471,13 +468,11 @@ def long_context_fp8(num_seqs=8, seq_len=131072, block_size=64,
                   src_kind="bf16", hq=32, hkv=8, d=128, bs=bs, nb=nb,
                   block_tables=tables, seq_lens=lens, cached_lens=cached,
                   slot_mapping=slots, copy_pairs=np.zeros((0, 2)),
-                  partition_size=partition_size,
                   note=f"{used} used blocks + 1 spare")
 
 
 def custom_decode(*, seed, num_seqs, lens, hq, hkv, d, bs, q_kind, kv_kind,
-                  src_kind=None, spare_blocks=3, partition_size=0,
-                  num_new_per_seq=1):
+                  src_kind=None, spare_blocks=3, num_new_per_seq=1):
     """Small free-form decode step (fuzz/edge cases): lengths given, blocks
     from a random permutation with a few spare poisoned blocks."""
     rng = np.random.default_rng([SEED_BASE, 100, seed])
@@ -503,8 +498,7 @@ def custom_decode(*, seed, num_seqs, lens, hq, hkv, d, bs, q_kind, kv_kind,
     return _build(f"custom_{seed}", rng, q_kind=q_kind, kv_kind=kv_kind,
                   src_kind=src_kind, hq=hq, hkv=hkv, d=d, bs=bs, nb=nb,
                   block_tables=tables, seq_lens=lens, cached_lens=cached,
-                  slot_mapping=slots, copy_pairs=np.zeros((0, 2)),
-                  partition_size=partition_size)
+                  slot_mapping=slots, copy_pairs=np.zeros((0, 2)),)
 
 
 # ----------------------------------------------------------------------------

@@ -51,9 +51,9 @@ def max_abs_err(got, ref):
     return float(np.max(np.abs(got - ref))) if got.size else 0.0
 
 
-def check_attention(dev, w, pools, rows=None, tol=None, partition_size=None):
+def check_attention(dev, w, pools, rows=None, tol=None, max_waves=0):
     import torch
-    dev.attend(partition_size=partition_size)
+    dev.attend(max_waves=max_waves)
     torch.cuda.synchronize()
     out = dev.out.cpu().numpy()
     ref = oracle_out(w, pools, rows)

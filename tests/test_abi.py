@@ -35,7 +35,7 @@ def header_functions():
 def test_header_declares_the_boundary():
     names = header_functions()
     for n in ("cache_write_slots", "copy_blocks", "paged_attn_decode",
-              "paged_attn_workspace_size", "paged_attn_partition_size",
+              "paged_attn_workspace_size",
               "pkv_status_string"):
         assert n in names
     assert set(names) == set(ops.EXPORTED)
@@ -103,14 +103,14 @@ def test_copy_blocks_validation(lib):
 def pa(lib, **kw):
     a = dict(out=FAKE, q=FAKE, qd=BF16, kc=FAKE, vc=FAKE, cache=BF16, ks=None,
              vs=None, bt=FAKE, mb=256, sl=FAKE, maxlen=4096, S=32, hq=32,
-             hkv=8, d=128, nb=16384, bs=16, scale=0.088, P=0, ws=FAKE,
+             hkv=8, d=128, nb=16384, bs=16, scale=0.088, waves=0, ws=FAKE,
              wsb=1 << 30)
     a.update(kw)
     return lib.paged_attn_decode(a["out"], a["q"], a["qd"], a["kc"], a["vc"],
                                  a["cache"], a["ks"], a["vs"], a["bt"], a["mb"],
                                  a["sl"], a["maxlen"], a["S"], a["hq"],
                                  a["hkv"], a["d"], a["nb"], a["bs"], a["scale"],
-                                 a["P"], a["ws"], a["wsb"], None)
+                                 a["waves"], a["ws"], a["wsb"], None)
 
 
 def test_attention_validation(lib):
@@ -120,34 +120,32 @@ def test_attention_validation(lib):
     assert pa(lib, qd=BF16, cache=FP8) == NULL          # scales required
     assert pa(lib, hq=30, hkv=8) == SHAPE               # not a multiple
     assert pa(lib, d=256) == UNSUP
-    assert pa(lib, P=48) == SHAPE                       # not a multiple of 32
+    assert pa(lib, waves=-1) == SHAPE                   # negative wave cap
+    assert pa(lib, S=8193, sl=FAKE, mb=256) == UNSUP    # too many sequences
+    assert pa(lib, S=1, maxlen=64, ws=None) == WS       # workspace always needed
     assert pa(lib, mb=255) == SHAPE                     # table too short
+    assert pa(lib, maxlen=-1) == SHAPE
     assert pa(lib, out=None) == NULL
     assert pa(lib, sl=None) == NULL
     assert pa(lib, q=MISALIGNED) == ALIGN
     assert pa(lib, ws=None) == WS
     assert pa(lib, wsb=1024) == WS
-    # one partition only: no workspace needed, none checked
-    assert lib.paged_attn_workspace_size(4, 8, 8, 128, 64, 64) == 0
+    assert pa(lib, ws=ctypes.c_void_p(4096 + 16)) == ALIGN   # 256-byte aligned
+    # too many sequences for one call
+    assert lib.paged_attn_workspace_size(8193, 8, 8, 128) == \
+        ctypes.c_size_t(-1).value
 
 
-def test_partition_choice_and_workspace_size(lib):
-    # explicit sizes are taken as given
-    assert ops.paged_attn_partition_size(8, 32, 8, 131072, 512) == 512
-    # automatic sizes are multiples of 128 within 128..512
-    for args in [(32, 32, 8, 4096), (256, 64, 8, 8192), (1, 1, 1, 22),
-                 (64, 32, 8, 2561)]:
-        p = ops.paged_attn_partition_size(*args, 0)
-        assert p % 128 == 0 and 128 <= p <= 512
-    # the largest explicit partition is 4096 tokens
-    assert ops.paged_attn_partition_size(8, 32, 8, 131072, 4096) == 4096
+def test_workspace_size(lib):
+    # tile prefix + two partial slots of min(16, G) heads per wave (4096)
+    S, hq, hkv, d = 8, 32, 8, 128
+    ws = ops.paged_attn_workspace_size(S, hq, hkv, d)
+    slots = 4096 * 2 * 4
+    assert ws >= slots * (d + 2) * 4
+    assert ws <= slots * (d + 2) * 4 + 4 * 256 + (S + 1) * 4 + 4097 * 4
+    # 48 query heads per kv head: 16 per slot
+    assert ops.paged_attn_workspace_size(1, 48, 1, 64) >= 4096 * 2 * 16 * 66 * 4
     with pytest.raises(ops.PagedKVError):
-        ops.paged_attn_partition_size(8, 32, 8, 131072, 4096 + 32)
-    # workspace = (m, l, o) rows for every partition slot (+ alignment)
-    S, hq, hkv, d, L, P = 8, 32, 8, 128, 131072, 512
-    rows = S * hq * (L // P)
-    ws = ops.paged_attn_workspace_size(S, hq, hkv, d, L, P)
-    assert ws >= rows * (d + 2) * 4
-    assert ws <= rows * (d + 2) * 4 + 1024
+        ops.paged_attn_workspace_size(S, 30, hkv, d)
     with pytest.raises(ops.PagedKVError):
-        ops.paged_attn_workspace_size(S, 30, hkv, d, L, P)
+        ops.paged_attn_workspace_size(8193, 32, 8, 128)
