@@ -54,6 +54,7 @@ namespace pkv {
 
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
+constexpr int kWorkgroupsPerCU = 1;       // default grid: one workgroup per CU
 constexpr uint32_t kRawBufferFlags = 0x00020000;  // dword3: 32-bit data format
 
 template <typename QT, typename CT> struct PvOperand { typedef CT type; };
@@ -85,17 +86,23 @@ template <typename QT, typename CT, int D> struct Shape {
   static constexpr int VCH = EP * PVB / 16;           // LDS chunks per piece
   static constexpr int QWORDS = D / 4 * QT::bytes / 4;
   static constexpr int NBLK = D / 16;                 // 16-wide output blocks
-  static constexpr int STAGE_BYTES = 32 * LDS_ROW;    // V tile, one wave
+  static constexpr int STAGE_BYTES = 32 * LDS_ROW;    // V sub-tile, one wave
+  // A tile -- the unit of the split and of each load request -- is SUB
+  // 32-token sub-tiles (the MFMA tile).  One sub-tile per request measured
+  // fastest: larger requests deepen the memory queues and push the loop's
+  // registers into spills without adding bandwidth.
+  static constexpr int SUB = 1;
+  static constexpr int TT = 32 * SUB;                 // tokens per tile
   static_assert(NV >= 1 && KPIECES >= 1, "head_dim too small");
   static_assert(LDS_ROW / 16 >= 4 * PVB, "swizzle needs 4 distinct spans");
   static_assert(16 % TOK_PER_V == 0, "a V load must not straddle halves");
 };
 
-// One tile's raw K and V bytes as loaded from the pool.
+// One tile's raw K and V bytes as loaded from the pool, per sub-tile.
 template <typename QT, typename CT, int D> struct TileRegs {
   typedef Shape<QT, CT, D> S;
-  uint32_t kw[2][S::KWORDS];
-  u32x4_t vraw[S::NV];
+  uint32_t kw[S::SUB][2][S::KWORDS];
+  u32x4_t vraw[S::SUB][S::NV];
 };
 
 // Online-softmax state of one wave: running max (log2 domain) and this
@@ -122,58 +129,61 @@ __device__ __forceinline__ void load_tile_uniform(
   typedef Shape<QT, CT, D> S;
   const int c = lane & 15;
   const int j = lane >> 4;
-  // Everything addressing the half-tile is wave-uniform; readfirstlane says
-  // so to the compiler, which keeps it in SGPRs (scalar table loads, buffer
-  // resources in SGPRs) instead of looping over lanes.
+  // Everything addressing a half-tile is wave-uniform; readfirstlane says
+  // so to the compiler, which keeps it in SGPRs (buffer resources in SGPRs)
+  // instead of looping over lanes.
   t0 = __builtin_amdgcn_readfirstlane(t0);
-  __amdgpu_buffer_rsrc_t kr[2], vr[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int tb = t0 + 16 * hh;
-    int nvalid = t_end - tb;
-    nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
-    int64_t row0 = 0;
-    if (nvalid > 0) {
-      const int lb = tb / bs;
-      const int idx = lb - wb;  // 0 .. 127
-      int phys;
-      if (idx < 64)  // (tab_b may still be in flight: touch it only if needed)
-        phys = __builtin_amdgcn_readlane(tab_a, idx);
-      else
-        phys = __builtin_amdgcn_readlane(tab_b, idx - 64);
-      row0 = (int64_t)phys * bs + (tb - lb * bs);
-    }
-    // (the clamp above may be selected as a vector min/max)
-    const int nrec = __builtin_amdgcn_readfirstlane(nvalid * (int)stride);
-    kr[hh] = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(kbase + row0 * stride), (short)0, nrec,
-        kRawBufferFlags);
-    vr[hh] = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(vbase + row0 * stride), (short)0, nrec,
-        kRawBufferFlags);
-  }
   const int kofs = c * (int)stride + j * 16;
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-    for (int r = 0; r < S::KPIECES; ++r) {
-      const u32x4_t v =
-          __builtin_amdgcn_raw_buffer_load_b128(kr[hh], kofs + r * 64, 0, 0);
-      tr.kw[hh][4 * r + 0] = v[0];
-      tr.kw[hh][4 * r + 1] = v[1];
-      tr.kw[hh][4 * r + 2] = v[2];
-      tr.kw[hh][4 * r + 3] = v[3];
-    }
-  }
   const int vtok = lane / S::PPR;
   const int vofs = vtok * (int)stride + (lane % S::PPR) * 16;
 #pragma unroll
-  for (int v = 0; v < S::NV; ++v) {
-    const int hh = (v * S::TOK_PER_V) >> 4;
-    const int tin = (v * S::TOK_PER_V) & 15;
-    // the whole offset goes in the per-lane operand: the range check covers it
-    tr.vraw[v] = __builtin_amdgcn_raw_buffer_load_b128(
-        vr[hh], vofs + tin * (int)stride, 0, 0);
+  for (int sb = 0; sb < S::SUB; ++sb) {
+    __amdgpu_buffer_rsrc_t kr[2], vr[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int tb = t0 + 32 * sb + 16 * hh;
+      int nvalid = t_end - tb;
+      nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
+      int64_t row0 = 0;
+      if (nvalid > 0) {
+        const int lb = tb / bs;
+        const int idx = lb - wb;  // 0 .. 127
+        int phys;
+        if (idx < 64)  // (tab_b may still be in flight: touch it only if needed)
+          phys = __builtin_amdgcn_readlane(tab_a, idx);
+        else
+          phys = __builtin_amdgcn_readlane(tab_b, idx - 64);
+        row0 = (int64_t)phys * bs + (tb - lb * bs);
+      }
+      // (the clamp above may be selected as a vector min/max)
+      const int nrec = __builtin_amdgcn_readfirstlane(nvalid * (int)stride);
+      kr[hh] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(kbase + row0 * stride), (short)0, nrec,
+          kRawBufferFlags);
+      vr[hh] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(vbase + row0 * stride), (short)0, nrec,
+          kRawBufferFlags);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int r = 0; r < S::KPIECES; ++r) {
+        const u32x4_t v =
+            __builtin_amdgcn_raw_buffer_load_b128(kr[hh], kofs + r * 64, 0, 0);
+        tr.kw[sb][hh][4 * r + 0] = v[0];
+        tr.kw[sb][hh][4 * r + 1] = v[1];
+        tr.kw[sb][hh][4 * r + 2] = v[2];
+        tr.kw[sb][hh][4 * r + 3] = v[3];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < S::NV; ++v) {
+      const int hh = (v * S::TOK_PER_V) >> 4;
+      const int tin = (v * S::TOK_PER_V) & 15;
+      // the whole offset goes in the per-lane operand: the range check covers it
+      tr.vraw[sb][v] = __builtin_amdgcn_raw_buffer_load_b128(
+          vr[hh], vofs + tin * (int)stride, 0, 0);
+    }
   }
 }
 
@@ -187,35 +197,39 @@ __device__ __forceinline__ void load_tile_any(
   typedef Shape<QT, CT, D> S;
   const int c = lane & 15;
   const int j = lane >> 4;
-  const int tok = t0 + (lane & 31);
-  int myslot = 0;
-  if (tok < t_end) {
-    const int lb = tok / bs;
-    myslot = trow[lb] * bs + (tok - lb * bs);
-  }
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int ks = __shfl(myslot, 16 * hh + c, 64);
-    const bool ok = t0 + 16 * hh + c < t_end;
-    const uint8_t* row = kbase + (int64_t)ks * stride;
-#pragma unroll
-    for (int r = 0; r < S::KPIECES; ++r) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const u32x4_t*>(row + (4 * r + j) * 16);
-      tr.kw[hh][4 * r + 0] = v[0];
-      tr.kw[hh][4 * r + 1] = v[1];
-      tr.kw[hh][4 * r + 2] = v[2];
-      tr.kw[hh][4 * r + 3] = v[3];
+  for (int sb = 0; sb < S::SUB; ++sb) {
+    const int ts = t0 + 32 * sb;
+    const int tok = ts + (lane & 31);
+    int myslot = 0;
+    if (tok < t_end) {
+      const int lb = tok / bs;
+      myslot = trow[lb] * bs + (tok - lb * bs);
     }
-  }
 #pragma unroll
-  for (int v = 0; v < S::NV; ++v) {
-    const int tv = lane / S::PPR + v * S::TOK_PER_V;
-    const int vs = __shfl(myslot, tv, 64);
-    tr.vraw[v] = u32x4_t{0u, 0u, 0u, 0u};
-    if (t0 + tv < t_end)
-      tr.vraw[v] = *reinterpret_cast<const u32x4_t*>(
-          vbase + (int64_t)vs * stride + (lane % S::PPR) * 16);
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ks = __shfl(myslot, 16 * hh + c, 64);
+      const bool ok = ts + 16 * hh + c < t_end;
+      const uint8_t* row = kbase + (int64_t)ks * stride;
+#pragma unroll
+      for (int r = 0; r < S::KPIECES; ++r) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (ok) v = *reinterpret_cast<const u32x4_t*>(row + (4 * r + j) * 16);
+        tr.kw[sb][hh][4 * r + 0] = v[0];
+        tr.kw[sb][hh][4 * r + 1] = v[1];
+        tr.kw[sb][hh][4 * r + 2] = v[2];
+        tr.kw[sb][hh][4 * r + 3] = v[3];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < S::NV; ++v) {
+      const int tv = lane / S::PPR + v * S::TOK_PER_V;
+      const int vs = __shfl(myslot, tv, 64);
+      tr.vraw[sb][v] = u32x4_t{0u, 0u, 0u, 0u};
+      if (ts + tv < t_end)
+        tr.vraw[sb][v] = *reinterpret_cast<const u32x4_t*>(
+            vbase + (int64_t)vs * stride + (lane % S::PPR) * 16);
+    }
   }
 }
 
@@ -401,15 +415,21 @@ __device__ __forceinline__ void compute_tile(
 // The split of the tile list.  tex[s] (s = 0 .. num_seqs) is the exclusive
 // prefix of the per-sequence tile counts ceil(L_s / 32); row (s, u), u =
 // kv_head * chunks + chunk, holds tiles [U tex[s] + u T_s, + T_s) of the
-// T = U tex[num_seqs] tiles, T_s = tex[s + 1] - tex[s].  Wave w of W owns
-// tiles [ceil(w T / W), ceil((w + 1) T / W)): tile t belongs to wave
-// floor(t W / T).
+// T = U tex[num_seqs] tiles, T_s = tex[s + 1] - tex[s].  With V = min(W, T)
+// of the W waves in use, wave w < V owns tiles [ceil(w T / V),
+// ceil((w + 1) T / V)) -- at least one -- and the waves from V on own none,
+// so the waves holding pieces of one row are consecutive and all hold one.
+// Tile t belongs to wave floor(t V / T).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int waves_in_use(int64_t T, int W) {
+  return T < W ? (int)T : W;
+}
 __device__ __forceinline__ int wave_of_tile(int64_t t, int64_t T, int W) {
-  return (int)(t * W / T);
+  return (int)(t * waves_in_use(T, W) / T);
 }
 __device__ __forceinline__ int64_t first_tile_of_wave(int w, int64_t T, int W) {
-  return ((int64_t)w * T + W - 1) / W;
+  const int V = waves_in_use(T, W);
+  return w >= V ? T : ((int64_t)w * T + V - 1) / V;
 }
 
 // Partial slot of (wave w, slot q): o [gmax][D], then m [gmax], l [gmax] in
@@ -419,70 +439,52 @@ __device__ __forceinline__ int64_t slot_index(int w, int q) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the pieces of one cut row: one workgroup per row (s, u).  A wave
-// per query head first folds the pieces' (m, l) pairs into (M, sum 2^(m-M) l)
-// with every lane on its own pieces; then every thread takes 4 output columns
-// of one head and a strided subset of the pieces (independent loads, four at
-// a time), and the subsets are summed through LDS.  Waves of the partition
-// kernel that own no tile (more waves than tiles) wrote nothing; their slots
-// are skipped with selects, so stale values never enter the sums.
+// Merge of the pieces of one cut row: one workgroup per row (s, u).  Every
+// thread takes 4 output columns of one query head and a strided subset of the
+// pieces, loads each piece's (m, l, o) independently (four pieces at a time)
+// and folds them online:  M = max m_i, l = sum 2^(m_i - M) l_i,
+// acc = sum 2^(m_i - M) o_i; the subsets are folded the same way through LDS.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void lse_fold(float& m, float& l, float m2, float l2) {
+__device__ __forceinline__ void lse_fold(float& m, float& l, f32x4_t& acc,
+                                         float m2, float l2, f32x4_t acc2) {
   const float M = fmaxf(m, m2);
   if (M == -INFINITY) return;  // both empty
-  l = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
+  const float a1 = fast_exp2(m - M), a2 = fast_exp2(m2 - M);
+  l = l * a1 + l2 * a2;
+  acc = acc * a1 + acc2 * a2;
   m = M;
 }
 
 template <int D, bool SCALED>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
   constexpr int D4 = D / 4;
-  __shared__ __attribute__((aligned(16))) float red[kThreads * 4];
-  __shared__ float sm_stat[16][2];
+  __shared__ __attribute__((aligned(16))) f32x4_t red_o[kThreads];
+  __shared__ float red_m[kThreads], red_l[kThreads];
 
   const int tid = threadIdx.x;
   const int U = a.num_kv_heads * a.group_chunks;
   const int s = blockIdx.x / U;
   const int u = blockIdx.x - s * U;
   const int* tex = a.tile_prefix;
-  const int* wfirst = a.wave_first;
   const int ts = tex[s + 1] - tex[s];
   if (ts == 0) return;  // zeros written by the partition kernel
   const int64_t T = (int64_t)U * tex[a.num_seqs];
   const int W = a.num_waves;
-  const int r0 = U * tex[s] + u * ts;
+  const int64_t r0 = (int64_t)U * tex[s] + (int64_t)u * ts;
   const int wf = wave_of_tile(r0, T, W);
   const int wl = wave_of_tile(r0 + ts - 1, T, W);
   if (wf == wl) return;  // finished by one wave
   const int npieces = wl - wf + 1;
-  const int q_first = wfirst[wf] < r0 ? 1 : 0;
+  const int q_first = first_tile_of_wave(wf, T, W) < r0 ? 1 : 0;
 
   const int h = u / a.group_chunks;
   const int gc = u - h * a.group_chunks;
   const int gcount = min(16, a.group - gc * 16);
   const int gmax = a.slot_heads;
   const int64_t head0 = (int64_t)s * a.num_q_heads + h * a.group + gc * 16;
-  // piece i: slot of wave wf + i; present unless that wave owns no tile
-  auto slot_of = [&](int i) { return slot_index(wf + i, i == 0 ? q_first : 0); };
-  auto present = [&](int i) { return i == 0 || wfirst[wf + i] < wfirst[wf + i + 1]; };
-
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int g = wave; g < gcount; g += kWaves) {
-    float m = -INFINITY, l = 0.f;
-    for (int i = lane; i < npieces; i += 64) {
-      const int64_t sl = slot_of(i) * gmax + g;
-      const float mi = a.part_m[sl], li = a.part_l[sl];
-      if (present(i)) lse_fold(m, l, mi, li);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-      lse_fold(m, l, __shfl_xor(m, o, 64), __shfl_xor(l, o, 64));
-    if (lane == 0) {
-      sm_stat[g][0] = m;
-      sm_stat[g][1] = l;
-    }
-  }
-  __syncthreads();
+  auto slot_of = [&](int i) {
+    return slot_index(wf + i, i == 0 ? q_first : 0);
+  };
 
   const int items = gcount * D4;
   const int nsub = items >= kThreads ? 1 : kThreads / items;
@@ -491,38 +493,34 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
     const int sub = it / items;
     const int g = item / D4;
     const int d4 = item - g * D4;
-    const float M = sm_stat[g][0];
+    float m = -INFINITY, l = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     int i = sub;
     for (; i + 3 * nsub < npieces; i += 4 * nsub) {
-      float mi[4];
+      float mi[4], li[4];
       f32x4_t oi[4];
-      bool pi[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int ii = i + k * nsub;
-        const int64_t sl = slot_of(ii) * gmax + g;
+        const int64_t sl = slot_of(i + k * nsub) * gmax + g;
         mi[k] = a.part_m[sl];
+        li[k] = a.part_l[sl];
         oi[k] = *reinterpret_cast<const f32x4_t*>(a.part_o + sl * D + 4 * d4);
-        pi[k] = present(ii);
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4_t t = fast_exp2(mi[k] - M) * oi[k];
-        acc += pi[k] ? t : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int k = 0; k < 4; ++k) lse_fold(m, l, acc, mi[k], li[k], oi[k]);
     }
     for (; i < npieces; i += nsub) {
       const int64_t sl = slot_of(i) * gmax + g;
-      const f32x4_t t = fast_exp2(a.part_m[sl] - M) *
-                        *reinterpret_cast<const f32x4_t*>(a.part_o + sl * D + 4 * d4);
-      acc += present(i) ? t : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      lse_fold(m, l, acc, a.part_m[sl], a.part_l[sl],
+               *reinterpret_cast<const f32x4_t*>(a.part_o + sl * D + 4 * d4));
     }
     if (nsub == 1) {
-      const float f = (SCALED ? *a.v_scale : 1.f) / sm_stat[g][1];
+      const float f = (SCALED ? *a.v_scale : 1.f) / l;
       *reinterpret_cast<f32x4_t*>(a.out + (head0 + g) * D + 4 * d4) = acc * f;
     } else {
-      *reinterpret_cast<f32x4_t*>(red + 4 * (sub * items + item)) = acc;
+      red_o[sub * items + item] = acc;
+      red_m[sub * items + item] = m;
+      red_l[sub * items + item] = l;
     }
   }
   if (nsub > 1) {
@@ -530,10 +528,12 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
     for (int item = tid; item < items; item += kThreads) {
       const int g = item / D4;
       const int d4 = item - g * D4;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      for (int sub = 0; sub < nsub; ++sub)
-        acc += *reinterpret_cast<const f32x4_t*>(red + 4 * (sub * items + item));
-      const float f = (SCALED ? *a.v_scale : 1.f) / sm_stat[g][1];
+      float m = red_m[item], l = red_l[item];
+      f32x4_t acc = red_o[item];
+      for (int sub = 1; sub < nsub; ++sub)
+        lse_fold(m, l, acc, red_m[sub * items + item], red_l[sub * items + item],
+                 red_o[sub * items + item]);
+      const float f = (SCALED ? *a.v_scale : 1.f) / l;
       *reinterpret_cast<f32x4_t*>(a.out + (head0 + g) * D + 4 * d4) = acc * f;
     }
   }
@@ -568,6 +568,7 @@ struct Seg {
 // The segment starting at tile t of the wave's range [.., te): the largest s
 // with tex[s] <= t / U (binary search in LDS; every lane runs it with the
 // same values), then the row and the tile within it.
+template <int TT>
 __device__ __forceinline__ Seg segment_at(int64_t t, int64_t te, int U,
                                           const int* tex, const int* lens,
                                           const AttnArgs& a) {
@@ -601,8 +602,8 @@ __device__ __forceinline__ Seg segment_at(int64_t t, int64_t te, int U,
   g.h = u / a.group_chunks;
   g.gc = u - g.h * a.group_chunks;
   g.ntiles = (int)(end - t);
-  g.t_begin = 32 * k0;
-  g.t_end = min(L, 32 * (k0 + g.ntiles));
+  g.t_begin = TT * k0;
+  g.t_end = min(L, TT * (k0 + g.ntiles));
   g.wb = g.t_begin / a.block_size;
   g.full = k0 == 0 && end == row_end;
   return g;
@@ -692,13 +693,13 @@ void attn_decode_kernel(AttnArgs a) {
     for (int i = b0; i < b1; ++i) {
       const int L = a.seq_lens[i];
       lens[i] = L;
-      sum += (L + 31) / 32;
+      sum += (L + S::TT - 1) / S::TT;
     }
     const int incl = block_inclusive_scan(sum, sm_wsum);
     int run = incl - sum;
     for (int i = b0; i < b1; ++i) {
       tex[i] = run;
-      run += (lens[i] + 31) / 32;
+      run += (lens[i] + S::TT - 1) / S::TT;
     }
     if (tid == kThreads - 1) tex[nS] = incl;
   }
@@ -711,10 +712,6 @@ void attn_decode_kernel(AttnArgs a) {
   const int64_t T = (int64_t)U * tex[nS];
   const int64_t tb = first_tile_of_wave(w, T, W);
   const int64_t te = first_tile_of_wave(w + 1, T, W);
-  if (lane == 0) {  // the merge kernel reads the split from here
-    a.wave_first[w] = (int)tb;
-    if (w == W - 1) a.wave_first[W] = (int)T;
-  }
 
   float vscale = 1.f, kscale = 1.f;
   if constexpr (is_fp8<CT>::value) {
@@ -734,7 +731,9 @@ void attn_decode_kernel(AttnArgs a) {
     }
     for (int s = lo; s < nS; ++s) {
       const int64_t pos = (int64_t)U * __builtin_amdgcn_readfirstlane(tex[s]);
-      if (pos >= te && !(w == W - 1 && pos == T)) break;
+      if (pos >= te && !(w == waves_in_use(T, W) - 1 && pos == T) &&
+          !(T == 0 && w == 0))
+        break;
       if (__builtin_amdgcn_readfirstlane(lens[s]) != 0) continue;
       float* dst = a.out + (int64_t)s * a.num_q_heads * D;
       for (int i = lane; i < a.num_q_heads * D / 4; i += 64)
@@ -749,9 +748,9 @@ void attn_decode_kernel(AttnArgs a) {
   uint8_t* vt = smem + wave * S::STAGE_BYTES;
   const int gmax = a.slot_heads;
 
-  Seg X = segment_at(tb, te, U, tex, lens, a);
+  Seg X = segment_at<S::TT>(tb, te, U, tex, lens, a);
   int64_t pos_n = tb + X.ntiles;  // first tile of the next segment
-  Seg Xn = segment_at(pos_n, te, U, tex, lens, a);
+  Seg Xn = segment_at<S::TT>(pos_n, te, U, tex, lens, a);
   bool first_seg = true;
   uint32_t ta = 0, tbw = 0, ta_n = 0, tb_n = 0;
   if constexpr (UNIFORM) {
@@ -786,14 +785,15 @@ void attn_decode_kernel(AttnArgs a) {
       const uint8_t* vbase_n = vpool + (int64_t)Xn.h * S::ROW_BYTES;
       int wb = X.wb;
       for (int k = 0; k < X.ntiles; ++k) {
-        stage_v<QT, CT, D>(cur.vraw, vt, lane);
+        const int t0 = X.t_begin + S::TT * k;
+        stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
         // the next tile of this wave's stream: tile k + 1 of X, else the
         // first tile of the next segment (an empty range past the end);
         // requested before this tile is computed, which the scheduling
         // barrier keeps (the compiler would otherwise sink the loads to
         // shorten register lifetimes)
         const bool same_seg = k + 1 < X.ntiles;
-        const int t_next = X.t_begin + 32 * (k + 1);
+        const int t_next = t0 + S::TT;
         if (same_seg && t_next / a.block_size - wb >= 64) {
           // the window moves on by 64 blocks; the new upper half is needed
           // only 64 blocks later
@@ -811,14 +811,22 @@ void attn_decode_kernel(AttnArgs a) {
             same_seg ? t_next : Xn.t_begin, same_seg ? X.t_end : Xn.t_end,
             lane);
         __builtin_amdgcn_sched_barrier(0);
-        compute_tile<QT, CT, D>(cur.kw, qw, st, vt, X.t_begin + 32 * k,
-                                X.t_end, qk_mul, lane);
+        compute_tile<QT, CT, D>(cur.kw[0], qw, st, vt, t0, X.t_end, qk_mul,
+                                lane);
+#pragma unroll
+        for (int sb = 1; sb < S::SUB; ++sb) {
+          if (t0 + 32 * sb < X.t_end) {  // (only the last tile has empty ones)
+            stage_v<QT, CT, D>(cur.vraw[sb], vt, lane);
+            compute_tile<QT, CT, D>(cur.kw[sb], qw, st, vt, t0 + 32 * sb,
+                                    X.t_end, qk_mul, lane);
+          }
+        }
         cur = nxt;
       }
     } else {
       const int32_t* trow = a.block_tables + (int64_t)X.s * a.max_blocks_per_seq;
       for (int k = 0; k < X.ntiles; ++k) {
-        const int t0 = X.t_begin + 32 * k;
+        const int t0 = X.t_begin + S::TT * k;
         if constexpr (UNIFORM) {
           const int wb = X.wb + (t0 / a.block_size - X.wb) / 64 * 64;
           Seg shifted = X;
@@ -831,9 +839,14 @@ void attn_decode_kernel(AttnArgs a) {
           load_tile_any<QT, CT, D>(cur, a.block_size, trow, kbase, vbase,
                                    stride, t0, X.t_end, lane);
         }
-        stage_v<QT, CT, D>(cur.vraw, vt, lane);
-        compute_tile<QT, CT, D>(cur.kw, qw, st, vt, t0, X.t_end, qk_mul,
-                                lane);
+#pragma unroll
+        for (int sb = 0; sb < S::SUB; ++sb) {
+          if (t0 + 32 * sb < X.t_end) {
+            stage_v<QT, CT, D>(cur.vraw[sb], vt, lane);
+            compute_tile<QT, CT, D>(cur.kw[sb], qw, st, vt, t0 + 32 * sb,
+                                    X.t_end, qk_mul, lane);
+          }
+        }
       }
     }
 
@@ -875,7 +888,7 @@ void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int q = 0; q < S::QWORDS; ++q) qw[q] = qn[q];
     pos_n += X.ntiles;
-    Xn = segment_at(pos_n, te, U, tex, lens, a);
+    Xn = segment_at<S::TT>(pos_n, te, U, tex, lens, a);
     if constexpr (UNIFORM) {
       ta_n = load_window(Xn, 0, a, lane);
       tb_n = load_window(Xn, 1, a, lane);
@@ -898,7 +911,11 @@ static int resident_grid(K kernel, size_t dyn_lds, int max_waves) {
           &per_cu, reinterpret_cast<const void*>(kernel), kThreads, dyn_lds) !=
           hipSuccess)
     return -1;
-  int64_t g = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
+  // One workgroup (one wave per SIMD) per CU measured fastest for the
+  // streaming loop: more resident waves deepen the memory queues without
+  // adding bandwidth.
+  int64_t g = (int64_t)(per_cu < kWorkgroupsPerCU ? per_cu : kWorkgroupsPerCU) * cus;
+  if (g < cus) g = cus;
   int64_t cap = kMaxWaves / kWaves;
   if (max_waves > 0 && max_waves / kWaves < cap) cap = max_waves / kWaves;
   if (g > cap) g = cap;

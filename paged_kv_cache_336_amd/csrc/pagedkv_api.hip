@@ -27,14 +27,13 @@ struct AttnShape {
   int32_t group_chunks;
   int32_t slot_heads;
   size_t ws_bytes;
-  size_t off_w, off_m, off_l, off_o;
+  size_t off_m, off_l, off_o;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace: tile prefix [num_seqs + 1] int32 | first tile of each wave
-// [kMaxWaves + 1] int32 | part_m | part_l | part_o, each 256-byte aligned;
-// two partial slots of slot_heads query heads per wave.
+// Workspace: tile prefix [num_seqs + 1] int32 | part_m | part_l | part_o,
+// each 256-byte aligned; two partial slots of slot_heads query heads per wave.
 int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                int32_t head_dim, AttnShape* out) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1) return PKV_ERR_SHAPE;
@@ -46,8 +45,7 @@ int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   s.group_chunks = (s.group + 15) / 16;
   s.slot_heads = s.group < 16 ? s.group : 16;
   const size_t slots = (size_t)kMaxWaves * 2 * s.slot_heads;
-  s.off_w = align_up((size_t)(num_seqs + 1) * 4, 256);
-  s.off_m = align_up(s.off_w + (size_t)(kMaxWaves + 1) * 4, 256);
+  s.off_m = align_up((size_t)(num_seqs + 1) * 4, 256);
   s.off_l = align_up(s.off_m + slots * 4, 256);
   s.off_o = align_up(s.off_l + slots * 4, 256);
   s.ws_bytes = s.off_o + slots * (size_t)head_dim * 4;
@@ -184,7 +182,6 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
   a.seq_lens = seq_lens;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.tile_prefix = reinterpret_cast<int32_t*>(ws);
-  a.wave_first = reinterpret_cast<int32_t*>(ws + s.off_w);
   a.part_m = reinterpret_cast<float*>(ws + s.off_m);
   a.part_l = reinterpret_cast<float*>(ws + s.off_l);
   a.part_o = reinterpret_cast<float*>(ws + s.off_o);

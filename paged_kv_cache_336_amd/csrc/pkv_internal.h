@@ -30,7 +30,6 @@ struct AttnArgs {
   float* part_m;          // [kMaxWaves][2][slot_heads]      running max (log2)
   float* part_l;          // [kMaxWaves][2][slot_heads]      running sum
   int32_t* tile_prefix;   // [num_seqs + 1]  tiles of the sequences before s
-  int32_t* wave_first;    // [num_waves + 1] first tile of each wave (+ total)
   int32_t num_seqs;
   int32_t max_blocks_per_seq;
   int32_t num_q_heads;
