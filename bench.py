@@ -127,6 +127,22 @@ def timed_region(torch, clock, enqueue, host_ms_estimate):
     return start.elapsed_time(stop), host_ms
 
 
+def copy_calibration(nbytes):
+    """Three plain device-to-device copies of nbytes each: under rocprofv3
+    --pmc their FETCH_SIZE / WRITE_SIZE readings against the known byte count
+    give the factor that turns those counters into bytes."""
+    import torch
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": nbytes,
+                                           "bytes_written": nbytes,
+                                           "copies": 3}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +157,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(
         ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    metavar="BYTES", help="only run plain copies of BYTES "
+                    "(byte-counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -148,6 +167,10 @@ def main():
               f"{args.gpus}); the multi-GPU split is a design note, not a "
               "measured path", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     from paged_kv_cache_336_amd import ops
@@ -188,18 +211,13 @@ def main():
                                           host_step_ms * K)
     ms_step = step_ms_total / K
 
-    # ---- the attention call alone, one event pair per call ----
-    evs = [(torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-
+    # ---- the attention call alone: K calls back to back between one event
+    # pair on the stream the kernels run on (torch's current stream) ----
     def run_attn():
-        for i, (a, b) in enumerate(evs):
-            a.record()
+        for i in range(K):
             dev.attend(i % R, max_waves=args.max_waves)
-            b.record()
-    timed_region(torch, clock, run_attn, host_step_ms * K)
-    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    attn_avg_ms = float(attn_ms.mean())
+    attn_total, _ = timed_region(torch, clock, run_attn, host_step_ms * K)
+    attn_avg_ms = attn_total / K
 
     # ---- the cache write alone (for the report) ----
     def run_write():

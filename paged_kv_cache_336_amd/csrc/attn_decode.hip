@@ -17,9 +17,9 @@
 // and waves never wait for one another while streaming.
 //
 // Per 32-token tile (one wave):
-//   * When bs % 16 == 0 each wave holds the partition's block-table window in
-//     one VGPR and reads one entry per 16-token half-tile with a wave-uniform
-//     readlane.  The half-tile's base address then lives in SGPRs as a
+//   * When bs % 16 == 0 each wave holds a 128-entry window of its row's
+//     block table in two VGPRs and reads one entry per 16-token half-tile
+//     with a wave-uniform readlane.  The half-tile's base address then lives in SGPRs as a
 //     buffer resource whose size covers exactly the live rows, so rows past
 //     the end of the sequence are neither fetched nor need a branch, and the
 //     next tile's rows are requested before the current one is computed.
@@ -30,9 +30,10 @@
 //   * Scores are scaled into the log2 domain; the running max uses xor
 //     shuffles across the 4 lanes that hold one query head's column.
 //   * V rows are loaded as 16-byte pieces, converted to the PV operand type
-//     and staged in the wave's own LDS slice (XOR-swizzled 16-byte chunks),
-//     then read back transposed as the A operand of O^T += V^T . P^T, so P
-//     never leaves the registers the QK product left it in.  For bf16/f16
+//     and staged in the wave's own LDS slice (32-byte spans permuted per
+//     token), then read back with gfx950's transposing LDS read as the A
+//     operand of O^T += V^T . P^T, so P never leaves the registers the QK
+//     product left it in.  For bf16/f16
 //     caches P is split into a high and a low part (two MFMAs), which keeps
 //     the weights exact to ~2^-16 relative.
 //
@@ -87,6 +88,7 @@ template <typename QT, typename CT, int D> struct Shape {
   static constexpr int QWORDS = D / 4 * QT::bytes / 4;
   static constexpr int NBLK = D / 16;                 // 16-wide output blocks
   static constexpr int STAGE_BYTES = 32 * LDS_ROW;    // V sub-tile, one wave
+  static constexpr int SPANS = LDS_ROW / 32;          // 32-byte spans per row
   // A tile -- the unit of the split and of each load request -- is SUB
   // 32-token sub-tiles (the MFMA tile).  One sub-tile per request measured
   // fastest: larger requests deepen the memory queues and push the loop's
@@ -251,20 +253,29 @@ __device__ __forceinline__ void stage_v(const u32x4_t (&vraw)[Shape<QT, CT, D>::
     const int swz = ((tv >> 2) & 3) * PVB;
     uint8_t* rowp = vt + tv * S::LDS_ROW;
     const int ch0 = (lane % S::PPR) * S::VCH;
-    if constexpr (same<PVT, CT>::value) {
+    if constexpr (PVB == 2) {
+      // 16-bit rows: 32-byte spans (16 columns, one output block) permuted
+      // by token, so the 8 rows one transposing read touches per pass land
+      // on distinct banks
+      const int span = (ch0 >> 1) ^ (tv & (S::SPANS - 1));
+      uint8_t* dst = rowp + (span << 5) + ((ch0 & 1) << 4);
+      if constexpr (same<PVT, CT>::value) {
+        *reinterpret_cast<u32x4_t*>(dst) = vraw[v];
+      } else {  // fp8 -> f16: the piece's 16 elements fill the whole span
+        u32x4_t lo, hi;
+        lo[0] = fp8x2_to_f16x2(vraw[v][0], false);
+        lo[1] = fp8x2_to_f16x2(vraw[v][0], true);
+        lo[2] = fp8x2_to_f16x2(vraw[v][1], false);
+        lo[3] = fp8x2_to_f16x2(vraw[v][1], true);
+        hi[0] = fp8x2_to_f16x2(vraw[v][2], false);
+        hi[1] = fp8x2_to_f16x2(vraw[v][2], true);
+        hi[2] = fp8x2_to_f16x2(vraw[v][3], false);
+        hi[3] = fp8x2_to_f16x2(vraw[v][3], true);
+        *reinterpret_cast<u32x4_t*>(dst) = lo;
+        *reinterpret_cast<u32x4_t*>(dst + 16) = hi;
+      }
+    } else if constexpr (same<PVT, CT>::value) {
       *reinterpret_cast<u32x4_t*>(rowp + ((ch0 ^ swz) << 4)) = vraw[v];
-    } else if constexpr (PVB == 2) {  // fp8 -> f16, two chunks
-      u32x4_t lo, hi;
-      lo[0] = fp8x2_to_f16x2(vraw[v][0], false);
-      lo[1] = fp8x2_to_f16x2(vraw[v][0], true);
-      lo[2] = fp8x2_to_f16x2(vraw[v][1], false);
-      lo[3] = fp8x2_to_f16x2(vraw[v][1], true);
-      hi[0] = fp8x2_to_f16x2(vraw[v][2], false);
-      hi[1] = fp8x2_to_f16x2(vraw[v][2], true);
-      hi[2] = fp8x2_to_f16x2(vraw[v][3], false);
-      hi[3] = fp8x2_to_f16x2(vraw[v][3], true);
-      *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 0) ^ swz) << 4)) = lo;
-      *reinterpret_cast<u32x4_t*>(rowp + (((ch0 + 1) ^ swz) << 4)) = hi;
     } else {  // fp8 -> f32, four chunks
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -386,22 +397,25 @@ __device__ __forceinline__ void compute_tile(
 #pragma unroll
     for (int e = 0; e < 8; ++e) pb_hi[e] = pv[e];
   }
-  const int swz_j = j * PVB;
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) {
-    const int byte = (16 * n + c) * PVB;
-    const int col = (((byte >> 4) ^ swz_j) << 4) + (byte & 15);
     typename Mma<PVT>::operand va;
     if constexpr (PVB == 2) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t e0 = *reinterpret_cast<const uint16_t*>(
-            vt + slot_token(j, 2 * w) * S::LDS_ROW + col);
-        const uint32_t e1 = *reinterpret_cast<const uint16_t*>(
-            vt + slot_token(j, 2 * w + 1) * S::LDS_ROW + col);
-        va[w] = e0 | (e1 << 16);
-      }
+      // Transposing LDS reads: within each 16-lane group, lane 4k + q
+      // addresses 4 columns (4q .. 4q + 3 of output block n) of token
+      // 4j + k, and lane c receives column c of the four tokens 4j .. 4j+3
+      // -- operand slots 0-3; the same read 16 tokens on gives slots 4-7.
+      const int tk = 4 * j + (c >> 2);
+      const int off = ((n ^ (tk & (S::SPANS - 1))) << 5) + ((c & 3) << 3);
+      const v4i16_t lo = lds_read_tr16(vt + tk * S::LDS_ROW + off);
+      const v4i16_t hi = lds_read_tr16(vt + (tk + 16) * S::LDS_ROW + off);
+      va[0] = pack_u16x2(lo[0], lo[1]);
+      va[1] = pack_u16x2(lo[2], lo[3]);
+      va[2] = pack_u16x2(hi[0], hi[1]);
+      va[3] = pack_u16x2(hi[2], hi[3]);
     } else {
+      const int byte = (16 * n + c) * PVB;
+      const int col = (((byte >> 4) ^ (j * PVB)) << 4) + (byte & 15);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         va[e] = *reinterpret_cast<const float*>(vt + slot_token(j, e) * S::LDS_ROW + col);

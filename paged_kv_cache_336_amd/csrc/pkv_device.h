@@ -14,6 +14,20 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(4))) short v4i16_t;
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte pieces addressed by
+// lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group, in that
+// order.  The address must be 8-byte aligned and point into LDS.
+__device__ __forceinline__ v4i16_t lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(p));
+}
+
+__device__ __forceinline__ uint32_t pack_u16x2(short lo, short hi) {
+  return (uint32_t)(uint16_t)lo | ((uint32_t)(uint16_t)hi << 16);
+}
 
 // Storage element tags (the byte layout of one cache or query element).
 struct F32 { typedef float scalar; static constexpr int bytes = 4; };
