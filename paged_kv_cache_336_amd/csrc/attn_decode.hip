@@ -455,10 +455,24 @@ __device__ __forceinline__ int64_t slot_index(int w, int q) {
 // ---------------------------------------------------------------------------
 // Merge of the pieces of one cut row: one workgroup per row (s, u).  Every
 // thread takes 4 output columns of one query head and a strided subset of the
-// pieces, loads each piece's (m, l, o) independently (four pieces at a time)
-// and folds them online:  M = max m_i, l = sum 2^(m_i - M) l_i,
-// acc = sum 2^(m_i - M) o_i; the subsets are folded the same way through LDS.
+// pieces (nsub threads share an output column), requests the (m, l, o) of up
+// to BATCH of its pieces at once, and folds them online:  M = max m_i,
+// l = sum 2^(m_i - M) l_i, acc = sum 2^(m_i - M) o_i; the subsets are then
+// folded the same way through LDS.  A row of G <= 4 query heads at head_dim
+// 128 has 2 threads per column, so with BATCH 16 up to 32 pieces take one
+// round of loads.  (Workgroups are kept small: most rows of a large batch
+// are not cut, and their workgroups only launch and exit.)
 // ---------------------------------------------------------------------------
+constexpr int kMergeThreads = 256;
+
+// base[byte_off] with a 32-bit offset, so the load can keep the base in
+// scalar registers.
+template <typename T>
+__device__ __forceinline__ T load_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const T*>(static_cast<const uint8_t*>(base) +
+                                     byte_off);
+}
+
 __device__ __forceinline__ void lse_fold(float& m, float& l, f32x4_t& acc,
                                          float m2, float l2, f32x4_t acc2) {
   const float M = fmaxf(m, m2);
@@ -469,11 +483,11 @@ __device__ __forceinline__ void lse_fold(float& m, float& l, f32x4_t& acc,
   m = M;
 }
 
-template <int D, bool SCALED>
-__global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
+template <int D, bool SCALED, int BATCH>
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   constexpr int D4 = D / 4;
-  __shared__ __attribute__((aligned(16))) f32x4_t red_o[kThreads];
-  __shared__ float red_m[kThreads], red_l[kThreads];
+  __shared__ __attribute__((aligned(16))) f32x4_t red_o[kMergeThreads];
+  __shared__ float red_m[kMergeThreads], red_l[kMergeThreads];
 
   const int tid = threadIdx.x;
   const int U = a.num_kv_heads * a.group_chunks;
@@ -496,50 +510,52 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
   const int gcount = min(16, a.group - gc * 16);
   const int gmax = a.slot_heads;
   const int64_t head0 = (int64_t)s * a.num_q_heads + h * a.group + gc * 16;
-  auto slot_of = [&](int i) {
-    return slot_index(wf + i, i == 0 ? q_first : 0);
-  };
 
   const int items = gcount * D4;
-  const int nsub = items >= kThreads ? 1 : kThreads / items;
-  for (int it = tid; it < items * nsub; it += kThreads) {
+  const int nsub = items >= kMergeThreads ? 1 : kMergeThreads / items;
+  for (int it = tid; it < items * nsub; it += kMergeThreads) {
     const int item = it % items;
     const int sub = it / items;
     const int g = item / D4;
     const int d4 = item - g * D4;
     float m = -INFINITY, l = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    int i = sub;
-    for (; i + 3 * nsub < npieces; i += 4 * nsub) {
-      float mi[4], li[4];
-      f32x4_t oi[4];
+    // slot of piece i: slot_index(wf + i, i == 0 ? q_first : 0) * gmax + g,
+    // as a 32-bit offset (slots * head_dim < 2^24)
+    const uint32_t sl0 = (uint32_t)(slot_index(wf, 0) * gmax + g);
+    const uint32_t step = 2u * (uint32_t)gmax;
+    for (int i0 = sub; i0 < npieces; i0 += BATCH * nsub) {
+      float mi[BATCH], li[BATCH];
+      f32x4_t oi[BATCH];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int64_t sl = slot_of(i + k * nsub) * gmax + g;
-        mi[k] = a.part_m[sl];
-        li[k] = a.part_l[sl];
-        oi[k] = *reinterpret_cast<const f32x4_t*>(a.part_o + sl * D + 4 * d4);
+      for (int k = 0; k < BATCH; ++k) {
+        const int i = i0 + k * nsub;
+        mi[k] = -INFINITY;
+        li[k] = 0.f;
+        oi[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (i < npieces) {
+          const uint32_t sl = sl0 + step * (uint32_t)i +
+                              (i == 0 ? (uint32_t)(q_first * gmax) : 0u);
+          mi[k] = load_at<float>(a.part_m, sl * 4u);
+          li[k] = load_at<float>(a.part_l, sl * 4u);
+          oi[k] = load_at<f32x4_t>(a.part_o, (sl * (uint32_t)D + 4u * d4) * 4u);
+        }
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) lse_fold(m, l, acc, mi[k], li[k], oi[k]);
-    }
-    for (; i < npieces; i += nsub) {
-      const int64_t sl = slot_of(i) * gmax + g;
-      lse_fold(m, l, acc, a.part_m[sl], a.part_l[sl],
-               *reinterpret_cast<const f32x4_t*>(a.part_o + sl * D + 4 * d4));
+      for (int k = 0; k < BATCH; ++k) lse_fold(m, l, acc, mi[k], li[k], oi[k]);
     }
     if (nsub == 1) {
       const float f = (SCALED ? *a.v_scale : 1.f) / l;
       *reinterpret_cast<f32x4_t*>(a.out + (head0 + g) * D + 4 * d4) = acc * f;
     } else {
-      red_o[sub * items + item] = acc;
-      red_m[sub * items + item] = m;
-      red_l[sub * items + item] = l;
+      red_o[it] = acc;
+      red_m[it] = m;
+      red_l[it] = l;
     }
   }
   if (nsub > 1) {
     __syncthreads();
-    for (int item = tid; item < items; item += kThreads) {
+    for (int item = tid; item < items; item += kMergeThreads) {
       const int g = item / D4;
       const int d4 = item - g * D4;
       float m = red_m[item], l = red_l[item];
@@ -944,9 +960,17 @@ static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
   if (grid < 0) return hipErrorInvalidValue;
   a.num_waves = grid * kWaves;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
-  hipLaunchKernelGGL((attn_merge_kernel<D, is_fp8<CT>::value>),
-                     dim3(a.num_seqs * a.num_kv_heads * a.group_chunks),
-                     dim3(kThreads), 0, stream, a);
+  // Pieces per cut row grow with the wave boundaries per row: fetch them in
+  // batches of 16 when there are about 4 or more boundaries per row, else 4
+  // (fewer registers, so the mostly idle workgroups of many-row batches
+  // launch in one round).
+  const int rows = a.num_seqs * a.num_kv_heads * a.group_chunks;
+  if (rows > 0 && a.num_waves >= 4 * rows)
+    hipLaunchKernelGGL((attn_merge_kernel<D, is_fp8<CT>::value, 16>),
+                       dim3(rows), dim3(kMergeThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<D, is_fp8<CT>::value, 4>),
+                       dim3(rows), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 

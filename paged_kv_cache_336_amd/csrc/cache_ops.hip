@@ -39,16 +39,20 @@ __device__ __forceinline__ uint32_t encode_e4m3(float y) {
   return sign | code;
 }
 
+// Element e (0..15) of a 16-element source piece held as 16-byte words.
 template <typename ST>
-__device__ __forceinline__ float load_elem(const uint8_t* p);
-template <> __device__ __forceinline__ float load_elem<F32>(const uint8_t* p) {
-  return *reinterpret_cast<const float*>(p);
+__device__ __forceinline__ float piece_elem(const u32x4_t* w, int e);
+template <> __device__ __forceinline__ float piece_elem<F32>(const u32x4_t* w, int e) {
+  return __uint_as_float(w[e >> 2][e & 3]);
 }
-template <> __device__ __forceinline__ float load_elem<F16>(const uint8_t* p) {
-  return static_cast<float>(*reinterpret_cast<const _Float16*>(p));
+template <> __device__ __forceinline__ float piece_elem<F16>(const u32x4_t* w, int e) {
+  const uint32_t word = w[e >> 3][(e >> 1) & 3];
+  const uint16_t h = (uint16_t)(word >> (16 * (e & 1)));
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
-template <> __device__ __forceinline__ float load_elem<BF16>(const uint8_t* p) {
-  return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
+template <> __device__ __forceinline__ float piece_elem<BF16>(const u32x4_t* w, int e) {
+  const uint32_t word = w[e >> 3][(e >> 1) & 3];
+  return __uint_as_float((word >> (16 * (e & 1))) << 16);
 }
 
 // Same dtype: bit copy of 16-byte pieces.
@@ -84,11 +88,21 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(WriteArgs a) {
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / pieces;
     const int pc = (int)(i - t * pieces);
+    // the slot, the scales and the source piece are requested together
     const int32_t slot = a.slot_mapping[t];
-    if (slot < 0) continue;
+    constexpr int NW = ST::bytes;  // 16-byte words per 16-element piece
     const int64_t e0 = t * a.row_elems + pc * 16;
-    const uint8_t* ksrc = static_cast<const uint8_t*>(a.key) + e0 * ST::bytes;
-    const uint8_t* vsrc = static_cast<const uint8_t*>(a.value) + e0 * ST::bytes;
+    const u32x4_t* ksrc = reinterpret_cast<const u32x4_t*>(
+        static_cast<const uint8_t*>(a.key) + e0 * ST::bytes);
+    const u32x4_t* vsrc = reinterpret_cast<const u32x4_t*>(
+        static_cast<const uint8_t*>(a.value) + e0 * ST::bytes);
+    u32x4_t kin[NW], vin[NW];
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      kin[q] = ksrc[q];
+      vin[q] = vsrc[q];
+    }
+    if (slot < 0) continue;
     u32x4_t kout, vout;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -96,8 +110,8 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(WriteArgs a) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int e = 4 * w + b;
-        kw |= encode_e4m3(load_elem<ST>(ksrc + e * ST::bytes) / ks) << (8 * b);
-        vw |= encode_e4m3(load_elem<ST>(vsrc + e * ST::bytes) / vs) << (8 * b);
+        kw |= encode_e4m3(piece_elem<ST>(kin, e) / ks) << (8 * b);
+        vw |= encode_e4m3(piece_elem<ST>(vin, e) / vs) << (8 * b);
       }
       kout[w] = kw;
       vout[w] = vw;
