@@ -74,7 +74,9 @@ typedef enum pkv_status {
   PKV_ERR_UNSUPPORTED = 4, /* valid request this build does not implement  */
   PKV_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned             */
   PKV_ERR_WORKSPACE = 6,   /* attention workspace missing or too small     */
-  PKV_ERR_HIP = 8          /* the HIP runtime reported an error            */
+  PKV_ERR_HIP = 8,         /* the HIP runtime reported an error            */
+  PKV_ERR_NO_BLOCKS = 9,   /* block manager: too few free blocks or slots  */
+  PKV_ERR_SEQ = 10         /* block manager: sequence not live / in use    */
 } pkv_status;
 
 /* Human-readable name of a status code (static string, never NULL). */

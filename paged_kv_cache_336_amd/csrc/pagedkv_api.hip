@@ -67,6 +67,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PKV_ERR_SEQ: return "sequence not live, or already live";
   }
   return "unknown status";
 }
