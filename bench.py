@@ -138,6 +138,30 @@ def cpu_baseline(w, budget_s):
             f"step ran once beforehand, untimed", threads)
 
 
+def contiguous_table_sets(w, count):
+    """Block tables that give every sequence consecutive physical blocks
+    (sequence after sequence), in up to `count` disjoint ranges of the pool:
+    the unpaged layout the paging overhead is measured against.  Only the
+    addresses matter for that measurement, not what the blocks hold.  Empty
+    when the pool cannot hold every sequence's blocks unshared (a batch whose
+    sequences share blocks can need more than the pool has)."""
+    L = w.seq_lens.astype(np.int64)
+    bs = w.block_size
+    nblk = (L + bs - 1) // bs
+    need = int(nblk.sum())
+    count = min(count, w.num_blocks // max(need, 1))
+    first = np.concatenate([[0], np.cumsum(nblk)[:-1]])
+    sets = []
+    for r in range(count):
+        t = np.zeros_like(w.block_tables)
+        for s in range(w.num_seqs):
+            t[s, :nblk[s]] = r * need + first[s] + np.arange(nblk[s])
+        if int(t.min()) < 0 or int(t.max()) >= w.num_blocks:
+            raise AssertionError("contiguous table entry outside the pool")
+        sets.append(t)
+    return sets
+
+
 class GpuClock:
     """Keeps the GPU busy with torch's spin kernel while the host enqueues a
     timed region, so that region runs back to back on the GPU."""
@@ -203,6 +227,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paging-overhead", action="store_true",
+                    help="skip the contiguous-table comparison")
     ap.add_argument("--traffic-json", default=os.path.join(
         ROOT, "profiles", "traffic.json"))
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -266,6 +292,34 @@ def main():
             dev.attend(i % R, max_waves=args.max_waves)
     attn_total, _ = timed_region(torch, clock, run_attn, host_step_ms * K)
     attn_avg_ms = attn_total / K
+
+    # ---- paging overhead: the same calls with contiguous block tables ----
+    paging = None
+    csets = [] if args.no_paging_overhead else [
+        torch.from_numpy(t).to("cuda:0") for t in contiguous_table_sets(w, R)]
+    if not args.no_paging_overhead and not csets:
+        paging = {"skipped": "the pool cannot hold every sequence's blocks "
+                             "unshared"}
+    if csets:
+
+        def run_contig():
+            for i in range(K):
+                ops.paged_attn_decode(dev.out, dev.query, dev.k_cache,
+                                      dev.v_cache, csets[i % len(csets)],
+                                      dev.seq_lens, dev.max_seq_len, w.scale,
+                                      k_scale=dev.k_scale, v_scale=dev.v_scale,
+                                      max_waves=args.max_waves,
+                                      workspace=dev.workspace,
+                                      cache_kind=dev.cache_kind)
+        run_contig()
+        contig_total, _ = timed_region(torch, clock, run_contig,
+                                       host_step_ms * K)
+        contig_ms = contig_total / K
+        paging = {"contiguous_tables_us": round(contig_ms * 1e3, 3),
+                  "paged_tables_us": round(attn_avg_ms * 1e3, 3),
+                  "gbps_ratio_contiguous_over_paged":
+                      round(attn_avg_ms / contig_ms, 4),
+                  "contiguous_table_sets": len(csets)}
 
     # ---- the cache write alone (for the report) ----
     def run_write():
@@ -352,6 +406,7 @@ def main():
             "algorithmic_bytes_per_launch": B,
         },
         "cpu_baseline": cpu,
+        "paging_overhead": paging,
     }
     print(json.dumps(line), flush=True)
 

@@ -38,10 +38,14 @@
  *
  * Errors: every host-checkable precondition is checked before any HIP call;
  * a failed check returns a non-zero pkv_status and launches nothing.  The
- * contents of device buffers (table entries in range, slots in range, no
- * duplicate slots, copy pairs with distinct destinations that are not also
- * sources) are the caller's contract and are not checked.  A failed launch
- * returns PKV_ERR_HIP.  The library allocates no memory, never synchronises
+ * contents of device buffers (table entries in range, slots in range,
+ * lengths within the table's reach, no duplicate slots, copy pairs with
+ * distinct destinations that are not also sources) are the caller's
+ * contract.  Breaking it gives unspecified results but never an access
+ * outside the buffers: table entries outside [0, num_blocks) are clamped
+ * into the pool, slots and copy pairs outside it are skipped, and lengths
+ * are cut to max_blocks_per_seq * block_size.  A failed launch returns
+ * PKV_ERR_HIP.  The library allocates no memory, never synchronises
  * and keeps no state: calls are thread-safe, and two calls that share an
  * attention workspace must not overlap in time.
  */

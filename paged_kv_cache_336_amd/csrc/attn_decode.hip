@@ -125,9 +125,9 @@ template <int NBLK> struct WaveState {
 // ---------------------------------------------------------------------------
 template <typename QT, typename CT, int D>
 __device__ __forceinline__ void load_tile_uniform(
-    TileRegs<QT, CT, D>& tr, int bs, uint32_t tab_a, uint32_t tab_b, int wb,
-    const uint8_t* kbase, const uint8_t* vbase, int64_t stride, int t0,
-    int t_end, int lane) {
+    TileRegs<QT, CT, D>& tr, int bs, int nblocks, uint32_t tab_a,
+    uint32_t tab_b, int wb, const uint8_t* kbase, const uint8_t* vbase,
+    int64_t stride, int t0, int t_end, int lane) {
   typedef Shape<QT, CT, D> S;
   const int c = lane & 15;
   const int j = lane >> 4;
@@ -155,6 +155,9 @@ __device__ __forceinline__ void load_tile_uniform(
           phys = __builtin_amdgcn_readlane(tab_a, idx);
         else
           phys = __builtin_amdgcn_readlane(tab_b, idx - 64);
+        // an entry outside the pool (the caller's error) is clamped into
+        // it: unspecified values, never an access outside the pool
+        phys = (uint32_t)phys < (uint32_t)nblocks ? phys : nblocks - 1;
         row0 = (int64_t)phys * bs + (tb - lb * bs);
       }
       // (the clamp above may be selected as a vector min/max)
@@ -193,7 +196,7 @@ __device__ __forceinline__ void load_tile_uniform(
 // lanes skip the load and hold zeros.
 template <typename QT, typename CT, int D>
 __device__ __forceinline__ void load_tile_any(
-    TileRegs<QT, CT, D>& tr, int bs, const int32_t* trow,
+    TileRegs<QT, CT, D>& tr, int bs, int nblocks, const int32_t* trow,
     const uint8_t* kbase, const uint8_t* vbase, int64_t stride, int t0,
     int t_end, int lane) {
   typedef Shape<QT, CT, D> S;
@@ -206,7 +209,9 @@ __device__ __forceinline__ void load_tile_any(
     int myslot = 0;
     if (tok < t_end) {
       const int lb = tok / bs;
-      myslot = trow[lb] * bs + (tok - lb * bs);
+      const int pb = trow[lb];
+      myslot = ((uint32_t)pb < (uint32_t)nblocks ? pb : nblocks - 1) * bs +
+               (tok - lb * bs);
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -721,7 +726,9 @@ void attn_decode_kernel(AttnArgs a) {
     const int b1 = min(b0 + per, nS);
     int sum = 0;
     for (int i = b0; i < b1; ++i) {
-      const int L = a.seq_lens[i];
+      // a length beyond the table's reach (the caller's error) is cut to it,
+      // so the table reads stay inside the sequence's row
+      const int L = min(max(a.seq_lens[i], 0), a.max_seq_tokens);
       lens[i] = L;
       sum += (L + S::TT - 1) / S::TT;
     }
@@ -793,7 +800,7 @@ void attn_decode_kernel(AttnArgs a) {
   load_query<QT, CT, D>(qw, X, a, lane);
   TileRegs<QT, CT, D> cur;
   if constexpr (PREFETCH)
-    load_tile_uniform<QT, CT, D>(cur, a.block_size, ta, tbw, X.wb,
+    load_tile_uniform<QT, CT, D>(cur, a.block_size, a.num_blocks, ta, tbw, X.wb,
                                  kpool + (int64_t)X.h * S::ROW_BYTES,
                                  vpool + (int64_t)X.h * S::ROW_BYTES, stride,
                                  X.t_begin, X.t_end, lane);
@@ -835,7 +842,7 @@ void attn_decode_kernel(AttnArgs a) {
         }
         TileRegs<QT, CT, D> nxt;
         load_tile_uniform<QT, CT, D>(
-            nxt, a.block_size, same_seg ? ta : ta_n, same_seg ? tbw : tb_n,
+            nxt, a.block_size, a.num_blocks, same_seg ? ta : ta_n, same_seg ? tbw : tb_n,
             same_seg ? wb : Xn.wb, same_seg ? kbase : kbase_n,
             same_seg ? vbase : vbase_n, stride,
             same_seg ? t_next : Xn.t_begin, same_seg ? X.t_end : Xn.t_end,
@@ -863,10 +870,12 @@ void attn_decode_kernel(AttnArgs a) {
           shifted.wb = wb;
           const uint32_t wa = load_window(shifted, 0, a, lane);
           const uint32_t wbb = load_window(shifted, 1, a, lane);
-          load_tile_uniform<QT, CT, D>(cur, a.block_size, wa, wbb, wb, kbase,
+          load_tile_uniform<QT, CT, D>(cur, a.block_size, a.num_blocks, wa,
+                                       wbb, wb, kbase,
                                        vbase, stride, t0, X.t_end, lane);
         } else {
-          load_tile_any<QT, CT, D>(cur, a.block_size, trow, kbase, vbase,
+          load_tile_any<QT, CT, D>(cur, a.block_size, a.num_blocks, trow,
+                                   kbase, vbase,
                                    stride, t0, X.t_end, lane);
         }
 #pragma unroll

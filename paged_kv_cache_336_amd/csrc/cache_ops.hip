@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void cache_write_copy_kernel(WriteArgs a,
     const int64_t t = i / pieces;
     const int pc = (int)(i - t * pieces);
     const int32_t slot = a.slot_mapping[t];
-    if (slot < 0) continue;
+    if (slot < 0 || slot >= a.num_slots) continue;
     const int64_t off_src = t * row_bytes + pc * 16;
     const int64_t off_dst = (int64_t)slot * row_bytes + pc * 16;
     const u32x4_t k = *reinterpret_cast<const u32x4_t*>(
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(WriteArgs a) {
       kin[q] = ksrc[q];
       vin[q] = vsrc[q];
     }
-    if (slot < 0) continue;
+    if (slot < 0 || slot >= a.num_slots) continue;
     u32x4_t kout, vout;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -157,6 +157,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
   for (int64_t pair = blockIdx.y; pair < a.num_pairs; pair += gridDim.y) {
     const int64_t src = a.pairs[2 * pair];
     const int64_t dst = a.pairs[2 * pair + 1];
+    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks)
+      continue;  // (a pair outside the pool is the caller's error: skipped)
     const uint8_t* ks = static_cast<const uint8_t*>(a.k_cache) + src * a.block_bytes;
     const uint8_t* vs = static_cast<const uint8_t*>(a.v_cache) + src * a.block_bytes;
     uint8_t* kd = static_cast<uint8_t*>(a.k_cache) + dst * a.block_bytes;

@@ -4,6 +4,8 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 #include "pkv_internal.h"
 
 using namespace pkv;
@@ -102,6 +104,7 @@ int cache_write_slots(const void* key, const void* value, int src_dtype,
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.num_tokens = num_tokens;
+  a.num_slots = num_blocks * (int64_t)block_size;
   a.block_size = block_size;
   a.row_elems = num_kv_heads * head_dim;
   return launch_cache_write(a, src_dtype, cache_dtype, stream) == hipSuccess
@@ -125,6 +128,7 @@ int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
   a.v_cache = v_cache;
   a.pairs = block_pairs;
   a.num_pairs = num_pairs;
+  a.num_blocks = num_blocks;
   a.block_bytes = (int64_t)block_size * num_kv_heads * head_dim *
                   dtype_bytes(cache_dtype);
   return launch_copy_blocks(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
@@ -195,6 +199,9 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
   a.group_chunks = s.group_chunks;
   a.slot_heads = s.slot_heads;
   a.block_size = block_size;
+  a.num_blocks = (int32_t)num_blocks;
+  a.max_seq_tokens = (int32_t)std::min<int64_t>(
+      (int64_t)max_blocks_per_seq * block_size, INT_MAX);
   a.qk_scale_log2 = scale * 1.4426950408889634f;
   return launch_attn_decode(a, q_dtype, cache_dtype, head_dim, max_waves,
                             stream) == hipSuccess

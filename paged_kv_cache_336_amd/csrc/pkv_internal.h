@@ -38,6 +38,8 @@ struct AttnArgs {
   int32_t group_chunks;   // ceil(group / 16)
   int32_t slot_heads;     // min(16, group): query heads per partial slot
   int32_t block_size;
+  int32_t num_blocks;     // table entries are clamped into [0, num_blocks)
+  int32_t max_seq_tokens; // min(max_blocks_per_seq * block_size, INT32_MAX)
   int32_t num_waves;      // waves of the partition kernel's grid
   float qk_scale_log2;    // softmax scale * log2(e)
 };
@@ -54,6 +56,7 @@ struct WriteArgs {
   const float* k_scale;
   const float* v_scale;
   int64_t num_tokens;
+  int64_t num_slots;      // num_blocks * block_size: larger slots are skipped
   int32_t block_size;
   int32_t row_elems;      // num_kv_heads * head_dim
 };
@@ -66,6 +69,7 @@ struct CopyArgs {
   void* v_cache;
   const int32_t* pairs;
   int64_t num_pairs;
+  int64_t num_blocks;     // pairs naming a block outside the pool are skipped
   int64_t block_bytes;
 };
 
