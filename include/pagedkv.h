@@ -10,7 +10,8 @@
  *   copy_blocks        whole-block copies for copy-on-write ("PagedAttention",
  *                      shubhamtatvamasi.com, section "Sharing and
  *                      copy-on-write" and the FAQ entry on copy-on-write for
- *                      parallel sampling);
+ *                      parallel sampling), and copy_block_prefixes, which
+ *                      copies only the tokens a block holds;
  *   paged_attn_decode  one decode query per sequence attends over its tokens
  *                      by walking its block table over the shared pool
  *                      ("PagedAttention", section "How attention reads paged
@@ -126,6 +127,24 @@ int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
                 const int32_t* block_pairs, int64_t num_pairs,
                 int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                 int32_t head_dim, hipStream_t stream);
+
+/*
+ * copy_block_prefixes -- copy-on-write of the tokens a block already holds
+ * ("PagedAttention", shubhamtatvamasi.com, FAQ entry on copy-on-write for
+ * parallel sampling: the engine copies the existing tokens into the new
+ * block).  For each triple {src, dst, tokens}, slots 0 .. tokens-1 of block
+ * dst in both pools take the bytes of the same slots of block src; slots from
+ * tokens on are left as they are.  tokens is clamped to [0, block_size].
+ *
+ * block_triples  device int32 [num_copies][3].  The same rules as
+ *                copy_blocks otherwise (distinct destinations that are not
+ *                sources; num_copies == 0 is a no-op).
+ */
+int copy_block_prefixes(void* k_cache, void* v_cache, int cache_dtype,
+                        const int32_t* block_triples, int64_t num_copies,
+                        int64_t num_blocks, int32_t block_size,
+                        int32_t num_kv_heads, int32_t head_dim,
+                        hipStream_t stream);
 
 /*
  * paged_attn_workspace_size -- bytes of device workspace paged_attn_decode

@@ -72,13 +72,15 @@ int pkv_bm_fork(pkv_block_manager* bm, int32_t parent, int32_t child);
  * old is dropped (so a later sharer in the same batch whose count has fallen
  * to one writes in place).  slot_mapping[i] gets the new token's slot;
  * pairs_out[2k], pairs_out[2k+1] get the k-th {src, dst} pair (capacity n
- * pairs) and *num_pairs_out their count.  All or nothing: PKV_ERR_NO_BLOCKS
+ * pairs) and *num_pairs_out their count; copy_tokens_out[k] (may be NULL)
+ * the number of tokens the copy must carry (those src holds), for
+ * copy_block_prefixes.  All or nothing: PKV_ERR_NO_BLOCKS
  * if the batch needs more blocks than are free, PKV_ERR_SEQ for a sequence
  * that is not live or listed twice, PKV_ERR_SHAPE if one would exceed
  * max_blocks_per_seq. */
 int pkv_bm_append(pkv_block_manager* bm, const int32_t* seqs, int32_t n,
                   int32_t* slot_mapping, int32_t* pairs_out,
-                  int32_t* num_pairs_out);
+                  int32_t* num_pairs_out, int32_t* copy_tokens_out);
 
 /* End sequence seq: every block of it loses a reference; blocks left with
  * none return to the free list. */

@@ -38,7 +38,7 @@ from .fp8_e4m3 import e4m3_decode, e4m3_encode, E4M3_MAX
 from .storage import to_float64
 from .attention import (paged_attention, paged_attention_rows,
                         gather_sequence, attention_one_head)
-from .cache_ops import cache_write, copy_blocks
+from .cache_ops import cache_write, copy_block_prefixes, copy_blocks
 
 __all__ = [
     "e4m3_decode",
@@ -51,4 +51,5 @@ __all__ = [
     "attention_one_head",
     "cache_write",
     "copy_blocks",
+    "copy_block_prefixes",
 ]

@@ -83,7 +83,7 @@ class BlockManager:
             self.refs[b] += 1
         self.lengths[child] = self.lengths[parent]
 
-    def _append_one(self, seq, pairs):
+    def _append_one(self, seq, pairs, counts):
         table = self.tables[seq]
         n = self.lengths[seq]
         offset = n % self.block_size
@@ -94,6 +94,7 @@ class BlockManager:
             old = table[-1]
             new = self._take()
             self.tokens_in[new] = self.tokens_in[old]  # the copied tokens
+            counts.append(self.tokens_in[old])
             self._release(old)
             table[-1] = new
             pairs.append((old, new))
@@ -102,21 +103,24 @@ class BlockManager:
         self.lengths[seq] = n + 1
         return b * self.block_size + offset
 
-    def append(self, seqs):
+    def append(self, seqs, with_counts=False):
         """One new token for each sequence, in order.  Returns (slots,
-        copy pairs); raises OutOfBlocks (and changes nothing) if the free
-        list runs out part way."""
+        copy pairs) and, with_counts, the tokens each copy carries (those the
+        old block holds); raises OutOfBlocks (and changes nothing) if the
+        free list runs out part way."""
         assert len(set(seqs)) == len(seqs)
         saved = (list(self.free), list(self.refs), list(self.tokens_in),
                  {s: list(t) for s, t in self.tables.items()},
                  dict(self.lengths))
-        pairs = []
+        pairs, counts = [], []
         try:
-            slots = [self._append_one(s, pairs) for s in seqs]
+            slots = [self._append_one(s, pairs, counts) for s in seqs]
         except OutOfBlocks:
             (self.free, self.refs, self.tokens_in, self.tables,
              self.lengths) = saved
             raise
+        if with_counts:
+            return slots, pairs, counts
         return slots, pairs
 
     def free_sequence(self, seq):

@@ -54,6 +54,21 @@ def cache_write(k_pool, v_pool, cache_kind, key, value, src_kind,
     return kp, vp
 
 
+def copy_block_prefixes(k_pool, v_pool, triples):
+    """Copies of the tokens a block holds (the FAQ entry on copy-on-write:
+    the existing tokens go into the new block): for each (src, dst, tokens),
+    slots 0 .. tokens-1 of dst take those of src in both pools; the rest of
+    dst is left as it was.  Reading: tokens is clamped to [0, block_size]."""
+    kp = k_pool.copy()
+    vp = v_pool.copy()
+    bs = k_pool.shape[1]
+    for src, dst, n in np.asarray(triples, dtype=np.int64).reshape(-1, 3):
+        n = min(max(int(n), 0), bs)
+        kp[dst, :n] = kp[src, :n]
+        vp[dst, :n] = vp[src, :n]
+    return kp, vp
+
+
 def copy_blocks(k_pool, v_pool, pairs):
     """Whole-block copies src -> dst in both pools; returns (k_pool, v_pool)."""
     kp = k_pool.copy()

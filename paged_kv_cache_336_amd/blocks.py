@@ -55,7 +55,7 @@ def _lib():
         lib.pkv_bm_fork.restype = ci
         lib.pkv_bm_fork.argtypes = [vp, i32, i32]
         lib.pkv_bm_append.restype = ci
-        lib.pkv_bm_append.argtypes = [vp, vp, i32, vp, vp, vp]
+        lib.pkv_bm_append.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         lib.pkv_bm_free.restype = ci
         lib.pkv_bm_free.argtypes = [vp, i32]
         lib.pkv_bm_tables.restype = ci
@@ -123,18 +123,24 @@ class BlockManager:
     def fork(self, parent, child):
         _check(self.lib.pkv_bm_fork(self.h, parent, child), "fork")
 
-    def append(self, seqs):
+    def append(self, seqs, with_counts=False):
         """One token for each sequence: (slot_mapping int32 [n], copy pairs
-        int32 [p, 2])."""
+        int32 [p, 2]) and, with_counts, the tokens each copy carries
+        (int32 [p]; rows {src, dst, tokens} for copy_block_prefixes)."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
         n = len(seqs)
         slots = np.empty(max(n, 1), dtype=np.int32)
         pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        counts = np.empty(max(n, 1), dtype=np.int32)
         npairs = ctypes.c_int32(0)
         _check(self.lib.pkv_bm_append(self.h, _ptr(seqs), n, _ptr(slots),
-                                      _ptr(pairs), ctypes.byref(npairs)),
+                                      _ptr(pairs), ctypes.byref(npairs),
+                                      _ptr(counts)),
                "append")
-        return slots[:n], pairs[:npairs.value].copy()
+        p = npairs.value
+        if with_counts:
+            return slots[:n], pairs[:p].copy(), counts[:p].copy()
+        return slots[:n], pairs[:p].copy()
 
     def free(self, seq):
         _check(self.lib.pkv_bm_free(self.h, seq), "free")

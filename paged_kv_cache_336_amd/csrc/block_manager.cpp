@@ -115,7 +115,7 @@ int pkv_bm_fork(pkv_block_manager* bm, int32_t parent, int32_t child) {
 
 int pkv_bm_append(pkv_block_manager* bm, const int32_t* seqs, int32_t n,
                   int32_t* slot_mapping, int32_t* pairs_out,
-                  int32_t* num_pairs_out) {
+                  int32_t* num_pairs_out, int32_t* copy_tokens_out) {
   if (!bm) return PKV_ERR_NULL;
   if (n < 0) return PKV_ERR_SHAPE;
   if (n > 0 && (!seqs || !slot_mapping || !pairs_out)) return PKV_ERR_NULL;
@@ -161,6 +161,7 @@ int pkv_bm_append(pkv_block_manager* bm, const int32_t* seqs, int32_t n,
       t.back() = fresh;
       pairs_out[2 * np] = old;
       pairs_out[2 * np + 1] = fresh;
+      if (copy_tokens_out) copy_tokens_out[np] = bm->stored[old];
       ++np;
     }
     const int32_t b = t.back();

@@ -153,12 +153,18 @@ hipError_t launch_cache_write(const WriteArgs& a, int src_dtype,
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
-  const int64_t pieces = a.block_bytes / 16;
+  const int w = a.prefix ? 3 : 2;
   for (int64_t pair = blockIdx.y; pair < a.num_pairs; pair += gridDim.y) {
-    const int64_t src = a.pairs[2 * pair];
-    const int64_t dst = a.pairs[2 * pair + 1];
+    const int64_t src = a.pairs[w * pair];
+    const int64_t dst = a.pairs[w * pair + 1];
     if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks)
       continue;  // (a pair outside the pool is the caller's error: skipped)
+    int64_t pieces = a.block_bytes / 16;
+    if (a.prefix) {  // the first `tokens` token rows, clamped to the block
+      const int64_t t = a.pairs[w * pair + 2];
+      pieces = (t < 0 ? 0 : (t > a.block_size ? a.block_size : t)) *
+               a.token_bytes / 16;
+    }
     const uint8_t* ks = static_cast<const uint8_t*>(a.k_cache) + src * a.block_bytes;
     const uint8_t* vs = static_cast<const uint8_t*>(a.v_cache) + src * a.block_bytes;
     uint8_t* kd = static_cast<uint8_t*>(a.k_cache) + dst * a.block_bytes;
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
 }
 
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream) {
-  const int64_t pieces = a.block_bytes / 16;
+  const int64_t pieces = a.block_bytes / 16;  // the most one copy moves
   int gx = (int)((pieces + 255) / 256);
   if (gx > 64) gx = 64;
   if (gx < 1) gx = 1;

@@ -111,10 +111,12 @@ int cache_write_slots(const void* key, const void* value, int src_dtype,
              ? PKV_OK : PKV_ERR_HIP;
 }
 
-int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
+namespace {
+
+int copy_common(void* k_cache, void* v_cache, int cache_dtype,
                 const int32_t* block_pairs, int64_t num_pairs,
                 int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
-                int32_t head_dim, hipStream_t stream) {
+                int32_t head_dim, int prefix, hipStream_t stream) {
   if (!valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
   if (num_pairs < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1)
     return PKV_ERR_SHAPE;
@@ -129,9 +131,32 @@ int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
   a.pairs = block_pairs;
   a.num_pairs = num_pairs;
   a.num_blocks = num_blocks;
-  a.block_bytes = (int64_t)block_size * num_kv_heads * head_dim *
-                  dtype_bytes(cache_dtype);
+  a.token_bytes = (int64_t)num_kv_heads * head_dim * dtype_bytes(cache_dtype);
+  a.block_bytes = (int64_t)block_size * a.token_bytes;
+  a.block_size = block_size;
+  a.prefix = prefix;
   return launch_copy_blocks(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
+                const int32_t* block_pairs, int64_t num_pairs,
+                int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                int32_t head_dim, hipStream_t stream) {
+  return copy_common(k_cache, v_cache, cache_dtype, block_pairs, num_pairs,
+                     num_blocks, block_size, num_kv_heads, head_dim, 0,
+                     stream);
+}
+
+int copy_block_prefixes(void* k_cache, void* v_cache, int cache_dtype,
+                        const int32_t* block_triples, int64_t num_copies,
+                        int64_t num_blocks, int32_t block_size,
+                        int32_t num_kv_heads, int32_t head_dim,
+                        hipStream_t stream) {
+  return copy_common(k_cache, v_cache, cache_dtype, block_triples, num_copies,
+                     num_blocks, block_size, num_kv_heads, head_dim, 1,
+                     stream);
 }
 
 size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,

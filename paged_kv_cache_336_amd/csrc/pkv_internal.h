@@ -67,10 +67,13 @@ hipError_t launch_cache_write(const WriteArgs& a, int src_dtype,
 struct CopyArgs {
   void* k_cache;
   void* v_cache;
-  const int32_t* pairs;
+  const int32_t* pairs;   // {src, dst} or, with prefix, {src, dst, tokens}
   int64_t num_pairs;
   int64_t num_blocks;     // pairs naming a block outside the pool are skipped
   int64_t block_bytes;
+  int64_t token_bytes;    // one token's rows of all kv heads
+  int32_t block_size;
+  int32_t prefix;         // 1: copy only the first `tokens` token rows
 };
 
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);

@@ -21,7 +21,8 @@ KIND_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
               "fp8_e4m3": PKV_FP8_E4M3}
 
 EXPORTED = ("pkv_status_string", "cache_write_slots", "copy_blocks",
-            "paged_attn_workspace_size", "paged_attn_decode")
+            "copy_block_prefixes", "paged_attn_workspace_size",
+            "paged_attn_decode")
 
 _lib = None
 
@@ -54,6 +55,9 @@ def load_library(path=None):
                                       i32, i32, vp, vp, vp]
     lib.copy_blocks.restype = ci
     lib.copy_blocks.argtypes = [vp, vp, ci, vp, i64, i64, i32, i32, i32, vp]
+    lib.copy_block_prefixes.restype = ci
+    lib.copy_block_prefixes.argtypes = [vp, vp, ci, vp, i64, i64, i32, i32,
+                                        i32, vp]
     lib.paged_attn_workspace_size.restype = sz
     lib.paged_attn_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.paged_attn_decode.restype = ci
@@ -131,6 +135,18 @@ def copy_blocks(k_cache, v_cache, block_pairs, cache_kind=None, stream=None):
     _check("copy_blocks", lib.copy_blocks(
         _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache, cache_kind),
         _ptr(block_pairs), int(block_pairs.shape[0]), nb, bs, hkv, d,
+        _stream(stream)))
+
+
+def copy_block_prefixes(k_cache, v_cache, block_triples, cache_kind=None,
+                        stream=None):
+    """Copy the first `tokens` slots of block src to block dst for every
+    row {src, dst, tokens} of block_triples [P, 3]."""
+    lib = load_library()
+    nb, bs, hkv, d = k_cache.shape
+    _check("copy_block_prefixes", lib.copy_block_prefixes(
+        _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache, cache_kind),
+        _ptr(block_triples), int(block_triples.shape[0]), nb, bs, hkv, d,
         _stream(stream)))
 
 

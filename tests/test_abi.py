@@ -94,6 +94,24 @@ def cb(lib, **kw):
                            a["nb"], a["bs"], a["hkv"], a["d"], None)
 
 
+def cbp(lib, **kw):
+    a = dict(kc=FAKE, vc=FAKE, cache=BF16, t=FAKE, P=4, nb=64, bs=16, hkv=8,
+             d=128)
+    a.update(kw)
+    return lib.copy_block_prefixes(a["kc"], a["vc"], a["cache"], a["t"],
+                                   a["P"], a["nb"], a["bs"], a["hkv"], a["d"],
+                                   None)
+
+
+def test_copy_block_prefixes_validation(lib):
+    assert cbp(lib, P=0) == OK
+    assert cbp(lib, t=None) == NULL
+    assert cbp(lib, cache=9) == DTYPE
+    assert cbp(lib, P=-1) == SHAPE
+    assert cbp(lib, d=96) == UNSUP
+    assert cbp(lib, vc=MISALIGNED) == ALIGN
+
+
 def test_copy_blocks_validation(lib):
     assert cb(lib, P=0) == OK
     assert cb(lib, P=0, pairs=None) == OK

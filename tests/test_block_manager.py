@@ -69,14 +69,15 @@ def test_matches_oracle_on_random_operations(seed, nblocks, bs):
             k = int(rng.integers(1, len(live) + 1))
             seqs = [int(x) for x in rng.choice(sorted(live), k, replace=False)]
             try:
-                want_slots, want_pairs = ob.append(seqs)
+                want_slots, want_pairs, want_n = ob.append(seqs, True)
             except OutOfBlocks:
                 with pytest.raises(NoFreeBlocks):
                     bm.append(seqs)
             else:
-                slots, pairs = bm.append(seqs)
+                slots, pairs, counts = bm.append(seqs, with_counts=True)
                 assert list(slots) == want_slots
                 assert [tuple(p) for p in pairs] == want_pairs
+                assert list(counts) == want_n
         elif live:
             s = int(rng.choice(sorted(live)))
             ob.free_sequence(s)

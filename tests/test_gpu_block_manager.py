@@ -55,12 +55,22 @@ def test_decode_loop_driven_by_block_manager(kv_kind):
         pk, pv = oracle.cache_write(pk, pv, kv_kind, key, val, src_kind, sl,
                                     bs, k_scale, v_scale)
 
-    def copy(pairs):
+    prefix = kv_kind == "fp8_e4m3"  # one run copies whole blocks, one only
+                                    # the tokens a block holds
+
+    def copy(pairs, counts):
         nonlocal pk, pv
         p = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
-        ops.copy_blocks(kc, vc, torch.from_numpy(p).cuda(),
-                        cache_kind=cache_kind)
-        pk, pv = oracle.copy_blocks(pk, pv, p)
+        if prefix:
+            t = np.concatenate([p, np.asarray(counts, np.int32).reshape(-1, 1)],
+                               axis=1)
+            ops.copy_block_prefixes(kc, vc, torch.from_numpy(t).cuda(),
+                                    cache_kind=cache_kind)
+            pk, pv = oracle.copy_block_prefixes(pk, pv, t)
+        else:
+            ops.copy_blocks(kc, vc, torch.from_numpy(p).cuda(),
+                            cache_kind=cache_kind)
+            pk, pv = oracle.copy_blocks(pk, pv, p)
 
     def add(seq, n):
         slots = bm.add_sequence(seq, n)
@@ -88,12 +98,13 @@ def test_decode_loop_driven_by_block_manager(kv_kind):
         if step == 20:
             add(5, 20)              # takes blocks freed by sequence 1
             live.append(5)
-        slots, pairs = bm.append(live)
-        want_slots, want_pairs = ob.append(live)
+        slots, pairs, counts = bm.append(live, with_counts=True)
+        want_slots, want_pairs, want_counts = ob.append(live, True)
         assert list(slots) == want_slots
         assert [tuple(p) for p in pairs] == want_pairs
+        assert list(counts) == want_counts
         copies += len(pairs)
-        copy(pairs)                 # copy-on-write before the new token
+        copy(pairs, counts)         # copy-on-write before the new token
         write(slots)
         tab, lens = bm.tables(live, fill=0)
         q = W._cast_from_f32(rng.standard_normal((len(live), hq, d),

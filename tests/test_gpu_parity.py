@@ -114,6 +114,20 @@ def test_cache_write_and_copy_bitwise(kind, src):
     torch.cuda.synchronize()
     assert to_host_storage(kc, kind).tobytes() == ek.tobytes()
     assert to_host_storage(vc, kind).tobytes() == ev.tobytes()
+    # copies of the tokens a block holds: 0, some, all, and counts outside
+    # [0, block_size] (clamped)
+    # (sources: blocks of sequence 3; destinations: the last free block and
+    # blocks of sequence 2, overwritten -- a pure copy test)
+    dsts = [free[2]] + [int(b) for b in w.block_tables[2, 1:5]]
+    triples = np.array([[w.block_tables[3, i], dsts[i], n]
+                        for i, n in enumerate([0, 5, 8, 11, -3])],
+                       dtype=np.int32)
+    ops.copy_block_prefixes(kc, vc, torch.from_numpy(triples).cuda(),
+                            cache_kind=ck)
+    ek, ev = oracle.copy_block_prefixes(ek, ev, triples)
+    torch.cuda.synchronize()
+    assert to_host_storage(kc, kind).tobytes() == ek.tobytes()
+    assert to_host_storage(vc, kind).tobytes() == ev.tobytes()
 
 
 # ---------------------------------------------------------------------------

@@ -127,3 +127,23 @@ def test_copy_blocks_bitwise():
     assert k2[untouched].tobytes() == kp[untouched].tobytes()
     k3, v3 = copy_blocks(kp, vp, np.zeros((0, 2), dtype=np.int32))
     assert k3.tobytes() == kp.tobytes() and v3.tobytes() == vp.tobytes()
+
+
+def test_copy_of_the_tokens_a_block_holds():
+    # the FAQ entry on copy-on-write: the existing tokens go into the new
+    # block; slots past them are not copied
+    rng = np.random.default_rng(3)
+    kp = rng.standard_normal((6, 4, 2, 8)).astype(np.float32)
+    vp = rng.standard_normal((6, 4, 2, 8)).astype(np.float32)
+    k2, v2 = oracle.copy_block_prefixes(kp, vp, [[1, 4, 3], [2, 5, 0]])
+    assert np.array_equal(k2[4, :3], kp[1, :3]) and np.array_equal(k2[4, 3], kp[4, 3])
+    assert np.array_equal(v2[4, :3], vp[1, :3]) and np.array_equal(v2[4, 3], vp[4, 3])
+    assert np.array_equal(k2[5], kp[5]) and np.array_equal(v2[5], vp[5])
+    untouched = [0, 1, 2, 3]
+    assert np.array_equal(k2[untouched], kp[untouched])
+    # a count of a whole block (or more) is the whole-block copy
+    kw, vw = oracle.copy_blocks(kp, vp, [[1, 4]])
+    kf, vf = oracle.copy_block_prefixes(kp, vp, [[1, 4, 4]])
+    kc, vc = oracle.copy_block_prefixes(kp, vp, [[1, 4, 9]])
+    assert np.array_equal(kw, kf) and np.array_equal(kw, kc)
+    assert np.array_equal(vw, vf) and np.array_equal(vw, vc)
