@@ -39,6 +39,7 @@ from .storage import to_float64
 from .attention import (paged_attention, paged_attention_rows,
                         gather_sequence, attention_one_head)
 from .cache_ops import cache_write, copy_block_prefixes, copy_blocks
+from .multi_query import paged_attention_multi
 
 __all__ = [
     "e4m3_decode",
@@ -52,4 +53,5 @@ __all__ = [
     "cache_write",
     "copy_blocks",
     "copy_block_prefixes",
+    "paged_attention_multi",
 ]

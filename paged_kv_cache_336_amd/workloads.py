@@ -502,6 +502,74 @@ def custom_decode(*, seed, num_seqs, lens, hq, hkv, d, bs, q_kind, kv_kind,
 
 
 # ----------------------------------------------------------------------------
+# several new query tokens per sequence (chunked prefill, draft verification)
+# ----------------------------------------------------------------------------
+
+@dataclass
+class MultiQuery:
+    """A step with qlens[s] new tokens per sequence: ``w`` holds the pools
+    before the step (the new tokens' slots poisoned), the tables, the lengths
+    after it, and the new rows (``w.key``/``w.value``/``w.slot_mapping``,
+    sequence after sequence); ``query`` [T, Hq, D] has one row per new token
+    in the same order, and ``query_start`` [S + 1] the exclusive prefix of
+    qlens."""
+    w: Workload
+    query: np.ndarray
+    query_start: np.ndarray
+
+    @property
+    def max_query_len(self):
+        q = np.diff(self.query_start)
+        return int(q.max()) if len(q) else 0
+
+
+def _multi(name, rng, *, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
+           src_kind, nb, perm, replicas=1):
+    lens = np.asarray(lens, dtype=np.int64)
+    qlens = np.asarray(qlens, dtype=np.int64)
+    assert (qlens <= lens).all() and (qlens >= 0).all()
+    filler = int(perm[-1])
+    max_blocks = max(1, max(blocks_for(L, bs) for L in lens))
+    need = sum(blocks_for(max(int(L), 1), bs) for L in lens)
+    sets = []
+    for r in range(replicas):
+        tables, _, _ = _decode_layout(np.maximum(lens, 1), bs,
+                                      perm[r * need:(r + 1) * need],
+                                      max_blocks, filler)
+        for i, L in enumerate(lens):
+            if L == 0:
+                tables[i, :] = filler
+        slots = [slot_of(tables[i], p, bs) for i, L in enumerate(lens)
+                 for p in range(int(L - qlens[i]), int(L))]
+        sets.append({"block_tables": tables, "slot_mapping": slots,
+                     "copy_pairs": np.zeros((0, 2), dtype=np.int32)})
+    cached = [int(L - q) for L, q in zip(lens, qlens)]
+    w = _build(name, rng, q_kind=q_kind, kv_kind=kv_kind, src_kind=src_kind,
+               hq=hq, hkv=hkv, d=d, bs=bs, nb=nb,
+               block_tables=sets[0]["block_tables"], seq_lens=lens,
+               cached_lens=cached, slot_mapping=sets[0]["slot_mapping"],
+               copy_pairs=np.zeros((0, 2)), replicas=sets[1:])
+    T = int(qlens.sum())
+    query = _cast_from_f32(_normal(rng, (T, hq, d)), q_kind)
+    query_start = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    return MultiQuery(w=w, query=query, query_start=query_start)
+
+
+def custom_multi(*, seed, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
+                 src_kind=None, spare_blocks=3):
+    """Small free-form multi-query step: lengths (after the step) and new
+    tokens per sequence given; blocks from a random permutation."""
+    rng = np.random.default_rng([SEED_BASE, 200, seed])
+    src_kind = src_kind or (q_kind if kv_kind == "fp8_e4m3" else kv_kind)
+    need = sum(blocks_for(max(int(L), 1), bs) for L in lens)
+    nb = need + spare_blocks
+    perm = rng.permutation(nb).astype(np.int32)
+    return _multi(f"custom_multi_{seed}", rng, lens=lens, qlens=qlens, hq=hq,
+                  hkv=hkv, d=d, bs=bs, q_kind=q_kind, kv_kind=kv_kind,
+                  src_kind=src_kind, nb=nb, perm=perm)
+
+
+# ----------------------------------------------------------------------------
 # relabelling (for the block-permutation invariance check)
 # ----------------------------------------------------------------------------
 
