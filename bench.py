@@ -54,9 +54,17 @@ def algorithmic_bytes(w):
     return {"attention": attn, "cache_write": write, "copy_blocks": copy}
 
 
-def kernel_source_sha():
+DECODE_SOURCES = ("attn_decode.hip", "attn_tile.h", "pkv_device.h",
+                  "pkv_internal.h")
+MULTI_SOURCES = ("attn_multi.hip", "attn_tile.h", "pkv_device.h",
+                 "pkv_internal.h")
+
+
+def kernel_source_sha(sources=DECODE_SOURCES):
+    """Hash of the sources the attention kernels are built from: a traffic
+    record taken with other sources no longer describes the kernel."""
     h = hashlib.sha256()
-    for name in ("attn_decode.hip", "pkv_device.h", "pkv_internal.h"):
+    for name in sources:
         with open(os.path.join(ROOT, "paged_kv_cache_336_amd", "csrc", name),
                   "rb") as f:
             h.update(f.read())
@@ -138,6 +146,79 @@ def cpu_baseline(w, budget_s):
             f"step ran once beforehand, untimed", threads)
 
 
+def multi_algorithmic(mq):
+    """Bytes and flops one paged_attn_multi call must move / do: every live
+    K and V row of every sequence read once, the new tokens' queries read
+    and their float32 outputs written, the tables, lengths and query starts;
+    flops 2 * 2 * D per (query head, visible key) -- Q.K and P.V -- over the
+    causal extent of each new token."""
+    w = mq.w
+    e, eq = ELEM_BYTES[w.kv_kind], ELEM_BYTES[w.q_kind]
+    L = w.seq_lens.astype(np.int64)
+    q = np.diff(mq.query_start).astype(np.int64)
+    hkv, d, bs, hq = w.num_kv_heads, w.head_dim, w.block_size, w.num_q_heads
+    T = int(q.sum())
+    nbytes = (int(L.sum()) * hkv * d * e * 2 + T * hq * d * (eq + 4) +
+              int(((L + bs - 1) // bs).sum()) * 4 + 4 * (2 * len(L) + 1))
+    # token j of q new ones sees L - q + j + 1 keys: sum = q (L - q) + q (q+1)/2
+    visible = int((q * (L - q) + q * (q + 1) // 2).sum())
+    flops = 4 * d * hq * visible
+    write = T * hkv * d * (ELEM_BYTES[w.src_kind] + e) * 2 + 4 * T
+    return {"attention": nbytes, "flops": flops, "cache_write": write}
+
+
+def multi_seq_cost(mq, s):
+    """(bytes, new tokens) of sequence s alone."""
+    w = mq.w
+    e, eq = ELEM_BYTES[w.kv_kind], ELEM_BYTES[w.q_kind]
+    L = int(w.seq_lens[s])
+    q = int(mq.query_start[s + 1] - mq.query_start[s])
+    return (L * w.num_kv_heads * w.head_dim * e * 2 +
+            q * w.num_q_heads * w.head_dim * (eq + 4) +
+            -(-L // w.block_size) * 4 + 12, q)
+
+
+def cpu_baseline_multi(mq, budget_s):
+    """The oracle on replica 0: attention of sequences 0, 1, 2, ... (all new
+    tokens, all heads, on the pools after the step's write) one at a time,
+    going round the batch again if it ends first, until the budget is used.
+    Returns (GB/s, new tokens/s, sample text, threads)."""
+    import oracle
+    w = mq.w
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()]
+                      or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    kp, vp = oracle.cache_write(w.k_pool, w.v_pool, w.kv_kind, w.key,
+                                w.value, w.src_kind, w.slot_mapping,
+                                w.block_size, w.k_scale, w.v_scale)
+    qs = mq.query_start
+    nbytes = ntok = n = 0
+    el = 0.0
+    while el < budget_s or n == 0:
+        i = n % w.num_seqs
+        t0 = time.perf_counter()
+        oracle.paged_attention_multi(
+            mq.query[qs[i]:qs[i + 1]], w.q_kind, kp, vp, w.kv_kind,
+            w.block_tables[i:i + 1], w.seq_lens[i:i + 1],
+            np.asarray([0, qs[i + 1] - qs[i]]), w.block_size, w.scale,
+            w.k_scale, w.v_scale)
+        el += time.perf_counter() - t0
+        b, q = multi_seq_cost(mq, i)
+        nbytes += b
+        ntok += q
+        n += 1
+    what = (f"sequences 0..{n - 1}" if n <= w.num_seqs else
+            f"{n} sequences ({n / w.num_seqs:.2f} passes over the batch)")
+    return (nbytes / el / 1e9, ntok / el,
+            f"attention of {what} of {w.name} (replica 0, {ntok} new "
+            f"tokens, all {w.num_q_heads} query heads, "
+            f"{nbytes / 1e6:.1f} MB) in {el:.1f} s; the step's write ran "
+            f"once beforehand, untimed", threads)
+
+
 def contiguous_table_sets(w, count):
     """Block tables that give every sequence consecutive physical blocks
     (sequence after sequence), in up to `count` disjoint ranges of the pool:
@@ -215,12 +296,154 @@ def copy_calibration(nbytes):
                                            "copies": 3}}), flush=True)
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+MULTI_METRIC = ("paged multi-query attention (causal new tokens) KV-read GB/s "
+                "+ TFLOP/s, 1 GPU")
+
+
+def warm_and_estimate(torch, step, warmup):
+    """Warm-up steps; returns the host's enqueue time per step (ms)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for i in range(max(warmup, 1)):
+        step(i)
+    ms = (time.perf_counter() - h0) * 1e3 / max(warmup, 1)
+    torch.cuda.synchronize()
+    return ms
+
+
+def load_traffic(path, workload, sources):
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if rec and rec.get("kernel_source_sha") == kernel_source_sha(sources):
+        return rec.get("bytes_per_call")
+    return None
+
+
+def bench_multi(args):
+    """Steps of several new tokens per sequence: cache_write_slots of the
+    new tokens, then paged_attn_multi."""
+    import torch
+    from paged_kv_cache_336_amd import workloads as W
+    from paged_kv_cache_336_amd.step import MultiStep
+
+    mq = W.MULTI_WORKLOADS[args.workload](replicas=args.replicas)
+    w = mq.w
+    dev = MultiStep(mq, device="cuda:0")
+    R = len(dev.sets)
+    cost = multi_algorithmic(mq)
+    K = args.steps
+
+    def step(i):
+        dev.write(i % R)
+        dev.attend(i % R, max_waves=args.max_waves)
+
+    host_step_ms = warm_and_estimate(torch, step, args.warmup)
+    clock = GpuClock(torch)
+    step_total, host_ms = timed_region(
+        torch, clock, lambda: [step(i) for i in range(K)], host_step_ms * K)
+    ms_step = step_total / K
+    attn_total, _ = timed_region(
+        torch, clock,
+        lambda: [dev.attend(i % R, max_waves=args.max_waves)
+                 for i in range(K)], host_step_ms * K)
+    attn_ms = attn_total / K
+    write_total, _ = timed_region(
+        torch, clock, lambda: [dev.write(i % R) for i in range(K)],
+        host_step_ms * K)
+    write_ms = write_total / K
+
+    B, F = cost["attention"], cost["flops"]
+    T = int(mq.query.shape[0])
+    peak_tf = MFMA_PEAK_TFLOPS[w.q_kind]
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop per byte
+    attn_gbps = B / (attn_ms * 1e-3) / 1e9
+    attn_tflops = F / (attn_ms * 1e-3) / 1e12
+    if F / B > ridge:
+        roof = {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(attn_tflops / peak_tf, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(attn_gbps, 2),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(attn_gbps / HBM_PEAK_GBPS, 4)}
+    roof.update({
+        "kernel": "paged_attn_multi (attn_multi_kernel + "
+                  "attn_multi_merge_kernel)",
+        "traffic": load_traffic(args.traffic_json, args.workload,
+                                MULTI_SOURCES),
+        "algorithmic_bytes_per_launch": B,
+        "algorithmic_flops_per_launch": F,
+        "kv_read_gbps": round(attn_gbps, 2),
+        "tflops": round(attn_tflops, 3),
+        "flop_per_byte": round(F / B, 2),
+        "ridge_flop_per_byte": round(ridge, 1),
+    })
+    cpu = None
+    if not args.no_cpu_baseline:
+        gbps, tps, sample, threads = cpu_baseline_multi(mq, args.cpu_budget)
+        cpu = {"value": round(gbps, 4), "unit": "GB/s",
+               "cores": int(threads), "kind": "oracle", "sample": sample,
+               "new_tokens_per_s": round(tps, 2)}
+    line = {
+        "metric": MULTI_METRIC,
+        "value": round(B / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[w.kv_kind],
+        "data": "synthetic (seeded N(0,1) values)",
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs,
+            "new_tokens": T,
+            "max_query_len": mq.max_query_len,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "kv_dtype": w.kv_kind,
+            "q_dtype": w.q_kind,
+            "sum_seq_len": int(w.seq_lens.sum()),
+            "max_seq_len": w.max_seq_len,
+            "replicas": R,
+            "max_waves": args.max_waves,
+        },
+        "new_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "tflops_step": round(F / (ms_step * 1e-3) / 1e12, 3),
+        "attention_us": round(attn_ms * 1e3, 3),
+        "cache_write_us": round(write_ms * 1e3, 3),
+        "cache_write_gbps": round(cost["cache_write"] / (write_ms * 1e-3)
+                                  / 1e9, 2),
+        "host_enqueue_ms": round(host_ms, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b_decode")
+    ap.add_argument("--workload", default="llama8b_decode",
+                    help="llama8b_decode (default), llama70b_decode, "
+                    "prefix_sharing_{prompt,divergent}_bs{32,544}, "
+                    "long_context_fp8, worked_example; several new tokens "
+                    "per sequence: spec_verify_llama8b, "
+                    "chunked_prefill_llama8b")
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--max-waves", type=int, default=0,
                     help="cap on the attention kernel's waves (0 = all)")
@@ -252,6 +475,9 @@ def main():
     from paged_kv_cache_336_amd.step import DeviceStep
 
     ops.load_library()
+    if args.workload in W.MULTI_WORKLOADS:
+        bench_multi(args)
+        return
     kw = {"replicas": args.replicas} if args.workload == "llama8b_decode" \
         else {}
     w = W.workload_by_name(args.workload, **kw)
@@ -342,14 +568,7 @@ def main():
     attn_gbps = B / (attn_avg_ms * 1e-3) / 1e9
     tokens_per_s = w.num_seqs / (ms_step * 1e-3)
 
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            rec = json.load(open(args.traffic_json)).get(args.workload)
-            if rec and rec.get("kernel_source_sha") == kernel_source_sha():
-                traffic = rec.get("bytes_per_call")
-        except (OSError, ValueError):
-            traffic = None
+    traffic = load_traffic(args.traffic_json, args.workload, DECODE_SOURCES)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -44,8 +44,9 @@
  * distinct destinations that are not also sources) are the caller's
  * contract.  Breaking it gives unspecified results but never an access
  * outside the buffers: table entries outside [0, num_blocks) are clamped
- * into the pool, slots and copy pairs outside it are skipped, and lengths
- * are cut to max_blocks_per_seq * block_size.  A failed launch returns
+ * into the pool, slots and copy pairs outside it are skipped, lengths are
+ * cut to max_seq_len, and query extents (paged_attn_multi) to the query rows
+ * there are.  A failed launch returns
  * PKV_ERR_HIP.  The library allocates no memory, never synchronises
  * and keeps no state: calls are thread-safe, and two calls that share an
  * attention workspace must not overlap in time.
@@ -172,7 +173,7 @@ size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * k_scale,
  * v_scale      device float32 scalars, required for an fp8 cache.
  * max_seq_len  host-side upper bound of seq_lens (a sequence longer than it
- *              is the caller's error).
+ *              is the caller's error: it is cut to max_seq_len).
  * scale        softmax scale applied to q . k.
  * max_waves    0 to spread the work over every wave the GPU holds at once,
  *              else at most this many (rounded down to a multiple of 4).
@@ -200,6 +201,65 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
                       int32_t block_size, float scale, int32_t max_waves,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * paged_attn_multi_workspace_size -- bytes of device workspace
+ * paged_attn_multi needs for these arguments, or (size_t)-1 for invalid ones
+ * (about 2 * 4096 * 16 * (head_dim + 2) * 4 bytes).  Same contract as
+ * paged_attn_workspace_size.
+ */
+size_t paged_attn_multi_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim);
+
+/*
+ * paged_attn_multi -- paged attention for several new query tokens per
+ * sequence: a chunk of a prompt attending to its cached prefix, or the draft
+ * tokens of a speculative decoder being verified.  The read path of
+ * "PagedAttention" (shubhamtatvamasi.com, section "How attention reads paged
+ * memory") with the causal rule of decoder attention among the new tokens:
+ * sequence s holds seq_lens[s] = L tokens (the new ones included, their keys
+ * and values already written, e.g. by cache_write_slots), its last
+ * q = query_start[s+1] - query_start[s] tokens are new, and new token j
+ * (position L - q + j) attends to tokens 0 .. L - q + j:
+ *
+ *   out[query_start[s] + j, h, :] =
+ *       softmax(scale * query[query_start[s] + j, h] . K_s[0 .. L-q+j]^T)
+ *       V_s[0 .. L-q+j]
+ *
+ * query        [num_query_tokens, num_q_heads, head_dim] of q_dtype, the new
+ *              tokens sequence after sequence.
+ * out          float32 [num_query_tokens, num_q_heads, head_dim]; rows that
+ *              belong to no sequence are left as they are.
+ * query_start  int32 [num_seqs + 1], non-decreasing, query_start[0] >= 0,
+ *              query_start[num_seqs] <= num_query_tokens, and q <= L for
+ *              every sequence.
+ * max_query_len  host-side upper bound of q over the sequences
+ *              (<= max_seq_len).
+ * The remaining arguments are those of paged_attn_decode; with one new token
+ * per sequence (query_start[s] = s) the result is paged_attn_decode's, bit
+ * for bit.
+ *
+ * Work split: the 16 query columns of an MFMA tile hold 16 / G new tokens of
+ * all G = num_q_heads / num_kv_heads heads of one kv head, so the keys and
+ * values of a sequence are read once per 16 / G new tokens; all 32-token
+ * tiles of all such rows are divided evenly among the waves and split rows
+ * are merged by log-sum-exp, as in paged_attn_decode.  At most 4096 sequences
+ * and G <= 16 (PKV_ERR_UNSUPPORTED beyond); the query tensor below 2 GiB and
+ * num_seqs * num_kv_heads * ceil(max_query_len / (16 / G)) *
+ * ceil(max_seq_len / 32) < 2^31 (PKV_ERR_SHAPE beyond).  A call with no query
+ * token launches nothing.
+ */
+int paged_attn_multi(float* out, const void* query, int q_dtype,
+                     const void* k_cache, const void* v_cache, int cache_dtype,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, const int32_t* query_start,
+                     int32_t num_query_tokens, int32_t max_query_len,
+                     int32_t max_seq_len, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                     float scale, int32_t max_waves, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -14,8 +14,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["pagedkv_api.hip", "attn_decode.hip", "cache_ops.hip",
-           "block_manager.cpp"]
+SOURCES = ["pagedkv_api.hip", "attn_decode.hip", "attn_multi.hip",
+           "cache_ops.hip", "block_manager.cpp"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -1,0 +1,428 @@
+// attn_multi.hip -- paged attention for several new query tokens per
+// sequence (a prompt chunk against a cached prefix, or the draft tokens a
+// speculative decoder verifies) on gfx950.
+//
+// What it computes: the read path of "PagedAttention" (shubhamtatvamasi.com,
+// section "How attention reads paged memory") with more than one query per
+// sequence.  Sequence s holds L_s tokens; its last q_s are new (their K/V
+// already written), and new token j, at position L_s - q_s + j, attends to
+// tokens 0 .. L_s - q_s + j: causal within the new tokens, everything before
+// them.
+//
+// Work split: as for one token per sequence (attn_decode.hip), with the
+// MFMA's 16 query columns packing (token, head) pairs: a row is (sequence,
+// kv head, tpr = 16 / G consecutive new tokens), its columns are those tokens'
+// G query heads, token-major.  Every row of a sequence spans the sequence's
+// ceil(L_s / 32) tiles in the unit list; tiles past the row's last column
+// limit are neither loaded nor computed, and inside the row each column
+// masks keys past its own token.  All units of all rows are divided evenly
+// among the waves and rows cut between waves are merged by log-sum-exp in a
+// second kernel, exactly as in the one-token case.  With one new token per
+// sequence this is the one-token kernel's split and arithmetic.
+
+#include "attn_tile.h"
+
+namespace pkv {
+
+// A segment of a multi-query row.
+struct MSeg : Seg {
+  int rr;  // row within its (sequence, kv head): tokens rr * tpr ..
+  int q0;  // first query row of the sequence
+  int nq;  // new tokens of the sequence
+  int L;   // its length
+};
+
+// Extent of sequence i as the kernels use it.  Values outside the caller's
+// contract are clamped so that nothing is addressed outside the buffers: the
+// length to [0, max_seq_len], the first query row to [0, num_query_tokens],
+// the new-token count to the rows left, the length and max_query_len.
+struct MqSeq {
+  int L, q0, nq;
+};
+__device__ __forceinline__ MqSeq mq_seq(const AttnArgs& a, int i) {
+  MqSeq m;
+  m.L = min(max(a.seq_lens[i], 0), a.max_seq_tokens);
+  m.q0 = min(max(a.query_start[i], 0), a.num_query_tokens);
+  const int q1 = min(max(a.query_start[i + 1], m.q0), a.num_query_tokens);
+  m.nq = min(min(q1 - m.q0, m.L), a.max_query_len);
+  return m;
+}
+
+// LDS per sequence: tex[num_seqs + 1] (exclusive prefix of the unit counts)
+// | lens | first query row | new-token count.
+__device__ __forceinline__ MSeg mseg_at(int64_t t, int64_t te, const int* tex,
+                                        const int* lens, const int* qs0,
+                                        const int* qn, const AttnArgs& a) {
+  MSeg g;
+  g.valid = t < te;
+  g.gc = 0;
+  if (!g.valid) {
+    g.s = g.h = g.rr = g.q0 = g.nq = g.L = 0;
+    g.t_begin = g.t_end = g.ntiles = g.wb = 0;
+    g.full = false;
+    return g;
+  }
+  const int ti = (int)t;  // unit indices fit an int32 (checked on the host)
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(tex[mid]) <= ti) lo = mid;
+    else hi = mid - 1;
+  }
+  const int base = __builtin_amdgcn_readfirstlane(tex[lo]);
+  const int L = __builtin_amdgcn_readfirstlane(lens[lo]);
+  const int nq = __builtin_amdgcn_readfirstlane(qn[lo]);
+  const int ts = (L + 31) / 32;
+  const int rps = (nq + a.tpr - 1) / a.tpr;
+  const int r = ti - base;
+  const int u = r / ts;
+  const int k0 = r - u * ts;
+  const int64_t row_end = (int64_t)base + (int64_t)(u + 1) * ts;
+  const int64_t end = te < row_end ? te : row_end;
+  g.s = lo;
+  g.h = u / rps;
+  g.rr = u - g.h * rps;
+  g.q0 = __builtin_amdgcn_readfirstlane(qs0[lo]);
+  g.nq = nq;
+  g.L = L;
+  g.ntiles = (int)(end - t);
+  g.t_begin = 32 * k0;
+  // the row's last column sees tokens up to L - nq + (its token) + 1
+  const int tok_end = L - nq + min(nq, (g.rr + 1) * a.tpr);
+  g.t_end = min(tok_end, 32 * (k0 + g.ntiles));
+  g.wb = g.t_begin / a.block_size;
+  g.full = k0 == 0 && end == row_end;
+  return g;
+}
+
+// Lane column c of a row: token rr * tpr + c / G of the sequence's new ones,
+// query head h * G + c % G; -1 past the row's tokens.
+__device__ __forceinline__ int mq_token(const MSeg& g, const AttnArgs& a,
+                                        int c) {
+  const int tok = g.rr * a.tpr + c / a.group;
+  return g.valid && c < a.tpr * a.group && tok < g.nq ? tok : -1;
+}
+
+// The row's query rows as the B operand (zeros for columns past its tokens).
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void load_query_mq(uint32_t* qw, const MSeg& g,
+                                              const AttnArgs& a, int lane) {
+  typedef Shape<QT, CT, D> S;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+  const int tok = mq_token(g, a, c);
+  // a column past the row's tokens reads beyond the range: zeros, no traffic
+  const uint32_t rowoff =
+      tok >= 0 ? ((uint32_t)(g.q0 + tok) * (uint32_t)a.num_q_heads +
+                  (uint32_t)(g.h * a.group + c % a.group)) *
+                     (uint32_t)(D * QT::bytes)
+               : 0x80000000u;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.query), (short)0,
+      __builtin_amdgcn_readfirstlane((int)a.query_bytes), kRawBufferFlags);
+  constexpr int QBYTES_PER_R = S::EP * QT::bytes;
+  constexpr int QLOADS = QBYTES_PER_R / 16;
+#pragma unroll
+  for (int rr = 0; rr < D / (4 * S::EP); ++rr) {
+#pragma unroll
+    for (int k = 0; k < QLOADS; ++k) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+          r, rowoff + (4 * rr + j) * QBYTES_PER_R + 16 * k, 0, 0);
+      const int w0 = (rr * QBYTES_PER_R + 16 * k) / 4;
+      qw[w0 + 0] = v[0];
+      qw[w0 + 1] = v[1];
+      qw[w0 + 2] = v[2];
+      qw[w0 + 3] = v[3];
+    }
+  }
+}
+
+// Key limit of this lane's column in segment g (0: the column sees nothing).
+__device__ __forceinline__ int mq_limit(const MSeg& g, const AttnArgs& a,
+                                        int lane) {
+  const int tok = mq_token(g, a, lane & 15);
+  return tok >= 0 ? min(g.t_end, g.L - g.nq + tok + 1) : 0;
+}
+
+template <typename QT, typename CT, int D, bool UNIFORM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_multi_kernel(AttnArgs a) {
+  typedef Shape<QT, CT, D> S;
+  static_assert(S::SUB == 1, "one 32-token sub-tile per tile");
+  constexpr int NBLK = S::NBLK;
+  constexpr bool PREFETCH = UNIFORM && CT::bytes <= 2;
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * S::STAGE_BYTES];
+  __shared__ int sm_wsum[kWaves];
+  extern __shared__ int sm_seq[];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+  const int nS = a.num_seqs;
+  int* tex = sm_seq;
+  int* lens = tex + nS + 1;
+  int* qs0 = lens + nS;
+  int* qn = qs0 + nS;
+
+  // ---- unit counts of all sequences (kv heads x rows x tiles) and their
+  // exclusive prefix ----
+  {
+    const int per = (nS + kThreads - 1) / kThreads;
+    const int b0 = min(tid * per, nS);
+    const int b1 = min(b0 + per, nS);
+    int sum = 0;
+    for (int i = b0; i < b1; ++i) {
+      const MqSeq m = mq_seq(a, i);
+      lens[i] = m.L;
+      qs0[i] = m.q0;
+      qn[i] = m.nq;
+      sum += a.num_kv_heads * ((m.nq + a.tpr - 1) / a.tpr) * ((m.L + 31) / 32);
+    }
+    const int incl = block_inclusive_scan(sum, sm_wsum);
+    int run = incl - sum;
+    for (int i = b0; i < b1; ++i) {
+      tex[i] = run;
+      run += a.num_kv_heads * ((qn[i] + a.tpr - 1) / a.tpr) *
+             ((lens[i] + 31) / 32);
+    }
+    if (tid == kThreads - 1) tex[nS] = incl;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)  // the merge kernel reads the prefix from here
+    for (int i = tid; i <= nS; i += kThreads) a.tile_prefix[i] = tex[i];
+
+  const int W = a.num_waves;
+  const int w = blockIdx.x * kWaves + wave;
+  const int64_t T = tex[nS];
+  const int64_t tb = first_tile_of_wave(w, T, W);
+  const int64_t te = first_tile_of_wave(w + 1, T, W);
+
+  float vscale = 1.f, kscale = 1.f;
+  if constexpr (is_fp8<CT>::value) {
+    kscale = *a.k_scale;
+    vscale = *a.v_scale;
+  }
+  const float qk_mul = a.qk_scale_log2 * kscale;
+  const int64_t stride = (int64_t)a.num_kv_heads * S::ROW_BYTES;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_cache);
+  uint8_t* vt = smem + wave * S::STAGE_BYTES;
+  const int gmax = a.slot_heads;
+
+  MSeg X = mseg_at(tb, te, tex, lens, qs0, qn, a);
+  int64_t pos_n = tb + X.ntiles;
+  MSeg Xn = mseg_at(pos_n, te, tex, lens, qs0, qn, a);
+  bool first_seg = true;
+  uint32_t ta = 0, tbw = 0, ta_n = 0, tb_n = 0;
+  if constexpr (UNIFORM) {
+    ta = load_window(X, 0, a, lane);
+    tbw = load_window(X, 1, a, lane);
+    ta_n = load_window(Xn, 0, a, lane);
+    tb_n = load_window(Xn, 1, a, lane);
+  }
+  uint32_t qw[S::QWORDS];
+  load_query_mq<QT, CT, D>(qw, X, a, lane);
+  TileRegs<QT, CT, D> cur;
+  if constexpr (PREFETCH)
+    load_tile_uniform<QT, CT, D>(cur, a.block_size, a.num_blocks, ta, tbw,
+                                 X.wb, kpool + (int64_t)X.h * S::ROW_BYTES,
+                                 vpool + (int64_t)X.h * S::ROW_BYTES, stride,
+                                 X.t_begin, X.t_end, lane);
+
+  while (X.valid) {
+    uint32_t qn_w[S::QWORDS];
+    load_query_mq<QT, CT, D>(qn_w, Xn, a, lane);
+    const int lim = mq_limit(X, a, lane);
+
+    WaveState<NBLK> st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int n = 0; n < NBLK; ++n) st.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const uint8_t* kbase = kpool + (int64_t)X.h * S::ROW_BYTES;
+    const uint8_t* vbase = vpool + (int64_t)X.h * S::ROW_BYTES;
+    if constexpr (PREFETCH) {
+      const uint8_t* kbase_n = kpool + (int64_t)Xn.h * S::ROW_BYTES;
+      const uint8_t* vbase_n = vpool + (int64_t)Xn.h * S::ROW_BYTES;
+      int wb = X.wb;
+      for (int k = 0; k < X.ntiles; ++k) {
+        const int t0 = X.t_begin + 32 * k;
+        const bool live = t0 < X.t_end;  // tiles past the row's columns: none
+        if (live) stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
+        const bool same_seg = k + 1 < X.ntiles;
+        const int t_next = t0 + 32;
+        if (same_seg && t_next / a.block_size - wb >= 64) {
+          wb += 64;
+          ta = tbw;
+          Seg shifted = X;
+          shifted.wb = wb;
+          tbw = load_window(shifted, 1, a, lane);
+        }
+        TileRegs<QT, CT, D> nxt;
+        load_tile_uniform<QT, CT, D>(
+            nxt, a.block_size, a.num_blocks, same_seg ? ta : ta_n,
+            same_seg ? tbw : tb_n, same_seg ? wb : Xn.wb,
+            same_seg ? kbase : kbase_n, same_seg ? vbase : vbase_n, stride,
+            same_seg ? t_next : Xn.t_begin, same_seg ? X.t_end : Xn.t_end,
+            lane);
+        __builtin_amdgcn_sched_barrier(0);
+        if (live)
+          compute_tile<QT, CT, D, true>(cur.kw[0], qw, st, vt, t0, X.t_end,
+                                        qk_mul, lane, lim);
+        cur = nxt;
+      }
+    } else {
+      const int32_t* trow = a.block_tables + (int64_t)X.s * a.max_blocks_per_seq;
+      for (int k = 0; k < X.ntiles; ++k) {
+        const int t0 = X.t_begin + 32 * k;
+        if (t0 >= X.t_end) break;  // the rest of the row is past its columns
+        if constexpr (UNIFORM) {
+          const int wb = X.wb + (t0 / a.block_size - X.wb) / 64 * 64;
+          Seg shifted = X;
+          shifted.wb = wb;
+          const uint32_t wa = load_window(shifted, 0, a, lane);
+          const uint32_t wbb = load_window(shifted, 1, a, lane);
+          load_tile_uniform<QT, CT, D>(cur, a.block_size, a.num_blocks, wa,
+                                       wbb, wb, kbase, vbase, stride, t0,
+                                       X.t_end, lane);
+        } else {
+          load_tile_any<QT, CT, D>(cur, a.block_size, a.num_blocks, trow,
+                                   kbase, vbase, stride, t0, X.t_end, lane);
+        }
+        stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
+        compute_tile<QT, CT, D, true>(cur.kw[0], qw, st, vt, t0, X.t_end,
+                                      qk_mul, lane, lim);
+      }
+    }
+
+    // ---------------- the segment's output (this wave alone) ----------------
+    float l_tot = xor_sum(st.l, 16);
+    l_tot = xor_sum(l_tot, 32);
+    const int tok = mq_token(X, a, c);
+    if (tok >= 0) {
+      if (X.full) {
+        const int64_t row = (int64_t)(X.q0 + tok) * a.num_q_heads +
+                            X.h * a.group + c % a.group;
+        const float f = l_tot > 0.f ? vscale / l_tot : 0.f;
+        float* dst = a.out + row * D + 4 * j;
+#pragma unroll
+        for (int n = 0; n < NBLK; ++n)
+          *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st.o[n] * f;
+      } else {
+        const int64_t sl = slot_index(w, first_seg ? 0 : 1) * gmax + c;
+        float* dst = a.part_o + sl * D + 4 * j;
+#pragma unroll
+        for (int n = 0; n < NBLK; ++n)
+          *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st.o[n];
+        if (j == 0) {
+          a.part_m[sl] = st.m;
+          a.part_l[sl] = l_tot;
+        }
+      }
+    }
+
+    // ---------------- advance to the next segment ----------------
+    first_seg = false;
+    X = Xn;
+    if constexpr (UNIFORM) {
+      ta = ta_n;
+      tbw = tb_n;
+    }
+#pragma unroll
+    for (int q = 0; q < S::QWORDS; ++q) qw[q] = qn_w[q];
+    pos_n += X.ntiles;
+    Xn = mseg_at(pos_n, te, tex, lens, qs0, qn, a);
+    if constexpr (UNIFORM) {
+      ta_n = load_window(Xn, 0, a, lane);
+      tb_n = load_window(Xn, 1, a, lane);
+    }
+  }
+}
+
+// Merge of a cut multi-query row: workgroup (s, h, rr) over a grid of
+// num_seqs * num_kv_heads * max_rps (rows past a sequence's count exit).
+template <int D, bool SCALED, int BATCH>
+__global__ __launch_bounds__(kMergeThreads) void attn_multi_merge_kernel(
+    AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) f32x4_t red_o[kMergeThreads];
+  __shared__ float red_m[kMergeThreads], red_l[kMergeThreads];
+  const int rr = (int)(blockIdx.x % (unsigned)a.max_rps);
+  const int sh = (int)(blockIdx.x / (unsigned)a.max_rps);
+  const int h = sh % a.num_kv_heads;
+  const int s = sh / a.num_kv_heads;
+  const MqSeq m = mq_seq(a, s);
+  const int rps = (m.nq + a.tpr - 1) / a.tpr;
+  if (rr >= rps) return;
+  const int ts = (m.L + 31) / 32;
+  const int* tex = a.tile_prefix;
+  const int64_t T = tex[a.num_seqs];
+  const int W = a.num_waves;
+  const int64_t r0 = (int64_t)tex[s] + (int64_t)(h * rps + rr) * ts;
+  const int wf = wave_of_tile(r0, T, W);
+  const int wl = wave_of_tile(r0 + ts - 1, T, W);
+  if (wf == wl) return;  // finished by one wave
+  const int npieces = wl - wf + 1;
+  const int q_first = first_tile_of_wave(wf, T, W) < r0 ? 1 : 0;
+  const int G = a.group;
+  const int gcount = min(a.tpr, m.nq - rr * a.tpr) * G;
+  const int64_t tok0 = (int64_t)m.q0 + rr * a.tpr;
+  merge_row<D, SCALED, BATCH>(
+      a, wf, npieces, q_first, gcount,
+      [&](int g) {
+        return (tok0 + g / G) * a.num_q_heads + h * G + g % G;
+      },
+      red_o, red_m, red_l);
+}
+
+template <typename QT, typename CT, int D, bool UNIFORM>
+static hipError_t launch_mu(AttnArgs a, int max_waves, hipStream_t stream) {
+  auto kernel = attn_multi_kernel<QT, CT, D, UNIFORM>;
+  const size_t dyn = ((size_t)4 * a.num_seqs + 1) * sizeof(int);
+  const int grid = resident_grid(kernel, dyn, max_waves);
+  if (grid < 0) return hipErrorInvalidValue;
+  a.num_waves = grid * kWaves;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
+  const int64_t rows = (int64_t)a.num_seqs * a.num_kv_heads * a.max_rps;
+  if (rows > 0 && a.num_waves >= 4 * rows)
+    hipLaunchKernelGGL((attn_multi_merge_kernel<D, is_fp8<CT>::value, 16>),
+                       dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
+  else if (rows > 0)
+    hipLaunchKernelGGL((attn_multi_merge_kernel<D, is_fp8<CT>::value, 4>),
+                       dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename QT, typename CT, int D>
+static hipError_t launch_md(const AttnArgs& a, int max_waves, bool uniform,
+                            hipStream_t stream) {
+  if (uniform) return launch_mu<QT, CT, D, true>(a, max_waves, stream);
+  return launch_mu<QT, CT, D, false>(a, max_waves, stream);
+}
+
+template <typename QT, typename CT>
+static hipError_t launch_mt(const AttnArgs& a, int head_dim, int max_waves,
+                            bool uniform, hipStream_t stream) {
+  if (head_dim == 64) return launch_md<QT, CT, 64>(a, max_waves, uniform, stream);
+  return launch_md<QT, CT, 128>(a, max_waves, uniform, stream);
+}
+
+hipError_t launch_attn_multi(const AttnArgs& a, int q_dtype, int cache_dtype,
+                             int head_dim, int max_waves, hipStream_t stream) {
+  const bool uniform = (a.block_size % 16) == 0;
+  switch (cache_dtype) {
+    case PKV_F32: return launch_mt<F32, F32>(a, head_dim, max_waves, uniform, stream);
+    case PKV_F16: return launch_mt<F16, F16>(a, head_dim, max_waves, uniform, stream);
+    case PKV_BF16: return launch_mt<BF16, BF16>(a, head_dim, max_waves, uniform, stream);
+    case PKV_FP8_E4M3:
+      if (q_dtype == PKV_BF16) return launch_mt<BF16, FP8>(a, head_dim, max_waves, uniform, stream);
+      if (q_dtype == PKV_F16) return launch_mt<F16, FP8>(a, head_dim, max_waves, uniform, stream);
+      return launch_mt<F32, FP8>(a, head_dim, max_waves, uniform, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

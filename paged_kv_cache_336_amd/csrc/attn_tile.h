@@ -1,0 +1,593 @@
+// attn_tile.h -- device code shared by the paged attention kernels (one
+// query token per sequence in attn_decode.hip, several in attn_multi.hip):
+// launch constants, the 32-token tile shapes and loaders, V staging, the
+// MFMA tile step with the online softmax, the split of the unit list over
+// waves, the segment/window helpers and the fold of a cut row's pieces.
+#ifndef PKV_ATTN_TILE_H
+#define PKV_ATTN_TILE_H
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWorkgroupsPerCU = 1;       // default grid: one workgroup per CU
+constexpr uint32_t kRawBufferFlags = 0x00020000;  // dword3: 32-bit data format
+
+template <typename QT, typename CT> struct PvOperand { typedef CT type; };
+template <> struct PvOperand<BF16, FP8> { typedef F16 type; };
+template <> struct PvOperand<F16, FP8> { typedef F16 type; };
+template <> struct PvOperand<F32, FP8> { typedef F32 type; };
+
+// Token (within a 32-token tile) that lane group j, operand slot e stands for:
+// slots 0-3 are rows 4j..4j+3 of the first 16-token half, slots 4-7 the same
+// rows of the second half -- exactly where the QK accumulator left them.
+__device__ __forceinline__ int slot_token(int j, int e) {
+  return e < 4 ? 4 * j + e : 12 + 4 * j + e;
+}
+
+// Compile-time shape of one (query type, cache type, head_dim) instance.
+template <typename QT, typename CT, int D> struct Shape {
+  typedef typename PvOperand<QT, CT>::type PVT;
+  static constexpr bool PSPLIT = !is_fp8<CT>::value && CT::bytes == 2;
+  static constexpr int EP = 16 / CT::bytes;           // elements per piece
+  static constexpr int KPIECES = D * CT::bytes / 64;  // K pieces/lane/half
+  static constexpr int KWORDS = KPIECES * 4;
+  static constexpr int QSTEPS = D / 32;               // k32 steps over D
+  static constexpr int ROW_BYTES = D * CT::bytes;     // one token, one head
+  static constexpr int PPR = ROW_BYTES / 16;          // pieces per row
+  static constexpr int NV = PPR / 2;                  // V pieces/lane/tile
+  static constexpr int TOK_PER_V = 64 / PPR;
+  static constexpr int PVB = PVT::bytes;
+  static constexpr int LDS_ROW = D * PVB;
+  static constexpr int VCH = EP * PVB / 16;           // LDS chunks per piece
+  static constexpr int QWORDS = D / 4 * QT::bytes / 4;
+  static constexpr int NBLK = D / 16;                 // 16-wide output blocks
+  static constexpr int STAGE_BYTES = 32 * LDS_ROW;    // V sub-tile, one wave
+  static constexpr int SPANS = LDS_ROW / 32;          // 32-byte spans per row
+  // A tile -- the unit of the split and of each load request -- is SUB
+  // 32-token sub-tiles (the MFMA tile).  One sub-tile per request measured
+  // fastest: larger requests deepen the memory queues and push the loop's
+  // registers into spills without adding bandwidth.
+  static constexpr int SUB = 1;
+  static constexpr int TT = 32 * SUB;                 // tokens per tile
+  static_assert(NV >= 1 && KPIECES >= 1, "head_dim too small");
+  static_assert(LDS_ROW / 16 >= 4 * PVB, "swizzle needs 4 distinct spans");
+  static_assert(16 % TOK_PER_V == 0, "a V load must not straddle halves");
+};
+
+// One tile's raw K and V bytes as loaded from the pool, per sub-tile.
+template <typename QT, typename CT, int D> struct TileRegs {
+  typedef Shape<QT, CT, D> S;
+  uint32_t kw[S::SUB][2][S::KWORDS];
+  u32x4_t vraw[S::SUB][S::NV];
+};
+
+// Online-softmax state of one wave: running max (log2 domain) and this
+// lane's share of the running sum for query head column c, and O^T blocks.
+template <int NBLK> struct WaveState {
+  float m;
+  float l;
+  f32x4_t o[NBLK];
+};
+
+// ---------------------------------------------------------------------------
+// Tile loads, block_size % 16 == 0: one table entry per 16-token half, rows
+// addressed through a buffer resource spanning the half's live rows only
+// (rows past the end read as zero and are never fetched, so an empty tile --
+// t0 >= t_end -- costs no memory traffic).  The wave's block-table window is
+// two VGPRs: lane i of tab_a / tab_b holds the entry of logical block
+// wb + i / wb + 64 + i, and a wave-uniform readlane turns it into a scalar.
+// ---------------------------------------------------------------------------
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void load_tile_uniform(
+    TileRegs<QT, CT, D>& tr, int bs, int nblocks, uint32_t tab_a,
+    uint32_t tab_b, int wb, const uint8_t* kbase, const uint8_t* vbase,
+    int64_t stride, int t0, int t_end, int lane) {
+  typedef Shape<QT, CT, D> S;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+  // Everything addressing a half-tile is wave-uniform; readfirstlane says
+  // so to the compiler, which keeps it in SGPRs (buffer resources in SGPRs)
+  // instead of looping over lanes.
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  const int kofs = c * (int)stride + j * 16;
+  const int vtok = lane / S::PPR;
+  const int vofs = vtok * (int)stride + (lane % S::PPR) * 16;
+#pragma unroll
+  for (int sb = 0; sb < S::SUB; ++sb) {
+    __amdgpu_buffer_rsrc_t kr[2], vr[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int tb = t0 + 32 * sb + 16 * hh;
+      int nvalid = t_end - tb;
+      nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
+      int64_t row0 = 0;
+      if (nvalid > 0) {
+        const int lb = tb / bs;
+        const int idx = lb - wb;  // 0 .. 127
+        int phys;
+        if (idx < 64)  // (tab_b may still be in flight: touch it only if needed)
+          phys = __builtin_amdgcn_readlane(tab_a, idx);
+        else
+          phys = __builtin_amdgcn_readlane(tab_b, idx - 64);
+        // an entry outside the pool (the caller's error) is clamped into
+        // it: unspecified values, never an access outside the pool
+        phys = (uint32_t)phys < (uint32_t)nblocks ? phys : nblocks - 1;
+        row0 = (int64_t)phys * bs + (tb - lb * bs);
+      }
+      // (the clamp above may be selected as a vector min/max)
+      const int nrec = __builtin_amdgcn_readfirstlane(nvalid * (int)stride);
+      kr[hh] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(kbase + row0 * stride), (short)0, nrec,
+          kRawBufferFlags);
+      vr[hh] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(vbase + row0 * stride), (short)0, nrec,
+          kRawBufferFlags);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int r = 0; r < S::KPIECES; ++r) {
+        const u32x4_t v =
+            __builtin_amdgcn_raw_buffer_load_b128(kr[hh], kofs + r * 64, 0, 0);
+        tr.kw[sb][hh][4 * r + 0] = v[0];
+        tr.kw[sb][hh][4 * r + 1] = v[1];
+        tr.kw[sb][hh][4 * r + 2] = v[2];
+        tr.kw[sb][hh][4 * r + 3] = v[3];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < S::NV; ++v) {
+      const int hh = (v * S::TOK_PER_V) >> 4;
+      const int tin = (v * S::TOK_PER_V) & 15;
+      // the whole offset goes in the per-lane operand: the range check covers it
+      tr.vraw[sb][v] = __builtin_amdgcn_raw_buffer_load_b128(
+          vr[hh], vofs + tin * (int)stride, 0, 0);
+    }
+  }
+}
+
+// Tile loads for any block size: one table lookup per token (vector), masked
+// lanes skip the load and hold zeros.
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void load_tile_any(
+    TileRegs<QT, CT, D>& tr, int bs, int nblocks, const int32_t* trow,
+    const uint8_t* kbase, const uint8_t* vbase, int64_t stride, int t0,
+    int t_end, int lane) {
+  typedef Shape<QT, CT, D> S;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+#pragma unroll
+  for (int sb = 0; sb < S::SUB; ++sb) {
+    const int ts = t0 + 32 * sb;
+    const int tok = ts + (lane & 31);
+    int myslot = 0;
+    if (tok < t_end) {
+      const int lb = tok / bs;
+      const int pb = trow[lb];
+      myslot = ((uint32_t)pb < (uint32_t)nblocks ? pb : nblocks - 1) * bs +
+               (tok - lb * bs);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ks = __shfl(myslot, 16 * hh + c, 64);
+      const bool ok = ts + 16 * hh + c < t_end;
+      const uint8_t* row = kbase + (int64_t)ks * stride;
+#pragma unroll
+      for (int r = 0; r < S::KPIECES; ++r) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (ok) v = *reinterpret_cast<const u32x4_t*>(row + (4 * r + j) * 16);
+        tr.kw[sb][hh][4 * r + 0] = v[0];
+        tr.kw[sb][hh][4 * r + 1] = v[1];
+        tr.kw[sb][hh][4 * r + 2] = v[2];
+        tr.kw[sb][hh][4 * r + 3] = v[3];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < S::NV; ++v) {
+      const int tv = lane / S::PPR + v * S::TOK_PER_V;
+      const int vs = __shfl(myslot, tv, 64);
+      tr.vraw[sb][v] = u32x4_t{0u, 0u, 0u, 0u};
+      if (ts + tv < t_end)
+        tr.vraw[sb][v] = *reinterpret_cast<const u32x4_t*>(
+            vbase + (int64_t)vs * stride + (lane % S::PPR) * 16);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// A tile's V rows -> the wave's LDS slice, converted to the PV operand type and
+// XOR-swizzled in 16-byte chunks so the transposed reads are conflict-free.
+// The slice is private to the wave and one wave's LDS operations execute in
+// issue order, so no barrier is needed around it.
+// ---------------------------------------------------------------------------
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void stage_v(const u32x4_t (&vraw)[Shape<QT, CT, D>::NV],
+                                        uint8_t* vt, int lane) {
+  typedef Shape<QT, CT, D> S;
+  typedef typename S::PVT PVT;
+  constexpr int PVB = S::PVB;
+#pragma unroll
+  for (int v = 0; v < S::NV; ++v) {
+    const int tv = lane / S::PPR + v * S::TOK_PER_V;
+    const int swz = ((tv >> 2) & 3) * PVB;
+    uint8_t* rowp = vt + tv * S::LDS_ROW;
+    const int ch0 = (lane % S::PPR) * S::VCH;
+    if constexpr (PVB == 2) {
+      // 16-bit rows: 32-byte spans (16 columns, one output block) permuted
+      // by token, so the 8 rows one transposing read touches per pass land
+      // on distinct banks
+      const int span = (ch0 >> 1) ^ (tv & (S::SPANS - 1));
+      uint8_t* dst = rowp + (span << 5) + ((ch0 & 1) << 4);
+      if constexpr (same<PVT, CT>::value) {
+        *reinterpret_cast<u32x4_t*>(dst) = vraw[v];
+      } else {  // fp8 -> f16: the piece's 16 elements fill the whole span
+        u32x4_t lo, hi;
+        lo[0] = fp8x2_to_f16x2(vraw[v][0], false);
+        lo[1] = fp8x2_to_f16x2(vraw[v][0], true);
+        lo[2] = fp8x2_to_f16x2(vraw[v][1], false);
+        lo[3] = fp8x2_to_f16x2(vraw[v][1], true);
+        hi[0] = fp8x2_to_f16x2(vraw[v][2], false);
+        hi[1] = fp8x2_to_f16x2(vraw[v][2], true);
+        hi[2] = fp8x2_to_f16x2(vraw[v][3], false);
+        hi[3] = fp8x2_to_f16x2(vraw[v][3], true);
+        *reinterpret_cast<u32x4_t*>(dst) = lo;
+        *reinterpret_cast<u32x4_t*>(dst + 16) = hi;
+      }
+    } else if constexpr (same<PVT, CT>::value) {
+      *reinterpret_cast<u32x4_t*>(rowp + ((ch0 ^ swz) << 4)) = vraw[v];
+    } else {  // fp8 -> f32, four chunks
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2_t p0 = fp8x2_to_f32x2(vraw[v][w], false);
+        const f32x2_t p1 = fp8x2_to_f32x2(vraw[v][w], true);
+        f32x4_t q = {p0[0], p0[1], p1[0], p1[1]};
+        *reinterpret_cast<f32x4_t*>(rowp + (((ch0 + w) ^ swz) << 4)) = q;
+      }
+    }
+  }
+
+}
+
+// ---------------------------------------------------------------------------
+// One tile: S = K Q^T, online-softmax update, O^T += V^T P^T.  vt is this
+// wave's LDS slice (32 rows of D PV-operand elements), already holding the
+// tile's V rows (stage_v).
+// ---------------------------------------------------------------------------
+// CAUSAL: every lane column has its own key limit `lim` (the caller folds
+// t_end into it); a column may then see no key of a tile at all, and its
+// state stays empty instead of turning into 0 * inf.
+template <typename QT, typename CT, int D, bool CAUSAL = false>
+__device__ __forceinline__ void compute_tile(
+    const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS], const uint32_t* qw,
+    WaveState<Shape<QT, CT, D>::NBLK>& st, uint8_t* vt, int t0, int t_end,
+    float qk_mul, int lane, int lim = 0) {
+  typedef Shape<QT, CT, D> S;
+  typedef typename S::PVT PVT;
+  constexpr int PVB = S::PVB;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+
+  // ---------------- S = K . Q^T ----------------
+  f32x4_t sacc[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    sacc[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < S::QSTEPS; ++q) {
+      typename Mma<QT>::operand ka, qb;
+      if constexpr (same<QT, CT>::value && QT::bytes == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          ka[w] = kw[hh][4 * q + w];
+          qb[w] = qw[4 * q + w];
+        }
+      } else if constexpr (same<QT, CT>::value) {  // float32
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ka[e] = bitcast<float>(kw[hh][8 * q + e]);
+          qb[e] = bitcast<float>(qw[8 * q + e]);
+        }
+      } else if constexpr (QT::bytes == 2) {  // fp8 keys -> bf16/f16
+        const uint32_t w0 = kw[hh][2 * q], w1 = kw[hh][2 * q + 1];
+        if constexpr (same<QT, BF16>::value) {
+          ka[0] = fp8x2_to_bf16x2(w0, false);
+          ka[1] = fp8x2_to_bf16x2(w0, true);
+          ka[2] = fp8x2_to_bf16x2(w1, false);
+          ka[3] = fp8x2_to_bf16x2(w1, true);
+        } else {
+          ka[0] = fp8x2_to_f16x2(w0, false);
+          ka[1] = fp8x2_to_f16x2(w0, true);
+          ka[2] = fp8x2_to_f16x2(w1, false);
+          ka[3] = fp8x2_to_f16x2(w1, true);
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qb[w] = qw[4 * q + w];
+      } else {  // fp8 keys -> f32
+        const uint32_t w0 = kw[hh][2 * q], w1 = kw[hh][2 * q + 1];
+        const f32x2_t p0 = fp8x2_to_f32x2(w0, false), p1 = fp8x2_to_f32x2(w0, true);
+        const f32x2_t p2 = fp8x2_to_f32x2(w1, false), p3 = fp8x2_to_f32x2(w1, true);
+        ka[0] = p0[0]; ka[1] = p0[1]; ka[2] = p1[0]; ka[3] = p1[1];
+        ka[4] = p2[0]; ka[5] = p2[1]; ka[6] = p3[0]; ka[7] = p3[1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[e] = bitcast<float>(qw[8 * q + e]);
+      }
+      sacc[hh] = Mma<QT>::step(ka, qb, sacc[hh]);
+    }
+  }
+
+  // ---------------- online softmax (log2 domain) ----------------
+  float sv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
+    sv[e] = (t0 + slot_token(j, e) < (CAUSAL ? lim : t_end)) ? raw * qk_mul
+                                                             : -INFINITY;
+  }
+  float mx = sv[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+  mx = xor_max(mx, 16);
+  mx = xor_max(mx, 32);
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = CAUSAL && m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+  float pv[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pv[e] = fast_exp2(sv[e] - m_use);
+    psum += pv[e];
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+#pragma unroll
+  for (int n = 0; n < S::NBLK; ++n) st.o[n] *= alpha;
+
+  // ---------------- O^T += V^T . P^T ----------------
+  typename Mma<PVT>::operand pb_hi, pb_lo;
+  if constexpr (PVB == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t h0 = f32_to_bits(pv[2 * w], PVT{});
+      const uint32_t h1 = f32_to_bits(pv[2 * w + 1], PVT{});
+      pb_hi[w] = h0 | (h1 << 16);
+      if constexpr (S::PSPLIT) {
+        const uint32_t l0 = f32_to_bits(pv[2 * w] - bits_to_f32(h0, PVT{}), PVT{});
+        const uint32_t l1 = f32_to_bits(pv[2 * w + 1] - bits_to_f32(h1, PVT{}), PVT{});
+        pb_lo[w] = l0 | (l1 << 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb_hi[e] = pv[e];
+  }
+#pragma unroll
+  for (int n = 0; n < S::NBLK; ++n) {
+    typename Mma<PVT>::operand va;
+    if constexpr (PVB == 2) {
+      // Transposing LDS reads: within each 16-lane group, lane 4k + q
+      // addresses 4 columns (4q .. 4q + 3 of output block n) of token
+      // 4j + k, and lane c receives column c of the four tokens 4j .. 4j+3
+      // -- operand slots 0-3; the same read 16 tokens on gives slots 4-7.
+      const int tk = 4 * j + (c >> 2);
+      const int off = ((n ^ (tk & (S::SPANS - 1))) << 5) + ((c & 3) << 3);
+      const v4i16_t lo = lds_read_tr16(vt + tk * S::LDS_ROW + off);
+      const v4i16_t hi = lds_read_tr16(vt + (tk + 16) * S::LDS_ROW + off);
+      va[0] = pack_u16x2(lo[0], lo[1]);
+      va[1] = pack_u16x2(lo[2], lo[3]);
+      va[2] = pack_u16x2(hi[0], hi[1]);
+      va[3] = pack_u16x2(hi[2], hi[3]);
+    } else {
+      const int byte = (16 * n + c) * PVB;
+      const int col = (((byte >> 4) ^ (j * PVB)) << 4) + (byte & 15);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        va[e] = *reinterpret_cast<const float*>(vt + slot_token(j, e) * S::LDS_ROW + col);
+    }
+    st.o[n] = Mma<PVT>::step(va, pb_hi, st.o[n]);
+    if constexpr (S::PSPLIT) st.o[n] = Mma<PVT>::step(va, pb_lo, st.o[n]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The split of the tile list.  tex[s] (s = 0 .. num_seqs) is the exclusive
+// prefix of the per-sequence tile counts ceil(L_s / 32); row (s, u), u =
+// kv_head * chunks + chunk, holds tiles [U tex[s] + u T_s, + T_s) of the
+// T = U tex[num_seqs] tiles, T_s = tex[s + 1] - tex[s].  With V = min(W, T)
+// of the W waves in use, wave w < V owns tiles [ceil(w T / V),
+// ceil((w + 1) T / V)) -- at least one -- and the waves from V on own none,
+// so the waves holding pieces of one row are consecutive and all hold one.
+// Tile t belongs to wave floor(t V / T).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int waves_in_use(int64_t T, int W) {
+  return T < W ? (int)T : W;
+}
+__device__ __forceinline__ int wave_of_tile(int64_t t, int64_t T, int W) {
+  return (int)(t * waves_in_use(T, W) / T);
+}
+__device__ __forceinline__ int64_t first_tile_of_wave(int w, int64_t T, int W) {
+  const int V = waves_in_use(T, W);
+  return w >= V ? T : ((int64_t)w * T + V - 1) / V;
+}
+
+// Partial slot of (wave w, slot q): o [gmax][D], then m [gmax], l [gmax] in
+// separate arrays.
+__device__ __forceinline__ int64_t slot_index(int w, int q) {
+  return (int64_t)w * 2 + q;
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the pieces of one cut row: one workgroup per row (s, u).  Every
+// thread takes 4 output columns of one query head and a strided subset of the
+// pieces (nsub threads share an output column), requests the (m, l, o) of up
+// to BATCH of its pieces at once, and folds them online:  M = max m_i,
+// l = sum 2^(m_i - M) l_i, acc = sum 2^(m_i - M) o_i; the subsets are then
+// folded the same way through LDS.  A row of G <= 4 query heads at head_dim
+// 128 has 2 threads per column, so with BATCH 16 up to 32 pieces take one
+// round of loads.  (Workgroups are kept small: most rows of a large batch
+// are not cut, and their workgroups only launch and exit.)
+// ---------------------------------------------------------------------------
+constexpr int kMergeThreads = 256;
+
+// base[byte_off] with a 32-bit offset, so the load can keep the base in
+// scalar registers.
+template <typename T>
+__device__ __forceinline__ T load_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const T*>(static_cast<const uint8_t*>(base) +
+                                     byte_off);
+}
+
+__device__ __forceinline__ void lse_fold(float& m, float& l, f32x4_t& acc,
+                                         float m2, float l2, f32x4_t acc2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;  // both empty
+  const float a1 = fast_exp2(m - M), a2 = fast_exp2(m2 - M);
+  l = l * a1 + l2 * a2;
+  acc = acc * a1 + acc2 * a2;
+  m = M;
+}
+
+// The fold of one cut row's pieces (all threads of the workgroup call it):
+// wf is the row's first wave, npieces its piece count, q_first the slot of
+// its first piece in that wave; output column g goes to row row_of(g) of
+// ``out`` (head_dim floats each).
+template <int D, bool SCALED, int BATCH, typename RowOf>
+__device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
+                                          int npieces, int q_first,
+                                          int gcount, RowOf row_of,
+                                          f32x4_t* red_o, float* red_m,
+                                          float* red_l) {
+  constexpr int D4 = D / 4;
+  const int tid = threadIdx.x;
+  const int gmax = a.slot_heads;
+  const int items = gcount * D4;
+  const int nsub = items >= kMergeThreads ? 1 : kMergeThreads / items;
+  for (int it = tid; it < items * nsub; it += kMergeThreads) {
+    const int item = it % items;
+    const int sub = it / items;
+    const int g = item / D4;
+    const int d4 = item - g * D4;
+    float m = -INFINITY, l = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // slot of piece i: slot_index(wf + i, i == 0 ? q_first : 0) * gmax + g,
+    // as a 32-bit offset (slots * head_dim < 2^24)
+    const uint32_t sl0 = (uint32_t)(slot_index(wf, 0) * gmax + g);
+    const uint32_t step = 2u * (uint32_t)gmax;
+    for (int i0 = sub; i0 < npieces; i0 += BATCH * nsub) {
+      float mi[BATCH], li[BATCH];
+      f32x4_t oi[BATCH];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const int i = i0 + k * nsub;
+        mi[k] = -INFINITY;
+        li[k] = 0.f;
+        oi[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (i < npieces) {
+          const uint32_t sl = sl0 + step * (uint32_t)i +
+                              (i == 0 ? (uint32_t)(q_first * gmax) : 0u);
+          mi[k] = load_at<float>(a.part_m, sl * 4u);
+          li[k] = load_at<float>(a.part_l, sl * 4u);
+          oi[k] = load_at<f32x4_t>(a.part_o, (sl * (uint32_t)D + 4u * d4) * 4u);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) lse_fold(m, l, acc, mi[k], li[k], oi[k]);
+    }
+    if (nsub == 1) {
+      const float f = (SCALED ? *a.v_scale : 1.f) / l;
+      *reinterpret_cast<f32x4_t*>(a.out + row_of(g) * D + 4 * d4) = acc * f;
+    } else {
+      red_o[it] = acc;
+      red_m[it] = m;
+      red_l[it] = l;
+    }
+  }
+  if (nsub > 1) {
+    __syncthreads();
+    for (int item = tid; item < items; item += kMergeThreads) {
+      const int g = item / D4;
+      const int d4 = item - g * D4;
+      float m = red_m[item], l = red_l[item];
+      f32x4_t acc = red_o[item];
+      for (int sub = 1; sub < nsub; ++sub)
+        lse_fold(m, l, acc, red_m[sub * items + item], red_l[sub * items + item],
+                 red_o[sub * items + item]);
+      const float f = (SCALED ? *a.v_scale : 1.f) / l;
+      *reinterpret_cast<f32x4_t*>(a.out + row_of(g) * D + 4 * d4) = acc * f;
+    }
+  }
+}
+
+// Inclusive scan of one int per thread across the workgroup.
+__device__ __forceinline__ int block_inclusive_scan(int v, int* sm_wsum) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) sm_wsum[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += sm_wsum[w];
+  return v + add;
+}
+
+// A run of consecutive tiles of one row owned by one wave.
+struct Seg {
+  int s, h, gc;       // the row
+  int t_begin, t_end; // tokens of the sequence it covers
+  int ntiles;
+  int wb;             // first logical block of its table window
+  bool full;          // the whole row: write the final output
+  bool valid;
+};
+
+// Entries wb + 64 * half + lane of the segment's table row (0 past the blocks
+// the segment can reach; such lanes fetch nothing).
+__device__ __forceinline__ uint32_t load_window(const Seg& g, int half,
+                                                const AttnArgs& a, int lane) {
+  const int nblk = g.valid ? (g.t_end + a.block_size - 1) / a.block_size : 0;
+  const int nrec = __builtin_amdgcn_readfirstlane(nblk * 4);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.block_tables +
+                           (int64_t)g.s * a.max_blocks_per_seq),
+      (short)0, nrec, kRawBufferFlags);
+  return __builtin_amdgcn_raw_buffer_load_b32(
+      r, (g.wb + 64 * half + lane) * 4, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// host-side dispatch
+// ---------------------------------------------------------------------------
+// Workgroups of the partition kernel: as many as can be resident at once
+// (occupancy x CUs), capped by the caller's wave limit and kMaxWaves.
+template <typename K>
+static int resident_grid(K kernel, size_t dyn_lds, int max_waves) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(kernel), kThreads, dyn_lds) !=
+          hipSuccess)
+    return -1;
+  // One workgroup (one wave per SIMD) per CU measured fastest for the
+  // streaming loop: more resident waves deepen the memory queues without
+  // adding bandwidth.
+  int64_t g = (int64_t)(per_cu < kWorkgroupsPerCU ? per_cu : kWorkgroupsPerCU) * cus;
+  if (g < cus) g = cus;
+  int64_t cap = kMaxWaves / kWaves;
+  if (max_waves > 0 && max_waves / kWaves < cap) cap = max_waves / kWaves;
+  if (g > cap) g = cap;
+  return g < 1 ? 1 : (int)g;
+}
+
+}  // namespace pkv
+
+#endif  // PKV_ATTN_TILE_H

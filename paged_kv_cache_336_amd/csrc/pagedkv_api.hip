@@ -1,10 +1,9 @@
 // pagedkv_api.hip -- the C ABI declared in include/pagedkv.h: argument
 // validation (before any HIP call), workspace layout, launch sizing and
-// dispatch to the kernels in attn_decode.hip and cache_ops.hip.
+// dispatch to the kernels in attn_decode.hip, attn_multi.hip and
+// cache_ops.hip.
 
 #include <limits.h>
-
-#include <algorithm>
 
 #include "pkv_internal.h"
 
@@ -35,17 +34,21 @@ struct AttnShape {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace: tile prefix [num_seqs + 1] int32 | part_m | part_l | part_o,
-// each 256-byte aligned; two partial slots of slot_heads query heads per wave.
+// each 256-byte aligned; two partial slots of slot_heads query columns per
+// wave.  One query token per sequence: a slot holds up to 16 query heads of
+// one kv head.  Several (multi): a slot holds 16 / group tokens of all the
+// group's heads (group <= 16).
 int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-               int32_t head_dim, AttnShape* out) {
+               int32_t head_dim, bool multi, AttnShape* out) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1) return PKV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
-  if (num_seqs > kMaxSeqs) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs > (multi ? kMaxSeqsMulti : kMaxSeqs)) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   AttnShape s{};
   s.group = num_q_heads / num_kv_heads;
+  if (multi && s.group > 16) return PKV_ERR_UNSUPPORTED;
   s.group_chunks = (s.group + 15) / 16;
-  s.slot_heads = s.group < 16 ? s.group : 16;
+  s.slot_heads = multi ? 16 / s.group * s.group : (s.group < 16 ? s.group : 16);
   const size_t slots = (size_t)kMaxWaves * 2 * s.slot_heads;
   s.off_m = align_up((size_t)(num_seqs + 1) * 4, 256);
   s.off_l = align_up(s.off_m + slots * 4, 256);
@@ -162,7 +165,18 @@ int copy_block_prefixes(void* k_cache, void* v_cache, int cache_dtype,
 size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim) {
   AttnShape s;
-  if (attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, &s) != PKV_OK)
+  if (attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, false, &s) !=
+      PKV_OK)
+    return (size_t)-1;
+  return s.ws_bytes;
+}
+
+size_t paged_attn_multi_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads,
+                                       int32_t head_dim) {
+  AttnShape s;
+  if (attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, true, &s) !=
+      PKV_OK)
     return (size_t)-1;
   return s.ws_bytes;
 }
@@ -187,7 +201,8 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
   if (num_blocks * (int64_t)block_size > INT_MAX) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKV_ERR_SHAPE;
   AttnShape s;
-  const int rc = attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, &s);
+  const int rc =
+      attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, false, &s);
   if (rc != PKV_OK) return rc;
   // every tile index of the call fits an int32
   if ((int64_t)num_seqs * num_kv_heads * s.group_chunks *
@@ -225,11 +240,91 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
   a.slot_heads = s.slot_heads;
   a.block_size = block_size;
   a.num_blocks = (int32_t)num_blocks;
-  a.max_seq_tokens = (int32_t)std::min<int64_t>(
-      (int64_t)max_blocks_per_seq * block_size, INT_MAX);
+  a.max_seq_tokens = max_seq_len;  // within the table's reach (checked)
   a.qk_scale_log2 = scale * 1.4426950408889634f;
   return launch_attn_decode(a, q_dtype, cache_dtype, head_dim, max_waves,
                             stream) == hipSuccess
+             ? PKV_OK : PKV_ERR_HIP;
+}
+
+int paged_attn_multi(float* out, const void* query, int q_dtype,
+                     const void* k_cache, const void* v_cache, int cache_dtype,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, const int32_t* query_start,
+                     int32_t num_query_tokens, int32_t max_query_len,
+                     int32_t max_seq_len, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                     float scale, int32_t max_waves, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
+  if (q_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (cache_dtype != PKV_FP8_E4M3 && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
+  if (num_blocks < 1 || block_size < 1 || max_blocks_per_seq < 1 ||
+      max_seq_len < 0 || max_waves < 0 || num_query_tokens < 0 ||
+      max_query_len < 0 || max_query_len > max_seq_len)
+    return PKV_ERR_SHAPE;
+  if (num_blocks * (int64_t)block_size > INT_MAX) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKV_ERR_SHAPE;
+  AttnShape s;
+  const int rc =
+      attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, true, &s);
+  if (rc != PKV_OK) return rc;
+  const int64_t qbytes = (int64_t)num_query_tokens * num_q_heads * head_dim *
+                         dtype_bytes(q_dtype);
+  if (qbytes >= ((int64_t)1 << 31)) return PKV_ERR_SHAPE;
+  const int32_t tpr = 16 / s.group;
+  const int32_t max_rps = (max_query_len + tpr - 1) / tpr;
+  // every unit index of the call, and the merge grid, fit an int32
+  const int64_t rows = (int64_t)num_seqs * num_kv_heads * max_rps;
+  if (rows > INT_MAX || rows * (((int64_t)max_seq_len + 31) / 32) > INT_MAX)
+    return PKV_ERR_SHAPE;
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0)
+    return PKV_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens ||
+      !query_start)
+    return PKV_ERR_NULL;
+  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(block_tables, 4) ||
+      !aligned(seq_lens, 4) || !aligned(query_start, 4))
+    return PKV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < s.ws_bytes) return PKV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return PKV_ERR_ALIGN;
+  AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.tile_prefix = reinterpret_cast<int32_t*>(ws);
+  a.part_m = reinterpret_cast<float*>(ws + s.off_m);
+  a.part_l = reinterpret_cast<float*>(ws + s.off_l);
+  a.part_o = reinterpret_cast<float*>(ws + s.off_o);
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = s.group;
+  a.group_chunks = 1;
+  a.slot_heads = s.slot_heads;
+  a.block_size = block_size;
+  a.num_blocks = (int32_t)num_blocks;
+  a.max_seq_tokens = max_seq_len;
+  a.qk_scale_log2 = scale * 1.4426950408889634f;
+  a.query_start = query_start;
+  a.num_query_tokens = num_query_tokens;
+  a.max_query_len = max_query_len;
+  a.tpr = tpr;
+  a.max_rps = max_rps;
+  a.query_bytes = qbytes;
+  return launch_attn_multi(a, q_dtype, cache_dtype, head_dim, max_waves,
+                           stream) == hipSuccess
              ? PKV_OK : PKV_ERR_HIP;
 }
 

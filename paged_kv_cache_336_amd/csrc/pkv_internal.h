@@ -12,6 +12,7 @@ namespace pkv {
 // Most sequences per call: the tile prefix and the lengths of all sequences
 // are held in LDS (8 bytes per sequence).
 constexpr int kMaxSeqs = 8192;
+constexpr int kMaxSeqsMulti = 4096;  // four LDS words per sequence
 
 // Most waves of the partition kernel (16 per CU of a 256-CU part); the
 // workspace holds two partial slots per wave.
@@ -39,10 +40,20 @@ struct AttnArgs {
   int32_t slot_heads;     // min(16, group): query heads per partial slot
   int32_t block_size;
   int32_t num_blocks;     // table entries are clamped into [0, num_blocks)
-  int32_t max_seq_tokens; // min(max_blocks_per_seq * block_size, INT32_MAX)
+  int32_t max_seq_tokens; // max_seq_len: longer lengths are cut to it
   int32_t num_waves;      // waves of the partition kernel's grid
   float qk_scale_log2;    // softmax scale * log2(e)
+  // several query tokens per sequence (paged_attn_multi) only:
+  const int32_t* query_start;  // [num_seqs + 1] first query row of each
+  int32_t num_query_tokens;    // rows of query / out (starts clamped to it)
+  int32_t max_query_len;       // new tokens per sequence at most (clamped)
+  int32_t tpr;            // query tokens per row (16 / group)
+  int32_t max_rps;        // rows per (sequence, kv head): ceil(max_query_len / tpr)
+  int64_t query_bytes;    // bytes of the whole query tensor (< 2^31)
 };
+
+hipError_t launch_attn_multi(const AttnArgs& a, int q_dtype, int cache_dtype,
+                             int head_dim, int max_waves, hipStream_t stream);
 
 hipError_t launch_attn_decode(const AttnArgs& a, int q_dtype, int cache_dtype,
                               int head_dim, int max_waves, hipStream_t stream);

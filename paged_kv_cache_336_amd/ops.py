@@ -6,8 +6,9 @@ HIP kernels.  There is no fallback: if the shared library is missing the
 first call raises.
 
 Functions keep the C names: :func:`cache_write_slots`, :func:`copy_blocks`,
-:func:`paged_attn_decode`, :func:`paged_attn_workspace_size`,
-:func:`pkv_status_string`.
+:func:`copy_block_prefixes`, :func:`paged_attn_decode`,
+:func:`paged_attn_workspace_size`, :func:`paged_attn_multi`,
+:func:`paged_attn_multi_workspace_size`, :func:`pkv_status_string`.
 """
 
 import ctypes
@@ -22,7 +23,8 @@ KIND_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
 
 EXPORTED = ("pkv_status_string", "cache_write_slots", "copy_blocks",
             "copy_block_prefixes", "paged_attn_workspace_size",
-            "paged_attn_decode")
+            "paged_attn_decode", "paged_attn_multi_workspace_size",
+            "paged_attn_multi")
 
 _lib = None
 
@@ -64,6 +66,12 @@ def load_library(path=None):
     lib.paged_attn_decode.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp, vp, i32,
                                       vp, i32, i32, i32, i32, i32, i64, i32,
                                       f32, i32, vp, sz, vp]
+    lib.paged_attn_multi_workspace_size.restype = sz
+    lib.paged_attn_multi_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.paged_attn_multi.restype = ci
+    lib.paged_attn_multi.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp, vp, i32,
+                                     vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                     i64, i32, f32, i32, vp, sz, vp]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -158,6 +166,15 @@ def paged_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim):
     return v
 
 
+def paged_attn_multi_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                    head_dim):
+    v = load_library().paged_attn_multi_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim)
+    if v == ctypes.c_size_t(-1).value:
+        raise PagedKVError("paged_attn_multi_workspace_size", 2)
+    return v
+
+
 class Workspace:
     """A device workspace for paged_attn_decode, grown (never shrunk) to the
     largest size asked for; it needs no initialisation."""
@@ -197,6 +214,32 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
         _ptr(v_cache), dtype_code(k_cache, cache_kind), _ptr(k_scale),
         _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
         _ptr(seq_lens), int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
+        int(max_waves), _ptr(buf),
+        0 if buf is None else buf.numel() * buf.element_size(),
+        _stream(stream)))
+
+
+def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
+                     query_start, max_query_len, max_seq_len, scale,
+                     k_scale=None, v_scale=None, max_waves=0, workspace=None,
+                     cache_kind=None, stream=None):
+    """out[T, Hq, D] (float32) = paged attention of T new query tokens,
+    causal among each sequence's new tokens; see pagedkv.h."""
+    lib = load_library()
+    t, hq, d = query.shape
+    nb, bs, hkv, _ = k_cache.shape
+    s = int(seq_lens.shape[0])
+    need = paged_attn_multi_workspace_size(s, hq, hkv, d)
+    if workspace is None:
+        key = str(query.device)
+        workspace = _default_ws.setdefault(key, Workspace(query.device))
+    buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    _check("paged_attn_multi", lib.paged_attn_multi(
+        _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
+        _ptr(v_cache), dtype_code(k_cache, cache_kind), _ptr(k_scale),
+        _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(seq_lens), _ptr(query_start), t, int(max_query_len),
+        int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
         int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
         _stream(stream)))

@@ -569,6 +569,50 @@ def custom_multi(*, seed, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
                   src_kind=src_kind, nb=nb, perm=perm)
 
 
+def spec_verify_llama8b(num_seqs=32, draft=4, median=512, cap=4096,
+                        num_blocks=16384, replicas=1, seed_family=6):
+    """Speculative-decoding verification on the Llama-3-8B decode shape:
+    32 sequences, 32/8 heads, D 128, bs 16, bf16, cached lengths lognormal
+    (median 512, cap 4096) as in the decode batch, plus ``draft`` new tokens
+    per sequence (the drafted tokens the target model scores in one pass,
+    each seeing the cache and the drafts before it).  Block ids from a random
+    permutation of a 16384-block pool; ``replicas`` > 1 adds disjoint id
+    sets over the same pool."""
+    rng = np.random.default_rng([SEED_BASE, seed_family])
+    lens = lognormal_lengths(rng, num_seqs, median, cap - draft) + draft
+    qlens = np.full(num_seqs, draft, dtype=np.int64)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    need = sum(blocks_for(int(L), 16) for L in lens)
+    replicas = max(1, min(replicas, (num_blocks - 1) // max(need, 1)))
+    return _multi("spec_verify_llama8b", rng, lens=lens, qlens=qlens, hq=32,
+                  hkv=8, d=128, bs=16, q_kind="bf16", kv_kind="bf16",
+                  src_kind="bf16", nb=num_blocks, perm=perm,
+                  replicas=replicas)
+
+
+def chunked_prefill_llama8b(num_seqs=8, prefix=4096, chunk=512,
+                            num_blocks=16384, replicas=1, seed_family=7):
+    """Chunked prefill on the Llama-3-8B layer shape: 8 sequences whose
+    first ``prefix`` prompt tokens are already cached take the next
+    ``chunk`` prompt tokens in one pass (causal among them); 32/8 heads,
+    D 128, bs 16, bf16, blocks from a random permutation of a 16384-block
+    pool."""
+    rng = np.random.default_rng([SEED_BASE, seed_family])
+    lens = np.full(num_seqs, prefix + chunk, dtype=np.int64)
+    qlens = np.full(num_seqs, chunk, dtype=np.int64)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    need = num_seqs * blocks_for(prefix + chunk, 16)
+    replicas = max(1, min(replicas, (num_blocks - 1) // need))
+    return _multi("chunked_prefill_llama8b", rng, lens=lens, qlens=qlens,
+                  hq=32, hkv=8, d=128, bs=16, q_kind="bf16", kv_kind="bf16",
+                  src_kind="bf16", nb=num_blocks, perm=perm,
+                  replicas=replicas)
+
+
+MULTI_WORKLOADS = {"spec_verify_llama8b": spec_verify_llama8b,
+                   "chunked_prefill_llama8b": chunked_prefill_llama8b}
+
+
 # ----------------------------------------------------------------------------
 # relabelling (for the block-permutation invariance check)
 # ----------------------------------------------------------------------------

@@ -37,7 +37,8 @@ def header_functions():
 def test_header_declares_the_boundary():
     names = header_functions()
     for n in ("cache_write_slots", "copy_blocks", "paged_attn_decode",
-              "paged_attn_workspace_size",
+              "paged_attn_workspace_size", "paged_attn_multi",
+              "paged_attn_multi_workspace_size",
               "pkv_status_string", "pkv_bm_create", "pkv_bm_append",
               "pkv_bm_fork", "pkv_bm_free", "pkv_bm_tables", "pkv_ca_reserve"):
         assert n in names
@@ -171,3 +172,60 @@ def test_workspace_size(lib):
         ops.paged_attn_workspace_size(S, 30, hkv, d)
     with pytest.raises(ops.PagedKVError):
         ops.paged_attn_workspace_size(8193, 32, 8, 128)
+
+
+def pm(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, qd=BF16, kc=FAKE, vc=FAKE, cache=BF16, ks=None,
+             vs=None, bt=FAKE, mb=256, sl=FAKE, qs=FAKE, T=128, maxq=4,
+             maxlen=4096, S=32, hq=32, hkv=8, d=128, nb=16384, bs=16,
+             scale=0.088, waves=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.paged_attn_multi(a["out"], a["q"], a["qd"], a["kc"], a["vc"],
+                                a["cache"], a["ks"], a["vs"], a["bt"], a["mb"],
+                                a["sl"], a["qs"], a["T"], a["maxq"],
+                                a["maxlen"], a["S"], a["hq"], a["hkv"], a["d"],
+                                a["nb"], a["bs"], a["scale"], a["waves"],
+                                a["ws"], a["wsb"], None)
+
+
+def test_multi_validation(lib):
+    assert pm(lib, S=0) == OK                          # nothing to do
+    assert pm(lib, T=0) == OK
+    assert pm(lib, maxq=0) == OK
+    assert pm(lib, qd=FP8, cache=FP8) == DTYPE
+    assert pm(lib, qd=F16, cache=BF16) == DTYPE
+    assert pm(lib, qd=BF16, cache=FP8) == NULL          # scales required
+    assert pm(lib, hq=30, hkv=8) == SHAPE
+    assert pm(lib, hq=32, hkv=1) == UNSUP               # more than 16 heads/kv
+    assert pm(lib, d=256) == UNSUP
+    assert pm(lib, S=4097) == UNSUP                     # too many sequences
+    assert pm(lib, T=-1) == SHAPE
+    assert pm(lib, maxq=-1) == SHAPE
+    assert pm(lib, maxq=4097) == SHAPE                  # above max_seq_len
+    assert pm(lib, T=1 << 17, hq=64, hkv=8) == SHAPE    # query of 2 GiB
+    assert pm(lib, mb=255) == SHAPE                     # table too short
+    # unit indices beyond int32: 4096 seqs x 16 kv heads x 4096 rows x 2^10
+    assert pm(lib, S=4096, hq=16, hkv=16, maxq=4096, maxlen=32768,
+              mb=2048) == SHAPE
+    assert pm(lib, out=None) == NULL
+    assert pm(lib, qs=None) == NULL
+    assert pm(lib, qs=ctypes.c_void_p(4096 + 2)) == ALIGN
+    assert pm(lib, q=MISALIGNED) == ALIGN
+    assert pm(lib, ws=None) == WS
+    assert pm(lib, wsb=1024) == WS
+    assert pm(lib, ws=ctypes.c_void_p(4096 + 16)) == ALIGN
+    assert lib.paged_attn_multi_workspace_size(4097, 8, 8, 128) == \
+        ctypes.c_size_t(-1).value
+    assert lib.paged_attn_multi_workspace_size(8, 32, 1, 128) == \
+        ctypes.c_size_t(-1).value
+
+
+def test_multi_workspace_size(lib):
+    # partial slots of 16 / G tokens x G heads per wave: 16 columns for G = 4,
+    # 15 for G = 3
+    ws = ops.paged_attn_multi_workspace_size(8, 32, 8, 128)
+    assert 4096 * 2 * 16 * 130 * 4 <= ws <= 4096 * 2 * 16 * 130 * 4 + 4096
+    ws3 = ops.paged_attn_multi_workspace_size(8, 24, 8, 64)
+    assert 4096 * 2 * 15 * 66 * 4 <= ws3 <= 4096 * 2 * 15 * 66 * 4 + 4096
+    with pytest.raises(ops.PagedKVError):
+        ops.paged_attn_multi_workspace_size(8, 48, 2, 128)
