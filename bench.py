@@ -3,8 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch: copy_blocks (the
-copy-on-write pairs of the batch; none for a plain decode batch), then
-cache_write_slots (one new token per sequence), then paged_attn_decode.
+copy-on-write pairs of the batch; none for a plain decode batch), then the
+new token of every sequence written into its slot and paged decode attention
+-- in one launch (paged_attn_decode_fused) where the batch allows it, else
+cache_write_slots followed by paged_attn_decode.
 Inputs are seeded synthetic tensors already resident in HBM; steps rotate
 over disjoint replicas of the block tables where the workload has them, so
 the 256 MB Infinity Cache cannot serve one step's K/V to the next.
@@ -450,6 +452,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the step as separate write and attention "
+                    "calls even where they can go in one launch")
     ap.add_argument("--no-paging-overhead", action="store_true",
                     help="skip the contiguous-table comparison")
     ap.add_argument("--traffic-json", default=os.path.join(
@@ -486,7 +491,23 @@ def main():
     nbytes = algorithmic_bytes(w)
     K = args.steps
 
+    # the write and the attention go in one launch where the batch has one
+    # new token per (non-empty) sequence and at most 16 query heads per kv
+    # head; else as two calls
+    fused = (not args.unfused and w.num_tokens == w.num_seqs and
+             bool((w.seq_lens > 0).all()) and
+             w.num_q_heads // w.num_kv_heads <= 16)
+
     def step(i):
+        r = i % R
+        dev.copy(r)
+        if fused:
+            dev.attend_fused(r, max_waves=args.max_waves)
+        else:
+            dev.write(r)
+            dev.attend(r, max_waves=args.max_waves)
+
+    def step_unfused(i):
         r = i % R
         dev.copy(r)
         dev.write(r)
@@ -510,6 +531,14 @@ def main():
     step_ms_total, host_ms = timed_region(torch, clock, run_steps,
                                           host_step_ms * K)
     ms_step = step_ms_total / K
+    unfused_ms = ms_step
+    if fused:
+        for i in range(max(args.warmup, 1)):
+            step_unfused(i)
+        unfused_total, _ = timed_region(
+            torch, clock, lambda: [step_unfused(i) for i in range(K)],
+            host_step_ms * K)
+        unfused_ms = unfused_total / K
 
     # ---- the attention call alone: K calls back to back between one event
     # pair on the stream the kernels run on (torch's current stream) ----
@@ -604,6 +633,10 @@ def main():
             "replicas": R,
             "max_waves": args.max_waves,
         },
+        "step": ("copy_blocks + paged_attn_decode_fused (write and "
+                 "attention in one launch)" if fused else
+                 "copy_blocks + cache_write_slots + paged_attn_decode"),
+        "step_us_separate_write": round(unfused_ms * 1e3, 3),
         "tokens_per_s": round(tokens_per_s, 1),
         "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
         "attention_us": round(attn_avg_ms * 1e3, 3),

@@ -180,7 +180,8 @@ size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *              All 32-token tiles of all (sequence, kv head) rows are divided
  *              into equal contiguous shares, one per wave; a row split
  *              between waves is merged by log-sum-exp, giving the same result
- *              up to float32 rounding for any split.
+ *              up to float32 rounding for any split (and the same bits on
+ *              every run of one call).
  * workspace    device buffer of workspace_bytes >= paged_attn_workspace_size,
  *              256-byte aligned.
  *
@@ -201,6 +202,44 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
                       int32_t block_size, float scale, int32_t max_waves,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * paged_attn_decode_fused -- cache_write_slots of one new token per sequence
+ * and paged_attn_decode in one launch: the result (out and both pools) is
+ * that of cache_write_slots(key, value, ..., slot_mapping, num_seqs, ...)
+ * followed by paged_attn_decode(...), bit for bit.  The pages' step is
+ * "write the new token's key and value into its slot, then attend over the
+ * sequence through its block table" ("How PagedAttention Works in vLLM ...",
+ * instagit.com, section "write_to_paged_cache"; "PagedAttention",
+ * shubhamtatvamasi.com, section "How attention reads paged memory"); here
+ * the wave that reads a sequence's last tile for a kv head writes that head's
+ * new row first.
+ *
+ * key, value    [num_seqs, num_kv_heads, head_dim] of q_dtype (for an fp8
+ *               cache the new rows are encoded e4m3(x / scale) as by
+ *               cache_write_slots; otherwise q_dtype == cache_dtype).
+ * slot_mapping  int32 [num_seqs]: the slot of position seq_lens[s] - 1 of
+ *               sequence s (block * block_size + offset, through its table),
+ *               or negative to write nothing for s.  A slot elsewhere is the
+ *               caller's error (unspecified values, no access outside the
+ *               pools; slots outside the pool are skipped).
+ * Other arguments as paged_attn_decode (same workspace).  At most 16 query
+ * heads per kv head (PKV_ERR_UNSUPPORTED beyond): each kv head's last tile is
+ * then read by exactly the wave that writes it.
+ */
+int paged_attn_decode_fused(float* out, const void* query, int q_dtype,
+                            const void* key, const void* value,
+                            void* k_cache, void* v_cache, int cache_dtype,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* slot_mapping,
+                            const int32_t* block_tables,
+                            int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t max_seq_len,
+                            int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int64_t num_blocks, int32_t block_size,
+                            float scale, int32_t max_waves, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /*
  * paged_attn_multi_workspace_size -- bytes of device workspace

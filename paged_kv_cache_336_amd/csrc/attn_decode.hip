@@ -49,6 +49,7 @@
 // blocks leaves the output bit-identical.
 
 #include "attn_tile.h"
+#include "kv_encode.h"
 
 namespace pkv {
 
@@ -160,13 +161,58 @@ __device__ __forceinline__ void load_query(uint32_t* qw, const Seg& g,
 }
 
 // ---------------------------------------------------------------------------
+// Fused write (paged_attn_decode_fused): the new token of a row's sequence --
+// position L - 1, slot slot_mapping[s] -- is written into both pools by the
+// wave whose segment reaches the row's end, before that wave loads any tile
+// of the segment.  The row is the only reader of that position for its kv
+// head (one query-head chunk per kv head), so write-then-read within one wave
+// gives exactly the separate write followed by attention.  Lanes 0..PPR-1
+// write the K row's 16-byte pieces, lanes 32..32+PPR-1 the V row's; an fp8
+// cache stores e4m3(x / scale) as cache_write_slots does.
+// ---------------------------------------------------------------------------
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void write_new_token(const Seg& g, int L,
+                                                const AttnArgs& a, int lane) {
+  typedef Shape<QT, CT, D> S;
+  if (!g.valid || g.t_end != L || L == 0) return;
+  const int slot = a.slot_mapping[g.s];
+  if (slot < 0 || (int64_t)slot >= a.num_slots) return;  // no write
+  const int half = lane >> 5;  // 0: K, 1: V
+  const int pc = lane & 31;
+  if (pc >= S::PPR) return;
+  uint8_t* dst = static_cast<uint8_t*>(const_cast<void*>(
+                     half ? a.v_cache : a.k_cache)) +
+                 ((int64_t)slot * a.num_kv_heads + g.h) * S::ROW_BYTES + 16 * pc;
+  const uint8_t* src =
+      static_cast<const uint8_t*>(half ? a.new_value : a.new_key) +
+      ((int64_t)g.s * a.num_kv_heads + g.h) * D * QT::bytes;
+  if constexpr (is_fp8<CT>::value) {
+    u32x4_t in[QT::bytes];  // the piece's 16 source elements
+#pragma unroll
+    for (int q = 0; q < QT::bytes; ++q)
+      in[q] = *reinterpret_cast<const u32x4_t*>(src + 16 * (QT::bytes * pc + q));
+    const float sc = half ? *a.v_scale : *a.k_scale;
+    *reinterpret_cast<u32x4_t*>(dst) = encode_piece_e4m3<QT>(in, sc);
+  } else {
+    *reinterpret_cast<u32x4_t*>(dst) =
+        *reinterpret_cast<const u32x4_t*>(src + 16 * pc);
+  }
+}
+
+// Waits until this wave's stores have completed, so its later loads of the
+// same bytes see them.
+__device__ __forceinline__ void wait_stores() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt(7), lgkmcnt(15)
+}
+
+// ---------------------------------------------------------------------------
 // Partition kernel: wave w streams tiles [ceil(w T / W), ceil((w+1) T / W))
 // of the row-major tile list, one segment (run of one row) after another.
 // The next segment's query rows and table window are requested when a
 // segment starts and its first tile during the current segment's last tile,
 // so a wave's loads run on across segment boundaries.
 // ---------------------------------------------------------------------------
-template <typename QT, typename CT, int D, bool UNIFORM>
+template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_decode_kernel(AttnArgs a) {
   typedef Shape<QT, CT, D> S;
@@ -257,6 +303,11 @@ void attn_decode_kernel(AttnArgs a) {
   int64_t pos_n = tb + X.ntiles;  // first tile of the next segment
   Seg Xn = segment_at<S::TT>(pos_n, te, U, tex, lens, a);
   bool first_seg = true;
+  if constexpr (WRITE) {
+    write_new_token<QT, CT, D>(X, lens[X.s], a, lane);
+    write_new_token<QT, CT, D>(Xn, lens[Xn.s], a, lane);
+    wait_stores();
+  }
   uint32_t ta = 0, tbw = 0, ta_n = 0, tb_n = 0;
   if constexpr (UNIFORM) {
     ta = load_window(X, 0, a, lane);
@@ -396,6 +447,10 @@ void attn_decode_kernel(AttnArgs a) {
     for (int q = 0; q < S::QWORDS; ++q) qw[q] = qn[q];
     pos_n += X.ntiles;
     Xn = segment_at<S::TT>(pos_n, te, U, tex, lens, a);
+    if constexpr (WRITE) {
+      write_new_token<QT, CT, D>(Xn, lens[Xn.s], a, lane);
+      wait_stores();
+    }
     if constexpr (UNIFORM) {
       ta_n = load_window(Xn, 0, a, lane);
       tb_n = load_window(Xn, 1, a, lane);
@@ -406,9 +461,9 @@ void attn_decode_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <typename QT, typename CT, int D, bool UNIFORM>
+template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE>
 static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
-  auto kernel = attn_decode_kernel<QT, CT, D, UNIFORM>;
+  auto kernel = attn_decode_kernel<QT, CT, D, UNIFORM, WRITE>;
   const size_t dyn = ((size_t)2 * a.num_seqs + 1) * sizeof(int);
   const int grid = resident_grid(kernel, dyn, max_waves);
   if (grid < 0) return hipErrorInvalidValue;
@@ -430,30 +485,37 @@ static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
 
 template <typename QT, typename CT, int D>
 static hipError_t launch_d(const AttnArgs& a, int max_waves, bool uniform,
-                           hipStream_t stream) {
-  if (uniform) return launch_u<QT, CT, D, true>(a, max_waves, stream);
-  return launch_u<QT, CT, D, false>(a, max_waves, stream);
+                           bool fused, hipStream_t stream) {
+  if (fused) {
+    if (uniform) return launch_u<QT, CT, D, true, true>(a, max_waves, stream);
+    return launch_u<QT, CT, D, false, true>(a, max_waves, stream);
+  }
+  if (uniform) return launch_u<QT, CT, D, true, false>(a, max_waves, stream);
+  return launch_u<QT, CT, D, false, false>(a, max_waves, stream);
 }
 
 template <typename QT, typename CT>
 static hipError_t launch_t(const AttnArgs& a, int head_dim, int max_waves,
-                           bool uniform, hipStream_t stream) {
-  if (head_dim == 64) return launch_d<QT, CT, 64>(a, max_waves, uniform, stream);
-  return launch_d<QT, CT, 128>(a, max_waves, uniform, stream);
+                           bool uniform, bool fused, hipStream_t stream) {
+  if (head_dim == 64)
+    return launch_d<QT, CT, 64>(a, max_waves, uniform, fused, stream);
+  return launch_d<QT, CT, 128>(a, max_waves, uniform, fused, stream);
 }
 
 hipError_t launch_attn_decode(const AttnArgs& a, int q_dtype, int cache_dtype,
-                              int head_dim, int max_waves,
+                              int head_dim, int max_waves, bool fused,
                               hipStream_t stream) {
-  const bool uniform = (a.block_size % 16) == 0;
+  const bool u = (a.block_size % 16) == 0;
+  const int hd = head_dim;
+  const int mw = max_waves;
   switch (cache_dtype) {
-    case PKV_F32: return launch_t<F32, F32>(a, head_dim, max_waves, uniform, stream);
-    case PKV_F16: return launch_t<F16, F16>(a, head_dim, max_waves, uniform, stream);
-    case PKV_BF16: return launch_t<BF16, BF16>(a, head_dim, max_waves, uniform, stream);
+    case PKV_F32: return launch_t<F32, F32>(a, hd, mw, u, fused, stream);
+    case PKV_F16: return launch_t<F16, F16>(a, hd, mw, u, fused, stream);
+    case PKV_BF16: return launch_t<BF16, BF16>(a, hd, mw, u, fused, stream);
     case PKV_FP8_E4M3:
-      if (q_dtype == PKV_BF16) return launch_t<BF16, FP8>(a, head_dim, max_waves, uniform, stream);
-      if (q_dtype == PKV_F16) return launch_t<F16, FP8>(a, head_dim, max_waves, uniform, stream);
-      return launch_t<F32, FP8>(a, head_dim, max_waves, uniform, stream);
+      if (q_dtype == PKV_BF16) return launch_t<BF16, FP8>(a, hd, mw, u, fused, stream);
+      if (q_dtype == PKV_F16) return launch_t<F16, FP8>(a, hd, mw, u, fused, stream);
+      return launch_t<F32, FP8>(a, hd, mw, u, fused, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -10,15 +10,20 @@
 // them.
 //
 // Work split: as for one token per sequence (attn_decode.hip), with the
-// MFMA's 16 query columns packing (token, head) pairs: a row is (sequence,
-// kv head, tpr = 16 / G consecutive new tokens), its columns are those tokens'
-// G query heads, token-major.  Every row of a sequence spans the sequence's
-// ceil(L_s / 32) tiles in the unit list; tiles past the row's last column
-// limit are neither loaded nor computed, and inside the row each column
-// masks keys past its own token.  All units of all rows are divided evenly
-// among the waves and rows cut between waves are merged by log-sum-exp in a
-// second kernel, exactly as in the one-token case.  With one new token per
-// sequence this is the one-token kernel's split and arithmetic.
+// MFMA's 16 query columns packing (token, head) pairs: a column group holds
+// tpr = 16 / G consecutive new tokens of one kv head, their G query heads
+// token-major.  A row is (sequence, kv head, NG consecutive groups): the
+// wave computing a tile of it runs the tile's K registers and V reads
+// through all NG groups, so a sequence's keys and values are read once per
+// NG * tpr new tokens (NG = 4 for long query runs such as a prompt chunk,
+// 1 for a few drafted tokens).  Every row of a sequence spans the
+// sequence's ceil(L_s / 32) tiles in the unit list; tiles past the row's
+// last column limit are neither loaded nor computed, and inside the row
+// each column masks keys past its own token.  All units of all rows are
+// divided evenly among the waves and rows cut between waves are merged by
+// log-sum-exp in a second kernel, exactly as in the one-token case.  With
+// one new token per sequence this is the one-token kernel's split and
+// arithmetic.
 
 #include "attn_tile.h"
 
@@ -26,7 +31,7 @@ namespace pkv {
 
 // A segment of a multi-query row.
 struct MSeg : Seg {
-  int rr;  // row within its (sequence, kv head): tokens rr * tpr ..
+  int rr;  // row within its (sequence, kv head): tokens rr * row_tokens ..
   int q0;  // first query row of the sequence
   int nq;  // new tokens of the sequence
   int L;   // its length
@@ -73,7 +78,7 @@ __device__ __forceinline__ MSeg mseg_at(int64_t t, int64_t te, const int* tex,
   const int L = __builtin_amdgcn_readfirstlane(lens[lo]);
   const int nq = __builtin_amdgcn_readfirstlane(qn[lo]);
   const int ts = (L + 31) / 32;
-  const int rps = (nq + a.tpr - 1) / a.tpr;
+  const int rps = (nq + a.row_tokens - 1) / a.row_tokens;
   const int r = ti - base;
   const int u = r / ts;
   const int k0 = r - u * ts;
@@ -88,29 +93,32 @@ __device__ __forceinline__ MSeg mseg_at(int64_t t, int64_t te, const int* tex,
   g.ntiles = (int)(end - t);
   g.t_begin = 32 * k0;
   // the row's last column sees tokens up to L - nq + (its token) + 1
-  const int tok_end = L - nq + min(nq, (g.rr + 1) * a.tpr);
+  const int tok_end = L - nq + min(nq, (g.rr + 1) * a.row_tokens);
   g.t_end = min(tok_end, 32 * (k0 + g.ntiles));
   g.wb = g.t_begin / a.block_size;
   g.full = k0 == 0 && end == row_end;
   return g;
 }
 
-// Lane column c of a row: token rr * tpr + c / G of the sequence's new ones,
-// query head h * G + c % G; -1 past the row's tokens.
+// Lane column c of group grp of a row: token rr * row_tokens + grp * tpr +
+// c / G of the sequence's new ones, query head h * G + c % G; -1 past the
+// row's tokens.
 __device__ __forceinline__ int mq_token(const MSeg& g, const AttnArgs& a,
-                                        int c) {
-  const int tok = g.rr * a.tpr + c / a.group;
+                                        int grp, int c) {
+  const int tok = g.rr * a.row_tokens + grp * a.tpr + c / a.group;
   return g.valid && c < a.tpr * a.group && tok < g.nq ? tok : -1;
 }
 
-// The row's query rows as the B operand (zeros for columns past its tokens).
+// Group grp's query rows as a B operand (zeros for columns past the row's
+// tokens).
 template <typename QT, typename CT, int D>
 __device__ __forceinline__ void load_query_mq(uint32_t* qw, const MSeg& g,
-                                              const AttnArgs& a, int lane) {
+                                              const AttnArgs& a, int grp,
+                                              int lane) {
   typedef Shape<QT, CT, D> S;
   const int c = lane & 15;
   const int j = lane >> 4;
-  const int tok = mq_token(g, a, c);
+  const int tok = mq_token(g, a, grp, c);
   // a column past the row's tokens reads beyond the range: zeros, no traffic
   const uint32_t rowoff =
       tok >= 0 ? ((uint32_t)(g.q0 + tok) * (uint32_t)a.num_q_heads +
@@ -137,20 +145,29 @@ __device__ __forceinline__ void load_query_mq(uint32_t* qw, const MSeg& g,
   }
 }
 
-// Key limit of this lane's column in segment g (0: the column sees nothing).
+// Key limit of this lane's column of group grp in segment g (0: the column
+// sees nothing).
 __device__ __forceinline__ int mq_limit(const MSeg& g, const AttnArgs& a,
-                                        int lane) {
-  const int tok = mq_token(g, a, lane & 15);
+                                        int grp, int lane) {
+  const int tok = mq_token(g, a, grp, lane & 15);
   return tok >= 0 ? min(g.t_end, g.L - g.nq + tok + 1) : 0;
 }
 
-template <typename QT, typename CT, int D, bool UNIFORM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+// NG = 1 keeps the one-token kernel's register budget (two waves per SIMD
+// possible); NG = 4 needs up to 512 registers per lane (one wave per SIMD,
+// which is what the grid runs anyway).
+template <int NG> struct MultiOccupancy { static constexpr int waves = 2; };
+template <> struct MultiOccupancy<4> { static constexpr int waves = 1; };
+
+template <typename QT, typename CT, int D, bool UNIFORM, int NG>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(MultiOccupancy<NG>::waves)))
 void attn_multi_kernel(AttnArgs a) {
   typedef Shape<QT, CT, D> S;
   static_assert(S::SUB == 1, "one 32-token sub-tile per tile");
   constexpr int NBLK = S::NBLK;
-  constexpr bool PREFETCH = UNIFORM && CT::bytes <= 2;
+  // (four groups leave no registers for a second tile in flight)
+  constexpr bool PREFETCH = UNIFORM && CT::bytes <= 2 && NG == 1;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * S::STAGE_BYTES];
   __shared__ int sm_wsum[kWaves];
@@ -179,13 +196,14 @@ void attn_multi_kernel(AttnArgs a) {
       lens[i] = m.L;
       qs0[i] = m.q0;
       qn[i] = m.nq;
-      sum += a.num_kv_heads * ((m.nq + a.tpr - 1) / a.tpr) * ((m.L + 31) / 32);
+      sum += a.num_kv_heads * ((m.nq + a.row_tokens - 1) / a.row_tokens) *
+             ((m.L + 31) / 32);
     }
     const int incl = block_inclusive_scan(sum, sm_wsum);
     int run = incl - sum;
     for (int i = b0; i < b1; ++i) {
       tex[i] = run;
-      run += a.num_kv_heads * ((qn[i] + a.tpr - 1) / a.tpr) *
+      run += a.num_kv_heads * ((qn[i] + a.row_tokens - 1) / a.row_tokens) *
              ((lens[i] + 31) / 32);
     }
     if (tid == kThreads - 1) tex[nS] = incl;
@@ -223,8 +241,13 @@ void attn_multi_kernel(AttnArgs a) {
     ta_n = load_window(Xn, 0, a, lane);
     tb_n = load_window(Xn, 1, a, lane);
   }
-  uint32_t qw[S::QWORDS];
-  load_query_mq<QT, CT, D>(qw, X, a, lane);
+  // One group: the next segment's query rows are requested when a segment
+  // starts (as in the one-token kernel).  Four: there are no registers for a
+  // second set, and each segment's are loaded when it starts.
+  constexpr bool QPREFETCH = NG == 1;
+  uint32_t qw[NG][S::QWORDS];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) load_query_mq<QT, CT, D>(qw[g], X, a, g, lane);
   TileRegs<QT, CT, D> cur;
   if constexpr (PREFETCH)
     load_tile_uniform<QT, CT, D>(cur, a.block_size, a.num_blocks, ta, tbw,
@@ -233,15 +256,19 @@ void attn_multi_kernel(AttnArgs a) {
                                  X.t_begin, X.t_end, lane);
 
   while (X.valid) {
-    uint32_t qn_w[S::QWORDS];
-    load_query_mq<QT, CT, D>(qn_w, Xn, a, lane);
-    const int lim = mq_limit(X, a, lane);
-
-    WaveState<NBLK> st;
-    st.m = -INFINITY;
-    st.l = 0.f;
+    uint32_t qn_w[QPREFETCH ? NG : 1][S::QWORDS];
+    int lim[NG];
+    WaveState<NBLK> st[NG];
 #pragma unroll
-    for (int n = 0; n < NBLK; ++n) st.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < NG; ++g) {
+      if constexpr (QPREFETCH)
+        load_query_mq<QT, CT, D>(qn_w[g], Xn, a, g, lane);
+      lim[g] = mq_limit(X, a, g, lane);
+      st[g].m = -INFINITY;
+      st[g].l = 0.f;
+#pragma unroll
+      for (int n = 0; n < NBLK; ++n) st[g].o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     const uint8_t* kbase = kpool + (int64_t)X.h * S::ROW_BYTES;
     const uint8_t* vbase = vpool + (int64_t)X.h * S::ROW_BYTES;
@@ -271,8 +298,8 @@ void attn_multi_kernel(AttnArgs a) {
             lane);
         __builtin_amdgcn_sched_barrier(0);
         if (live)
-          compute_tile<QT, CT, D, true>(cur.kw[0], qw, st, vt, t0, X.t_end,
-                                        qk_mul, lane, lim);
+          compute_tile_groups<QT, CT, D, NG>(cur.kw[0], qw, st, vt, t0, lim,
+                                             qk_mul, lane);
         cur = nxt;
       }
     } else {
@@ -294,16 +321,18 @@ void attn_multi_kernel(AttnArgs a) {
                                    kbase, vbase, stride, t0, X.t_end, lane);
         }
         stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
-        compute_tile<QT, CT, D, true>(cur.kw[0], qw, st, vt, t0, X.t_end,
-                                      qk_mul, lane, lim);
+        compute_tile_groups<QT, CT, D, NG>(cur.kw[0], qw, st, vt, t0, lim,
+                                           qk_mul, lane);
       }
     }
 
     // ---------------- the segment's output (this wave alone) ----------------
-    float l_tot = xor_sum(st.l, 16);
-    l_tot = xor_sum(l_tot, 32);
-    const int tok = mq_token(X, a, c);
-    if (tok >= 0) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float l_tot = xor_sum(st[g].l, 16);
+      l_tot = xor_sum(l_tot, 32);
+      const int tok = mq_token(X, a, g, c);
+      if (tok < 0) continue;
       if (X.full) {
         const int64_t row = (int64_t)(X.q0 + tok) * a.num_q_heads +
                             X.h * a.group + c % a.group;
@@ -311,15 +340,17 @@ void attn_multi_kernel(AttnArgs a) {
         float* dst = a.out + row * D + 4 * j;
 #pragma unroll
         for (int n = 0; n < NBLK; ++n)
-          *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st.o[n] * f;
+          *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st[g].o[n] * f;
       } else {
-        const int64_t sl = slot_index(w, first_seg ? 0 : 1) * gmax + c;
+        // slot column: the token's place in the row times G plus the head
+        const int64_t sl = slot_index(w, first_seg ? 0 : 1) * gmax +
+                           g * a.tpr * a.group + c;
         float* dst = a.part_o + sl * D + 4 * j;
 #pragma unroll
         for (int n = 0; n < NBLK; ++n)
-          *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st.o[n];
+          *reinterpret_cast<f32x4_t*>(dst + 16 * n) = st[g].o[n];
         if (j == 0) {
-          a.part_m[sl] = st.m;
+          a.part_m[sl] = st[g].m;
           a.part_l[sl] = l_tot;
         }
       }
@@ -333,7 +364,14 @@ void attn_multi_kernel(AttnArgs a) {
       tbw = tb_n;
     }
 #pragma unroll
-    for (int q = 0; q < S::QWORDS; ++q) qw[q] = qn_w[q];
+    for (int g = 0; g < NG; ++g) {
+      if constexpr (QPREFETCH) {
+#pragma unroll
+        for (int q = 0; q < S::QWORDS; ++q) qw[g][q] = qn_w[g][q];
+      } else {
+        load_query_mq<QT, CT, D>(qw[g], X, a, g, lane);
+      }
+    }
     pos_n += X.ntiles;
     Xn = mseg_at(pos_n, te, tex, lens, qs0, qn, a);
     if constexpr (UNIFORM) {
@@ -355,7 +393,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_multi_merge_kernel(
   const int h = sh % a.num_kv_heads;
   const int s = sh / a.num_kv_heads;
   const MqSeq m = mq_seq(a, s);
-  const int rps = (m.nq + a.tpr - 1) / a.tpr;
+  const int rps = (m.nq + a.row_tokens - 1) / a.row_tokens;
   if (rr >= rps) return;
   const int ts = (m.L + 31) / 32;
   const int* tex = a.tile_prefix;
@@ -368,8 +406,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_multi_merge_kernel(
   const int npieces = wl - wf + 1;
   const int q_first = first_tile_of_wave(wf, T, W) < r0 ? 1 : 0;
   const int G = a.group;
-  const int gcount = min(a.tpr, m.nq - rr * a.tpr) * G;
-  const int64_t tok0 = (int64_t)m.q0 + rr * a.tpr;
+  const int gcount = min(a.row_tokens, m.nq - rr * a.row_tokens) * G;
+  const int64_t tok0 = (int64_t)m.q0 + rr * a.row_tokens;
   merge_row<D, SCALED, BATCH>(
       a, wf, npieces, q_first, gcount,
       [&](int g) {
@@ -378,11 +416,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_multi_merge_kernel(
       red_o, red_m, red_l);
 }
 
-template <typename QT, typename CT, int D, bool UNIFORM>
+template <typename QT, typename CT, int D, bool UNIFORM, int NG>
 static hipError_t launch_mu(AttnArgs a, int max_waves, hipStream_t stream) {
-  auto kernel = attn_multi_kernel<QT, CT, D, UNIFORM>;
+  auto kernel = attn_multi_kernel<QT, CT, D, UNIFORM, NG>;
   const size_t dyn = ((size_t)4 * a.num_seqs + 1) * sizeof(int);
-  const int grid = resident_grid(kernel, dyn, max_waves);
+  const int cap = max_waves > 0 && max_waves < kMaxWavesMulti ? max_waves
+                                                              : kMaxWavesMulti;
+  const int grid = resident_grid(kernel, dyn, cap);
   if (grid < 0) return hipErrorInvalidValue;
   a.num_waves = grid * kWaves;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
@@ -399,8 +439,14 @@ static hipError_t launch_mu(AttnArgs a, int max_waves, hipStream_t stream) {
 template <typename QT, typename CT, int D>
 static hipError_t launch_md(const AttnArgs& a, int max_waves, bool uniform,
                             hipStream_t stream) {
-  if (uniform) return launch_mu<QT, CT, D, true>(a, max_waves, stream);
-  return launch_mu<QT, CT, D, false>(a, max_waves, stream);
+  if constexpr (!same<QT, F32>::value) {
+    if (a.row_tokens / a.tpr == 4) {
+      if (uniform) return launch_mu<QT, CT, D, true, 4>(a, max_waves, stream);
+      return launch_mu<QT, CT, D, false, 4>(a, max_waves, stream);
+    }
+  }
+  if (uniform) return launch_mu<QT, CT, D, true, 1>(a, max_waves, stream);
+  return launch_mu<QT, CT, D, false, 1>(a, max_waves, stream);
 }
 
 template <typename QT, typename CT>
@@ -408,6 +454,13 @@ static hipError_t launch_mt(const AttnArgs& a, int head_dim, int max_waves,
                             bool uniform, hipStream_t stream) {
   if (head_dim == 64) return launch_md<QT, CT, 64>(a, max_waves, uniform, stream);
   return launch_md<QT, CT, 128>(a, max_waves, uniform, stream);
+}
+
+int multi_groups_per_row(int q_dtype, int max_query_len, int tpr) {
+  // four groups once a row would hold three or more (float32 queries keep
+  // one: their operands alone fill the registers)
+  if (q_dtype == PKV_F32) return 1;
+  return (max_query_len + tpr - 1) / tpr >= 3 ? 4 : 1;
 }
 
 hipError_t launch_attn_multi(const AttnArgs& a, int q_dtype, int cache_dtype,

@@ -253,26 +253,19 @@ __device__ __forceinline__ void stage_v(const u32x4_t (&vraw)[Shape<QT, CT, D>::
 }
 
 // ---------------------------------------------------------------------------
-// One tile: S = K Q^T, online-softmax update, O^T += V^T P^T.  vt is this
-// wave's LDS slice (32 rows of D PV-operand elements), already holding the
-// tile's V rows (stage_v).
+// One tile: S = K Q^T, online-softmax update, O^T += V^T P^T, in three parts
+// so that several 16-column query groups can share one tile's K registers
+// and V reads (compute_tile_groups).  vt is this wave's LDS slice (32 rows of
+// D PV-operand elements), already holding the tile's V rows (stage_v).
 // ---------------------------------------------------------------------------
-// CAUSAL: every lane column has its own key limit `lim` (the caller folds
-// t_end into it); a column may then see no key of a tile at all, and its
-// state stays empty instead of turning into 0 * inf.
-template <typename QT, typename CT, int D, bool CAUSAL = false>
-__device__ __forceinline__ void compute_tile(
-    const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS], const uint32_t* qw,
-    WaveState<Shape<QT, CT, D>::NBLK>& st, uint8_t* vt, int t0, int t_end,
-    float qk_mul, int lane, int lim = 0) {
-  typedef Shape<QT, CT, D> S;
-  typedef typename S::PVT PVT;
-  constexpr int PVB = S::PVB;
-  const int c = lane & 15;
-  const int j = lane >> 4;
 
-  // ---------------- S = K . Q^T ----------------
-  f32x4_t sacc[2];
+// S = K Q^T of one 16-column group: sacc[hh][e] is the score of token
+// 16 hh + 4 j + e against query column c (lane = c + 16 j).
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void qk_tile(
+    const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS], const uint32_t* qw,
+    f32x4_t (&sacc)[2]) {
+  typedef Shape<QT, CT, D> S;
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     sacc[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -318,8 +311,24 @@ __device__ __forceinline__ void compute_tile(
       sacc[hh] = Mma<QT>::step(ka, qb, sacc[hh]);
     }
   }
+}
 
-  // ---------------- online softmax (log2 domain) ----------------
+// Online-softmax update (log2 domain) of one group from its scores; leaves
+// P in the PV B-operand layout (for 16-bit caches split hi + lo).  Keys at or
+// past t_end -- with CAUSAL, past this lane column's own limit `lim`, which
+// the caller folds t_end into -- get weight 0.  With CAUSAL a column may see
+// no key of a tile at all; its state then stays empty instead of turning
+// into 0 * inf.
+template <typename QT, typename CT, int D, bool CAUSAL>
+__device__ __forceinline__ void softmax_tile(
+    const f32x4_t (&sacc)[2], WaveState<Shape<QT, CT, D>::NBLK>& st, int t0,
+    int t_end, int lim, float qk_mul, int lane,
+    typename Mma<typename Shape<QT, CT, D>::PVT>::operand& pb_hi,
+    typename Mma<typename Shape<QT, CT, D>::PVT>::operand& pb_lo) {
+  typedef Shape<QT, CT, D> S;
+  typedef typename S::PVT PVT;
+  constexpr int PVB = S::PVB;
+  const int j = lane >> 4;
   float sv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -347,8 +356,6 @@ __device__ __forceinline__ void compute_tile(
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) st.o[n] *= alpha;
 
-  // ---------------- O^T += V^T . P^T ----------------
-  typename Mma<PVT>::operand pb_hi, pb_lo;
   if constexpr (PVB == 2) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -365,31 +372,88 @@ __device__ __forceinline__ void compute_tile(
 #pragma unroll
     for (int e = 0; e < 8; ++e) pb_hi[e] = pv[e];
   }
+}
+
+// V^T of output block n (16 columns of D) in the PV A-operand layout.
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void v_operand(
+    const uint8_t* vt, int n, int lane,
+    typename Mma<typename Shape<QT, CT, D>::PVT>::operand& va) {
+  typedef Shape<QT, CT, D> S;
+  constexpr int PVB = S::PVB;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+  if constexpr (PVB == 2) {
+    // Transposing LDS reads: within each 16-lane group, lane 4k + q
+    // addresses 4 columns (4q .. 4q + 3 of output block n) of token
+    // 4j + k, and lane c receives column c of the four tokens 4j .. 4j+3
+    // -- operand slots 0-3; the same read 16 tokens on gives slots 4-7.
+    const int tk = 4 * j + (c >> 2);
+    const int off = ((n ^ (tk & (S::SPANS - 1))) << 5) + ((c & 3) << 3);
+    const v4i16_t lo = lds_read_tr16(vt + tk * S::LDS_ROW + off);
+    const v4i16_t hi = lds_read_tr16(vt + (tk + 16) * S::LDS_ROW + off);
+    va[0] = pack_u16x2(lo[0], lo[1]);
+    va[1] = pack_u16x2(lo[2], lo[3]);
+    va[2] = pack_u16x2(hi[0], hi[1]);
+    va[3] = pack_u16x2(hi[2], hi[3]);
+  } else {
+    const int byte = (16 * n + c) * PVB;
+    const int col = (((byte >> 4) ^ (j * PVB)) << 4) + (byte & 15);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      va[e] = *reinterpret_cast<const float*>(vt + slot_token(j, e) * S::LDS_ROW + col);
+  }
+}
+
+// One tile for one 16-column group.
+template <typename QT, typename CT, int D, bool CAUSAL = false>
+__device__ __forceinline__ void compute_tile(
+    const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS], const uint32_t* qw,
+    WaveState<Shape<QT, CT, D>::NBLK>& st, uint8_t* vt, int t0, int t_end,
+    float qk_mul, int lane, int lim = 0) {
+  typedef Shape<QT, CT, D> S;
+  typedef typename S::PVT PVT;
+  f32x4_t sacc[2];
+  qk_tile<QT, CT, D>(kw, qw, sacc);
+  typename Mma<PVT>::operand pb_hi, pb_lo;
+  softmax_tile<QT, CT, D, CAUSAL>(sacc, st, t0, t_end, lim, qk_mul, lane,
+                                  pb_hi, pb_lo);
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) {
     typename Mma<PVT>::operand va;
-    if constexpr (PVB == 2) {
-      // Transposing LDS reads: within each 16-lane group, lane 4k + q
-      // addresses 4 columns (4q .. 4q + 3 of output block n) of token
-      // 4j + k, and lane c receives column c of the four tokens 4j .. 4j+3
-      // -- operand slots 0-3; the same read 16 tokens on gives slots 4-7.
-      const int tk = 4 * j + (c >> 2);
-      const int off = ((n ^ (tk & (S::SPANS - 1))) << 5) + ((c & 3) << 3);
-      const v4i16_t lo = lds_read_tr16(vt + tk * S::LDS_ROW + off);
-      const v4i16_t hi = lds_read_tr16(vt + (tk + 16) * S::LDS_ROW + off);
-      va[0] = pack_u16x2(lo[0], lo[1]);
-      va[1] = pack_u16x2(lo[2], lo[3]);
-      va[2] = pack_u16x2(hi[0], hi[1]);
-      va[3] = pack_u16x2(hi[2], hi[3]);
-    } else {
-      const int byte = (16 * n + c) * PVB;
-      const int col = (((byte >> 4) ^ (j * PVB)) << 4) + (byte & 15);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        va[e] = *reinterpret_cast<const float*>(vt + slot_token(j, e) * S::LDS_ROW + col);
-    }
+    v_operand<QT, CT, D>(vt, n, lane, va);
     st.o[n] = Mma<PVT>::step(va, pb_hi, st.o[n]);
     if constexpr (S::PSPLIT) st.o[n] = Mma<PVT>::step(va, pb_lo, st.o[n]);
+  }
+}
+
+// One tile for NG 16-column groups of query columns (causal limits per
+// group): the tile's K registers and each V^T read serve every group.
+template <typename QT, typename CT, int D, int NG>
+__device__ __forceinline__ void compute_tile_groups(
+    const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS],
+    const uint32_t (&qw)[NG][Shape<QT, CT, D>::QWORDS],
+    WaveState<Shape<QT, CT, D>::NBLK> (&st)[NG], uint8_t* vt, int t0,
+    const int (&lim)[NG], float qk_mul, int lane) {
+  typedef Shape<QT, CT, D> S;
+  typedef typename S::PVT PVT;
+  typename Mma<PVT>::operand pb_hi[NG], pb_lo[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    f32x4_t sacc[2];
+    qk_tile<QT, CT, D>(kw, qw[g], sacc);
+    softmax_tile<QT, CT, D, true>(sacc, st[g], t0, 0, lim[g], qk_mul, lane,
+                                  pb_hi[g], pb_lo[g]);
+  }
+#pragma unroll
+  for (int n = 0; n < S::NBLK; ++n) {
+    typename Mma<PVT>::operand va;
+    v_operand<QT, CT, D>(vt, n, lane, va);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      st[g].o[n] = Mma<PVT>::step(va, pb_hi[g], st[g].o[n]);
+      if constexpr (S::PSPLIT) st[g].o[n] = Mma<PVT>::step(va, pb_lo[g], st[g].o[n]);
+    }
   }
 }
 
@@ -441,13 +505,17 @@ __device__ __forceinline__ T load_at(const void* base, uint32_t byte_off) {
                                      byte_off);
 }
 
+// (The fused multiply-adds are written out, so that every instance of the
+// fold rounds the same way whatever the compiler would contract: a row's
+// result then depends only on its pieces, not on the merge's batching.)
 __device__ __forceinline__ void lse_fold(float& m, float& l, f32x4_t& acc,
                                          float m2, float l2, f32x4_t acc2) {
   const float M = fmaxf(m, m2);
   if (M == -INFINITY) return;  // both empty
   const float a1 = fast_exp2(m - M), a2 = fast_exp2(m2 - M);
-  l = l * a1 + l2 * a2;
-  acc = acc * a1 + acc2 * a2;
+  l = __builtin_fmaf(l2, a2, l * a1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(acc2[e], a2, acc[e] * a1);
   m = M;
 }
 

@@ -12,48 +12,11 @@
 // copy-on-write"): each (src, dst) pair copies a whole block of both pools
 // with 16-byte loads/stores, one grid row per pair.
 
+#include "kv_encode.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
-
-// OCP E4M3 ("fn") encoder: round to nearest even on the float32 bit pattern,
-// values of magnitude >= 448 (including infinity) saturate to 448, NaN keeps
-// its sign with the all-ones code.
-__device__ __forceinline__ uint32_t encode_e4m3(float y) {
-  const uint32_t b = __float_as_uint(y);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const uint32_t mag = b & 0x7FFFFFFFu;
-  if (mag > 0x7F800000u) return sign | 0x7Fu;          // NaN
-  if (mag >= 0x43E00000u) return sign | 0x7Eu;         // >= 448
-  if (mag < 0x3C800000u) {                             // < 2^-6: step 2^-9
-    const float q = __uint_as_float(mag) * 512.0f;     // exact scaling
-    return sign | (uint32_t)__builtin_rintf(q);        // 0..8, ties to even
-  }
-  const uint32_t e = (mag >> 23) - 120u;               // biased for E4M3
-  const uint32_t m = (mag >> 20) & 7u;
-  const uint32_t rest = mag & 0xFFFFFu;
-  const uint32_t up = (rest > 0x80000u) | ((rest == 0x80000u) & (m & 1u));
-  uint32_t code = (e << 3) + m + up;                   // carry bumps e
-  code = code > 0x7Eu ? 0x7Eu : code;
-  return sign | code;
-}
-
-// Element e (0..15) of a 16-element source piece held as 16-byte words.
-template <typename ST>
-__device__ __forceinline__ float piece_elem(const u32x4_t* w, int e);
-template <> __device__ __forceinline__ float piece_elem<F32>(const u32x4_t* w, int e) {
-  return __uint_as_float(w[e >> 2][e & 3]);
-}
-template <> __device__ __forceinline__ float piece_elem<F16>(const u32x4_t* w, int e) {
-  const uint32_t word = w[e >> 3][(e >> 1) & 3];
-  const uint16_t h = (uint16_t)(word >> (16 * (e & 1)));
-  return static_cast<float>(__builtin_bit_cast(_Float16, h));
-}
-template <> __device__ __forceinline__ float piece_elem<BF16>(const u32x4_t* w, int e) {
-  const uint32_t word = w[e >> 3][(e >> 1) & 3];
-  return __uint_as_float((word >> (16 * (e & 1))) << 16);
-}
 
 // Same dtype: bit copy of 16-byte pieces.
 __global__ __launch_bounds__(256) void cache_write_copy_kernel(WriteArgs a,
@@ -103,19 +66,8 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(WriteArgs a) {
       vin[q] = vsrc[q];
     }
     if (slot < 0 || slot >= a.num_slots) continue;
-    u32x4_t kout, vout;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t kw = 0, vw = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int e = 4 * w + b;
-        kw |= encode_e4m3(piece_elem<ST>(kin, e) / ks) << (8 * b);
-        vw |= encode_e4m3(piece_elem<ST>(vin, e) / vs) << (8 * b);
-      }
-      kout[w] = kw;
-      vout[w] = vw;
-    }
+    const u32x4_t kout = encode_piece_e4m3<ST>(kin, ks);
+    const u32x4_t vout = encode_piece_e4m3<ST>(vin, vs);
     const int64_t off_dst = (int64_t)slot * a.row_elems + pc * 16;
     *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(a.k_cache) + off_dst) = kout;
     *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(a.v_cache) + off_dst) = vout;

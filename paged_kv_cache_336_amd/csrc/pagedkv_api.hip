@@ -36,8 +36,9 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace: tile prefix [num_seqs + 1] int32 | part_m | part_l | part_o,
 // each 256-byte aligned; two partial slots of slot_heads query columns per
 // wave.  One query token per sequence: a slot holds up to 16 query heads of
-// one kv head.  Several (multi): a slot holds 16 / group tokens of all the
-// group's heads (group <= 16).
+// one kv head.  Several (multi): a slot holds up to four column groups of
+// 16 / group tokens times the group's heads (group <= 16), for at most
+// kMaxWavesMulti waves.
 int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                int32_t head_dim, bool multi, AttnShape* out) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1) return PKV_ERR_SHAPE;
@@ -49,7 +50,9 @@ int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   if (multi && s.group > 16) return PKV_ERR_UNSUPPORTED;
   s.group_chunks = (s.group + 15) / 16;
   s.slot_heads = multi ? 16 / s.group * s.group : (s.group < 16 ? s.group : 16);
-  const size_t slots = (size_t)kMaxWaves * 2 * s.slot_heads;
+  const size_t slots =
+      multi ? (size_t)kMaxWavesMulti * 2 * kMaxGroupsMulti * s.slot_heads
+            : (size_t)kMaxWaves * 2 * s.slot_heads;
   s.off_m = align_up((size_t)(num_seqs + 1) * 4, 256);
   s.off_l = align_up(s.off_m + slots * 4, 256);
   s.off_o = align_up(s.off_l + slots * 4, 256);
@@ -181,17 +184,22 @@ size_t paged_attn_multi_workspace_size(int32_t num_seqs, int32_t num_q_heads,
   return s.ws_bytes;
 }
 
-int paged_attn_decode(float* out, const void* query, int q_dtype,
-                      const void* k_cache, const void* v_cache,
-                      int cache_dtype, const float* k_scale,
-                      const float* v_scale, const int32_t* block_tables,
-                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                      int32_t max_seq_len, int32_t num_seqs,
-                      int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_dim, int64_t num_blocks,
-                      int32_t block_size, float scale, int32_t max_waves,
-                      void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// paged_attn_decode and paged_attn_decode_fused: checks, then the launch.
+int decode_common(float* out, const void* query, int q_dtype,
+                  const void* k_cache, const void* v_cache, int cache_dtype,
+                  const float* k_scale, const float* v_scale,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* seq_lens, int32_t max_seq_len,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                  float scale, int32_t max_waves, void* workspace,
+                  size_t workspace_bytes, const void* key, const void* value,
+                  const int32_t* slot_mapping, bool fused,
+                  hipStream_t stream) {
   if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
   if (q_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
   if (cache_dtype != PKV_FP8_E4M3 && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
@@ -204,6 +212,8 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
   const int rc =
       attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, false, &s);
   if (rc != PKV_OK) return rc;
+  // the fused write relies on one query-head chunk per kv head
+  if (fused && s.group > 16) return PKV_ERR_UNSUPPORTED;
   // every tile index of the call fits an int32
   if ((int64_t)num_seqs * num_kv_heads * s.group_chunks *
           (((int64_t)max_seq_len + 31) / 32) > INT_MAX)
@@ -211,9 +221,13 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens)
     return PKV_ERR_NULL;
+  if (fused && (!key || !value || !slot_mapping)) return PKV_ERR_NULL;
   if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return PKV_ERR_ALIGN;
+  if (fused && (!aligned(key, 16) || !aligned(value, 16) ||
+                !aligned(slot_mapping, 4)))
     return PKV_ERR_ALIGN;
   if (!workspace || workspace_bytes < s.ws_bytes) return PKV_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return PKV_ERR_ALIGN;
@@ -242,9 +256,57 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
   a.num_blocks = (int32_t)num_blocks;
   a.max_seq_tokens = max_seq_len;  // within the table's reach (checked)
   a.qk_scale_log2 = scale * 1.4426950408889634f;
+  a.new_key = key;
+  a.new_value = value;
+  a.slot_mapping = slot_mapping;
+  a.num_slots = num_blocks * (int64_t)block_size;
   return launch_attn_decode(a, q_dtype, cache_dtype, head_dim, max_waves,
-                            stream) == hipSuccess
+                            fused, stream) == hipSuccess
              ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(float* out, const void* query, int q_dtype,
+                      const void* k_cache, const void* v_cache,
+                      int cache_dtype, const float* k_scale,
+                      const float* v_scale, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                      int32_t max_seq_len, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int64_t num_blocks,
+                      int32_t block_size, float scale, int32_t max_waves,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return decode_common(out, query, q_dtype, k_cache, v_cache, cache_dtype,
+                       k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       seq_lens, max_seq_len, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, num_blocks, block_size, scale,
+                       max_waves, workspace, workspace_bytes, nullptr, nullptr,
+                       nullptr, false, stream);
+}
+
+int paged_attn_decode_fused(float* out, const void* query, int q_dtype,
+                            const void* key, const void* value,
+                            void* k_cache, void* v_cache, int cache_dtype,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* slot_mapping,
+                            const int32_t* block_tables,
+                            int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t max_seq_len,
+                            int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int64_t num_blocks, int32_t block_size,
+                            float scale, int32_t max_waves, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(out, query, q_dtype, k_cache, v_cache, cache_dtype,
+                       k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       seq_lens, max_seq_len, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, num_blocks, block_size, scale,
+                       max_waves, workspace, workspace_bytes, key, value,
+                       slot_mapping, true, stream);
 }
 
 int paged_attn_multi(float* out, const void* query, int q_dtype,
@@ -275,7 +337,8 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
                          dtype_bytes(q_dtype);
   if (qbytes >= ((int64_t)1 << 31)) return PKV_ERR_SHAPE;
   const int32_t tpr = 16 / s.group;
-  const int32_t max_rps = (max_query_len + tpr - 1) / tpr;
+  const int32_t ng = multi_groups_per_row(q_dtype, max_query_len, tpr);
+  const int32_t max_rps = (max_query_len + ng * tpr - 1) / (ng * tpr);
   // every unit index of the call, and the merge grid, fit an int32
   const int64_t rows = (int64_t)num_seqs * num_kv_heads * max_rps;
   if (rows > INT_MAX || rows * (((int64_t)max_seq_len + 31) / 32) > INT_MAX)
@@ -312,7 +375,7 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
   a.num_kv_heads = num_kv_heads;
   a.group = s.group;
   a.group_chunks = 1;
-  a.slot_heads = s.slot_heads;
+  a.slot_heads = ng * s.slot_heads;  // columns of one partial slot
   a.block_size = block_size;
   a.num_blocks = (int32_t)num_blocks;
   a.max_seq_tokens = max_seq_len;
@@ -321,6 +384,7 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
   a.num_query_tokens = num_query_tokens;
   a.max_query_len = max_query_len;
   a.tpr = tpr;
+  a.row_tokens = ng * tpr;
   a.max_rps = max_rps;
   a.query_bytes = qbytes;
   return launch_attn_multi(a, q_dtype, cache_dtype, head_dim, max_waves,

@@ -14,6 +14,15 @@ namespace pkv {
 constexpr int kMaxSeqs = 8192;
 constexpr int kMaxSeqsMulti = 4096;  // four LDS words per sequence
 
+// Several query tokens per sequence: the partition kernel's waves are capped
+// at 1024 (one per SIMD of a 256-CU part) and a partial slot holds up to four
+// 16-column groups, so the workspace stays at 1024 * 2 * 64 columns.
+constexpr int kMaxWavesMulti = 1024;
+constexpr int kMaxGroupsMulti = 4;
+
+// Column groups per row of paged_attn_multi for these arguments.
+int multi_groups_per_row(int q_dtype, int max_query_len, int tpr);
+
 // Most waves of the partition kernel (16 per CU of a 256-CU part); the
 // workspace holds two partial slots per wave.
 constexpr int kMaxWaves = 4096;
@@ -47,16 +56,23 @@ struct AttnArgs {
   const int32_t* query_start;  // [num_seqs + 1] first query row of each
   int32_t num_query_tokens;    // rows of query / out (starts clamped to it)
   int32_t max_query_len;       // new tokens per sequence at most (clamped)
-  int32_t tpr;            // query tokens per row (16 / group)
-  int32_t max_rps;        // rows per (sequence, kv head): ceil(max_query_len / tpr)
+  int32_t tpr;            // query tokens per 16-column group (16 / group)
+  int32_t row_tokens;     // query tokens per row: groups per row * tpr
+  int32_t max_rps;        // rows per (sequence, kv head): ceil(max_query_len / row_tokens)
   int64_t query_bytes;    // bytes of the whole query tensor (< 2^31)
+  // fused write of each sequence's new token (paged_attn_decode_fused) only:
+  const void* new_key;         // [num_seqs, num_kv_heads, head_dim], query type
+  const void* new_value;
+  const int32_t* slot_mapping; // [num_seqs]; < 0 or >= num_slots: no write
+  int64_t num_slots;           // num_blocks * block_size
 };
 
 hipError_t launch_attn_multi(const AttnArgs& a, int q_dtype, int cache_dtype,
                              int head_dim, int max_waves, hipStream_t stream);
 
 hipError_t launch_attn_decode(const AttnArgs& a, int q_dtype, int cache_dtype,
-                              int head_dim, int max_waves, hipStream_t stream);
+                              int head_dim, int max_waves, bool fused_write,
+                              hipStream_t stream);
 
 struct WriteArgs {
   const void* key;

@@ -7,6 +7,7 @@ first call raises.
 
 Functions keep the C names: :func:`cache_write_slots`, :func:`copy_blocks`,
 :func:`copy_block_prefixes`, :func:`paged_attn_decode`,
+:func:`paged_attn_decode_fused`,
 :func:`paged_attn_workspace_size`, :func:`paged_attn_multi`,
 :func:`paged_attn_multi_workspace_size`, :func:`pkv_status_string`.
 """
@@ -23,8 +24,8 @@ KIND_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
 
 EXPORTED = ("pkv_status_string", "cache_write_slots", "copy_blocks",
             "copy_block_prefixes", "paged_attn_workspace_size",
-            "paged_attn_decode", "paged_attn_multi_workspace_size",
-            "paged_attn_multi")
+            "paged_attn_decode", "paged_attn_decode_fused",
+            "paged_attn_multi_workspace_size", "paged_attn_multi")
 
 _lib = None
 
@@ -66,6 +67,11 @@ def load_library(path=None):
     lib.paged_attn_decode.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp, vp, i32,
                                       vp, i32, i32, i32, i32, i32, i64, i32,
                                       f32, i32, vp, sz, vp]
+    lib.paged_attn_decode_fused.restype = ci
+    lib.paged_attn_decode_fused.argtypes = [vp, vp, ci, vp, vp, vp, vp, ci,
+                                            vp, vp, vp, vp, i32, vp, i32, i32,
+                                            i32, i32, i32, i64, i32, f32, i32,
+                                            vp, sz, vp]
     lib.paged_attn_multi_workspace_size.restype = sz
     lib.paged_attn_multi_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.paged_attn_multi.restype = ci
@@ -176,8 +182,8 @@ def paged_attn_multi_workspace_size(num_seqs, num_q_heads, num_kv_heads,
 
 
 class Workspace:
-    """A device workspace for paged_attn_decode, grown (never shrunk) to the
-    largest size asked for; it needs no initialisation."""
+    """A device workspace for the attention calls, grown (never shrunk) to
+    the largest size asked for; it needs no initialisation."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -215,6 +221,30 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
         _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
         _ptr(seq_lens), int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
         int(max_waves), _ptr(buf),
+        0 if buf is None else buf.numel() * buf.element_size(),
+        _stream(stream)))
+
+
+def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
+                            slot_mapping, block_tables, seq_lens, max_seq_len,
+                            scale, k_scale=None, v_scale=None, max_waves=0,
+                            workspace=None, cache_kind=None, stream=None):
+    """cache_write_slots of one new token per sequence fused into
+    paged_attn_decode; see pagedkv.h."""
+    lib = load_library()
+    s, hq, d = query.shape
+    nb, bs, hkv, _ = k_cache.shape
+    need = paged_attn_workspace_size(s, hq, hkv, d)
+    if workspace is None:
+        key_ = str(query.device)
+        workspace = _default_ws.setdefault(key_, Workspace(query.device))
+    buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    _check("paged_attn_decode_fused", lib.paged_attn_decode_fused(
+        _ptr(out), _ptr(query), dtype_code(query), _ptr(key), _ptr(value),
+        _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache, cache_kind),
+        _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), s, hq,
+        hkv, d, nb, bs, float(scale), int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
         _stream(stream)))
 

@@ -91,6 +91,16 @@ class DeviceStep:
                               max_waves=max_waves, workspace=self.workspace,
                               cache_kind=self.cache_kind, stream=stream)
 
+    def attend_fused(self, r=0, stream=None, max_waves=0):
+        """Write and attention in one launch (one new token per sequence)."""
+        ops.paged_attn_decode_fused(
+            self.out, self.query, self.key, self.value, self.k_cache,
+            self.v_cache, self.sets[r]["slot_mapping"],
+            self.sets[r]["block_tables"], self.seq_lens, self.max_seq_len,
+            self.w.scale, k_scale=self.k_scale, v_scale=self.v_scale,
+            max_waves=max_waves, workspace=self.workspace,
+            cache_kind=self.cache_kind, stream=stream)
+
     def run(self, r=0, stream=None):
         self.copy(r, stream)
         self.write(r, stream)

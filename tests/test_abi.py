@@ -229,3 +229,32 @@ def test_multi_workspace_size(lib):
     assert 4096 * 2 * 15 * 66 * 4 <= ws3 <= 4096 * 2 * 15 * 66 * 4 + 4096
     with pytest.raises(ops.PagedKVError):
         ops.paged_attn_multi_workspace_size(8, 48, 2, 128)
+
+
+def pf(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, qd=BF16, key=FAKE, val=FAKE, kc=FAKE, vc=FAKE,
+             cache=BF16, ks=None, vs=None, slots=FAKE, bt=FAKE, mb=256,
+             sl=FAKE, maxlen=4096, S=32, hq=32, hkv=8, d=128, nb=16384,
+             bs=16, scale=0.088, waves=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.paged_attn_decode_fused(
+        a["out"], a["q"], a["qd"], a["key"], a["val"], a["kc"], a["vc"],
+        a["cache"], a["ks"], a["vs"], a["slots"], a["bt"], a["mb"], a["sl"],
+        a["maxlen"], a["S"], a["hq"], a["hkv"], a["d"], a["nb"], a["bs"],
+        a["scale"], a["waves"], a["ws"], a["wsb"], None)
+
+
+def test_fused_validation(lib):
+    assert pf(lib, S=0) == OK
+    assert pf(lib, qd=F16, cache=BF16) == DTYPE
+    assert pf(lib, qd=BF16, cache=FP8) == NULL           # scales required
+    assert pf(lib, hq=48, hkv=1) == UNSUP                # > 16 heads per kv
+    assert pf(lib, key=None) == NULL
+    assert pf(lib, val=None) == NULL
+    assert pf(lib, slots=None) == NULL
+    assert pf(lib, key=MISALIGNED) == ALIGN
+    assert pf(lib, slots=ctypes.c_void_p(4096 + 2)) == ALIGN
+    assert pf(lib, mb=255) == SHAPE
+    assert pf(lib, ws=None) == WS
+    # the unfused call still takes more than 16 heads per kv head
+    assert pa(lib, hq=48, hkv=1, ws=None) == WS
