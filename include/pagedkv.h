@@ -225,7 +225,9 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
  *               pools; slots outside the pool are skipped).
  * Other arguments as paged_attn_decode (same workspace).  At most 16 query
  * heads per kv head (PKV_ERR_UNSUPPORTED beyond): each kv head's last tile is
- * then read by exactly the wave that writes it.
+ * then read by exactly the wave that writes it.  When the batch has more
+ * (sequence, kv head) rows than the GPU holds waves, the write goes as its
+ * own launch ahead of the attention (faster there; the same result).
  */
 int paged_attn_decode_fused(float* out, const void* query, int q_dtype,
                             const void* key, const void* value,

@@ -461,6 +461,12 @@ void attn_decode_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+template <typename T> struct DtypeCode;
+template <> struct DtypeCode<F32> { static constexpr int value = PKV_F32; };
+template <> struct DtypeCode<F16> { static constexpr int value = PKV_F16; };
+template <> struct DtypeCode<BF16> { static constexpr int value = PKV_BF16; };
+template <> struct DtypeCode<FP8> { static constexpr int value = PKV_FP8_E4M3; };
+
 template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE>
 static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
   auto kernel = attn_decode_kernel<QT, CT, D, UNIFORM, WRITE>;
@@ -468,6 +474,29 @@ static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
   const int grid = resident_grid(kernel, dyn, max_waves);
   if (grid < 0) return hipErrorInvalidValue;
   a.num_waves = grid * kWaves;
+  if constexpr (WRITE) {
+    // With more rows than waves most waves end several rows, and each row
+    // end waits for its store before streaming on; the write then goes
+    // faster as its own launch ahead of the plain kernel (same result).
+    if ((int64_t)a.num_seqs * a.num_kv_heads > a.num_waves) {
+      WriteArgs w{};
+      w.key = a.new_key;
+      w.value = a.new_value;
+      w.k_cache = const_cast<void*>(a.k_cache);
+      w.v_cache = const_cast<void*>(a.v_cache);
+      w.slot_mapping = a.slot_mapping;
+      w.k_scale = a.k_scale;
+      w.v_scale = a.v_scale;
+      w.num_tokens = a.num_seqs;
+      w.num_slots = a.num_slots;
+      w.block_size = a.block_size;
+      w.row_elems = a.num_kv_heads * D;
+      const hipError_t e = launch_cache_write(w, DtypeCode<QT>::value,
+                                              DtypeCode<CT>::value, stream);
+      if (e != hipSuccess) return e;
+      return launch_u<QT, CT, D, UNIFORM, false>(a, max_waves, stream);
+    }
+  }
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
   // Pieces per cut row grow with the wave boundaries per row: fetch them in
   // batches of 16 when there are about 4 or more boundaries per row, else 4

@@ -95,11 +95,15 @@ def test_fused_small(case):
     w = W.custom_decode(seed=500 + SMALL.index(case), num_seqs=len(lens),
                         lens=lens, hq=hq, hkv=hkv, d=d, bs=bs, q_kind=q,
                         kv_kind=kv)
-    sep, fus = run_pair(w, max_waves=waves)
-    assert_same(sep, fus)
-    assert_pools_bitwise(fus, oracle_pools(w))
-    err = max_abs_err(fus.out.cpu().numpy(), oracle_out(w, oracle_pools(w)))
-    assert err <= TOL[kv], f"{err:.3g}"
+    # the whole grid: one fused launch; a few waves: with more rows than
+    # waves the write goes as its own launch first
+    for wv in (0, waves) if waves else (0,):
+        sep, fus = run_pair(w, max_waves=wv)
+        assert_same(sep, fus)
+        assert_pools_bitwise(fus, oracle_pools(w))
+        err = max_abs_err(fus.out.cpu().numpy(),
+                          oracle_out(w, oracle_pools(w)))
+        assert err <= TOL[kv], f"waves {wv}: {err:.3g}"
 
 
 def test_fused_skipped_slots():
