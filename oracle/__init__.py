@@ -23,11 +23,13 @@ Sources (cited by page title and section):
 * "How PagedAttention Works in vLLM ..." (instagit.com), section
   "write_to_paged_cache: Direct In-Place Updates": the slot-mapped scatter,
   its ``kv_cache_dtype`` and per-tensor ``k_scale``/``v_scale``.
-* OCP 8-bit floating point specification (E4M3 "fn" variant): the fp8 codec.
+* OCP 8-bit floating point specification (E4M3 "fn" and E5M2 variants):
+  the fp8 codecs.
 
 Storage conventions shared with the generator (plain numpy dtypes):
 ``"f32"`` float32, ``"f16"`` float16, ``"bf16"`` uint16 holding bfloat16
-bits, ``"fp8_e4m3"`` uint8 holding OCP E4M3 codes.
+bits, ``"fp8_e4m3"`` / ``"fp8_e5m2"`` uint8 holding OCP E4M3 / E5M2 codes;
+fp8 scales per tensor or one per kv head.
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 something other than itself (library routines, closed forms, brute force
@@ -35,6 +37,7 @@ and the pages' worked example).  No function is "parity unpinned".
 """
 
 from .fp8_e4m3 import e4m3_decode, e4m3_encode, E4M3_MAX
+from .fp8_e5m2 import e5m2_decode, e5m2_encode, E5M2_MAX
 from .storage import to_float64
 from .attention import (paged_attention, paged_attention_rows,
                         gather_sequence, attention_one_head)
@@ -45,6 +48,9 @@ __all__ = [
     "e4m3_decode",
     "e4m3_encode",
     "E4M3_MAX",
+    "e5m2_decode",
+    "e5m2_encode",
+    "E5M2_MAX",
     "to_float64",
     "paged_attention",
     "paged_attention_rows",

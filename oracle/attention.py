@@ -20,14 +20,15 @@ notes):
   cache head ``h // (Hq // Hkv)`` (contiguous groups);
 * ``seq_lens`` counts the token written in the same step, and no other
   mask applies; a sequence of length 0 yields zeros;
-* fp8 caches hold codes of ``x / scale``; the stored value is
-  ``decode(code) * scale`` (the scale is applied exactly in float64);
+* fp8 caches (E4M3 or E5M2) hold codes of ``x / scale``; the stored value
+  is ``decode(code) * scale`` (the scale is applied exactly in float64);
+  the scale is per tensor, or one per kv head;
 * the output is returned in float64 (the GPU path writes float32).
 """
 
 import numpy as np
 
-from .storage import to_float64
+from .storage import FP8_KINDS, head_scales, to_float64
 
 
 def gather_sequence(pool, table_row, seq_len, block_size, head):
@@ -41,6 +42,15 @@ def gather_sequence(pool, table_row, seq_len, block_size, head):
     blocks = pool[phys, :, head, :]                 # [n, bs, D]
     rows = blocks.reshape(n_blocks * block_size, pool.shape[3])
     return rows[:seq_len]
+
+
+def kv_scales(kv_kind, k_scale, v_scale, num_kv_heads):
+    """Per-kv-head float64 scales of the stored values (ones unless fp8)."""
+    if kv_kind in FP8_KINDS:
+        return (head_scales(k_scale, num_kv_heads),
+                head_scales(v_scale, num_kv_heads))
+    one = np.ones(num_kv_heads)
+    return one, one
 
 
 def attention_one_head(q, k, v, scale):
@@ -65,7 +75,8 @@ def paged_attention(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
     k_pool, v_pool: [num_blocks, block_size, Hkv, D] of kind ``kv_kind``.
     block_tables: int32 [S, max_blocks]; only the first ceil(L/bs) columns
     of a row are read.  seq_lens: int32 [S].
-    k_scale, v_scale: per-tensor scales, used only for ``"fp8_e4m3"``.
+    k_scale, v_scale: per-tensor scales or one per kv head, used only for
+    fp8 caches.
     """
     S, Hq, D = query.shape
     Hkv = k_pool.shape[2]
@@ -73,8 +84,7 @@ def paged_attention(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
     assert k_pool.shape[1] == block_size
     G = Hq // Hkv
     q64 = to_float64(query, q_kind)
-    ks = float(np.float32(k_scale)) if kv_kind == "fp8_e4m3" else 1.0
-    vs = float(np.float32(v_scale)) if kv_kind == "fp8_e4m3" else 1.0
+    ks, vs = kv_scales(kv_kind, k_scale, v_scale, Hkv)
     out = np.zeros((S, Hq, D), dtype=np.float64)
     for s in range(S):
         L = int(seq_lens[s])
@@ -82,9 +92,9 @@ def paged_attention(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
             continue
         for h in range(Hkv):
             k = to_float64(gather_sequence(k_pool, block_tables[s], L,
-                                           block_size, h), kv_kind) * ks
+                                           block_size, h), kv_kind) * ks[h]
             v = to_float64(gather_sequence(v_pool, block_tables[s], L,
-                                           block_size, h), kv_kind) * vs
+                                           block_size, h), kv_kind) * vs[h]
             out[s, h * G:(h + 1) * G] = attention_one_head(
                 q64[s, h * G:(h + 1) * G], k, v, scale)
     return out
@@ -99,8 +109,7 @@ def paged_attention_rows(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
     S, Hq, D = query.shape
     Hkv = k_pool.shape[2]
     G = Hq // Hkv
-    ks = float(np.float32(k_scale)) if kv_kind == "fp8_e4m3" else 1.0
-    vs = float(np.float32(v_scale)) if kv_kind == "fp8_e4m3" else 1.0
+    ks, vs = kv_scales(kv_kind, k_scale, v_scale, Hkv)
     out = np.zeros((len(rows), D), dtype=np.float64)
     for i, (s, hq) in enumerate(rows):
         L = int(seq_lens[s])
@@ -108,9 +117,9 @@ def paged_attention_rows(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
             continue
         h = hq // G
         k = to_float64(gather_sequence(k_pool, block_tables[s], L,
-                                       block_size, h), kv_kind) * ks
+                                       block_size, h), kv_kind) * ks[h]
         v = to_float64(gather_sequence(v_pool, block_tables[s], L,
-                                       block_size, h), kv_kind) * vs
+                                       block_size, h), kv_kind) * vs[h]
         q = to_float64(query[s, hq:hq + 1], q_kind)
         out[i] = attention_one_head(q, k, v, scale)[0]
     return out

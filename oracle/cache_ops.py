@@ -10,9 +10,11 @@ offset (the slot numbering follows the block/offset addressing of
 "PagedAttention" (shubhamtatvamasi.com), "How attention reads paged memory").
 Readings: a negative slot means "skip this token" (padding); when the cache
 dtype equals the source dtype the row is copied bit for bit; for an fp8
-cache each element becomes ``e4m3(float32(x) / float32(scale))`` with an
-IEEE float32 division and the saturating round-to-nearest-even encoder of
-:mod:`oracle.fp8_e4m3`.
+cache each element becomes ``enc(float32(x) / float32(scale))`` with an
+IEEE float32 division and the round-to-nearest-even encoder of
+:mod:`oracle.fp8_e4m3` (saturating) or :mod:`oracle.fp8_e5m2` (IEEE
+overflow).  The scale is per tensor, or one per kv head (the pages' 0-d
+scale tensors generalised; element ``[h, d]`` of a row uses scale ``h``).
 
 copy_blocks — "PagedAttention" (shubhamtatvamasi.com), "Sharing and
 copy-on-write" and the FAQ entry on copy-on-write for parallel sampling:
@@ -26,16 +28,21 @@ carry no token counts).
 import numpy as np
 
 from .fp8_e4m3 import e4m3_encode
-from .storage import to_float64
+from .fp8_e5m2 import e5m2_encode
+from .storage import head_scales, to_float64
+
+_ENCODERS = {"fp8_e4m3": e4m3_encode, "fp8_e5m2": e5m2_encode}
 
 
 def _encode_row(row, src_kind, cache_kind, scale):
+    """One token's row [Hkv, D] in the cache's storage."""
     if cache_kind == src_kind:
         return row.copy()
-    if cache_kind == "fp8_e4m3":
+    if cache_kind in _ENCODERS:
         x32 = to_float64(row, src_kind).astype(np.float32)   # exact widening
-        y = x32 / np.float32(scale)                           # IEEE fp32 div
-        return e4m3_encode(y.astype(np.float64))
+        s32 = head_scales(scale, row.shape[0]).astype(np.float32)[:, None]
+        y = x32 / s32                                         # IEEE fp32 div
+        return _ENCODERS[cache_kind](y.astype(np.float64))
     raise ValueError(f"unsupported write {src_kind} -> {cache_kind}")
 
 

@@ -2,15 +2,18 @@
 
 Storage kinds: ``"f32"`` (float32), ``"f16"`` (float16), ``"bf16"`` (uint16
 holding the upper half of a float32 bit pattern), ``"fp8_e4m3"`` (uint8 OCP
-E4M3 codes, decoded by :mod:`oracle.fp8_e4m3`).  Every conversion here is
+E4M3 codes, decoded by :mod:`oracle.fp8_e4m3`), ``"fp8_e5m2"`` (uint8 OCP
+E5M2 codes, decoded by :mod:`oracle.fp8_e5m2`).  Every conversion here is
 exact: each stored value is representable in float64.
 """
 
 import numpy as np
 
 from .fp8_e4m3 import e4m3_decode
+from .fp8_e5m2 import e5m2_decode
 
-KINDS = ("f32", "f16", "bf16", "fp8_e4m3")
+KINDS = ("f32", "f16", "bf16", "fp8_e4m3", "fp8_e5m2")
+FP8_KINDS = ("fp8_e4m3", "fp8_e5m2")
 
 
 def to_float64(arr, kind):
@@ -28,4 +31,17 @@ def to_float64(arr, kind):
     if kind == "fp8_e4m3":
         assert a.dtype == np.uint8, a.dtype
         return e4m3_decode(a)
+    if kind == "fp8_e5m2":
+        assert a.dtype == np.uint8, a.dtype
+        return e5m2_decode(a)
     raise ValueError(f"unknown storage kind {kind!r}")
+
+
+def head_scales(scale, num_heads):
+    """A per-tensor scale, or one scale per kv head, as float64 [num_heads]
+    holding the float32 values the kernels read."""
+    s = np.asarray(scale, dtype=np.float32).reshape(-1)
+    if s.size == 1:
+        s = np.repeat(s, num_heads)
+    assert s.size == num_heads, (s.size, num_heads)
+    return s.astype(np.float64)

@@ -16,7 +16,7 @@ copy-on-write of a shared, partially filled last block, at most one per
 sequence ("Sharing and copy-on-write").
 
 Storage conventions: ``"f32"`` float32, ``"f16"`` float16, ``"bf16"`` uint16
-bfloat16 bits, ``"fp8_e4m3"`` uint8 OCP E4M3 codes.  Slots that hold no live
+bfloat16 bits, ``"fp8_e4m3"`` / ``"fp8_e5m2"`` uint8 OCP E4M3 / E5M2 codes.  Slots that hold no live
 token are poisoned with NaN (0x7F for fp8) so that a stray read shows up in
 the output instead of passing silently.
 
@@ -34,10 +34,11 @@ import math
 import numpy as np
 
 SEED_BASE = 336
-KINDS = ("f32", "f16", "bf16", "fp8_e4m3")
+KINDS = ("f32", "f16", "bf16", "fp8_e4m3", "fp8_e5m2")
+FP8_KINDS = ("fp8_e4m3", "fp8_e5m2")
 _NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16,
-               "fp8_e4m3": np.uint8}
-_E4M3_LIMIT = 448.0
+               "fp8_e4m3": np.uint8, "fp8_e5m2": np.uint8}
+_FP8_LIMIT = {"fp8_e4m3": 448.0, "fp8_e5m2": 57344.0}
 
 
 # ----------------------------------------------------------------------------
@@ -58,19 +59,25 @@ def _cast_from_f32(x, kind):
     raise ValueError(kind)
 
 
-def _fp8_codes_from_f32(x, scale):
-    """Pool contents of an fp8 cache: codes of x/scale via torch's e4m3fn
-    cast (library routine), clamped into the finite range first."""
+def _fp8_codes_from_f32(x, scale, kind="fp8_e4m3"):
+    """Pool contents of an fp8 cache [.., Hkv, D]: codes of x/scale via
+    torch's float8 cast (library routine), clamped into the finite range
+    first; scale is one value or one per kv head."""
     import torch
+    lim = _FP8_LIMIT[kind]
     y = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    y = (y / torch.tensor(scale, dtype=torch.float32)).clamp_(-_E4M3_LIMIT,
-                                                               _E4M3_LIMIT)
-    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    s = torch.from_numpy(np.asarray(scale, dtype=np.float32).reshape(-1))
+    if s.numel() > 1:
+        s = s.reshape(s.numel(), 1)        # broadcast over [.., Hkv, D]
+    y = (y / s).clamp_(-lim, lim)
+    dt = torch.float8_e4m3fn if kind == "fp8_e4m3" else torch.float8_e5m2
+    return y.to(dt).view(torch.uint8).numpy()
 
 
 def poison_value(kind):
     return {"f32": np.float32(np.nan), "f16": np.float16(np.nan),
-            "bf16": np.uint16(0x7FC0), "fp8_e4m3": np.uint8(0x7F)}[kind]
+            "bf16": np.uint16(0x7FC0), "fp8_e4m3": np.uint8(0x7F),
+            "fp8_e5m2": np.uint8(0x7F)}[kind]
 
 
 def _normal(rng, shape):
@@ -104,7 +111,7 @@ class Workload:
     value: np.ndarray
     slot_mapping: np.ndarray  # int32 [T]
     copy_pairs: np.ndarray   # int32 [P, 2] (src, dst)
-    k_scale: float = 1.0     # float32 values; meaningful for fp8 caches
+    k_scale: float = 1.0     # float32 value(s); fp8 caches: one or per kv head
     v_scale: float = 1.0
     # Extra disjoint copies of (tables, slots, pairs) over the same pool,
     # for rotating benchmark steps through more memory than the caches hold.
@@ -183,20 +190,27 @@ def _draw_chunks(seed_key, num_blocks, block_size, hkv, d, chunk_blocks):
 
 
 def _fill_pool(seed_key, num_blocks, block_size, hkv, d, kind, live,
-               chunk_blocks=512):
+               chunk_blocks=512, per_head=False):
     """N(0,1) values at live slots, poison elsewhere, in storage kind.
 
-    For an fp8 cache the per-tensor scale is max|live value| / 448 (as a
-    float32); returns (pool, scale), scale 1.0 for other kinds."""
+    For an fp8 cache the scale is max|live value| / (largest finite code
+    value: 448 for E4M3, 57344 for E5M2) as a float32, per tensor or, with
+    per_head, per kv head (float32 [Hkv]); returns (pool, scale), scale 1.0
+    for other kinds."""
     x = _draw_chunks(seed_key, num_blocks, block_size, hkv, d, chunk_blocks)
     poison = poison_value(kind)
     scale = 1.0
-    if kind == "fp8_e4m3":
-        sel = np.abs(x[live])
-        amax = float(sel.max()) if sel.size else 0.0
+    if kind in FP8_KINDS:
+        lim = _FP8_LIMIT[kind]
+        sel = np.abs(x[live])                      # [n_live, Hkv, D]
+        if per_head:
+            amax = sel.max(axis=(0, 2)) if sel.size else np.zeros(hkv)
+            scale = np.where(amax > 0, amax / lim, 1.0).astype(np.float32)
+        else:
+            amax = float(sel.max()) if sel.size else 0.0
+            scale = float(np.float32(amax / lim)) if amax > 0 else 1.0
         del sel
-        scale = float(np.float32(amax / _E4M3_LIMIT)) if amax > 0 else 1.0
-        pool = _fp8_codes_from_f32(x, scale)
+        pool = _fp8_codes_from_f32(x, scale, kind)
     else:
         pool = _cast_from_f32(x, kind)
     del x
@@ -215,7 +229,7 @@ def _unused_column_fill(block_tables, counts, filler):
 
 def _build(name, rng, *, q_kind, kv_kind, src_kind, hq, hkv, d, bs, nb,
            block_tables, seq_lens, cached_lens, slot_mapping, copy_pairs,
-           replicas=(), note="", live_extra=None):
+           replicas=(), note="", live_extra=None, per_head_scales=False):
     """Draw pool values and rows for an already-laid-out step."""
     live = live_slot_mask(nb, bs, block_tables, cached_lens)
     for rep in replicas:
@@ -226,9 +240,9 @@ def _build(name, rng, *, q_kind, kv_kind, src_kind, hq, hkv, d, bs, nb,
     T = len(slot_mapping)
     key_base = [int(v) for v in rng.integers(0, 2**31, size=2)]
     k_pool, k_scale = _fill_pool([SEED_BASE, key_base[0], 0], nb, bs, hkv, d,
-                                 kv_kind, live)
+                                 kv_kind, live, per_head=per_head_scales)
     v_pool, v_scale = _fill_pool([SEED_BASE, key_base[1], 1], nb, bs, hkv, d,
-                                 kv_kind, live)
+                                 kv_kind, live, per_head=per_head_scales)
     query = _cast_from_f32(_normal(rng, (S, hq, d)), q_kind)
     key = _cast_from_f32(_normal(rng, (T, hkv, d)), src_kind)
     value = _cast_from_f32(_normal(rng, (T, hkv, d)), src_kind)
@@ -472,11 +486,13 @@ def long_context_fp8(num_seqs=8, seq_len=131072, block_size=64,
 
 
 def custom_decode(*, seed, num_seqs, lens, hq, hkv, d, bs, q_kind, kv_kind,
-                  src_kind=None, spare_blocks=3, num_new_per_seq=1):
+                  src_kind=None, spare_blocks=3, num_new_per_seq=1,
+                  per_head_scales=False):
     """Small free-form decode step (fuzz/edge cases): lengths given, blocks
-    from a random permutation with a few spare poisoned blocks."""
+    from a random permutation with a few spare poisoned blocks; an fp8
+    cache's scales per tensor or, with per_head_scales, per kv head."""
     rng = np.random.default_rng([SEED_BASE, 100, seed])
-    src_kind = src_kind or (q_kind if kv_kind == "fp8_e4m3" else kv_kind)
+    src_kind = src_kind or (q_kind if kv_kind in FP8_KINDS else kv_kind)
     lens = np.asarray(lens, dtype=np.int64)
     need = sum(blocks_for(L, bs) for L in lens)
     nb = need + spare_blocks
@@ -498,7 +514,8 @@ def custom_decode(*, seed, num_seqs, lens, hq, hkv, d, bs, q_kind, kv_kind,
     return _build(f"custom_{seed}", rng, q_kind=q_kind, kv_kind=kv_kind,
                   src_kind=src_kind, hq=hq, hkv=hkv, d=d, bs=bs, nb=nb,
                   block_tables=tables, seq_lens=lens, cached_lens=cached,
-                  slot_mapping=slots, copy_pairs=np.zeros((0, 2)),)
+                  slot_mapping=slots, copy_pairs=np.zeros((0, 2)),
+                  per_head_scales=per_head_scales)
 
 
 # ----------------------------------------------------------------------------
@@ -524,7 +541,7 @@ class MultiQuery:
 
 
 def _multi(name, rng, *, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
-           src_kind, nb, perm, replicas=1):
+           src_kind, nb, perm, replicas=1, per_head_scales=False):
     lens = np.asarray(lens, dtype=np.int64)
     qlens = np.asarray(qlens, dtype=np.int64)
     assert (qlens <= lens).all() and (qlens >= 0).all()
@@ -548,7 +565,8 @@ def _multi(name, rng, *, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
                hq=hq, hkv=hkv, d=d, bs=bs, nb=nb,
                block_tables=sets[0]["block_tables"], seq_lens=lens,
                cached_lens=cached, slot_mapping=sets[0]["slot_mapping"],
-               copy_pairs=np.zeros((0, 2)), replicas=sets[1:])
+               copy_pairs=np.zeros((0, 2)), replicas=sets[1:],
+               per_head_scales=per_head_scales)
     T = int(qlens.sum())
     query = _cast_from_f32(_normal(rng, (T, hq, d)), q_kind)
     query_start = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
@@ -556,17 +574,18 @@ def _multi(name, rng, *, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
 
 
 def custom_multi(*, seed, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
-                 src_kind=None, spare_blocks=3):
+                 src_kind=None, spare_blocks=3, per_head_scales=False):
     """Small free-form multi-query step: lengths (after the step) and new
     tokens per sequence given; blocks from a random permutation."""
     rng = np.random.default_rng([SEED_BASE, 200, seed])
-    src_kind = src_kind or (q_kind if kv_kind == "fp8_e4m3" else kv_kind)
+    src_kind = src_kind or (q_kind if kv_kind in FP8_KINDS else kv_kind)
     need = sum(blocks_for(max(int(L), 1), bs) for L in lens)
     nb = need + spare_blocks
     perm = rng.permutation(nb).astype(np.int32)
     return _multi(f"custom_multi_{seed}", rng, lens=lens, qlens=qlens, hq=hq,
                   hkv=hkv, d=d, bs=bs, q_kind=q_kind, kv_kind=kv_kind,
-                  src_kind=src_kind, nb=nb, perm=perm)
+                  src_kind=src_kind, nb=nb, perm=perm,
+                  per_head_scales=per_head_scales)
 
 
 def spec_verify_llama8b(num_seqs=32, draft=4, median=512, cap=4096,
