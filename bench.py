@@ -31,8 +31,9 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
-DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8"}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1, "fp8_e5m2": 1}
+DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8",
+              "fp8_e5m2": "fp8_e5m2"}
 METRIC = ("paged decode attention KV-read GB/s (% of HBM peak) + "
           "decode tokens/s, 1 GPU")
 

@@ -64,13 +64,23 @@ extern "C" {
 #endif
 
 /* Element types.  PKV_FP8_E4M3 is the OCP E4M3 "fn" format (bias 7, no
- * infinities, S.1111.111 = NaN, largest magnitude 448). */
+ * infinities, S.1111.111 = NaN, largest magnitude 448); PKV_FP8_E5M2 the OCP
+ * E5M2 format (bias 15, IEEE infinities and NaNs, largest finite magnitude
+ * 57344).
+ *
+ * An fp8 cache's values are stored over scales: a cache dtype argument of
+ * PKV_FP8_E4M3 or PKV_FP8_E5M2 takes k_scale / v_scale as one float32 each;
+ * OR-ing in PKV_SCALE_PER_HEAD takes them as float32 [num_kv_heads], one per
+ * kv head (the flag is accepted, and ignored, by the copy calls). */
 typedef enum pkv_dtype {
   PKV_F32 = 0,
   PKV_F16 = 1,
   PKV_BF16 = 2,
-  PKV_FP8_E4M3 = 3
+  PKV_FP8_E4M3 = 3,
+  PKV_FP8_E5M2 = 4
 } pkv_dtype;
+
+#define PKV_SCALE_PER_HEAD 0x100
 
 typedef enum pkv_status {
   PKV_OK = 0,
@@ -97,14 +107,16 @@ const char* pkv_status_string(int status);
  * slot_mapping device int32 [num_tokens]; token t goes to block
  *              slot/block_size, offset slot%block_size; slot < 0 skips it.
  * k_scale,
- * v_scale      device float32 scalars, required when cache_dtype is
- *              PKV_FP8_E4M3, ignored otherwise.
+ * v_scale      device float32 scales (one, or [num_kv_heads] with
+ *              PKV_SCALE_PER_HEAD), required for an fp8 cache, ignored
+ *              otherwise.
  *
  * Element conversion: with src_dtype == cache_dtype the row is copied bit for
- * bit.  With an fp8 cache (src_dtype F32, F16 or BF16) each element is
- * encoded as e4m3(float32(x) / scale): IEEE float32 division, round to
- * nearest even, finite values beyond 448 saturate to +-448, NaN stays NaN.
- * No other pairing is accepted (PKV_ERR_DTYPE).  num_tokens == 0 is a valid
+ * bit.  With an fp8 cache (src_dtype F32, F16 or BF16) element [h, d] of a
+ * row is encoded as enc(float32(x) / scale_h): IEEE float32 division, round
+ * to nearest even; for E4M3 finite values beyond 448 saturate to +-448, for
+ * E5M2 magnitudes from 61440 on become infinity (IEEE overflow); NaN stays
+ * NaN.  No other pairing is accepted (PKV_ERR_DTYPE).  num_tokens == 0 is a valid
  * no-op.  head_dim must be 64 or 128; pointers 16-byte aligned.
  */
 int cache_write_slots(const void* key, const void* value, int src_dtype,

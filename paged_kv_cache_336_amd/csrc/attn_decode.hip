@@ -78,9 +78,10 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   const int gcount = min(16, a.group - gc * 16);
   const int64_t head0 = (int64_t)s * a.num_q_heads + h * a.group + gc * 16;
 
-  merge_row<D, SCALED, BATCH>(a, wf, npieces, q_first, gcount,
-                              [&](int g) { return head0 + g; }, red_o, red_m,
-                              red_l);
+  const float vscale = SCALED ? head_scale(a.v_scale, a, h) : 1.f;
+  merge_row<D, BATCH>(a, wf, npieces, q_first, gcount,
+                      [&](int g) { return head0 + g; }, vscale, red_o, red_m,
+                      red_l);
 }
 
 // The segment starting at tile t of the wave's range [.., te): the largest s
@@ -191,8 +192,8 @@ __device__ __forceinline__ void write_new_token(const Seg& g, int L,
 #pragma unroll
     for (int q = 0; q < QT::bytes; ++q)
       in[q] = *reinterpret_cast<const u32x4_t*>(src + 16 * (QT::bytes * pc + q));
-    const float sc = half ? *a.v_scale : *a.k_scale;
-    *reinterpret_cast<u32x4_t*>(dst) = encode_piece_e4m3<QT>(in, sc);
+    const float sc = head_scale(half ? a.v_scale : a.k_scale, a, g.h);
+    *reinterpret_cast<u32x4_t*>(dst) = encode_piece_fp8<QT, CT>(in, sc);
   } else {
     *reinterpret_cast<u32x4_t*>(dst) =
         *reinterpret_cast<const u32x4_t*>(src + 16 * pc);
@@ -264,11 +265,6 @@ void attn_decode_kernel(AttnArgs a) {
   const int64_t tb = first_tile_of_wave(w, T, W);
   const int64_t te = first_tile_of_wave(w + 1, T, W);
 
-  float vscale = 1.f, kscale = 1.f;
-  if constexpr (is_fp8<CT>::value) {
-    kscale = *a.k_scale;
-    vscale = *a.v_scale;
-  }
 
   // ---- rows of empty sequences sit at tile position U tex[s]; the wave
   // whose range holds that position (the last wave for position T) writes
@@ -292,7 +288,6 @@ void attn_decode_kernel(AttnArgs a) {
     }
   }
 
-  const float qk_mul = a.qk_scale_log2 * kscale;
   const int64_t stride = (int64_t)a.num_kv_heads * S::ROW_BYTES;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_cache);
@@ -327,6 +322,14 @@ void attn_decode_kernel(AttnArgs a) {
   while (X.valid) {
     uint32_t qn[S::QWORDS];
     load_query<QT, CT, D>(qn, Xn, a, lane);
+    // an fp8 cache's scales for this row's kv head: the key scale folds into
+    // the score multiplier, the value scale into the output
+    float kscale = 1.f, vscale = 1.f;
+    if constexpr (is_fp8<CT>::value) {
+      kscale = head_scale(a.k_scale, a, X.h);
+      vscale = head_scale(a.v_scale, a, X.h);
+    }
+    const float qk_mul = a.qk_scale_log2 * kscale;
 
     WaveState<NBLK> st;
     st.m = -INFINITY;
@@ -466,6 +469,7 @@ template <> struct DtypeCode<F32> { static constexpr int value = PKV_F32; };
 template <> struct DtypeCode<F16> { static constexpr int value = PKV_F16; };
 template <> struct DtypeCode<BF16> { static constexpr int value = PKV_BF16; };
 template <> struct DtypeCode<FP8> { static constexpr int value = PKV_FP8_E4M3; };
+template <> struct DtypeCode<FP8E5> { static constexpr int value = PKV_FP8_E5M2; };
 
 template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE>
 static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
@@ -491,6 +495,8 @@ static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
       w.num_slots = a.num_slots;
       w.block_size = a.block_size;
       w.row_elems = a.num_kv_heads * D;
+      w.head_dim = D;
+      w.scale_per_head = a.scale_per_head;
       const hipError_t e = launch_cache_write(w, DtypeCode<QT>::value,
                                               DtypeCode<CT>::value, stream);
       if (e != hipSuccess) return e;
@@ -545,6 +551,10 @@ hipError_t launch_attn_decode(const AttnArgs& a, int q_dtype, int cache_dtype,
       if (q_dtype == PKV_BF16) return launch_t<BF16, FP8>(a, hd, mw, u, fused, stream);
       if (q_dtype == PKV_F16) return launch_t<F16, FP8>(a, hd, mw, u, fused, stream);
       return launch_t<F32, FP8>(a, hd, mw, u, fused, stream);
+    case PKV_FP8_E5M2:
+      if (q_dtype == PKV_BF16) return launch_t<BF16, FP8E5>(a, hd, mw, u, fused, stream);
+      if (q_dtype == PKV_F16) return launch_t<F16, FP8E5>(a, hd, mw, u, fused, stream);
+      return launch_t<F32, FP8E5>(a, hd, mw, u, fused, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -218,12 +218,6 @@ void attn_multi_kernel(AttnArgs a) {
   const int64_t tb = first_tile_of_wave(w, T, W);
   const int64_t te = first_tile_of_wave(w + 1, T, W);
 
-  float vscale = 1.f, kscale = 1.f;
-  if constexpr (is_fp8<CT>::value) {
-    kscale = *a.k_scale;
-    vscale = *a.v_scale;
-  }
-  const float qk_mul = a.qk_scale_log2 * kscale;
   const int64_t stride = (int64_t)a.num_kv_heads * S::ROW_BYTES;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_cache);
@@ -256,6 +250,12 @@ void attn_multi_kernel(AttnArgs a) {
                                  X.t_begin, X.t_end, lane);
 
   while (X.valid) {
+    float kscale = 1.f, vscale = 1.f;  // an fp8 cache's, for this kv head
+    if constexpr (is_fp8<CT>::value) {
+      kscale = head_scale(a.k_scale, a, X.h);
+      vscale = head_scale(a.v_scale, a, X.h);
+    }
+    const float qk_mul = a.qk_scale_log2 * kscale;
     uint32_t qn_w[QPREFETCH ? NG : 1][S::QWORDS];
     int lim[NG];
     WaveState<NBLK> st[NG];
@@ -408,12 +408,12 @@ __global__ __launch_bounds__(kMergeThreads) void attn_multi_merge_kernel(
   const int G = a.group;
   const int gcount = min(a.row_tokens, m.nq - rr * a.row_tokens) * G;
   const int64_t tok0 = (int64_t)m.q0 + rr * a.row_tokens;
-  merge_row<D, SCALED, BATCH>(
+  merge_row<D, BATCH>(
       a, wf, npieces, q_first, gcount,
       [&](int g) {
         return (tok0 + g / G) * a.num_q_heads + h * G + g % G;
       },
-      red_o, red_m, red_l);
+      SCALED ? head_scale(a.v_scale, a, h) : 1.f, red_o, red_m, red_l);
 }
 
 template <typename QT, typename CT, int D, bool UNIFORM, int NG>
@@ -474,6 +474,10 @@ hipError_t launch_attn_multi(const AttnArgs& a, int q_dtype, int cache_dtype,
       if (q_dtype == PKV_BF16) return launch_mt<BF16, FP8>(a, head_dim, max_waves, uniform, stream);
       if (q_dtype == PKV_F16) return launch_mt<F16, FP8>(a, head_dim, max_waves, uniform, stream);
       return launch_mt<F32, FP8>(a, head_dim, max_waves, uniform, stream);
+    case PKV_FP8_E5M2:
+      if (q_dtype == PKV_BF16) return launch_mt<BF16, FP8E5>(a, head_dim, max_waves, uniform, stream);
+      if (q_dtype == PKV_F16) return launch_mt<F16, FP8E5>(a, head_dim, max_waves, uniform, stream);
+      return launch_mt<F32, FP8E5>(a, head_dim, max_waves, uniform, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -20,6 +20,9 @@ template <typename QT, typename CT> struct PvOperand { typedef CT type; };
 template <> struct PvOperand<BF16, FP8> { typedef F16 type; };
 template <> struct PvOperand<F16, FP8> { typedef F16 type; };
 template <> struct PvOperand<F32, FP8> { typedef F32 type; };
+template <> struct PvOperand<BF16, FP8E5> { typedef F16 type; };
+template <> struct PvOperand<F16, FP8E5> { typedef F16 type; };
+template <> struct PvOperand<F32, FP8E5> { typedef F32 type; };
 
 // Token (within a 32-token tile) that lane group j, operand slot e stands for:
 // slots 0-3 are rows 4j..4j+3 of the first 16-token half, slots 4-7 the same
@@ -226,14 +229,14 @@ __device__ __forceinline__ void stage_v(const u32x4_t (&vraw)[Shape<QT, CT, D>::
         *reinterpret_cast<u32x4_t*>(dst) = vraw[v];
       } else {  // fp8 -> f16: the piece's 16 elements fill the whole span
         u32x4_t lo, hi;
-        lo[0] = fp8x2_to_f16x2(vraw[v][0], false);
-        lo[1] = fp8x2_to_f16x2(vraw[v][0], true);
-        lo[2] = fp8x2_to_f16x2(vraw[v][1], false);
-        lo[3] = fp8x2_to_f16x2(vraw[v][1], true);
-        hi[0] = fp8x2_to_f16x2(vraw[v][2], false);
-        hi[1] = fp8x2_to_f16x2(vraw[v][2], true);
-        hi[2] = fp8x2_to_f16x2(vraw[v][3], false);
-        hi[3] = fp8x2_to_f16x2(vraw[v][3], true);
+        lo[0] = fp8x2_to_f16x2<CT>(vraw[v][0], false);
+        lo[1] = fp8x2_to_f16x2<CT>(vraw[v][0], true);
+        lo[2] = fp8x2_to_f16x2<CT>(vraw[v][1], false);
+        lo[3] = fp8x2_to_f16x2<CT>(vraw[v][1], true);
+        hi[0] = fp8x2_to_f16x2<CT>(vraw[v][2], false);
+        hi[1] = fp8x2_to_f16x2<CT>(vraw[v][2], true);
+        hi[2] = fp8x2_to_f16x2<CT>(vraw[v][3], false);
+        hi[3] = fp8x2_to_f16x2<CT>(vraw[v][3], true);
         *reinterpret_cast<u32x4_t*>(dst) = lo;
         *reinterpret_cast<u32x4_t*>(dst + 16) = hi;
       }
@@ -242,8 +245,8 @@ __device__ __forceinline__ void stage_v(const u32x4_t (&vraw)[Shape<QT, CT, D>::
     } else {  // fp8 -> f32, four chunks
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const f32x2_t p0 = fp8x2_to_f32x2(vraw[v][w], false);
-        const f32x2_t p1 = fp8x2_to_f32x2(vraw[v][w], true);
+        const f32x2_t p0 = fp8x2_to_f32x2<CT>(vraw[v][w], false);
+        const f32x2_t p1 = fp8x2_to_f32x2<CT>(vraw[v][w], true);
         f32x4_t q = {p0[0], p0[1], p1[0], p1[1]};
         *reinterpret_cast<f32x4_t*>(rowp + (((ch0 + w) ^ swz) << 4)) = q;
       }
@@ -287,22 +290,22 @@ __device__ __forceinline__ void qk_tile(
       } else if constexpr (QT::bytes == 2) {  // fp8 keys -> bf16/f16
         const uint32_t w0 = kw[hh][2 * q], w1 = kw[hh][2 * q + 1];
         if constexpr (same<QT, BF16>::value) {
-          ka[0] = fp8x2_to_bf16x2(w0, false);
-          ka[1] = fp8x2_to_bf16x2(w0, true);
-          ka[2] = fp8x2_to_bf16x2(w1, false);
-          ka[3] = fp8x2_to_bf16x2(w1, true);
+          ka[0] = fp8x2_to_bf16x2<CT>(w0, false);
+          ka[1] = fp8x2_to_bf16x2<CT>(w0, true);
+          ka[2] = fp8x2_to_bf16x2<CT>(w1, false);
+          ka[3] = fp8x2_to_bf16x2<CT>(w1, true);
         } else {
-          ka[0] = fp8x2_to_f16x2(w0, false);
-          ka[1] = fp8x2_to_f16x2(w0, true);
-          ka[2] = fp8x2_to_f16x2(w1, false);
-          ka[3] = fp8x2_to_f16x2(w1, true);
+          ka[0] = fp8x2_to_f16x2<CT>(w0, false);
+          ka[1] = fp8x2_to_f16x2<CT>(w0, true);
+          ka[2] = fp8x2_to_f16x2<CT>(w1, false);
+          ka[3] = fp8x2_to_f16x2<CT>(w1, true);
         }
 #pragma unroll
         for (int w = 0; w < 4; ++w) qb[w] = qw[4 * q + w];
       } else {  // fp8 keys -> f32
         const uint32_t w0 = kw[hh][2 * q], w1 = kw[hh][2 * q + 1];
-        const f32x2_t p0 = fp8x2_to_f32x2(w0, false), p1 = fp8x2_to_f32x2(w0, true);
-        const f32x2_t p2 = fp8x2_to_f32x2(w1, false), p3 = fp8x2_to_f32x2(w1, true);
+        const f32x2_t p0 = fp8x2_to_f32x2<CT>(w0, false), p1 = fp8x2_to_f32x2<CT>(w0, true);
+        const f32x2_t p2 = fp8x2_to_f32x2<CT>(w1, false), p3 = fp8x2_to_f32x2<CT>(w1, true);
         ka[0] = p0[0]; ka[1] = p0[1]; ka[2] = p1[0]; ka[3] = p1[1];
         ka[4] = p2[0]; ka[5] = p2[1]; ka[6] = p3[0]; ka[7] = p3[1];
 #pragma unroll
@@ -522,13 +525,14 @@ __device__ __forceinline__ void lse_fold(float& m, float& l, f32x4_t& acc,
 // The fold of one cut row's pieces (all threads of the workgroup call it):
 // wf is the row's first wave, npieces its piece count, q_first the slot of
 // its first piece in that wave; output column g goes to row row_of(g) of
-// ``out`` (head_dim floats each).
-template <int D, bool SCALED, int BATCH, typename RowOf>
+// ``out`` (head_dim floats each), times vscale (an fp8 cache's value scale
+// for the row's kv head, else 1).
+template <int D, int BATCH, typename RowOf>
 __device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
                                           int npieces, int q_first,
                                           int gcount, RowOf row_of,
-                                          f32x4_t* red_o, float* red_m,
-                                          float* red_l) {
+                                          float vscale, f32x4_t* red_o,
+                                          float* red_m, float* red_l) {
   constexpr int D4 = D / 4;
   const int tid = threadIdx.x;
   const int gmax = a.slot_heads;
@@ -566,7 +570,7 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
       for (int k = 0; k < BATCH; ++k) lse_fold(m, l, acc, mi[k], li[k], oi[k]);
     }
     if (nsub == 1) {
-      const float f = (SCALED ? *a.v_scale : 1.f) / l;
+      const float f = vscale / l;
       *reinterpret_cast<f32x4_t*>(a.out + row_of(g) * D + 4 * d4) = acc * f;
     } else {
       red_o[it] = acc;
@@ -584,10 +588,17 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
       for (int sub = 1; sub < nsub; ++sub)
         lse_fold(m, l, acc, red_m[sub * items + item], red_l[sub * items + item],
                  red_o[sub * items + item]);
-      const float f = (SCALED ? *a.v_scale : 1.f) / l;
+      const float f = vscale / l;
       *reinterpret_cast<f32x4_t*>(a.out + row_of(g) * D + 4 * d4) = acc * f;
     }
   }
+}
+
+// An fp8 cache's key / value scale for kv head h (one per tensor, or one per
+// kv head when a.scale_per_head).
+__device__ __forceinline__ float head_scale(const float* scale,
+                                            const AttnArgs& a, int h) {
+  return scale[a.scale_per_head ? h : 0];
 }
 
 // Inclusive scan of one int per thread across the workgroup.

@@ -40,13 +40,13 @@ __global__ __launch_bounds__(256) void cache_write_copy_kernel(WriteArgs a,
   }
 }
 
-// fp8 cache: each thread encodes 16 elements into one 16-byte piece.
-template <typename ST>
+// fp8 cache (CT: E4M3 or E5M2): each thread encodes 16 elements into one
+// 16-byte piece; with per-head scales, piece pc belongs to kv head
+// 16 pc / head_dim.
+template <typename ST, typename CT>
 __global__ __launch_bounds__(256) void cache_write_fp8_kernel(WriteArgs a) {
   const int pieces = a.row_elems / 16;
   const int64_t total = a.num_tokens * pieces;
-  const float ks = *a.k_scale;
-  const float vs = *a.v_scale;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / pieces;
@@ -66,8 +66,9 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(WriteArgs a) {
       vin[q] = vsrc[q];
     }
     if (slot < 0 || slot >= a.num_slots) continue;
-    const u32x4_t kout = encode_piece_e4m3<ST>(kin, ks);
-    const u32x4_t vout = encode_piece_e4m3<ST>(vin, vs);
+    const int h = a.scale_per_head ? pc * 16 / a.head_dim : 0;
+    const u32x4_t kout = encode_piece_fp8<ST, CT>(kin, a.k_scale[h]);
+    const u32x4_t vout = encode_piece_fp8<ST, CT>(vin, a.v_scale[h]);
     const int64_t off_dst = (int64_t)slot * a.row_elems + pc * 16;
     *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(a.k_cache) + off_dst) = kout;
     *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(a.v_cache) + off_dst) = vout;
@@ -81,25 +82,32 @@ static int grid_for(int64_t work, int threads) {
   return (int)g;
 }
 
+template <typename CT>
+static void launch_fp8(const WriteArgs& a, int src_dtype, hipStream_t stream) {
+  const int grid = grid_for(a.num_tokens * (a.row_elems / 16), 256);
+  if (src_dtype == PKV_BF16)
+    hipLaunchKernelGGL((cache_write_fp8_kernel<BF16, CT>), dim3(grid),
+                       dim3(256), 0, stream, a);
+  else if (src_dtype == PKV_F16)
+    hipLaunchKernelGGL((cache_write_fp8_kernel<F16, CT>), dim3(grid),
+                       dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((cache_write_fp8_kernel<F32, CT>), dim3(grid),
+                       dim3(256), 0, stream, a);
+}
+
 hipError_t launch_cache_write(const WriteArgs& a, int src_dtype,
                               int cache_dtype, hipStream_t stream) {
-  if (cache_dtype != PKV_FP8_E4M3) {
+  if (cache_dtype != PKV_FP8_E4M3 && cache_dtype != PKV_FP8_E5M2) {
     const int ebytes = cache_dtype == PKV_F32 ? 4 : 2;
     const int row_bytes = a.row_elems * ebytes;
     const int grid = grid_for(a.num_tokens * (row_bytes / 16), 256);
     hipLaunchKernelGGL(cache_write_copy_kernel, dim3(grid), dim3(256), 0,
                        stream, a, row_bytes);
+  } else if (cache_dtype == PKV_FP8_E4M3) {
+    launch_fp8<FP8>(a, src_dtype, stream);
   } else {
-    const int grid = grid_for(a.num_tokens * (a.row_elems / 16), 256);
-    if (src_dtype == PKV_BF16)
-      hipLaunchKernelGGL(cache_write_fp8_kernel<BF16>, dim3(grid), dim3(256),
-                         0, stream, a);
-    else if (src_dtype == PKV_F16)
-      hipLaunchKernelGGL(cache_write_fp8_kernel<F16>, dim3(grid), dim3(256),
-                         0, stream, a);
-    else
-      hipLaunchKernelGGL(cache_write_fp8_kernel<F32>, dim3(grid), dim3(256),
-                         0, stream, a);
+    launch_fp8<FP8E5>(a, src_dtype, stream);
   }
   return hipGetLastError();
 }

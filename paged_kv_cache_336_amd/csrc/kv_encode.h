@@ -1,4 +1,5 @@
-// kv_encode.h -- encoding of new key/value elements into an fp8 cache,
+// kv_encode.h -- encoding of new key/value elements into an fp8 cache (OCP
+// E4M3 or E5M2),
 // shared by the cache write (cache_ops.hip) and the decode kernel's fused
 // write of each sequence's new token (attn_decode.hip).  A stored code is
 // e4m3(float32(x) / scale): IEEE float32 division, then the encoder below
@@ -34,6 +35,27 @@ __device__ __forceinline__ uint32_t encode_e4m3(float y) {
   return sign | code;
 }
 
+// OCP E5M2 encoder: round to nearest even on the float32 bit pattern; a
+// magnitude that rounds past the largest finite value 57344 (from 61440 on,
+// including infinity) becomes infinity (E5M2 keeps IEEE overflow); NaN keeps
+// its sign with code S.11111.11.
+__device__ __forceinline__ uint32_t encode_e5m2(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t mag = b & 0x7FFFFFFFu;
+  if (mag > 0x7F800000u) return sign | 0x7Fu;          // NaN
+  if (mag < 0x38800000u) {                             // < 2^-14: step 2^-16
+    const float q = __uint_as_float(mag) * 65536.0f;   // exact scaling
+    return sign | (uint32_t)__builtin_rintf(q);        // 0..4, ties to even
+  }
+  if (mag >= 0x47700000u) return sign | 0x7Cu;         // >= 61440: infinity
+  const uint32_t e = (mag >> 23) - 112u;               // biased for E5M2
+  const uint32_t m = (mag >> 21) & 3u;
+  const uint32_t rest = mag & 0x1FFFFFu;
+  const uint32_t up = (rest > 0x100000u) | ((rest == 0x100000u) & (m & 1u));
+  return sign | ((e << 2) + m + up);                   // carry bumps e
+}
+
 // Element e (0..15) of a 16-element source piece held as 16-byte words.
 template <typename ST>
 __device__ __forceinline__ float piece_elem(const u32x4_t* w, int e);
@@ -50,17 +72,22 @@ template <> __device__ __forceinline__ float piece_elem<BF16>(const u32x4_t* w, 
   return __uint_as_float((word >> (16 * (e & 1))) << 16);
 }
 
-// The 16 codes of one 16-element source piece (ST::bytes 16-byte words).
-template <typename ST>
-__device__ __forceinline__ u32x4_t encode_piece_e4m3(const u32x4_t* in,
-                                                     float scale) {
+// The 16 codes of one 16-element source piece (ST::bytes 16-byte words) in
+// the cache's fp8 format CT (FP8: E4M3, FP8E5: E5M2).
+template <typename ST, typename CT>
+__device__ __forceinline__ u32x4_t encode_piece_fp8(const u32x4_t* in,
+                                                    float scale) {
   u32x4_t out;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     uint32_t word = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      word |= encode_e4m3(piece_elem<ST>(in, 4 * w + b) / scale) << (8 * b);
+    for (int b = 0; b < 4; ++b) {
+      const float y = piece_elem<ST>(in, 4 * w + b) / scale;
+      const uint32_t code =
+          same<CT, FP8E5>::value ? encode_e5m2(y) : encode_e4m3(y);
+      word |= code << (8 * b);
+    }
     out[w] = word;
   }
   return out;

@@ -12,11 +12,24 @@ using namespace pkv;
 namespace {
 
 bool valid_dtype(int d) {
-  return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16 || d == PKV_FP8_E4M3;
+  return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16 || d == PKV_FP8_E4M3 ||
+         d == PKV_FP8_E5M2;
 }
 
+bool is_fp8_dtype(int d) { return d == PKV_FP8_E4M3 || d == PKV_FP8_E5M2; }
+
 int dtype_bytes(int d) {
-  return d == PKV_F32 ? 4 : (d == PKV_FP8_E4M3 ? 1 : 2);
+  return d == PKV_F32 ? 4 : (is_fp8_dtype(d) ? 1 : 2);
+}
+
+// A cache dtype argument: the element type and the per-head-scale flag (only
+// for fp8 caches; any other bit is an error).  Returns false if invalid.
+bool split_cache_dtype(int arg, int* dtype, bool* per_head) {
+  *dtype = arg & 0xFF;
+  *per_head = (arg & PKV_SCALE_PER_HEAD) != 0;
+  if ((arg & ~(0xFF | PKV_SCALE_PER_HEAD)) != 0) return false;
+  if (!valid_dtype(*dtype)) return false;
+  return !*per_head || is_fp8_dtype(*dtype);
 }
 
 bool aligned(const void* p, uintptr_t n) {
@@ -88,20 +101,26 @@ int cache_write_slots(const void* key, const void* value, int src_dtype,
                       int32_t num_kv_heads, int32_t head_dim,
                       const float* k_scale, const float* v_scale,
                       hipStream_t stream) {
-  if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
-  if (src_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-  if (cache_dtype != PKV_FP8_E4M3 && src_dtype != cache_dtype) return PKV_ERR_DTYPE;
+  bool per_head = false;
+  const int cache_arg = cache_dtype;
+  if (!valid_dtype(src_dtype) ||
+      !split_cache_dtype(cache_arg, &cache_dtype, &per_head))
+    return PKV_ERR_DTYPE;
+  if (is_fp8_dtype(src_dtype)) return PKV_ERR_DTYPE;
+  if (!is_fp8_dtype(cache_dtype) && src_dtype != cache_dtype) return PKV_ERR_DTYPE;
   if (num_tokens < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1)
     return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (num_blocks * (int64_t)block_size > INT_MAX) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if (is_fp8_dtype(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_NULL;
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(slot_mapping, 4))
     return PKV_ERR_ALIGN;
   WriteArgs a{};
+  a.scale_per_head = per_head;
+  a.head_dim = head_dim;
   a.key = key;
   a.value = value;
   a.k_cache = k_cache;
@@ -123,7 +142,10 @@ int copy_common(void* k_cache, void* v_cache, int cache_dtype,
                 const int32_t* block_pairs, int64_t num_pairs,
                 int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                 int32_t head_dim, int prefix, hipStream_t stream) {
-  if (!valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
+  bool per_head = false;  // (scales play no part in a copy)
+  const int cache_arg = cache_dtype;
+  if (!split_cache_dtype(cache_arg, &cache_dtype, &per_head))
+    return PKV_ERR_DTYPE;
   if (num_pairs < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1)
     return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
@@ -200,9 +222,13 @@ int decode_common(float* out, const void* query, int q_dtype,
                   size_t workspace_bytes, const void* key, const void* value,
                   const int32_t* slot_mapping, bool fused,
                   hipStream_t stream) {
-  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
-  if (q_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-  if (cache_dtype != PKV_FP8_E4M3 && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
+  bool per_head = false;
+  const int cache_arg = cache_dtype;
+  if (!valid_dtype(q_dtype) ||
+      !split_cache_dtype(cache_arg, &cache_dtype, &per_head))
+    return PKV_ERR_DTYPE;
+  if (is_fp8_dtype(q_dtype)) return PKV_ERR_DTYPE;
+  if (!is_fp8_dtype(cache_dtype) && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
   if (num_blocks < 1 || block_size < 1 || max_blocks_per_seq < 1 ||
       max_seq_len < 0 || max_waves < 0)
     return PKV_ERR_SHAPE;
@@ -222,7 +248,7 @@ int decode_common(float* out, const void* query, int q_dtype,
   if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens)
     return PKV_ERR_NULL;
   if (fused && (!key || !value || !slot_mapping)) return PKV_ERR_NULL;
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if (is_fp8_dtype(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_NULL;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4))
     return PKV_ERR_ALIGN;
@@ -256,6 +282,7 @@ int decode_common(float* out, const void* query, int q_dtype,
   a.num_blocks = (int32_t)num_blocks;
   a.max_seq_tokens = max_seq_len;  // within the table's reach (checked)
   a.qk_scale_log2 = scale * 1.4426950408889634f;
+  a.scale_per_head = per_head;
   a.new_key = key;
   a.new_value = value;
   a.slot_mapping = slot_mapping;
@@ -320,9 +347,13 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
                      int32_t head_dim, int64_t num_blocks, int32_t block_size,
                      float scale, int32_t max_waves, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
-  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
-  if (q_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-  if (cache_dtype != PKV_FP8_E4M3 && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
+  bool per_head = false;
+  const int cache_arg = cache_dtype;
+  if (!valid_dtype(q_dtype) ||
+      !split_cache_dtype(cache_arg, &cache_dtype, &per_head))
+    return PKV_ERR_DTYPE;
+  if (is_fp8_dtype(q_dtype)) return PKV_ERR_DTYPE;
+  if (!is_fp8_dtype(cache_dtype) && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
   if (num_blocks < 1 || block_size < 1 || max_blocks_per_seq < 1 ||
       max_seq_len < 0 || max_waves < 0 || num_query_tokens < 0 ||
       max_query_len < 0 || max_query_len > max_seq_len)
@@ -348,7 +379,7 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
   if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens ||
       !query_start)
     return PKV_ERR_NULL;
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if (is_fp8_dtype(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_NULL;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(block_tables, 4) ||
       !aligned(seq_lens, 4) || !aligned(query_start, 4))
@@ -380,6 +411,7 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
   a.num_blocks = (int32_t)num_blocks;
   a.max_seq_tokens = max_seq_len;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
+  a.scale_per_head = per_head;
   a.query_start = query_start;
   a.num_query_tokens = num_query_tokens;
   a.max_query_len = max_query_len;

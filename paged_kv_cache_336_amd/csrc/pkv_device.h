@@ -33,10 +33,12 @@ __device__ __forceinline__ uint32_t pack_u16x2(short lo, short hi) {
 struct F32 { typedef float scalar; static constexpr int bytes = 4; };
 struct F16 { typedef _Float16 scalar; static constexpr int bytes = 2; };
 struct BF16 { typedef __bf16 scalar; static constexpr int bytes = 2; };
-struct FP8 { typedef uint8_t scalar; static constexpr int bytes = 1; };
+struct FP8 { typedef uint8_t scalar; static constexpr int bytes = 1; };    // E4M3
+struct FP8E5 { typedef uint8_t scalar; static constexpr int bytes = 1; };  // E5M2
 
 template <typename T> struct is_fp8 { static constexpr bool value = false; };
 template <> struct is_fp8<FP8> { static constexpr bool value = true; };
+template <> struct is_fp8<FP8E5> { static constexpr bool value = true; };
 
 template <typename A, typename B> struct same { static constexpr bool value = false; };
 template <typename A> struct same<A, A> { static constexpr bool value = true; };
@@ -105,22 +107,40 @@ template <> struct Mma<F32> {
 
 // ---------------------------------------------------------------------------
 // Conversions.  fp8 -> wider types use gfx950's scaled converts with scale 1,
-// which decode OCP E4M3 exactly (every E4M3 value is representable in f16,
-// bf16 and f32).
+// which decode OCP E4M3 ("fp8") and E5M2 ("bf8") exactly: every value of
+// either format is representable in f16, bf16 and f32.  FT selects the
+// format (FP8: E4M3, FP8E5: E5M2).
 // ---------------------------------------------------------------------------
+template <typename FT>
 __device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t word, bool hi) {
-  f16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true)
-                 : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
+  f16x2_t v;
+  if constexpr (same<FT, FP8E5>::value)
+    v = hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(word, 1.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(word, 1.0f, false);
+  else
+    v = hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
   return bitcast<uint32_t>(v);
 }
+template <typename FT>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word, bool hi) {
-  bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true)
-                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+  bf16x2_t v;
+  if constexpr (same<FT, FP8E5>::value)
+    v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(word, 1.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(word, 1.0f, false);
+  else
+    v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
   return bitcast<uint32_t>(v);
 }
+template <typename FT>
 __device__ __forceinline__ f32x2_t fp8x2_to_f32x2(uint32_t word, bool hi) {
-  return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, true)
-            : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);
+  if constexpr (same<FT, FP8E5>::value)
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(word, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(word, 1.0f, false);
+  else
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);
 }
 
 // float -> 16-bit storage, round to nearest even.

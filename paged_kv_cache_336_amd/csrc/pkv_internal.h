@@ -52,6 +52,7 @@ struct AttnArgs {
   int32_t max_seq_tokens; // max_seq_len: longer lengths are cut to it
   int32_t num_waves;      // waves of the partition kernel's grid
   float qk_scale_log2;    // softmax scale * log2(e)
+  int32_t scale_per_head; // fp8 scales: one per kv head (else one per tensor)
   // several query tokens per sequence (paged_attn_multi) only:
   const int32_t* query_start;  // [num_seqs + 1] first query row of each
   int32_t num_query_tokens;    // rows of query / out (starts clamped to it)
@@ -84,6 +85,8 @@ struct WriteArgs {
   const float* v_scale;
   int64_t num_tokens;
   int64_t num_slots;      // num_blocks * block_size: larger slots are skipped
+  int32_t scale_per_head; // fp8 scales: one per kv head (else one per tensor)
+  int32_t head_dim;
   int32_t block_size;
   int32_t row_elems;      // num_kv_heads * head_dim
 };

@@ -18,9 +18,10 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
-PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E5M2 = 0, 1, 2, 3, 4
+PKV_SCALE_PER_HEAD = 0x100
 KIND_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
-              "fp8_e4m3": PKV_FP8_E4M3}
+              "fp8_e4m3": PKV_FP8_E4M3, "fp8_e5m2": PKV_FP8_E5M2}
 
 EXPORTED = ("pkv_status_string", "cache_write_slots", "copy_blocks",
             "copy_block_prefixes", "paged_attn_workspace_size",
@@ -97,7 +98,8 @@ def _torch():
 
 
 def dtype_code(t, kind=None):
-    """pkv dtype of a tensor; uint8 tensors need kind='fp8_e4m3'."""
+    """pkv dtype of a tensor; uint8 tensors need kind='fp8_e4m3' or
+    'fp8_e5m2'."""
     if kind is not None:
         return KIND_CODES[kind]
     torch = _torch()
@@ -107,7 +109,19 @@ def dtype_code(t, kind=None):
         return table[t.dtype]
     if t.dtype == getattr(torch, "float8_e4m3fn", None):
         return PKV_FP8_E4M3
+    if t.dtype == getattr(torch, "float8_e5m2", None):
+        return PKV_FP8_E5M2
     raise TypeError(f"no pkv dtype for {t.dtype}; pass kind=")
+
+
+def cache_code(k_cache, cache_kind, k_scale):
+    """The cache dtype argument: the element type, with PKV_SCALE_PER_HEAD
+    when an fp8 cache's scales hold one value per kv head."""
+    code = dtype_code(k_cache, cache_kind)
+    if code in (PKV_FP8_E4M3, PKV_FP8_E5M2) and k_scale is not None \
+            and k_scale.numel() > 1:
+        code |= PKV_SCALE_PER_HEAD
+    return code
 
 
 def _ptr(t):
@@ -137,7 +151,7 @@ def cache_write_slots(key, value, k_cache, v_cache, slot_mapping,
     nb, bs, hkv, d = k_cache.shape
     _check("cache_write_slots", lib.cache_write_slots(
         _ptr(key), _ptr(value), dtype_code(key), _ptr(k_cache), _ptr(v_cache),
-        dtype_code(k_cache, cache_kind), _ptr(slot_mapping),
+        cache_code(k_cache, cache_kind, k_scale), _ptr(slot_mapping),
         int(slot_mapping.shape[0]), nb, bs, hkv, d, _ptr(k_scale),
         _ptr(v_scale), _stream(stream)))
 
@@ -217,7 +231,7 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
     buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
-        _ptr(v_cache), dtype_code(k_cache, cache_kind), _ptr(k_scale),
+        _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale), _ptr(k_scale),
         _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
         _ptr(seq_lens), int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
         int(max_waves), _ptr(buf),
@@ -241,7 +255,7 @@ def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
     buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
     _check("paged_attn_decode_fused", lib.paged_attn_decode_fused(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(key), _ptr(value),
-        _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache, cache_kind),
+        _ptr(k_cache), _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale),
         _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), s, hq,
         hkv, d, nb, bs, float(scale), int(max_waves), _ptr(buf),
@@ -266,7 +280,7 @@ def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
     buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
     _check("paged_attn_multi", lib.paged_attn_multi(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
-        _ptr(v_cache), dtype_code(k_cache, cache_kind), _ptr(k_scale),
+        _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale), _ptr(k_scale),
         _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
         _ptr(seq_lens), _ptr(query_start), t, int(max_query_len),
         int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),

@@ -24,7 +24,7 @@ def _to_torch(arr, kind, device):
     a = np.ascontiguousarray(arr)
     if kind == "bf16":
         t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
-    elif kind in ("f32", "f16", "fp8_e4m3"):
+    elif kind in ("f32", "f16", "fp8_e4m3", "fp8_e5m2"):
         t = torch.from_numpy(a)
     else:
         raise ValueError(kind)
@@ -52,8 +52,11 @@ class DeviceStep:
         self.key = _to_torch(w.key, w.src_kind, dev)
         self.value = _to_torch(w.value, w.src_kind, dev)
         self.seq_lens = torch.from_numpy(w.seq_lens.astype(np.int32)).to(dev)
-        self.k_scale = torch.tensor([w.k_scale], dtype=torch.float32, device=dev)
-        self.v_scale = torch.tensor([w.v_scale], dtype=torch.float32, device=dev)
+        # one scale, or one per kv head
+        self.k_scale = torch.from_numpy(np.atleast_1d(
+            np.asarray(w.k_scale, dtype=np.float32)).copy()).to(dev)
+        self.v_scale = torch.from_numpy(np.atleast_1d(
+            np.asarray(w.v_scale, dtype=np.float32)).copy()).to(dev)
         sets = [{"block_tables": w.block_tables, "slot_mapping": w.slot_mapping,
                  "copy_pairs": w.copy_pairs}]
         if replicas:
@@ -67,7 +70,7 @@ class DeviceStep:
                 np.asarray(r["copy_pairs"], dtype=np.int32).reshape(-1, 2))).to(dev),
         } for r in sets]
         self.out = torch.empty(w.query.shape, dtype=torch.float32, device=dev)
-        self.cache_kind = w.kv_kind if w.kv_kind == "fp8_e4m3" else None
+        self.cache_kind = w.kv_kind if w.kv_kind.startswith("fp8") else None
         self.workspace = ops.Workspace(dev)
         self.max_seq_len = w.max_seq_len
 

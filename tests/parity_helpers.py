@@ -7,7 +7,8 @@ import numpy as np
 
 import oracle
 
-TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "fp8_e4m3": 2e-2}
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "fp8_e4m3": 2e-2,
+       "fp8_e5m2": 2e-2}
 
 
 def say(msg):

@@ -258,3 +258,29 @@ def test_fused_validation(lib):
     assert pf(lib, ws=None) == WS
     # the unfused call still takes more than 16 heads per kv head
     assert pa(lib, hq=48, hkv=1, ws=None) == WS
+
+
+def test_cache_dtype_argument(lib):
+    """E5M2 caches and the per-head-scale flag: accepted for fp8 caches
+    only; unknown bits are a dtype error."""
+    E5M2, PER_HEAD = 4, 0x100
+    assert pa(lib, qd=BF16, cache=E5M2, ks=FAKE, vs=FAKE, ws=None) == WS
+    assert pa(lib, qd=BF16, cache=E5M2 | PER_HEAD, ks=FAKE, vs=FAKE,
+              ws=None) == WS
+    assert pa(lib, qd=BF16, cache=FP8 | PER_HEAD, ks=FAKE, vs=FAKE,
+              ws=None) == WS
+    assert pa(lib, qd=BF16, cache=E5M2) == NULL          # scales required
+    assert pa(lib, qd=BF16, cache=BF16 | PER_HEAD) == DTYPE
+    assert pa(lib, qd=BF16, cache=BF16 | 0x200) == DTYPE
+    assert pa(lib, qd=E5M2, cache=E5M2, ks=FAKE, vs=FAKE) == DTYPE
+    assert pa(lib, qd=BF16, cache=5) == DTYPE
+    assert pm(lib, qd=BF16, cache=E5M2 | PER_HEAD, ks=FAKE, vs=FAKE,
+              ws=None) == WS
+    assert pf(lib, qd=BF16, cache=E5M2 | PER_HEAD, ks=FAKE, vs=FAKE,
+              ws=None) == WS
+    # the copies take any cache dtype argument (scales play no part)
+    assert lib.copy_blocks(FAKE, FAKE, E5M2 | PER_HEAD, FAKE, 0, 16, 16, 8,
+                           128, None) == OK
+    assert lib.copy_blocks(FAKE, FAKE, 5, FAKE, 0, 16, 16, 8, 128,
+                           None) == DTYPE
+

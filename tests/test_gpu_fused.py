@@ -83,6 +83,8 @@ SMALL = [
     ("f16", "fp8_e4m3", 128, 16, 8, 8, [17, 600], 8),
     ("f32", "fp8_e4m3", 64, 16, 2, 1, [1, 33, 300], 8),
     ("bf16", "bf16", 128, 16, 8, 8, [0, 5, 0, 40], 4),
+    ("bf16", "fp8_e5m2", 128, 16, 16, 4, [3, 700, 65], 4),
+    ("f32", "fp8_e5m2", 64, 32, 4, 2, [100, 33], 0),
 ]
 
 
@@ -124,3 +126,16 @@ def test_fused_full_size(name):
     w = W.workload_by_name(name)
     sep, fus = run_pair(w)
     assert_same(sep, fus)
+
+
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "fp8_e5m2"])
+def test_fused_per_head_scales(kv):
+    """The fused write encodes each head over its own scale."""
+    w = W.custom_decode(seed=532, num_seqs=4, lens=[40, 300, 2, 65], hq=16,
+                        hkv=4, d=128, bs=16, q_kind="bf16", kv_kind=kv,
+                        per_head_scales=True)
+    for wv in (0, 4):
+        sep, fus = run_pair(w, max_waves=wv)
+        assert_same(sep, fus)
+        assert_pools_bitwise(fus, oracle_pools(w))
+

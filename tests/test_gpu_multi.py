@@ -60,6 +60,8 @@ CASES = [
      "bf16", "bf16"),
     ("fp8f32q_g2_d64_bs32", [129, 64, 480], [10, 64, 8], 4, 2, 64, 32,
      "f32", "fp8_e4m3"),
+    ("e5m2_g4_d128_bs16", [300, 1200, 9, 64], [3, 100, 9, 1], 8, 2, 128, 16,
+     "bf16", "fp8_e5m2"),
 ]
 
 
@@ -175,3 +177,15 @@ def test_chunked_prefill_full_sampled():
     err = max_abs_err(out[rows], ref)
     say(f"multi chunked_prefill_llama8b: max abs err {err:.3g}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kv_kind", ["fp8_e4m3", "fp8_e5m2"])
+def test_multi_per_head_scales(kv_kind):
+    lens, qlens = [300, 700, 40], [20, 64, 5]
+    mq = W.custom_multi(seed=77, lens=lens, qlens=qlens, hq=16, hkv=4, d=128,
+                        bs=16, q_kind="bf16", kv_kind=kv_kind,
+                        per_head_scales=True)
+    say(f"multi per-head scales {kv_kind}")
+    _, out = run_multi(mq)
+    err = max_abs_err(out, oracle_multi(mq, oracle_pools(mq.w)))
+    assert err <= TOL[kv_kind], f"{err:.3g}"

@@ -69,28 +69,39 @@ def test_page_one_write_example():
     assert vc.cpu().numpy().tobytes() == ev.tobytes()
 
 
-@pytest.mark.parametrize("kind,src", [("f32", "f32"), ("bf16", "bf16"),
-                                      ("f16", "f16"), ("fp8_e4m3", "bf16"),
-                                      ("fp8_e4m3", "f16"),
-                                      ("fp8_e4m3", "f32")])
-def test_cache_write_and_copy_bitwise(kind, src):
+@pytest.mark.parametrize("kind,src,per_head", [
+    ("f32", "f32", False), ("bf16", "bf16", False), ("f16", "f16", False),
+    ("fp8_e4m3", "bf16", False), ("fp8_e4m3", "f16", False),
+    ("fp8_e4m3", "f32", False), ("fp8_e5m2", "bf16", False),
+    ("fp8_e5m2", "f16", False), ("fp8_e5m2", "f32", False),
+    ("fp8_e4m3", "bf16", True), ("fp8_e5m2", "bf16", True),
+    ("fp8_e5m2", "f32", True)])
+def test_cache_write_and_copy_bitwise(kind, src, per_head):
     import torch
     from paged_kv_cache_336_amd import ops
     from paged_kv_cache_336_amd.step import _to_torch, to_host_storage
-    say(f"write+copy {src}->{kind}")
+    say(f"write+copy {src}->{kind} per_head={per_head}")
+    fp8 = kind.startswith("fp8")
     w = W.custom_decode(seed=40 + len(kind) + len(src), num_seqs=5,
                         lens=[1, 17, 40, 100, 3], hq=8, hkv=4, d=64, bs=8,
-                        q_kind=src if kind == "fp8_e4m3" else kind,
+                        q_kind=src if fp8 else kind,
                         kv_kind=kind, src_kind=src, num_new_per_seq=3)
-    # negative slots are skipped; scales are non-powers-of-two
+    # negative slots are skipped; scales are non-powers-of-two; with one
+    # scale per head, head 1's is small enough to overflow (E4M3 saturates,
+    # E5M2 goes to infinity)
     slots = w.slot_mapping.copy()
     slots[1] = -1
-    w = replace(w, slot_mapping=slots, k_scale=0.0173, v_scale=0.0291)
+    if per_head:
+        k_scale = np.array([0.0173, 5e-5, 0.5, 3.0], np.float32)
+        v_scale = np.array([0.0291, 0.25, 4e-5, 0.011], np.float32)
+    else:
+        k_scale, v_scale = 0.0173, 0.0291
+    w = replace(w, slot_mapping=slots, k_scale=k_scale, v_scale=v_scale)
     kc = _to_torch(w.k_pool, kind, "cuda")
     vc = _to_torch(w.v_pool, kind, "cuda")
-    ks = torch.tensor([w.k_scale], dtype=torch.float32, device="cuda")
-    vs = torch.tensor([w.v_scale], dtype=torch.float32, device="cuda")
-    ck = "fp8_e4m3" if kind == "fp8_e4m3" else None
+    ks = torch.from_numpy(np.atleast_1d(np.float32(k_scale))).cuda()
+    vs = torch.from_numpy(np.atleast_1d(np.float32(v_scale))).cuda()
+    ck = kind if fp8 else None
     ops.cache_write_slots(_to_torch(w.key, src, "cuda"),
                           _to_torch(w.value, src, "cuda"), kc, vc,
                           torch.from_numpy(slots).cuda(), k_scale=ks,
@@ -161,6 +172,10 @@ SMALL = [
     ("f32", "fp8_e4m3", 64, 16, 2, 1, [1, 33, 300], 8),
     ("bf16", "bf16", 128, 16, 8, 8, [0, 5, 0, 40], 4),
     ("bf16", "bf16", 128, 16, 8, 8, [0, 0, 0], 0),
+    ("bf16", "fp8_e5m2", 128, 64, 32, 8, [1, 63, 64, 65, 1500], 0),
+    ("bf16", "fp8_e5m2", 128, 16, 32, 8, [7, 900, 4100], 8),
+    ("f16", "fp8_e5m2", 64, 16, 8, 2, [17, 600], 8),
+    ("f32", "fp8_e5m2", 64, 16, 2, 1, [1, 33, 300], 4),
 ]
 
 
@@ -173,8 +188,28 @@ def test_small_cases(case):
                         num_seqs=len(lens),
                         lens=lens, hq=hq, hkv=hkv, d=d, bs=bs, q_kind=q,
                         kv_kind=kv)
+    # non-power-of-two scales that keep the stored values' magnitude that of
+    # the N(0,1) draws (the E5M2 range is 128 times the E4M3 one)
     if kv == "fp8_e4m3":
         w = replace(w, k_scale=0.0123, v_scale=0.0217)
+    elif kv == "fp8_e5m2":
+        w = replace(w, k_scale=0.0123 / 128, v_scale=0.0217 / 128)
+    run_full(w, max_waves=waves)
+
+
+@pytest.mark.parametrize("q,kv,waves", [("bf16", "fp8_e4m3", 0),
+                                        ("bf16", "fp8_e5m2", 8),
+                                        ("f16", "fp8_e4m3", 4),
+                                        ("f32", "fp8_e5m2", 0)])
+def test_per_head_scales(q, kv, waves):
+    """fp8 caches whose pools were quantised with one scale per kv head:
+    writes bit for bit, attention within tolerance, for any split."""
+    say(f"per-head scales {q}/{kv} waves {waves}")
+    w = W.custom_decode(seed=61, num_seqs=4, lens=[5, 130, 1025, 40],
+                        hq=16, hkv=4, d=128, bs=16, q_kind=q, kv_kind=kv,
+                        per_head_scales=True)
+    assert np.asarray(w.k_scale).shape == (4,)
+    assert len(set(np.asarray(w.k_scale).tolist())) == 4
     run_full(w, max_waves=waves)
 
 
@@ -191,28 +226,29 @@ def test_single_token_returns_its_value_exactly():
             assert np.array_equal(out[s, hq].astype(np.float64), v)
 
 
-def test_fp8_value_decode_all_codes():
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "fp8_e5m2"])
+def test_fp8_value_decode_all_codes(kv):
     """L = 1 makes the output the stored value times v_scale: with the
-    value rows holding every finite E4M3 code the kernel's decode is checked
+    value rows holding every finite code the kernel's decode is checked
     code by code (float32 product, rounded once)."""
     import torch
-    say("fp8 decode of all codes through attention")
+    say(f"{kv} decode of all codes through attention")
     w = W.custom_decode(seed=5, num_seqs=2, lens=[1, 1], hq=1, hkv=1, d=128,
-                        bs=16, q_kind="bf16", kv_kind="fp8_e4m3")
+                        bs=16, q_kind="bf16", kv_kind=kv)
     w = replace(w, k_scale=0.5, v_scale=0.0371)
     dev = DeviceStep(w, replicas=False)
     dev.copy()
     dev.write()
     codes = np.arange(256, dtype=np.uint8).reshape(2, 128)
-    codes[codes & 0x7F == 0x7F] = 0
+    decode = oracle.e4m3_decode if kv == "fp8_e4m3" else oracle.e5m2_decode
+    codes[~np.isfinite(decode(codes))] = 0   # NaN (and E5M2 infinity) codes
     for s in range(2):
         b, o = divmod(int(w.slot_mapping[s]), 16)
         dev.v_cache[b, o, 0] = torch.from_numpy(codes[s]).cuda()
     dev.attend()
     torch.cuda.synchronize()
     got = dev.out.cpu().numpy()[:, 0, :]
-    exp = (oracle.e4m3_decode(codes) * float(np.float32(w.v_scale))).astype(
-        np.float32)
+    exp = (decode(codes) * float(np.float32(w.v_scale))).astype(np.float32)
     assert np.array_equal(got, exp)
 
 
