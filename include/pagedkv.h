@@ -160,6 +160,36 @@ int copy_block_prefixes(void* k_cache, void* v_cache, int cache_dtype,
                         hipStream_t stream);
 
 /*
+ * copy_blocks_layers, copy_block_prefixes_layers -- the same copies in the
+ * pools of every layer of a model, in one launch.  A block id names the same
+ * block in every layer ("PagedAttention", shubhamtatvamasi.com, the table in
+ * "The idea: page the KV cache": a KV block is 16 tokens x all layers' K and
+ * V), so a copy-on-write copies it in each layer's pools.
+ *
+ * k_caches,
+ * v_caches      the first layer's pools; layer l's are layer_stride bytes
+ *               further on (e.g. one allocation [num_layers, num_blocks,
+ *               block_size, num_kv_heads, head_dim] per cache); layer_stride
+ *               a multiple of 16, at least one pool's bytes when
+ *               num_layers > 1 (layers must not overlap).
+ * num_layers    1 .. 65535.
+ * Other arguments, and the result in each layer, as copy_blocks /
+ * copy_block_prefixes.
+ */
+int copy_blocks_layers(void* k_caches, void* v_caches, int64_t layer_stride,
+                       int32_t num_layers, int cache_dtype,
+                       const int32_t* block_pairs, int64_t num_pairs,
+                       int64_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_dim,
+                       hipStream_t stream);
+int copy_block_prefixes_layers(void* k_caches, void* v_caches,
+                               int64_t layer_stride, int32_t num_layers,
+                               int cache_dtype, const int32_t* block_triples,
+                               int64_t num_copies, int64_t num_blocks,
+                               int32_t block_size, int32_t num_kv_heads,
+                               int32_t head_dim, hipStream_t stream);
+
+/*
  * paged_attn_workspace_size -- bytes of device workspace paged_attn_decode
  * needs for these arguments, or (size_t)-1 for invalid arguments.
  *

@@ -51,6 +51,25 @@ pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size,
                                  int32_t max_seqs, int32_t max_blocks_per_seq);
 void pkv_bm_destroy(pkv_block_manager* bm);
 
+/* A manager as above that also caches prompt prefixes ("PagedAttention",
+ * shubhamtatvamasi.com, "Sharing and copy-on-write": different requests with
+ * the same system prompt share blocks).  Every full block that
+ * pkv_bm_add_sequence_tokens fills from a prompt is registered under the
+ * contents of the prompt up to and including it; a later prompt whose leading
+ * full blocks have registered contents takes those blocks (one more
+ * reference each) instead of new ones, so its K/V for those tokens are
+ * already in the pool.  Partially filled blocks are never shared this way.
+ * A registered block whose last reference is dropped stays registered, on an
+ * evictable list (oldest release first); allocations take plain free blocks
+ * first and reuse evictable ones (dropping their registration) only when
+ * none is left.  Readings: a prompt's lookup stops at its first block that
+ * is not registered; blocks filled by pkv_bm_append (no token ids) are not
+ * registered. */
+pkv_block_manager* pkv_bm_create_prefix_cached(int32_t num_blocks,
+                                               int32_t block_size,
+                                               int32_t max_seqs,
+                                               int32_t max_blocks_per_seq);
+
 /* Start sequence seq with num_tokens tokens (a prompt, num_tokens >= 0):
  * takes ceil(num_tokens / block_size) blocks.  slots_out (may be NULL) gets
  * the slot block * block_size + offset of each token, for cache_write_slots.
@@ -59,6 +78,25 @@ void pkv_bm_destroy(pkv_block_manager* bm);
  * if the free list is too short. */
 int pkv_bm_add_sequence(pkv_block_manager* bm, int32_t seq, int32_t num_tokens,
                         int32_t* slots_out);
+
+/* Start sequence seq with the prompt tokens[0 .. num_tokens-1] (token ids).
+ * As pkv_bm_add_sequence, except that with a prefix-caching manager the
+ * leading full blocks whose contents are registered are shared, and
+ * *cached_tokens_out (may be NULL) gets the number of leading tokens whose
+ * K/V those blocks already hold: the caller writes and computes only the
+ * tokens from there on.  slots_out still gets every token's slot.  Without
+ * prefix caching this is pkv_bm_add_sequence with *cached_tokens_out = 0.
+ * PKV_ERR_NULL if tokens is NULL with num_tokens > 0. */
+int pkv_bm_add_sequence_tokens(pkv_block_manager* bm, int32_t seq,
+                               const int32_t* tokens, int32_t num_tokens,
+                               int32_t* slots_out, int32_t* cached_tokens_out);
+
+/* Prefix-cache counters: blocks registered (in use or evictable), blocks on
+ * the evictable list (no reference, still registered; they also count as
+ * free in pkv_bm_get_stats), and prompt blocks found in the cache so far.
+ * Any pointer may be NULL. */
+int pkv_bm_prefix_stats(const pkv_block_manager* bm, int64_t* registered,
+                        int64_t* evictable, int64_t* hit_blocks);
 
 /* Sequence child (not live) starts as a copy of sequence parent (live): the
  * same length and table, and every block of it gains a reference.  No block
@@ -96,7 +134,8 @@ int pkv_bm_tables(const pkv_block_manager* bm, const int32_t* seqs, int32_t n,
                   int32_t* lens);
 
 typedef struct pkv_bm_stats {
-  int64_t free_blocks;     /* blocks on the free list                       */
+  int64_t free_blocks;     /* blocks with no reference (the free list, and
+                              with prefix caching the evictable blocks)     */
   int64_t used_blocks;     /* blocks held by at least one sequence          */
   int64_t shared_blocks;   /* blocks held by more than one sequence         */
   int64_t live_sequences;

@@ -44,6 +44,9 @@ class BlockManager:
         self.lengths = {}                  # seq -> tokens
 
     # -- allocation ------------------------------------------------------
+    def _available(self):
+        return len(self.free)
+
     def _take(self):
         if not self.free:
             raise OutOfBlocks()
@@ -63,7 +66,7 @@ class BlockManager:
         assert seq not in self.tables
         nblocks = -(-num_tokens // self.block_size)
         assert nblocks <= self.max_blocks_per_seq
-        if nblocks > len(self.free):
+        if nblocks > self._available():
             raise OutOfBlocks()
         table = []
         for i in range(nblocks):
@@ -109,19 +112,25 @@ class BlockManager:
         old block holds); raises OutOfBlocks (and changes nothing) if the
         free list runs out part way."""
         assert len(set(seqs)) == len(seqs)
-        saved = (list(self.free), list(self.refs), list(self.tokens_in),
-                 {s: list(t) for s, t in self.tables.items()},
-                 dict(self.lengths))
+        saved = self._snapshot()
         pairs, counts = [], []
         try:
             slots = [self._append_one(s, pairs, counts) for s in seqs]
         except OutOfBlocks:
-            (self.free, self.refs, self.tokens_in, self.tables,
-             self.lengths) = saved
+            self._restore(saved)
             raise
         if with_counts:
             return slots, pairs, counts
         return slots, pairs
+
+    def _snapshot(self):
+        return (list(self.free), list(self.refs), list(self.tokens_in),
+                {s: list(t) for s, t in self.tables.items()},
+                dict(self.lengths))
+
+    def _restore(self, saved):
+        (self.free, self.refs, self.tokens_in, self.tables,
+         self.lengths) = saved
 
     def free_sequence(self, seq):
         for b in self.tables.pop(seq):
@@ -136,7 +145,7 @@ class BlockManager:
         used = [b for b, r in enumerate(self.refs) if r > 0]
         stored = sum(self.tokens_in[b] for b in used)
         return {
-            "free_blocks": len(self.free),
+            "free_blocks": self._available(),
             "used_blocks": len(used),
             "shared_blocks": sum(1 for b in used if self.refs[b] > 1),
             "live_sequences": len(self.tables),
@@ -144,6 +153,109 @@ class BlockManager:
             "stored_tokens": stored,
             "wasted_slots": len(used) * self.block_size - stored,
         }
+
+
+class PrefixCachingBlockManager(BlockManager):
+    """The manager with prompt-prefix caching ("PagedAttention",
+    shubhamtatvamasi.com, "Sharing and copy-on-write": different requests
+    with the same system prompt share blocks; "Choosing the block size":
+    sharing goes by whole blocks).
+
+    Readings: a full block filled from a prompt is registered under the
+    prompt's tokens up to and including that block; a later prompt takes the
+    registered blocks of its leading full blocks, in order, until the first
+    one that is not registered (and registers its new full blocks, as long
+    as their prefix is not registered already); partially filled blocks are
+    never shared this way; a registered block with no reference left stays
+    registered on an evictable list (oldest release first) and is reused --
+    losing its registration -- only when no plain free block is left; blocks
+    filled by appends carry no token ids and are not registered.  Written
+    with the whole prefix as the key (a tuple of token ids), so there is no
+    hashing here at all.
+    """
+
+    def __init__(self, num_blocks, block_size, max_blocks_per_seq):
+        super().__init__(num_blocks, block_size, max_blocks_per_seq)
+        self.registry = {}     # prefix tuple -> block
+        self.key_of = {}       # block -> prefix tuple
+        self.evictable = []    # oldest release first
+        self.hit_blocks = 0
+
+    def _available(self):
+        return len(self.free) + len(self.evictable)
+
+    def _take(self):
+        if self.free:
+            return super()._take()
+        if not self.evictable:
+            raise OutOfBlocks()
+        b = self.evictable.pop(0)
+        del self.registry[self.key_of.pop(b)]
+        self.refs[b] = 1
+        self.tokens_in[b] = 0
+        return b
+
+    def _release(self, b):
+        self.refs[b] -= 1
+        if self.refs[b] == 0:
+            if b in self.key_of:
+                self.evictable.append(b)
+            else:
+                self.free.append(b)
+
+    def add_sequence_tokens(self, seq, tokens):
+        """Returns (slots of every token, tokens whose blocks were cached)."""
+        assert seq not in self.tables
+        tokens = [int(t) for t in tokens]
+        bs = self.block_size
+        n = len(tokens)
+        nblocks = -(-n // bs)
+        assert nblocks <= self.max_blocks_per_seq
+        hits = []
+        for i in range(n // bs):
+            b = self.registry.get(tuple(tokens[:(i + 1) * bs]))
+            if b is None:
+                break
+            hits.append(b)
+        revived = sum(1 for b in hits if self.refs[b] == 0)
+        if nblocks - len(hits) > self._available() - revived:
+            raise OutOfBlocks()
+        table = []
+        for b in hits:
+            if self.refs[b] == 0:
+                self.evictable.remove(b)
+            self.refs[b] += 1
+            table.append(b)
+        self.hit_blocks += len(hits)
+        registering = True
+        for i in range(len(hits), nblocks):
+            b = self._take()
+            self.tokens_in[b] = min(bs, n - i * bs)
+            if registering and n - i * bs >= bs:
+                key = tuple(tokens[:(i + 1) * bs])
+                if key in self.registry:
+                    registering = False
+                else:
+                    self.registry[key] = b
+                    self.key_of[b] = key
+            table.append(b)
+        self.tables[seq] = table
+        self.lengths[seq] = n
+        slots = [table[t // bs] * bs + t % bs for t in range(n)]
+        return slots, len(hits) * bs
+
+    def _snapshot(self):
+        return (super()._snapshot(), dict(self.registry), dict(self.key_of),
+                list(self.evictable))
+
+    def _restore(self, saved):
+        base, self.registry, self.key_of, self.evictable = saved
+        super()._restore(base)
+
+    def prefix_stats(self):
+        return {"registered": len(self.key_of),
+                "evictable": len(self.evictable),
+                "hit_blocks": self.hit_blocks}
 
 
 class ContiguousAllocator:

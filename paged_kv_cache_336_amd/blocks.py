@@ -13,7 +13,9 @@ from . import ops
 
 PKV_ERR_NO_BLOCKS = 9
 
-EXPORTED = ("pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence",
+EXPORTED = ("pkv_bm_create", "pkv_bm_create_prefix_cached",
+            "pkv_bm_add_sequence_tokens", "pkv_bm_prefix_stats",
+            "pkv_bm_destroy", "pkv_bm_add_sequence",
             "pkv_bm_fork", "pkv_bm_append", "pkv_bm_free", "pkv_bm_tables",
             "pkv_bm_get_stats", "pkv_bm_refcount", "pkv_bm_seq_len",
             "pkv_ca_create", "pkv_ca_destroy", "pkv_ca_reserve",
@@ -48,6 +50,14 @@ def _lib():
         ci = ctypes.c_int
         lib.pkv_bm_create.restype = vp
         lib.pkv_bm_create.argtypes = [i32, i32, i32, i32]
+        lib.pkv_bm_create_prefix_cached.restype = vp
+        lib.pkv_bm_create_prefix_cached.argtypes = [i32, i32, i32, i32]
+        lib.pkv_bm_add_sequence_tokens.restype = ci
+        lib.pkv_bm_add_sequence_tokens.argtypes = [vp, i32, vp, i32, vp, vp]
+        lib.pkv_bm_prefix_stats.restype = ci
+        lib.pkv_bm_prefix_stats.argtypes = [vp, ctypes.POINTER(i64),
+                                            ctypes.POINTER(i64),
+                                            ctypes.POINTER(i64)]
         lib.pkv_bm_destroy.restype = None
         lib.pkv_bm_destroy.argtypes = [vp]
         lib.pkv_bm_add_sequence.restype = ci
@@ -96,12 +106,14 @@ def _ptr(a):
 class BlockManager:
     """Physical-block bookkeeping for one paged pool (see pagedkv_blocks.h)."""
 
-    def __init__(self, num_blocks, block_size, max_seqs, max_blocks_per_seq):
+    def __init__(self, num_blocks, block_size, max_seqs, max_blocks_per_seq,
+                 prefix_cache=False):
         self.lib = _lib()
         self.block_size = block_size
         self.max_blocks_per_seq = max_blocks_per_seq
-        self.h = self.lib.pkv_bm_create(num_blocks, block_size, max_seqs,
-                                        max_blocks_per_seq)
+        create = (self.lib.pkv_bm_create_prefix_cached if prefix_cache
+                  else self.lib.pkv_bm_create)
+        self.h = create(num_blocks, block_size, max_seqs, max_blocks_per_seq)
         if not self.h:
             raise ValueError("pkv_bm_create rejected its arguments")
 
@@ -119,6 +131,26 @@ class BlockManager:
         _check(self.lib.pkv_bm_add_sequence(self.h, seq, num_tokens,
                                             _ptr(slots)), "add_sequence")
         return slots[:num_tokens]
+
+    def add_sequence_tokens(self, seq, tokens):
+        """A prompt given by its token ids: (slots int32 [n], the number of
+        leading tokens whose blocks came from the prefix cache)."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = len(toks)
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        cached = ctypes.c_int32(0)
+        _check(self.lib.pkv_bm_add_sequence_tokens(
+            self.h, seq, _ptr(toks) if n else None, n, _ptr(slots),
+            ctypes.byref(cached)), "add_sequence_tokens")
+        return slots[:n], int(cached.value)
+
+    def prefix_stats(self):
+        r, e, h = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(self.lib.pkv_bm_prefix_stats(self.h, ctypes.byref(r),
+                                            ctypes.byref(e), ctypes.byref(h)),
+               "prefix_stats")
+        return {"registered": r.value, "evictable": e.value,
+                "hit_blocks": h.value}
 
     def fork(self, parent, child):
         _check(self.lib.pkv_bm_fork(self.h, parent, child), "fork")

@@ -29,15 +29,55 @@ struct pkv_block_manager {
   std::vector<int32_t> len;         // per sequence id
   std::vector<std::vector<int32_t>> table;
 
+  // Prefix caching ("PagedAttention", shubhamtatvamasi.com, "Sharing and
+  // copy-on-write": requests with the same system prompt share blocks).  A
+  // full prompt block is registered under its content -- the key of the
+  // prefix before it and its token ids -- and a later prompt whose leading
+  // blocks have the same contents takes those blocks instead of new ones.
+  // A registered block whose last reference goes stays registered, on the
+  // evictable list (oldest release first), until an allocation finds the
+  // free stack empty and reuses it.
+  bool prefix_cache = false;
+  std::vector<char> registered;          // per block
+  std::vector<uint64_t> parent;          // key of the prefix before a block
+  std::vector<int32_t> block_tokens;     // [num_blocks * block_size]
+  std::vector<uint64_t> key;             // per registered block
+  std::unordered_map<uint64_t, int32_t> index;  // key -> block
+  std::map<int64_t, int32_t> evictable;  // release stamp -> block
+  std::vector<int64_t> stamp;            // per block on the evictable list
+  int64_t next_stamp = 0;
+  int64_t hit_blocks = 0;
+
+  int64_t available() const {
+    return (int64_t)free_stack.size() + (int64_t)evictable.size();
+  }
   int32_t take() {
-    const int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {  // reuse the longest-released cached block
+      b = evictable.begin()->second;
+      evictable.erase(evictable.begin());
+      unregister(b);
+    }
     refcount[b] = 1;
     stored[b] = 0;
     return b;
   }
   void drop(int32_t b) {
-    if (--refcount[b] == 0) free_stack.push_back(b);
+    if (--refcount[b] != 0) return;
+    if (prefix_cache && registered[b]) {
+      stamp[b] = next_stamp++;
+      evictable[stamp[b]] = b;
+    } else {
+      free_stack.push_back(b);
+    }
+  }
+  void unregister(int32_t b) {
+    const auto it = index.find(key[b]);
+    if (it != index.end() && it->second == b) index.erase(it);
+    registered[b] = 0;
   }
   bool seq_ok(int32_t s) const { return s >= 0 && s < max_seqs; }
 };
@@ -45,6 +85,39 @@ struct pkv_block_manager {
 namespace {
 
 int64_t blocks_for(int64_t tokens, int32_t bs) { return (tokens + bs - 1) / bs; }
+
+// Key of a full block: FNV-1a over the key of the prefix before it (0 for a
+// sequence's first block) and its token ids, so a key stands for the whole
+// prefix through that block.  A lookup also compares the stored parent key
+// and tokens, so a collision of the final hash only costs a miss.
+constexpr uint64_t kRootKey = 0;
+
+uint64_t block_key(uint64_t parent, const int32_t* toks, int32_t n) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&](uint32_t v) {
+    for (int i = 0; i < 4; ++i) {
+      h ^= (v >> (8 * i)) & 0xFFu;
+      h *= 1099511628211ull;
+    }
+  };
+  mix((uint32_t)parent);
+  mix((uint32_t)(parent >> 32));
+  for (int32_t i = 0; i < n; ++i) mix((uint32_t)toks[i]);
+  return h;
+}
+
+// The registered block with these contents, or -1.
+int32_t lookup(const pkv_block_manager* bm, uint64_t parent,
+               const int32_t* toks) {
+  const int32_t bs = bm->block_size;
+  const auto it = bm->index.find(block_key(parent, toks, bs));
+  if (it == bm->index.end()) return -1;
+  const int32_t b = it->second;
+  if (bm->parent[b] != parent) return -1;
+  if (!std::equal(toks, toks + bs, bm->block_tokens.begin() + (int64_t)b * bs))
+    return -1;
+  return b;
+}
 
 }  // namespace
 
@@ -76,7 +149,107 @@ pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size,
   return bm;
 }
 
+pkv_block_manager* pkv_bm_create_prefix_cached(int32_t num_blocks,
+                                               int32_t block_size,
+                                               int32_t max_seqs,
+                                               int32_t max_blocks_per_seq) {
+  pkv_block_manager* bm =
+      pkv_bm_create(num_blocks, block_size, max_seqs, max_blocks_per_seq);
+  if (!bm) return nullptr;
+  try {
+    bm->prefix_cache = true;
+    bm->registered.assign(num_blocks, 0);
+    bm->parent.assign(num_blocks, 0);
+    bm->block_tokens.assign((size_t)num_blocks * block_size, 0);
+    bm->key.assign(num_blocks, 0);
+    bm->stamp.assign(num_blocks, 0);
+  } catch (...) {
+    delete bm;
+    return nullptr;
+  }
+  return bm;
+}
+
 void pkv_bm_destroy(pkv_block_manager* bm) { delete bm; }
+
+int pkv_bm_add_sequence_tokens(pkv_block_manager* bm, int32_t seq,
+                               const int32_t* tokens, int32_t num_tokens,
+                               int32_t* slots_out, int32_t* cached_tokens_out) {
+  if (!bm) return PKV_ERR_NULL;
+  if (!bm->seq_ok(seq) || num_tokens < 0) return PKV_ERR_SHAPE;
+  if (num_tokens > 0 && !tokens) return PKV_ERR_NULL;
+  if (bm->live[seq]) return PKV_ERR_SEQ;
+  const int32_t bs = bm->block_size;
+  const int64_t nb = blocks_for(num_tokens, bs);
+  if (nb > bm->max_blocks_per_seq) return PKV_ERR_SHAPE;
+  // the leading full blocks whose contents are registered
+  std::vector<int32_t> hits;
+  if (bm->prefix_cache) {
+    uint64_t prev = kRootKey;
+    for (int64_t i = 0; i < num_tokens / bs; ++i) {
+      const int32_t b = lookup(bm, prev, tokens + i * bs);
+      if (b < 0) break;
+      hits.push_back(b);
+      prev = bm->key[b];
+    }
+  }
+  int64_t hits_evictable = 0;
+  for (int32_t b : hits)
+    if (bm->refcount[b] == 0) ++hits_evictable;
+  if (nb - (int64_t)hits.size() > bm->available() - hits_evictable)
+    return PKV_ERR_NO_BLOCKS;
+  std::vector<int32_t>& t = bm->table[seq];
+  t.clear();
+  for (int32_t b : hits) {  // taken off the evictable list first
+    if (bm->refcount[b] == 0) bm->evictable.erase(bm->stamp[b]);
+    ++bm->refcount[b];
+    t.push_back(b);
+  }
+  bm->hit_blocks += (int64_t)hits.size();
+  // the new full blocks are registered under the key chain of the prefix,
+  // until a key turns out to be taken (a hash collision: stop registering)
+  uint64_t prev = hits.empty() ? kRootKey : bm->key[hits.back()];
+  bool chain = bm->prefix_cache;
+  for (int64_t i = (int64_t)hits.size(); i < nb; ++i) {
+    const int32_t b = bm->take();
+    const int64_t left = num_tokens - i * bs;
+    bm->stored[b] = (int32_t)std::min<int64_t>(left, bs);
+    if (chain && left >= bs) {
+      const uint64_t k = block_key(prev, tokens + i * bs, bs);
+      if (!bm->index.count(k)) {
+        bm->index[k] = b;
+        bm->key[b] = k;
+        bm->parent[b] = prev;
+        std::copy(tokens + i * bs, tokens + (i + 1) * bs,
+                  bm->block_tokens.begin() + (int64_t)b * bs);
+        bm->registered[b] = 1;
+        prev = k;
+      } else {
+        chain = false;
+      }
+    }
+    t.push_back(b);
+  }
+  bm->live[seq] = 1;
+  bm->len[seq] = num_tokens;
+  if (slots_out)
+    for (int32_t k = 0; k < num_tokens; ++k)
+      slots_out[k] = t[k / bs] * bs + k % bs;
+  if (cached_tokens_out) *cached_tokens_out = (int32_t)hits.size() * bs;
+  return PKV_OK;
+}
+
+int pkv_bm_prefix_stats(const pkv_block_manager* bm, int64_t* registered,
+                        int64_t* evictable, int64_t* hit_blocks) {
+  if (!bm) return PKV_ERR_NULL;
+  int64_t r = 0;
+  if (bm->prefix_cache)
+    for (int32_t b = 0; b < bm->num_blocks; ++b) r += bm->registered[b];
+  if (registered) *registered = r;
+  if (evictable) *evictable = (int64_t)bm->evictable.size();
+  if (hit_blocks) *hit_blocks = bm->hit_blocks;
+  return PKV_OK;
+}
 
 int pkv_bm_add_sequence(pkv_block_manager* bm, int32_t seq, int32_t num_tokens,
                         int32_t* slots_out) {
@@ -85,7 +258,7 @@ int pkv_bm_add_sequence(pkv_block_manager* bm, int32_t seq, int32_t num_tokens,
   if (bm->live[seq]) return PKV_ERR_SEQ;
   const int64_t nb = blocks_for(num_tokens, bm->block_size);
   if (nb > bm->max_blocks_per_seq) return PKV_ERR_SHAPE;
-  if (nb > (int64_t)bm->free_stack.size()) return PKV_ERR_NO_BLOCKS;
+  if (nb > bm->available()) return PKV_ERR_NO_BLOCKS;
   std::vector<int32_t>& t = bm->table[seq];
   t.clear();
   for (int64_t i = 0; i < nb; ++i) {
@@ -145,7 +318,7 @@ int pkv_bm_append(pkv_block_manager* bm, const int32_t* seqs, int32_t n,
       }
     }
   }
-  if (need > (int64_t)bm->free_stack.size()) return PKV_ERR_NO_BLOCKS;
+  if (need > bm->available()) return PKV_ERR_NO_BLOCKS;
   int32_t np = 0;
   for (int32_t i = 0; i < n; ++i) {
     const int32_t s = seqs[i];
@@ -207,7 +380,7 @@ int pkv_bm_tables(const pkv_block_manager* bm, const int32_t* seqs, int32_t n,
 int pkv_bm_get_stats(const pkv_block_manager* bm, pkv_bm_stats* out) {
   if (!bm || !out) return PKV_ERR_NULL;
   pkv_bm_stats st{};
-  st.free_blocks = (int64_t)bm->free_stack.size();
+  st.free_blocks = bm->available();
   for (int32_t b = 0; b < bm->num_blocks; ++b) {
     if (bm->refcount[b] == 0) continue;
     ++st.used_blocks;

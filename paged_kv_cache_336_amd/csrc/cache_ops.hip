@@ -10,7 +10,9 @@
 //
 // copy_blocks ("PagedAttention", shubhamtatvamasi.com, section "Sharing and
 // copy-on-write"): each (src, dst) pair copies a whole block of both pools
-// with 16-byte loads/stores, one grid row per pair.
+// with 16-byte loads/stores, one grid row per pair -- and, for the pools of
+// every layer at once (a block is "16 tokens x all layers' K and V", the
+// same page's table), one grid slice per layer.
 
 #include "kv_encode.h"
 #include "pkv_device.h"
@@ -114,6 +116,9 @@ hipError_t launch_cache_write(const WriteArgs& a, int src_dtype,
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
   const int w = a.prefix ? 3 : 2;
+  // grid z: the layer whose pools this workgroup copies in (one block id
+  // names the same block in every layer's pools)
+  const int64_t lofs = (int64_t)blockIdx.z * a.layer_stride;
   for (int64_t pair = blockIdx.y; pair < a.num_pairs; pair += gridDim.y) {
     const int64_t src = a.pairs[w * pair];
     const int64_t dst = a.pairs[w * pair + 1];
@@ -125,10 +130,12 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
       pieces = (t < 0 ? 0 : (t > a.block_size ? a.block_size : t)) *
                a.token_bytes / 16;
     }
-    const uint8_t* ks = static_cast<const uint8_t*>(a.k_cache) + src * a.block_bytes;
-    const uint8_t* vs = static_cast<const uint8_t*>(a.v_cache) + src * a.block_bytes;
-    uint8_t* kd = static_cast<uint8_t*>(a.k_cache) + dst * a.block_bytes;
-    uint8_t* vd = static_cast<uint8_t*>(a.v_cache) + dst * a.block_bytes;
+    uint8_t* kl = static_cast<uint8_t*>(a.k_cache) + lofs;
+    uint8_t* vl = static_cast<uint8_t*>(a.v_cache) + lofs;
+    const uint8_t* ks = kl + src * a.block_bytes;
+    const uint8_t* vs = vl + src * a.block_bytes;
+    uint8_t* kd = kl + dst * a.block_bytes;
+    uint8_t* vd = vl + dst * a.block_bytes;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < pieces;
          i += (int64_t)gridDim.x * blockDim.x) {
       const u32x4_t k = *reinterpret_cast<const u32x4_t*>(ks + 16 * i);
@@ -145,7 +152,8 @@ hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream) {
   if (gx > 64) gx = 64;
   if (gx < 1) gx = 1;
   const unsigned gy = (unsigned)(a.num_pairs < 65535 ? a.num_pairs : 65535);
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, gy), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, gy, a.num_layers),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

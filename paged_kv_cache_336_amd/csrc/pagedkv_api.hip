@@ -141,7 +141,8 @@ namespace {
 int copy_common(void* k_cache, void* v_cache, int cache_dtype,
                 const int32_t* block_pairs, int64_t num_pairs,
                 int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
-                int32_t head_dim, int prefix, hipStream_t stream) {
+                int32_t head_dim, int prefix, int32_t num_layers,
+                int64_t layer_stride, hipStream_t stream) {
   bool per_head = false;  // (scales play no part in a copy)
   const int cache_arg = cache_dtype;
   if (!split_cache_dtype(cache_arg, &cache_dtype, &per_head))
@@ -149,11 +150,20 @@ int copy_common(void* k_cache, void* v_cache, int cache_dtype,
   if (num_pairs < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1)
     return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  const int64_t pool_bytes = num_blocks * block_size * (int64_t)num_kv_heads *
+                             head_dim * dtype_bytes(cache_dtype);
+  // the layers' pools must not overlap
+  if (num_layers < 1 || num_layers > 65535 ||
+      (num_layers > 1 && layer_stride < pool_bytes))
+    return PKV_ERR_SHAPE;
+  if (num_layers > 1 && layer_stride % 16 != 0) return PKV_ERR_ALIGN;
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !block_pairs) return PKV_ERR_NULL;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 4))
     return PKV_ERR_ALIGN;
   CopyArgs a{};
+  a.num_layers = num_layers;
+  a.layer_stride = num_layers > 1 ? layer_stride : 0;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.pairs = block_pairs;
@@ -173,8 +183,30 @@ int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
                 int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                 int32_t head_dim, hipStream_t stream) {
   return copy_common(k_cache, v_cache, cache_dtype, block_pairs, num_pairs,
-                     num_blocks, block_size, num_kv_heads, head_dim, 0,
+                     num_blocks, block_size, num_kv_heads, head_dim, 0, 1, 0,
                      stream);
+}
+
+int copy_blocks_layers(void* k_caches, void* v_caches, int64_t layer_stride,
+                       int32_t num_layers, int cache_dtype,
+                       const int32_t* block_pairs, int64_t num_pairs,
+                       int64_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_dim,
+                       hipStream_t stream) {
+  return copy_common(k_caches, v_caches, cache_dtype, block_pairs, num_pairs,
+                     num_blocks, block_size, num_kv_heads, head_dim, 0,
+                     num_layers, layer_stride, stream);
+}
+
+int copy_block_prefixes_layers(void* k_caches, void* v_caches,
+                               int64_t layer_stride, int32_t num_layers,
+                               int cache_dtype, const int32_t* block_triples,
+                               int64_t num_copies, int64_t num_blocks,
+                               int32_t block_size, int32_t num_kv_heads,
+                               int32_t head_dim, hipStream_t stream) {
+  return copy_common(k_caches, v_caches, cache_dtype, block_triples,
+                     num_copies, num_blocks, block_size, num_kv_heads,
+                     head_dim, 1, num_layers, layer_stride, stream);
 }
 
 int copy_block_prefixes(void* k_cache, void* v_cache, int cache_dtype,
@@ -183,7 +215,7 @@ int copy_block_prefixes(void* k_cache, void* v_cache, int cache_dtype,
                         int32_t num_kv_heads, int32_t head_dim,
                         hipStream_t stream) {
   return copy_common(k_cache, v_cache, cache_dtype, block_triples, num_copies,
-                     num_blocks, block_size, num_kv_heads, head_dim, 1,
+                     num_blocks, block_size, num_kv_heads, head_dim, 1, 1, 0,
                      stream);
 }
 

@@ -104,6 +104,8 @@ struct CopyArgs {
   int64_t token_bytes;    // one token's rows of all kv heads
   int32_t block_size;
   int32_t prefix;         // 1: copy only the first `tokens` token rows
+  int32_t num_layers;     // pools of every layer, layer_stride bytes apart
+  int64_t layer_stride;
 };
 
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);

@@ -25,6 +25,7 @@ KIND_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
 
 EXPORTED = ("pkv_status_string", "cache_write_slots", "copy_blocks",
             "copy_block_prefixes", "paged_attn_workspace_size",
+            "copy_blocks_layers", "copy_block_prefixes_layers",
             "paged_attn_decode", "paged_attn_decode_fused",
             "paged_attn_multi_workspace_size", "paged_attn_multi")
 
@@ -62,6 +63,9 @@ def load_library(path=None):
     lib.copy_block_prefixes.restype = ci
     lib.copy_block_prefixes.argtypes = [vp, vp, ci, vp, i64, i64, i32, i32,
                                         i32, vp]
+    for fn in (lib.copy_blocks_layers, lib.copy_block_prefixes_layers):
+        fn.restype = ci
+        fn.argtypes = [vp, vp, i64, i32, ci, vp, i64, i64, i32, i32, i32, vp]
     lib.paged_attn_workspace_size.restype = sz
     lib.paged_attn_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.paged_attn_decode.restype = ci
@@ -176,6 +180,34 @@ def copy_block_prefixes(k_cache, v_cache, block_triples, cache_kind=None,
         _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache, cache_kind),
         _ptr(block_triples), int(block_triples.shape[0]), nb, bs, hkv, d,
         _stream(stream)))
+
+
+def _layers_copy(fn, k_caches, v_caches, rows, cache_kind, stream, width):
+    """k_caches, v_caches: [num_layers, num_blocks, block_size, Hkv, D]."""
+    lib = load_library()
+    nl, nb, bs, hkv, d = k_caches.shape
+    stride = k_caches.stride(0) * k_caches.element_size()
+    assert v_caches.shape == k_caches.shape and \
+        v_caches.stride(0) == k_caches.stride(0)
+    assert rows.shape[1:] == (width,)
+    _check(fn.__name__, fn(
+        _ptr(k_caches), _ptr(v_caches), stride, nl,
+        dtype_code(k_caches, cache_kind), _ptr(rows), int(rows.shape[0]), nb,
+        bs, hkv, d, _stream(stream)))
+
+
+def copy_blocks_layers(k_caches, v_caches, block_pairs, cache_kind=None,
+                       stream=None):
+    """Whole-block copies src -> dst in every layer's pools (one launch)."""
+    _layers_copy(load_library().copy_blocks_layers, k_caches, v_caches,
+                 block_pairs, cache_kind, stream, 2)
+
+
+def copy_block_prefixes_layers(k_caches, v_caches, block_triples,
+                               cache_kind=None, stream=None):
+    """copy_block_prefixes in every layer's pools (one launch)."""
+    _layers_copy(load_library().copy_block_prefixes_layers, k_caches,
+                 v_caches, block_triples, cache_kind, stream, 3)
 
 
 def paged_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim):

@@ -284,3 +284,18 @@ def test_cache_dtype_argument(lib):
     assert lib.copy_blocks(FAKE, FAKE, 5, FAKE, 0, 16, 16, 8, 128,
                            None) == DTYPE
 
+
+
+def test_layers_copy_validation(lib):
+    # bf16 pool of 16 blocks x 16 tokens x 8 heads x 128 = 512 KiB per layer
+    pool = 16 * 16 * 8 * 128 * 2
+    args = lambda stride, nl, n=2: (FAKE, FAKE, stride, nl, BF16, FAKE, n,
+                                    16, 16, 8, 128, None)
+    assert lib.copy_blocks_layers(*args(pool, 0)) == SHAPE
+    assert lib.copy_blocks_layers(*args(pool, 65536)) == SHAPE
+    assert lib.copy_blocks_layers(*args(pool - 16, 4)) == SHAPE  # overlap
+    assert lib.copy_blocks_layers(*args(pool + 8, 4)) == ALIGN
+    assert lib.copy_blocks_layers(*args(pool, 4, 0)) == OK       # no pairs
+    assert lib.copy_blocks_layers(*args(0, 1, 0)) == OK          # one layer
+    assert lib.copy_block_prefixes_layers(*args(pool, 0)) == SHAPE
+    assert lib.copy_block_prefixes_layers(*args(pool, 3, 0)) == OK

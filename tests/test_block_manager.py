@@ -190,3 +190,94 @@ def test_waste_simulator():
     assert f["contiguous_waiting"] == ["D", "E"]
     assert f["paged_blocks_used"] <= f["paged_blocks_total"]
     assert all(x < 4 for x in f["paged_waste_per_request"])
+
+
+def assert_same_prefix(bm, ob, nblocks, max_seqs):
+    assert_same(bm, ob, nblocks, max_seqs)
+    assert bm.prefix_stats() == ob.prefix_stats()
+
+
+@pytest.mark.parametrize("seed,nblocks,bs", [(11, 40, 4), (12, 24, 3),
+                                             (13, 64, 16), (14, 30, 1)])
+def test_prefix_cache_matches_oracle(seed, nblocks, bs):
+    """Prompts built from a few shared system prompts, forks, appends and
+    frees on a small pool (so cached blocks are evicted and revived): the
+    C++ manager and the oracle agree on every slot, cached-token count,
+    table, reference count and counter."""
+    from oracle.block_manager import PrefixCachingBlockManager
+    rng = np.random.default_rng(seed)
+    max_seqs, mbps = 16, 40
+    bm = blocks.BlockManager(nblocks, bs, max_seqs, mbps, prefix_cache=True)
+    ob = PrefixCachingBlockManager(nblocks, bs, mbps)
+    systems = [[int(t) for t in rng.integers(0, 6, 3 * bs + 1)]
+               for _ in range(3)]
+    live = set()
+    for step in range(600):
+        op = int(rng.integers(0, 12))
+        idle = [s for s in range(max_seqs) if s not in live]
+        if op < 3 and idle:
+            s = int(rng.choice(idle))
+            sysp = systems[int(rng.integers(0, 3))]
+            p = sysp[:int(rng.integers(0, len(sysp) + 1))] + \
+                [int(t) for t in rng.integers(0, 6, int(rng.integers(0, 2 * bs)))]
+            try:
+                want = ob.add_sequence_tokens(s, p)
+            except OutOfBlocks:
+                with pytest.raises(NoFreeBlocks):
+                    bm.add_sequence_tokens(s, p)
+            else:
+                slots, cached = bm.add_sequence_tokens(s, p)
+                assert (list(slots), cached) == want
+                live.add(s)
+        elif op < 4 and idle:                 # a prompt without token ids
+            s, n = int(rng.choice(idle)), int(rng.integers(0, 2 * bs + 2))
+            try:
+                want = ob.add_sequence(s, n)
+            except OutOfBlocks:
+                with pytest.raises(NoFreeBlocks):
+                    bm.add_sequence(s, n)
+            else:
+                assert list(bm.add_sequence(s, n)) == want
+                live.add(s)
+        elif op < 5 and live and idle:
+            p, c = int(rng.choice(sorted(live))), int(rng.choice(idle))
+            ob.fork(p, c)
+            bm.fork(p, c)
+            live.add(c)
+        elif op < 9 and live:
+            k = int(rng.integers(1, len(live) + 1))
+            seqs = [int(x) for x in rng.choice(sorted(live), k, replace=False)]
+            try:
+                want = ob.append(seqs, True)
+            except OutOfBlocks:
+                with pytest.raises(NoFreeBlocks):
+                    bm.append(seqs)
+            else:
+                slots, pairs, counts = bm.append(seqs, with_counts=True)
+                assert (list(slots), [tuple(p) for p in pairs],
+                        list(counts)) == want
+        elif live:
+            s = int(rng.choice(sorted(live)))
+            ob.free_sequence(s)
+            bm.free(s)
+            live.discard(s)
+        assert_same_prefix(bm, ob, nblocks, max_seqs)
+    assert ob.prefix_stats()["hit_blocks"] > 0
+
+
+def test_prefix_cache_status_codes():
+    bm = blocks.BlockManager(4, 4, 2, 4, prefix_cache=True)
+    NULL = 1
+    assert bm.lib.pkv_bm_add_sequence_tokens(bm.h, 0, None, 3, None,
+                                             None) == NULL  # tokens NULL
+    slots, cached = bm.add_sequence_tokens(0, [])
+    assert len(slots) == 0 and cached == 0
+    with pytest.raises(BlockError) as e:
+        bm.add_sequence_tokens(0, [1])               # already live
+    assert e.value.status == SEQ
+    # a plain manager takes token ids too and never reports cached tokens
+    plain = blocks.BlockManager(8, 4, 2, 4)
+    plain.add_sequence_tokens(0, list(range(8)))
+    assert plain.add_sequence_tokens(1, list(range(8)))[1] == 0
+    assert plain.prefix_stats() == {"registered": 0, "evictable": 0,
+                                    "hit_blocks": 0}

@@ -126,3 +126,88 @@ def test_decode_loop_driven_by_block_manager(kv_kind):
     assert copies == 2              # 0 and 3 copied; 4, the last sharer, kept it
     assert bm.stats() == ob.stats()
     say(f"decode loop: {kv_kind} ok, {copies} copy-on-write pairs")
+
+
+def test_prefix_cached_prompts_share_blocks_and_results():
+    """Two requests with the same system prompt: the second one's leading
+    full blocks come from the prefix cache, so only its remaining prompt
+    tokens are written and attended as new queries (paged_attn_multi).  Its
+    output equals, bit for bit, the same request run on private blocks with
+    every prompt token written, and the oracle within tolerance."""
+    import torch
+    nb, bs, hkv, hq, d = 48, 16, 2, 8, 128
+    kind = "bf16"
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+
+    def kv_row(prefix):
+        # a K/V row fixed by the tokens up to and including its position
+        # (as a model's would be), so equal prefixes give equal rows
+        r = np.random.default_rng([336, 7] + [int(t) for t in prefix])
+        return r.standard_normal((2, hkv, d), np.float32)
+
+    rng = np.random.default_rng(123)
+    system = [int(t) for t in rng.integers(0, 1000, 40)]     # 2.5 blocks
+    prompt_a = system + [int(t) for t in rng.integers(0, 1000, 10)]
+    prompt_b = system + [int(t) for t in rng.integers(0, 1000, 7)]
+    kc = _to_torch(np.full((nb, bs, hkv, d), W.poison_value(kind)), kind, "cuda")
+    vc = kc.clone()
+    bm = blocks.BlockManager(nb, bs, 4, 8, prefix_cache=True)
+
+    def prefill(seq, prompt):
+        slots, cached = bm.add_sequence_tokens(seq, prompt)
+        n = len(prompt)
+        rows = np.stack([kv_row(prompt[:p + 1]) for p in range(cached, n)])
+        key = W._cast_from_f32(rows[:, 0], kind)
+        val = W._cast_from_f32(rows[:, 1], kind)
+        ops.cache_write_slots(_to_torch(key, kind, "cuda"),
+                              _to_torch(val, kind, "cuda"), kc, vc,
+                              torch.from_numpy(slots[cached:].copy()).cuda())
+        q = W._cast_from_f32(rng.standard_normal((n - cached, hq, d),
+                                                 np.float32), kind)
+        tab, lens = bm.tables([seq], fill=0)
+        out = torch.empty((n - cached, hq, d), dtype=torch.float32,
+                          device="cuda")
+        qs = torch.tensor([0, n - cached], dtype=torch.int32, device="cuda")
+        ops.paged_attn_multi(out, _to_torch(q, kind, "cuda"), kc, vc,
+                             torch.from_numpy(tab).cuda(),
+                             torch.from_numpy(lens).cuda(), qs, n - cached,
+                             n, scale)
+        torch.cuda.synchronize()
+        return cached, q, tab, lens, out.cpu().numpy()
+
+    say("prefix cache: request A (no cache), request B (system prompt cached)")
+    ca, _, tab_a, _, _ = prefill(0, prompt_a)
+    cb, qb, tab_b, lens_b, out_b = prefill(1, prompt_b)
+    assert ca == 0 and cb == 32
+    assert list(tab_b[0, :2]) == list(tab_a[0, :2])        # shared blocks
+    assert bm.refcount(int(tab_a[0, 0])) == 2
+    # the oracle on the shared pools
+    pk = to_host_storage(kc, kind)
+    pv = to_host_storage(vc, kind)
+    ref = oracle.paged_attention_multi(qb, kind, pk, pv, kind, tab_b, lens_b,
+                                       np.array([0, len(qb)]), bs, scale)
+    assert max_abs_err(out_b, ref) <= TOL[kind]
+    # the same request on private blocks, every prompt token written
+    priv = blocks.BlockManager(nb, bs, 4, 8)
+    slots_p = priv.add_sequence(1, len(prompt_b))
+    n = len(prompt_b)
+    rows = np.stack([kv_row(prompt_b[:p + 1]) for p in range(n)])
+    kc2 = _to_torch(np.full((nb, bs, hkv, d), W.poison_value(kind)), kind,
+                    "cuda")
+    vc2 = kc2.clone()
+    ops.cache_write_slots(_to_torch(W._cast_from_f32(rows[:, 0], kind), kind,
+                                    "cuda"),
+                          _to_torch(W._cast_from_f32(rows[:, 1], kind), kind,
+                                    "cuda"), kc2, vc2,
+                          torch.from_numpy(slots_p).cuda())
+    tab_p, lens_p = priv.tables([1], fill=0)
+    out2 = torch.empty((n - 32, hq, d), dtype=torch.float32, device="cuda")
+    ops.paged_attn_multi(out2, _to_torch(qb, kind, "cuda"), kc2, vc2,
+                         torch.from_numpy(tab_p).cuda(),
+                         torch.from_numpy(lens_p).cuda(),
+                         torch.tensor([0, n - 32], dtype=torch.int32,
+                                      device="cuda"), n - 32, n, scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.cpu().numpy().view(np.uint32),
+                          out_b.view(np.uint32))
+    say(f"prefix cache: {bm.prefix_stats()}")

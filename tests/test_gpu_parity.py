@@ -353,3 +353,39 @@ def test_long_context_fp8_full():
     w = W.long_context_fp8()
     rows = [(0, 0), (1, 5), (3, 13), (4, 31), (6, 16), (7, 2)]
     run_full(w, rows=rows)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8_e4m3", "f32"])
+def test_copies_in_every_layer(kind):
+    """copy_blocks_layers / copy_block_prefixes_layers on the pools of 5
+    layers held in one allocation: each layer's pools end up as the oracle's
+    copies of that layer's pools, bit for bit."""
+    import torch
+    from paged_kv_cache_336_amd import ops
+    from paged_kv_cache_336_amd.step import _to_torch, to_host_storage
+    say(f"copies in every layer: {kind}")
+    rng = np.random.default_rng(17)
+    nl, nb, bs, hkv, d = 5, 24, 16, 4, 128
+    dt = {"bf16": np.uint16, "fp8_e4m3": np.uint8, "f32": np.float32}[kind]
+    if kind == "f32":
+        kp = rng.standard_normal((nl, nb, bs, hkv, d), np.float32)
+        vp = rng.standard_normal((nl, nb, bs, hkv, d), np.float32)
+    else:
+        hi = 0x7F00 if kind == "bf16" else 0x7F
+        kp = rng.integers(0, hi, (nl, nb, bs, hkv, d)).astype(dt)
+        vp = rng.integers(0, hi, (nl, nb, bs, hkv, d)).astype(dt)
+    kc, vc = _to_torch(kp, kind, "cuda"), _to_torch(vp, kind, "cuda")
+    ck = kind if kind.startswith("fp8") else None
+    pairs = np.array([[3, 20], [7, 21], [11, 22]], np.int32)
+    ops.copy_blocks_layers(kc, vc, torch.from_numpy(pairs).cuda(),
+                           cache_kind=ck)
+    triples = np.array([[0, 23, 5], [1, 19, 16], [2, 18, 0]], np.int32)
+    ops.copy_block_prefixes_layers(kc, vc, torch.from_numpy(triples).cuda(),
+                                   cache_kind=ck)
+    torch.cuda.synchronize()
+    gk, gv = to_host_storage(kc, kind), to_host_storage(vc, kind)
+    for layer in range(nl):
+        ek, ev = oracle.copy_blocks(kp[layer], vp[layer], pairs)
+        ek, ev = oracle.copy_block_prefixes(ek, ev, triples)
+        assert gk[layer].tobytes() == ek.tobytes(), layer
+        assert gv[layer].tobytes() == ev.tobytes(), layer
