@@ -29,7 +29,8 @@ Sources (cited by page title and section):
 Storage conventions shared with the generator (plain numpy dtypes):
 ``"f32"`` float32, ``"f16"`` float16, ``"bf16"`` uint16 holding bfloat16
 bits, ``"fp8_e4m3"`` / ``"fp8_e5m2"`` uint8 holding OCP E4M3 / E5M2 codes;
-fp8 scales per tensor or one per kv head.
+fp8 scales per tensor, one per kv head, or one per (token slot, kv head)
+in a float32 array shaped like the pool without its head_dim axis.
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 something other than itself (library routines, closed forms, brute force
@@ -41,7 +42,8 @@ from .fp8_e5m2 import e5m2_decode, e5m2_encode, E5M2_MAX
 from .storage import to_float64
 from .attention import (paged_attention, paged_attention_rows,
                         gather_sequence, attention_one_head)
-from .cache_ops import cache_write, copy_block_prefixes, copy_blocks
+from .cache_ops import (cache_write, cache_write_token_scales,
+                        copy_block_prefixes, copy_blocks, copy_token_scales)
 from .multi_query import paged_attention_multi
 
 __all__ = [
@@ -57,6 +59,8 @@ __all__ = [
     "gather_sequence",
     "attention_one_head",
     "cache_write",
+    "cache_write_token_scales",
+    "copy_token_scales",
     "copy_blocks",
     "copy_block_prefixes",
     "paged_attention_multi",

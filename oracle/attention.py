@@ -22,7 +22,9 @@ notes):
   mask applies; a sequence of length 0 yields zeros;
 * fp8 caches (E4M3 or E5M2) hold codes of ``x / scale``; the stored value
   is ``decode(code) * scale`` (the scale is applied exactly in float64);
-  the scale is per tensor, or one per kv head;
+  the scale is per tensor, one per kv head, or one per (token slot, kv
+  head) -- a float32 array shaped like the pool without its head_dim axis,
+  ``[num_blocks, block_size, kv_heads]``, written beside each row;
 * the output is returned in float64 (the GPU path writes float32).
 """
 
@@ -53,6 +55,28 @@ def kv_scales(kv_kind, k_scale, v_scale, num_kv_heads):
     return one, one
 
 
+def is_token_scales(scale):
+    """True for per-token scales: a [num_blocks, block_size, kv_heads]
+    array (one float32 per slot and kv head)."""
+    return np.ndim(scale) == 3
+
+
+def stored_rows(pool, kind, table_row, seq_len, block_size, head, scale):
+    """The values one sequence's rows of cache head ``head`` stand for, in
+    float64 [L, D]: the gathered storage widened exactly, times the fp8
+    scale that applies to each row (per tensor, per kv head, or the row's
+    own per-token scale gathered through the same table walk)."""
+    rows = to_float64(gather_sequence(pool, table_row, seq_len, block_size,
+                                      head), kind)
+    if kind not in FP8_KINDS:
+        return rows
+    if is_token_scales(scale):
+        sc = np.asarray(scale, dtype=np.float32)[..., None]  # [nb, bs, Hkv, 1]
+        per_row = gather_sequence(sc, table_row, seq_len, block_size, head)
+        return rows * per_row.astype(np.float64)
+    return rows * head_scales(scale, pool.shape[2])[head]
+
+
 def attention_one_head(q, k, v, scale):
     """softmax(scale * q k^T) v for a block of query rows, in float64.
 
@@ -75,8 +99,8 @@ def paged_attention(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
     k_pool, v_pool: [num_blocks, block_size, Hkv, D] of kind ``kv_kind``.
     block_tables: int32 [S, max_blocks]; only the first ceil(L/bs) columns
     of a row are read.  seq_lens: int32 [S].
-    k_scale, v_scale: per-tensor scales or one per kv head, used only for
-    fp8 caches.
+    k_scale, v_scale: per-tensor scales, one per kv head, or per-token
+    scale arrays [num_blocks, block_size, Hkv], used only for fp8 caches.
     """
     S, Hq, D = query.shape
     Hkv = k_pool.shape[2]
@@ -84,17 +108,16 @@ def paged_attention(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
     assert k_pool.shape[1] == block_size
     G = Hq // Hkv
     q64 = to_float64(query, q_kind)
-    ks, vs = kv_scales(kv_kind, k_scale, v_scale, Hkv)
     out = np.zeros((S, Hq, D), dtype=np.float64)
     for s in range(S):
         L = int(seq_lens[s])
         if L == 0:
             continue
         for h in range(Hkv):
-            k = to_float64(gather_sequence(k_pool, block_tables[s], L,
-                                           block_size, h), kv_kind) * ks[h]
-            v = to_float64(gather_sequence(v_pool, block_tables[s], L,
-                                           block_size, h), kv_kind) * vs[h]
+            k = stored_rows(k_pool, kv_kind, block_tables[s], L, block_size,
+                            h, k_scale)
+            v = stored_rows(v_pool, kv_kind, block_tables[s], L, block_size,
+                            h, v_scale)
             out[s, h * G:(h + 1) * G] = attention_one_head(
                 q64[s, h * G:(h + 1) * G], k, v, scale)
     return out
@@ -109,17 +132,16 @@ def paged_attention_rows(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
     S, Hq, D = query.shape
     Hkv = k_pool.shape[2]
     G = Hq // Hkv
-    ks, vs = kv_scales(kv_kind, k_scale, v_scale, Hkv)
     out = np.zeros((len(rows), D), dtype=np.float64)
     for i, (s, hq) in enumerate(rows):
         L = int(seq_lens[s])
         if L == 0:
             continue
         h = hq // G
-        k = to_float64(gather_sequence(k_pool, block_tables[s], L,
-                                       block_size, h), kv_kind) * ks[h]
-        v = to_float64(gather_sequence(v_pool, block_tables[s], L,
-                                       block_size, h), kv_kind) * vs[h]
+        k = stored_rows(k_pool, kv_kind, block_tables[s], L, block_size, h,
+                        k_scale)
+        v = stored_rows(v_pool, kv_kind, block_tables[s], L, block_size, h,
+                        v_scale)
         q = to_float64(query[s, hq:hq + 1], q_kind)
         out[i] = attention_one_head(q, k, v, scale)[0]
     return out

@@ -16,6 +16,16 @@ IEEE float32 division and the round-to-nearest-even encoder of
 overflow).  The scale is per tensor, or one per kv head (the pages' 0-d
 scale tensors generalised; element ``[h, d]`` of a row uses scale ``h``).
 
+cache_write_token_scales -- the same write with a scale per token row
+(reading: the pages' scale is per tensor; here each written (token, kv
+head) row picks its own, so that one large row does not coarsen the others).
+The row's scale is its largest magnitude (NaN ignored; 0 when there is
+none) over the format's largest finite value (448 for E4M3, 57344 for
+E5M2), an IEEE float32 division, and 1 for a row without a nonzero
+element; it is stored at the row's slot and head of a float32
+``[num_blocks, block_size, kv_heads]`` array beside the pool, and the
+row's codes are those of ``float32(x) / scale`` as above.
+
 copy_blocks — "PagedAttention" (shubhamtatvamasi.com), "Sharing and
 copy-on-write" and the FAQ entry on copy-on-write for parallel sampling:
 before a sequence appends to a shared, partially filled block, the engine
@@ -27,11 +37,12 @@ carry no token counts).
 
 import numpy as np
 
-from .fp8_e4m3 import e4m3_encode
-from .fp8_e5m2 import e5m2_encode
+from .fp8_e4m3 import E4M3_MAX, e4m3_encode
+from .fp8_e5m2 import E5M2_MAX, e5m2_encode
 from .storage import head_scales, to_float64
 
 _ENCODERS = {"fp8_e4m3": e4m3_encode, "fp8_e5m2": e5m2_encode}
+_LARGEST = {"fp8_e4m3": E4M3_MAX, "fp8_e5m2": E5M2_MAX}
 
 
 def _encode_row(row, src_kind, cache_kind, scale):
@@ -59,6 +70,55 @@ def cache_write(k_pool, v_pool, cache_kind, key, value, src_kind,
         kp[b, o] = _encode_row(key[t], src_kind, cache_kind, k_scale)
         vp[b, o] = _encode_row(value[t], src_kind, cache_kind, v_scale)
     return kp, vp
+
+
+def token_row_scale(row32, cache_kind):
+    """float32 scale of one written row (float32 [D])."""
+    amax = np.float32(0.0)
+    for x in np.abs(row32):
+        amax = np.fmax(amax, x)            # NaN ignored, as fmax does
+    if amax == 0:
+        return np.float32(1.0)
+    return np.float32(amax) / np.float32(_LARGEST[cache_kind])  # IEEE fp32
+
+
+def cache_write_token_scales(k_pool, v_pool, k_scales, v_scales, cache_kind,
+                             key, value, src_kind, slot_mapping, block_size):
+    """Per-token-scaled fp8 write into copies of the pools and of their
+    scale arrays; returns (k_pool, v_pool, k_scales, v_scales)."""
+    assert cache_kind in _ENCODERS, cache_kind
+    kp, vp = k_pool.copy(), v_pool.copy()
+    ks = np.array(k_scales, dtype=np.float32, copy=True)
+    vs = np.array(v_scales, dtype=np.float32, copy=True)
+    enc = _ENCODERS[cache_kind]
+    for t in range(len(slot_mapping)):
+        slot = int(slot_mapping[t])
+        if slot < 0:
+            continue
+        b, o = divmod(slot, int(block_size))
+        for pool, scales, rows in ((kp, ks, key), (vp, vs, value)):
+            x32 = to_float64(rows[t], src_kind).astype(np.float32)  # [Hkv, D]
+            for h in range(x32.shape[0]):
+                sc = token_row_scale(x32[h], cache_kind)
+                scales[b, o, h] = sc
+                pool[b, o, h] = enc((x32[h] / sc).astype(np.float64))
+    return kp, vp, ks, vs
+
+
+def copy_token_scales(k_scales, v_scales, records, prefix=False):
+    """The per-token scale arrays follow their rows through a copy: with
+    pairs (src, dst) whole blocks, with triples (src, dst, tokens) the
+    first ``tokens`` slots (clamped to [0, block_size])."""
+    ks = np.array(k_scales, copy=True)
+    vs = np.array(v_scales, copy=True)
+    bs = ks.shape[1]
+    w = 3 if prefix else 2
+    for rec in np.asarray(records, dtype=np.int64).reshape(-1, w):
+        src, dst = int(rec[0]), int(rec[1])
+        n = min(max(int(rec[2]), 0), bs) if prefix else bs
+        ks[dst, :n] = ks[src, :n]
+        vs[dst, :n] = vs[src, :n]
+    return ks, vs
 
 
 def copy_block_prefixes(k_pool, v_pool, triples):

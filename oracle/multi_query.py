@@ -20,7 +20,7 @@ query_start[s+1]-1 of ``query`` belong to sequence s.  Everything else
 
 import numpy as np
 
-from .attention import attention_one_head, gather_sequence, kv_scales
+from .attention import attention_one_head, stored_rows
 from .storage import to_float64
 
 
@@ -32,7 +32,6 @@ def paged_attention_multi(query, q_kind, k_pool, v_pool, kv_kind,
     Hkv = k_pool.shape[2]
     G = Hq // Hkv
     q64 = to_float64(query, q_kind)
-    ks, vs = kv_scales(kv_kind, k_scale, v_scale, Hkv)
     out = np.zeros((T, Hq, D), dtype=np.float64)
     for s in range(len(seq_lens)):
         L = int(seq_lens[s])
@@ -42,10 +41,10 @@ def paged_attention_multi(query, q_kind, k_pool, v_pool, kv_kind,
         if nq == 0:
             continue
         for h in range(Hkv):
-            k = to_float64(gather_sequence(k_pool, block_tables[s], L,
-                                           block_size, h), kv_kind) * ks[h]
-            v = to_float64(gather_sequence(v_pool, block_tables[s], L,
-                                           block_size, h), kv_kind) * vs[h]
+            k = stored_rows(k_pool, kv_kind, block_tables[s], L,
+                            block_size, h, k_scale)
+            v = stored_rows(v_pool, kv_kind, block_tables[s], L,
+                            block_size, h, v_scale)
             for j in range(nq):
                 p = L - nq + j
                 out[q0 + j, h * G:(h + 1) * G] = attention_one_head(

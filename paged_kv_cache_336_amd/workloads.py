@@ -66,9 +66,13 @@ def _fp8_codes_from_f32(x, scale, kind="fp8_e4m3"):
     import torch
     lim = _FP8_LIMIT[kind]
     y = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    s = torch.from_numpy(np.asarray(scale, dtype=np.float32).reshape(-1))
-    if s.numel() > 1:
-        s = s.reshape(s.numel(), 1)        # broadcast over [.., Hkv, D]
+    s = np.asarray(scale, dtype=np.float32)
+    if s.ndim == 3:                        # per token: [nb, bs, Hkv]
+        s = torch.from_numpy(np.ascontiguousarray(s)[..., None])
+    else:
+        s = torch.from_numpy(s.reshape(-1))
+        if s.numel() > 1:
+            s = s.reshape(s.numel(), 1)    # broadcast over [.., Hkv, D]
     y = (y / s).clamp_(-lim, lim)
     dt = torch.float8_e4m3fn if kind == "fp8_e4m3" else torch.float8_e5m2
     return y.to(dt).view(torch.uint8).numpy()
@@ -111,7 +115,8 @@ class Workload:
     value: np.ndarray
     slot_mapping: np.ndarray  # int32 [T]
     copy_pairs: np.ndarray   # int32 [P, 2] (src, dst)
-    k_scale: float = 1.0     # float32 value(s); fp8 caches: one or per kv head
+    k_scale: float = 1.0     # float32 value(s); fp8 caches: one, per kv head,
+                             # or per (slot, kv head) [nb, bs, Hkv]
     v_scale: float = 1.0
     # Extra disjoint copies of (tables, slots, pairs) over the same pool,
     # for rotating benchmark steps through more memory than the caches hold.
@@ -190,16 +195,30 @@ def _draw_chunks(seed_key, num_blocks, block_size, hkv, d, chunk_blocks):
 
 
 def _fill_pool(seed_key, num_blocks, block_size, hkv, d, kind, live,
-               chunk_blocks=512, per_head=False):
+               chunk_blocks=512, per_head=False, per_token=False):
     """N(0,1) values at live slots, poison elsewhere, in storage kind.
 
     For an fp8 cache the scale is max|live value| / (largest finite code
     value: 448 for E4M3, 57344 for E5M2) as a float32, per tensor or, with
-    per_head, per kv head (float32 [Hkv]); returns (pool, scale), scale 1.0
-    for other kinds."""
+    per_head, per kv head (float32 [Hkv]); with per_token, each live (slot,
+    kv head) row gets its own, that row's max|value| / largest code times a
+    factor drawn from [1, 1.5) (so not every row reaches the largest code),
+    as float32 [num_blocks, block_size, Hkv] with NaN at slots that hold no
+    token; returns (pool, scale), scale 1.0 for other kinds."""
     x = _draw_chunks(seed_key, num_blocks, block_size, hkv, d, chunk_blocks)
     poison = poison_value(kind)
     scale = 1.0
+    if kind in FP8_KINDS and per_token:
+        lim = np.float32(_FP8_LIMIT[kind])
+        amax = np.abs(x).max(axis=3)               # [nb, bs, Hkv]
+        widen = np.random.default_rng(list(seed_key) + [9]).uniform(
+            1.0, 1.5, size=amax.shape).astype(np.float32)
+        scale = np.where(amax > 0, amax / lim * widen,
+                         np.float32(1)).astype(np.float32)
+        scale[~live] = np.nan
+        pool = _fp8_codes_from_f32(x, scale, kind)
+        pool[~live] = poison
+        return pool, scale
     if kind in FP8_KINDS:
         lim = _FP8_LIMIT[kind]
         sel = np.abs(x[live])                      # [n_live, Hkv, D]
@@ -229,7 +248,8 @@ def _unused_column_fill(block_tables, counts, filler):
 
 def _build(name, rng, *, q_kind, kv_kind, src_kind, hq, hkv, d, bs, nb,
            block_tables, seq_lens, cached_lens, slot_mapping, copy_pairs,
-           replicas=(), note="", live_extra=None, per_head_scales=False):
+           replicas=(), note="", live_extra=None, per_head_scales=False,
+           per_token_scales=False):
     """Draw pool values and rows for an already-laid-out step."""
     live = live_slot_mask(nb, bs, block_tables, cached_lens)
     for rep in replicas:
@@ -240,9 +260,11 @@ def _build(name, rng, *, q_kind, kv_kind, src_kind, hq, hkv, d, bs, nb,
     T = len(slot_mapping)
     key_base = [int(v) for v in rng.integers(0, 2**31, size=2)]
     k_pool, k_scale = _fill_pool([SEED_BASE, key_base[0], 0], nb, bs, hkv, d,
-                                 kv_kind, live, per_head=per_head_scales)
+                                 kv_kind, live, per_head=per_head_scales,
+                                 per_token=per_token_scales)
     v_pool, v_scale = _fill_pool([SEED_BASE, key_base[1], 1], nb, bs, hkv, d,
-                                 kv_kind, live, per_head=per_head_scales)
+                                 kv_kind, live, per_head=per_head_scales,
+                                 per_token=per_token_scales)
     query = _cast_from_f32(_normal(rng, (S, hq, d)), q_kind)
     key = _cast_from_f32(_normal(rng, (T, hkv, d)), src_kind)
     value = _cast_from_f32(_normal(rng, (T, hkv, d)), src_kind)
@@ -487,10 +509,11 @@ def long_context_fp8(num_seqs=8, seq_len=131072, block_size=64,
 
 def custom_decode(*, seed, num_seqs, lens, hq, hkv, d, bs, q_kind, kv_kind,
                   src_kind=None, spare_blocks=3, num_new_per_seq=1,
-                  per_head_scales=False):
+                  per_head_scales=False, per_token_scales=False):
     """Small free-form decode step (fuzz/edge cases): lengths given, blocks
     from a random permutation with a few spare poisoned blocks; an fp8
-    cache's scales per tensor or, with per_head_scales, per kv head."""
+    cache's scales per tensor, per kv head (per_head_scales) or per (slot,
+    kv head) (per_token_scales)."""
     rng = np.random.default_rng([SEED_BASE, 100, seed])
     src_kind = src_kind or (q_kind if kv_kind in FP8_KINDS else kv_kind)
     lens = np.asarray(lens, dtype=np.int64)
@@ -515,7 +538,8 @@ def custom_decode(*, seed, num_seqs, lens, hq, hkv, d, bs, q_kind, kv_kind,
                   src_kind=src_kind, hq=hq, hkv=hkv, d=d, bs=bs, nb=nb,
                   block_tables=tables, seq_lens=lens, cached_lens=cached,
                   slot_mapping=slots, copy_pairs=np.zeros((0, 2)),
-                  per_head_scales=per_head_scales)
+                  per_head_scales=per_head_scales,
+                  per_token_scales=per_token_scales)
 
 
 # ----------------------------------------------------------------------------
@@ -541,7 +565,8 @@ class MultiQuery:
 
 
 def _multi(name, rng, *, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
-           src_kind, nb, perm, replicas=1, per_head_scales=False):
+           src_kind, nb, perm, replicas=1, per_head_scales=False,
+           per_token_scales=False):
     lens = np.asarray(lens, dtype=np.int64)
     qlens = np.asarray(qlens, dtype=np.int64)
     assert (qlens <= lens).all() and (qlens >= 0).all()
@@ -566,7 +591,8 @@ def _multi(name, rng, *, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
                block_tables=sets[0]["block_tables"], seq_lens=lens,
                cached_lens=cached, slot_mapping=sets[0]["slot_mapping"],
                copy_pairs=np.zeros((0, 2)), replicas=sets[1:],
-               per_head_scales=per_head_scales)
+               per_head_scales=per_head_scales,
+               per_token_scales=per_token_scales)
     T = int(qlens.sum())
     query = _cast_from_f32(_normal(rng, (T, hq, d)), q_kind)
     query_start = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
@@ -574,7 +600,8 @@ def _multi(name, rng, *, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
 
 
 def custom_multi(*, seed, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
-                 src_kind=None, spare_blocks=3, per_head_scales=False):
+                 src_kind=None, spare_blocks=3, per_head_scales=False,
+                 per_token_scales=False):
     """Small free-form multi-query step: lengths (after the step) and new
     tokens per sequence given; blocks from a random permutation."""
     rng = np.random.default_rng([SEED_BASE, 200, seed])
@@ -585,7 +612,8 @@ def custom_multi(*, seed, lens, qlens, hq, hkv, d, bs, q_kind, kv_kind,
     return _multi(f"custom_multi_{seed}", rng, lens=lens, qlens=qlens, hq=hq,
                   hkv=hkv, d=d, bs=bs, q_kind=q_kind, kv_kind=kv_kind,
                   src_kind=src_kind, nb=nb, perm=perm,
-                  per_head_scales=per_head_scales)
+                  per_head_scales=per_head_scales,
+                  per_token_scales=per_token_scales)
 
 
 def spec_verify_llama8b(num_seqs=32, draft=4, median=512, cap=4096,
