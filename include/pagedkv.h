@@ -71,7 +71,14 @@ extern "C" {
  * An fp8 cache's values are stored over scales: a cache dtype argument of
  * PKV_FP8_E4M3 or PKV_FP8_E5M2 takes k_scale / v_scale as one float32 each;
  * OR-ing in PKV_SCALE_PER_HEAD takes them as float32 [num_kv_heads], one per
- * kv head (the flag is accepted, and ignored, by the copy calls). */
+ * kv head; OR-ing in PKV_SCALE_PER_TOKEN takes them as float32 [num_blocks,
+ * block_size, num_kv_heads] arrays laid out like the pools without the
+ * head_dim axis: one scale per (token slot, kv head), written beside each
+ * row by cache_write_slots_token_scaled and carried through copies by
+ * copy_token_scales.  (The copy calls accept, and ignore, both flags.)
+ * The pages' scale is one per tensor ("How PagedAttention Works in vLLM
+ * ...", instagit.com, section "write_to_paged_cache": k_scale / v_scale
+ * with the cache dtype); the per-head and per-token layouts generalise it. */
 typedef enum pkv_dtype {
   PKV_F32 = 0,
   PKV_F16 = 1,
@@ -81,6 +88,7 @@ typedef enum pkv_dtype {
 } pkv_dtype;
 
 #define PKV_SCALE_PER_HEAD 0x100
+#define PKV_SCALE_PER_TOKEN 0x200
 
 typedef enum pkv_status {
   PKV_OK = 0,
@@ -117,7 +125,9 @@ const char* pkv_status_string(int status);
  * to nearest even; for E4M3 finite values beyond 448 saturate to +-448, for
  * E5M2 magnitudes from 61440 on become infinity (IEEE overflow); NaN stays
  * NaN.  No other pairing is accepted (PKV_ERR_DTYPE).  num_tokens == 0 is a valid
- * no-op.  head_dim must be 64 or 128; pointers 16-byte aligned.
+ * no-op.  head_dim must be 64 or 128; pointers 16-byte aligned.  Per-token
+ * scales (PKV_SCALE_PER_TOKEN) are written by cache_write_slots_token_scaled
+ * only (PKV_ERR_DTYPE here).
  */
 int cache_write_slots(const void* key, const void* value, int src_dtype,
                       void* k_cache, void* v_cache, int cache_dtype,
@@ -126,6 +136,53 @@ int cache_write_slots(const void* key, const void* value, int src_dtype,
                       int32_t num_kv_heads, int32_t head_dim,
                       const float* k_scale, const float* v_scale,
                       hipStream_t stream);
+
+/*
+ * cache_write_slots_token_scaled -- cache_write_slots into an fp8 cache with
+ * a scale per written row: each (token, kv head) row of key and value gets
+ * its own scale, the largest magnitude of the row (NaN elements left out)
+ * over the format's largest finite value (448 for E4M3, 57344 for E5M2) as
+ * an IEEE float32 division, or 1 for a row with no nonzero element; the row
+ * is encoded over that scale as by cache_write_slots (its largest element
+ * lands on the largest finite code), and the scale is stored at
+ * [slot / block_size, slot % block_size, head] of k_scales / v_scales.
+ * (The pages scale per tensor, "How PagedAttention Works in vLLM ...",
+ * instagit.com, section "write_to_paged_cache"; a scale per row keeps one
+ * large row from coarsening the codes of all others.)
+ *
+ * cache_dtype   PKV_FP8_E4M3 or PKV_FP8_E5M2, with or without
+ *               PKV_SCALE_PER_TOKEN (anything else: PKV_ERR_DTYPE).
+ * k_scales,
+ * v_scales      device float32 [num_blocks, block_size, num_kv_heads],
+ *               4-byte aligned; only the written slots' entries change.
+ * Other arguments and rules as cache_write_slots.
+ */
+int cache_write_slots_token_scaled(const void* key, const void* value,
+                                   int src_dtype, void* k_cache,
+                                   void* v_cache, int cache_dtype,
+                                   float* k_scales, float* v_scales,
+                                   const int32_t* slot_mapping,
+                                   int64_t num_tokens, int64_t num_blocks,
+                                   int32_t block_size, int32_t num_kv_heads,
+                                   int32_t head_dim, hipStream_t stream);
+
+/*
+ * copy_token_scales, copy_token_scale_prefixes -- the per-token scale
+ * arrays (float32 [num_blocks, block_size, num_kv_heads], 4-byte aligned)
+ * through the copies copy_blocks / copy_block_prefixes make of the pools:
+ * the same pairs {src, dst} (whole blocks) or triples {src, dst, tokens}
+ * (slots 0 .. tokens-1, tokens clamped to [0, block_size]), with the same
+ * rules.  A copy-on-write of a per-token-scaled fp8 cache calls both.
+ */
+int copy_token_scales(float* k_scales, float* v_scales,
+                      const int32_t* block_pairs, int64_t num_pairs,
+                      int64_t num_blocks, int32_t block_size,
+                      int32_t num_kv_heads, hipStream_t stream);
+int copy_token_scale_prefixes(float* k_scales, float* v_scales,
+                              const int32_t* block_triples,
+                              int64_t num_copies, int64_t num_blocks,
+                              int32_t block_size, int32_t num_kv_heads,
+                              hipStream_t stream);
 
 /*
  * copy_blocks -- for each pair (src, dst), every slot of block dst in both
@@ -211,9 +268,15 @@ size_t paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * out          float32 [num_seqs, num_q_heads, head_dim].
  * k_cache,
  * v_cache      pools of cache_dtype; (q_dtype, cache_dtype) is one of
- *              (F32,F32) (F16,F16) (BF16,BF16) or (F32|F16|BF16, FP8_E4M3).
+ *              (F32,F32) (F16,F16) (BF16,BF16) or (F32|F16|BF16, FP8_E4M3|
+ *              FP8_E5M2).
  * k_scale,
- * v_scale      device float32 scalars, required for an fp8 cache.
+ * v_scale      device float32 scales, required for an fp8 cache: one each,
+ *              [num_kv_heads] with PKV_SCALE_PER_HEAD, or the per-token
+ *              arrays [num_blocks, block_size, num_kv_heads] with
+ *              PKV_SCALE_PER_TOKEN (token t of a sequence is then read as
+ *              decode(code) * its own scale, in its score and in its share
+ *              of the value sum).
  * max_seq_len  host-side upper bound of seq_lens (a sequence longer than it
  *              is the caller's error: it is cut to max_seq_len).
  * scale        softmax scale applied to q . k.
@@ -267,7 +330,9 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
  *               pools; slots outside the pool are skipped).
  * Other arguments as paged_attn_decode (same workspace).  At most 16 query
  * heads per kv head (PKV_ERR_UNSUPPORTED beyond): each kv head's last tile is
- * then read by exactly the wave that writes it.  When the batch has more
+ * then read by exactly the wave that writes it.  Per-token scales are not
+ * written here (PKV_ERR_UNSUPPORTED): use cache_write_slots_token_scaled and
+ * paged_attn_decode.  When the batch has more
  * (sequence, kv head) rows than the GPU holds waves, the write goes as its
  * own launch ahead of the attention (faster there; the same result).
  */

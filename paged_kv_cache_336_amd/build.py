@@ -26,14 +26,7 @@ def hipcc():
     return "hipcc"
 
 
-def build_library(verbose=False, extra_flags=()):
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-           "-shared", "-Wall", "-Wno-unused-result",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(HERE, "..", "include"),
-           *extra_flags,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,6 +35,27 @@ def build_library(verbose=False, extra_flags=()):
         raise RuntimeError("hipcc failed building libpagedkv.so")
     if verbose and res.stderr.strip():
         sys.stderr.write(res.stderr)
+
+
+def build_library(verbose=False, extra_flags=()):
+    """Compile every source to an object (in parallel), then link."""
+    from concurrent.futures import ThreadPoolExecutor
+    tmp = LIB + ".tmp"
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-Wall", "-Wno-unused-result",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", os.path.join(HERE, "..", "include"), *extra_flags]
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o")
+            for s in SOURCES]
+    jobs = [[hipcc(), *flags, "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs))
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+          "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

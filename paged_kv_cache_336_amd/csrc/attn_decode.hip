@@ -213,12 +213,17 @@ __device__ __forceinline__ void wait_stores() {
 // segment starts and its first tile during the current segment's last tile,
 // so a wave's loads run on across segment boundaries.
 // ---------------------------------------------------------------------------
-template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE>
+// PT: per-token fp8 scales (a.k_scale / a.v_scale are [num_blocks,
+// block_size, num_kv_heads] arrays read beside the rows).
+template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE,
+          bool PT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_decode_kernel(AttnArgs a) {
   typedef Shape<QT, CT, D> S;
   constexpr int NBLK = S::NBLK;
   constexpr bool PREFETCH = UNIFORM && CT::bytes <= 2;
+  static_assert(!PT || (is_fp8<CT>::value && !WRITE),
+                "per-token scales: fp8 caches, separate write");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * S::STAGE_BYTES];
   __shared__ int sm_wsum[kWaves];
@@ -312,27 +317,35 @@ void attn_decode_kernel(AttnArgs a) {
   }
   uint32_t qw[S::QWORDS];
   load_query<QT, CT, D>(qw, X, a, lane);
+  // per-token scales of a row's kv head
+  auto token_scales = [&](const Seg& g) {
+    return TokenScales{a.k_scale + g.h, a.v_scale + g.h, a.num_kv_heads};
+  };
   TileRegs<QT, CT, D> cur;
   if constexpr (PREFETCH)
-    load_tile_uniform<QT, CT, D>(cur, a.block_size, a.num_blocks, ta, tbw, X.wb,
-                                 kpool + (int64_t)X.h * S::ROW_BYTES,
-                                 vpool + (int64_t)X.h * S::ROW_BYTES, stride,
-                                 X.t_begin, X.t_end, lane);
+    load_tile_uniform<QT, CT, D, PT>(cur, a.block_size, a.num_blocks, ta, tbw,
+                                     X.wb, kpool + (int64_t)X.h * S::ROW_BYTES,
+                                     vpool + (int64_t)X.h * S::ROW_BYTES,
+                                     stride, X.t_begin, X.t_end, lane,
+                                     token_scales(X));
 
   while (X.valid) {
     uint32_t qn[S::QWORDS];
     load_query<QT, CT, D>(qn, Xn, a, lane);
     // an fp8 cache's scales for this row's kv head: the key scale folds into
-    // the score multiplier, the value scale into the output
+    // the score multiplier, the value scale into the output (per-token
+    // scales go into each token's score and PV weight instead)
     float kscale = 1.f, vscale = 1.f;
-    if constexpr (is_fp8<CT>::value) {
+    if constexpr (is_fp8<CT>::value && !PT) {
       kscale = head_scale(a.k_scale, a, X.h);
       vscale = head_scale(a.v_scale, a, X.h);
     }
     const float qk_mul = a.qk_scale_log2 * kscale;
+    const TokenScales tsc = token_scales(X);
 
     WaveState<NBLK> st;
     st.m = -INFINITY;
+    st.mv = -INFINITY;
     st.l = 0.f;
 #pragma unroll
     for (int n = 0; n < NBLK; ++n) st.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -363,21 +376,22 @@ void attn_decode_kernel(AttnArgs a) {
           tbw = load_window(shifted, 1, a, lane);
         }
         TileRegs<QT, CT, D> nxt;
-        load_tile_uniform<QT, CT, D>(
+        load_tile_uniform<QT, CT, D, PT>(
             nxt, a.block_size, a.num_blocks, same_seg ? ta : ta_n, same_seg ? tbw : tb_n,
             same_seg ? wb : Xn.wb, same_seg ? kbase : kbase_n,
             same_seg ? vbase : vbase_n, stride,
             same_seg ? t_next : Xn.t_begin, same_seg ? X.t_end : Xn.t_end,
-            lane);
+            lane, same_seg ? tsc : token_scales(Xn));
         __builtin_amdgcn_sched_barrier(0);
-        compute_tile<QT, CT, D>(cur.kw[0], qw, st, vt, t0, X.t_end, qk_mul,
-                                lane);
+        compute_tile<QT, CT, D, false, PT>(cur.kw[0], qw, st, vt, t0, X.t_end,
+                                           qk_mul, lane, 0, cur.sc[0]);
 #pragma unroll
         for (int sb = 1; sb < S::SUB; ++sb) {
           if (t0 + 32 * sb < X.t_end) {  // (only the last tile has empty ones)
             stage_v<QT, CT, D>(cur.vraw[sb], vt, lane);
-            compute_tile<QT, CT, D>(cur.kw[sb], qw, st, vt, t0 + 32 * sb,
-                                    X.t_end, qk_mul, lane);
+            compute_tile<QT, CT, D, false, PT>(cur.kw[sb], qw, st, vt,
+                                               t0 + 32 * sb, X.t_end, qk_mul,
+                                               lane, 0, cur.sc[sb]);
           }
         }
         cur = nxt;
@@ -392,24 +406,26 @@ void attn_decode_kernel(AttnArgs a) {
           shifted.wb = wb;
           const uint32_t wa = load_window(shifted, 0, a, lane);
           const uint32_t wbb = load_window(shifted, 1, a, lane);
-          load_tile_uniform<QT, CT, D>(cur, a.block_size, a.num_blocks, wa,
-                                       wbb, wb, kbase,
-                                       vbase, stride, t0, X.t_end, lane);
+          load_tile_uniform<QT, CT, D, PT>(cur, a.block_size, a.num_blocks,
+                                           wa, wbb, wb, kbase, vbase, stride,
+                                           t0, X.t_end, lane, tsc);
         } else {
-          load_tile_any<QT, CT, D>(cur, a.block_size, a.num_blocks, trow,
-                                   kbase, vbase,
-                                   stride, t0, X.t_end, lane);
+          load_tile_any<QT, CT, D, PT>(cur, a.block_size, a.num_blocks, trow,
+                                       kbase, vbase, stride, t0, X.t_end,
+                                       lane, tsc);
         }
 #pragma unroll
         for (int sb = 0; sb < S::SUB; ++sb) {
           if (t0 + 32 * sb < X.t_end) {
             stage_v<QT, CT, D>(cur.vraw[sb], vt, lane);
-            compute_tile<QT, CT, D>(cur.kw[sb], qw, st, vt, t0 + 32 * sb,
-                                    X.t_end, qk_mul, lane);
+            compute_tile<QT, CT, D, false, PT>(cur.kw[sb], qw, st, vt,
+                                               t0 + 32 * sb, X.t_end, qk_mul,
+                                               lane, 0, cur.sc[sb]);
           }
         }
       }
     }
+    if constexpr (PT) fold_value_scales(st);
 
     // ---------------- the segment's output (this wave alone) ----------------
     // lane (c + 16 j) holds O^T rows 16 n + 4 j .. + 3 of query head c
@@ -471,9 +487,11 @@ template <> struct DtypeCode<BF16> { static constexpr int value = PKV_BF16; };
 template <> struct DtypeCode<FP8> { static constexpr int value = PKV_FP8_E4M3; };
 template <> struct DtypeCode<FP8E5> { static constexpr int value = PKV_FP8_E5M2; };
 
-template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE>
+template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE,
+          bool PT = false>
 static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
-  auto kernel = attn_decode_kernel<QT, CT, D, UNIFORM, WRITE>;
+  auto kernel = attn_decode_kernel<QT, CT, D, UNIFORM, WRITE, PT>;
+  constexpr bool SCALED = is_fp8<CT>::value && !PT;  // merge: output scale
   const size_t dyn = ((size_t)2 * a.num_seqs + 1) * sizeof(int);
   const int grid = resident_grid(kernel, dyn, max_waves);
   if (grid < 0) return hipErrorInvalidValue;
@@ -510,10 +528,10 @@ static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
   // launch in one round).
   const int rows = a.num_seqs * a.num_kv_heads * a.group_chunks;
   if (rows > 0 && a.num_waves >= 4 * rows)
-    hipLaunchKernelGGL((attn_merge_kernel<D, is_fp8<CT>::value, 16>),
+    hipLaunchKernelGGL((attn_merge_kernel<D, SCALED, 16>),
                        dim3(rows), dim3(kMergeThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_merge_kernel<D, is_fp8<CT>::value, 4>),
+    hipLaunchKernelGGL((attn_merge_kernel<D, SCALED, 4>),
                        dim3(rows), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -521,6 +539,14 @@ static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
 template <typename QT, typename CT, int D>
 static hipError_t launch_d(const AttnArgs& a, int max_waves, bool uniform,
                            bool fused, hipStream_t stream) {
+  if constexpr (is_fp8<CT>::value) {
+    if (a.scale_per_token) {  // (never fused: the host rejects it)
+      if (fused) return hipErrorInvalidValue;
+      if (uniform)
+        return launch_u<QT, CT, D, true, false, true>(a, max_waves, stream);
+      return launch_u<QT, CT, D, false, false, true>(a, max_waves, stream);
+    }
+  }
   if (fused) {
     if (uniform) return launch_u<QT, CT, D, true, true>(a, max_waves, stream);
     return launch_u<QT, CT, D, false, true>(a, max_waves, stream);

@@ -159,11 +159,15 @@ __device__ __forceinline__ int mq_limit(const MSeg& g, const AttnArgs& a,
 template <int NG> struct MultiOccupancy { static constexpr int waves = 2; };
 template <> struct MultiOccupancy<4> { static constexpr int waves = 1; };
 
-template <typename QT, typename CT, int D, bool UNIFORM, int NG>
+// PT: per-token fp8 scales (a.k_scale / a.v_scale are [num_blocks,
+// block_size, num_kv_heads] arrays read beside the rows).
+template <typename QT, typename CT, int D, bool UNIFORM, int NG,
+          bool PT = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(MultiOccupancy<NG>::waves)))
 void attn_multi_kernel(AttnArgs a) {
   typedef Shape<QT, CT, D> S;
+  static_assert(!PT || is_fp8<CT>::value, "per-token scales: fp8 caches");
   static_assert(S::SUB == 1, "one 32-token sub-tile per tile");
   constexpr int NBLK = S::NBLK;
   // (four groups leave no registers for a second tile in flight)
@@ -242,20 +246,25 @@ void attn_multi_kernel(AttnArgs a) {
   uint32_t qw[NG][S::QWORDS];
 #pragma unroll
   for (int g = 0; g < NG; ++g) load_query_mq<QT, CT, D>(qw[g], X, a, g, lane);
+  auto token_scales = [&](const MSeg& g) {
+    return TokenScales{a.k_scale + g.h, a.v_scale + g.h, a.num_kv_heads};
+  };
   TileRegs<QT, CT, D> cur;
   if constexpr (PREFETCH)
-    load_tile_uniform<QT, CT, D>(cur, a.block_size, a.num_blocks, ta, tbw,
-                                 X.wb, kpool + (int64_t)X.h * S::ROW_BYTES,
-                                 vpool + (int64_t)X.h * S::ROW_BYTES, stride,
-                                 X.t_begin, X.t_end, lane);
+    load_tile_uniform<QT, CT, D, PT>(cur, a.block_size, a.num_blocks, ta, tbw,
+                                     X.wb, kpool + (int64_t)X.h * S::ROW_BYTES,
+                                     vpool + (int64_t)X.h * S::ROW_BYTES,
+                                     stride, X.t_begin, X.t_end, lane,
+                                     token_scales(X));
 
   while (X.valid) {
     float kscale = 1.f, vscale = 1.f;  // an fp8 cache's, for this kv head
-    if constexpr (is_fp8<CT>::value) {
+    if constexpr (is_fp8<CT>::value && !PT) {
       kscale = head_scale(a.k_scale, a, X.h);
       vscale = head_scale(a.v_scale, a, X.h);
     }
     const float qk_mul = a.qk_scale_log2 * kscale;
+    const TokenScales tsc = token_scales(X);
     uint32_t qn_w[QPREFETCH ? NG : 1][S::QWORDS];
     int lim[NG];
     WaveState<NBLK> st[NG];
@@ -265,6 +274,7 @@ void attn_multi_kernel(AttnArgs a) {
         load_query_mq<QT, CT, D>(qn_w[g], Xn, a, g, lane);
       lim[g] = mq_limit(X, a, g, lane);
       st[g].m = -INFINITY;
+      st[g].mv = -INFINITY;
       st[g].l = 0.f;
 #pragma unroll
       for (int n = 0; n < NBLK; ++n) st[g].o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -290,16 +300,16 @@ void attn_multi_kernel(AttnArgs a) {
           tbw = load_window(shifted, 1, a, lane);
         }
         TileRegs<QT, CT, D> nxt;
-        load_tile_uniform<QT, CT, D>(
+        load_tile_uniform<QT, CT, D, PT>(
             nxt, a.block_size, a.num_blocks, same_seg ? ta : ta_n,
             same_seg ? tbw : tb_n, same_seg ? wb : Xn.wb,
             same_seg ? kbase : kbase_n, same_seg ? vbase : vbase_n, stride,
             same_seg ? t_next : Xn.t_begin, same_seg ? X.t_end : Xn.t_end,
-            lane);
+            lane, same_seg ? tsc : token_scales(Xn));
         __builtin_amdgcn_sched_barrier(0);
         if (live)
-          compute_tile_groups<QT, CT, D, NG>(cur.kw[0], qw, st, vt, t0, lim,
-                                             qk_mul, lane);
+          compute_tile_groups<QT, CT, D, NG, PT>(cur.kw[0], qw, st, vt, t0,
+                                                 lim, qk_mul, lane, cur.sc[0]);
         cur = nxt;
       }
     } else {
@@ -313,17 +323,22 @@ void attn_multi_kernel(AttnArgs a) {
           shifted.wb = wb;
           const uint32_t wa = load_window(shifted, 0, a, lane);
           const uint32_t wbb = load_window(shifted, 1, a, lane);
-          load_tile_uniform<QT, CT, D>(cur, a.block_size, a.num_blocks, wa,
-                                       wbb, wb, kbase, vbase, stride, t0,
-                                       X.t_end, lane);
+          load_tile_uniform<QT, CT, D, PT>(cur, a.block_size, a.num_blocks,
+                                           wa, wbb, wb, kbase, vbase, stride,
+                                           t0, X.t_end, lane, tsc);
         } else {
-          load_tile_any<QT, CT, D>(cur, a.block_size, a.num_blocks, trow,
-                                   kbase, vbase, stride, t0, X.t_end, lane);
+          load_tile_any<QT, CT, D, PT>(cur, a.block_size, a.num_blocks, trow,
+                                       kbase, vbase, stride, t0, X.t_end,
+                                       lane, tsc);
         }
         stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
-        compute_tile_groups<QT, CT, D, NG>(cur.kw[0], qw, st, vt, t0, lim,
-                                           qk_mul, lane);
+        compute_tile_groups<QT, CT, D, NG, PT>(cur.kw[0], qw, st, vt, t0, lim,
+                                               qk_mul, lane, cur.sc[0]);
       }
+    }
+    if constexpr (PT) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) fold_value_scales(st[g]);
     }
 
     // ---------------- the segment's output (this wave alone) ----------------
@@ -416,9 +431,11 @@ __global__ __launch_bounds__(kMergeThreads) void attn_multi_merge_kernel(
       SCALED ? head_scale(a.v_scale, a, h) : 1.f, red_o, red_m, red_l);
 }
 
-template <typename QT, typename CT, int D, bool UNIFORM, int NG>
+template <typename QT, typename CT, int D, bool UNIFORM, int NG,
+          bool PT = false>
 static hipError_t launch_mu(AttnArgs a, int max_waves, hipStream_t stream) {
-  auto kernel = attn_multi_kernel<QT, CT, D, UNIFORM, NG>;
+  auto kernel = attn_multi_kernel<QT, CT, D, UNIFORM, NG, PT>;
+  constexpr bool SCALED = is_fp8<CT>::value && !PT;  // merge: output scale
   const size_t dyn = ((size_t)4 * a.num_seqs + 1) * sizeof(int);
   const int cap = max_waves > 0 && max_waves < kMaxWavesMulti ? max_waves
                                                               : kMaxWavesMulti;
@@ -428,10 +445,10 @@ static hipError_t launch_mu(AttnArgs a, int max_waves, hipStream_t stream) {
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
   const int64_t rows = (int64_t)a.num_seqs * a.num_kv_heads * a.max_rps;
   if (rows > 0 && a.num_waves >= 4 * rows)
-    hipLaunchKernelGGL((attn_multi_merge_kernel<D, is_fp8<CT>::value, 16>),
+    hipLaunchKernelGGL((attn_multi_merge_kernel<D, SCALED, 16>),
                        dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
   else if (rows > 0)
-    hipLaunchKernelGGL((attn_multi_merge_kernel<D, is_fp8<CT>::value, 4>),
+    hipLaunchKernelGGL((attn_multi_merge_kernel<D, SCALED, 4>),
                        dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -439,6 +456,20 @@ static hipError_t launch_mu(AttnArgs a, int max_waves, hipStream_t stream) {
 template <typename QT, typename CT, int D>
 static hipError_t launch_md(const AttnArgs& a, int max_waves, bool uniform,
                             hipStream_t stream) {
+  if constexpr (is_fp8<CT>::value) {
+    if (a.scale_per_token) {
+      if constexpr (!same<QT, F32>::value) {
+        if (a.row_tokens / a.tpr == 4) {
+          if (uniform)
+            return launch_mu<QT, CT, D, true, 4, true>(a, max_waves, stream);
+          return launch_mu<QT, CT, D, false, 4, true>(a, max_waves, stream);
+        }
+      }
+      if (uniform)
+        return launch_mu<QT, CT, D, true, 1, true>(a, max_waves, stream);
+      return launch_mu<QT, CT, D, false, 1, true>(a, max_waves, stream);
+    }
+  }
   if constexpr (!same<QT, F32>::value) {
     if (a.row_tokens / a.tpr == 4) {
       if (uniform) return launch_mu<QT, CT, D, true, 4>(a, max_waves, stream);

@@ -61,17 +61,31 @@ template <typename QT, typename CT, int D> struct Shape {
   static_assert(16 % TOK_PER_V == 0, "a V load must not straddle halves");
 };
 
-// One tile's raw K and V bytes as loaded from the pool, per sub-tile.
+// One tile's raw K and V bytes as loaded from the pool, per sub-tile; with
+// per-token fp8 scales also the tile's scales: lane i < 32 holds token i's
+// key scale, lane 32 + i its value scale.
 template <typename QT, typename CT, int D> struct TileRegs {
   typedef Shape<QT, CT, D> S;
   uint32_t kw[S::SUB][2][S::KWORDS];
   u32x4_t vraw[S::SUB][S::NV];
+  float sc[S::SUB];
+};
+
+// Per-token fp8 scale arrays [num_blocks, block_size, num_kv_heads], both
+// already offset to one kv head (token slot t's scale at [t * hkv]).
+struct TokenScales {
+  const float* k;
+  const float* v;
+  int hkv;
 };
 
 // Online-softmax state of one wave: running max (log2 domain) and this
 // lane's share of the running sum for query head column c, and O^T blocks.
+// With per-token value scales O^T is kept in units of 2^mv, mv the running
+// maximum of score + log2(value scale) (see softmax_tile).
 template <int NBLK> struct WaveState {
   float m;
+  float mv;
   float l;
   f32x4_t o[NBLK];
 };
@@ -84,11 +98,11 @@ template <int NBLK> struct WaveState {
 // two VGPRs: lane i of tab_a / tab_b holds the entry of logical block
 // wb + i / wb + 64 + i, and a wave-uniform readlane turns it into a scalar.
 // ---------------------------------------------------------------------------
-template <typename QT, typename CT, int D>
+template <typename QT, typename CT, int D, bool PT = false>
 __device__ __forceinline__ void load_tile_uniform(
     TileRegs<QT, CT, D>& tr, int bs, int nblocks, uint32_t tab_a,
     uint32_t tab_b, int wb, const uint8_t* kbase, const uint8_t* vbase,
-    int64_t stride, int t0, int t_end, int lane) {
+    int64_t stride, int t0, int t_end, int lane, TokenScales tsc = {}) {
   typedef Shape<QT, CT, D> S;
   const int c = lane & 15;
   const int j = lane >> 4;
@@ -102,6 +116,8 @@ __device__ __forceinline__ void load_tile_uniform(
 #pragma unroll
   for (int sb = 0; sb < S::SUB; ++sb) {
     __amdgpu_buffer_rsrc_t kr[2], vr[2];
+    int64_t first_slot[2];
+    int live[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int tb = t0 + 32 * sb + 16 * hh;
@@ -121,6 +137,8 @@ __device__ __forceinline__ void load_tile_uniform(
         phys = (uint32_t)phys < (uint32_t)nblocks ? phys : nblocks - 1;
         row0 = (int64_t)phys * bs + (tb - lb * bs);
       }
+      first_slot[hh] = row0;
+      live[hh] = nvalid;
       // (the clamp above may be selected as a vector min/max)
       const int nrec = __builtin_amdgcn_readfirstlane(nvalid * (int)stride);
       kr[hh] = __builtin_amdgcn_make_buffer_rsrc(
@@ -150,16 +168,25 @@ __device__ __forceinline__ void load_tile_uniform(
       tr.vraw[sb][v] = __builtin_amdgcn_raw_buffer_load_b128(
           vr[hh], vofs + tin * (int)stride, 0, 0);
     }
+    if constexpr (PT) {
+      // lane (i + 32 kv): token i's key (kv 0) or value (kv 1) scale
+      const int hl = (lane >> 4) & 1;
+      const int tin = lane & 15;
+      const int64_t slot = (hl ? first_slot[1] : first_slot[0]) + tin;
+      tr.sc[sb] = 0.f;
+      if (tin < (hl ? live[1] : live[0]))
+        tr.sc[sb] = (lane < 32 ? tsc.k : tsc.v)[slot * tsc.hkv];
+    }
   }
 }
 
 // Tile loads for any block size: one table lookup per token (vector), masked
 // lanes skip the load and hold zeros.
-template <typename QT, typename CT, int D>
+template <typename QT, typename CT, int D, bool PT = false>
 __device__ __forceinline__ void load_tile_any(
     TileRegs<QT, CT, D>& tr, int bs, int nblocks, const int32_t* trow,
     const uint8_t* kbase, const uint8_t* vbase, int64_t stride, int t0,
-    int t_end, int lane) {
+    int t_end, int lane, TokenScales tsc = {}) {
   typedef Shape<QT, CT, D> S;
   const int c = lane & 15;
   const int j = lane >> 4;
@@ -197,6 +224,11 @@ __device__ __forceinline__ void load_tile_any(
       if (ts + tv < t_end)
         tr.vraw[sb][v] = *reinterpret_cast<const u32x4_t*>(
             vbase + (int64_t)vs * stride + (lane % S::PPR) * 16);
+    }
+    if constexpr (PT) {  // lane (i + 32 kv): token i's key / value scale
+      tr.sc[sb] = 0.f;
+      if (tok < t_end)
+        tr.sc[sb] = (lane < 32 ? tsc.k : tsc.v)[(int64_t)myslot * tsc.hkv];
     }
   }
 }
@@ -322,22 +354,38 @@ __device__ __forceinline__ void qk_tile(
 // the caller folds t_end into -- get weight 0.  With CAUSAL a column may see
 // no key of a tile at all; its state then stays empty instead of turning
 // into 0 * inf.
-template <typename QT, typename CT, int D, bool CAUSAL>
+//
+// PT (per-token fp8 scales; sc as TileRegs::sc): token t's score takes its
+// key scale ks_t, and its value row its value scale vs_t, which cannot be
+// factored out of the sum.  The PV weight of token t is then 2^(s_t - m)
+// vs_t = 2^(u_t - m) with u_t = s_t + log2 vs_t; it is formed as
+// 2^(u_t - mv) against a second running maximum mv of u, so the weights fed
+// to the PV product stay in (0, 1] whatever the scales' range, and O^T is
+// rescaled by 2^(mv_old - mv_new) as the sum l is by 2^(m_old - m_new).
+// fold_value_scales turns O^T back into units of 2^m at the end.
+template <typename QT, typename CT, int D, bool CAUSAL, bool PT = false>
 __device__ __forceinline__ void softmax_tile(
     const f32x4_t (&sacc)[2], WaveState<Shape<QT, CT, D>::NBLK>& st, int t0,
     int t_end, int lim, float qk_mul, int lane,
     typename Mma<typename Shape<QT, CT, D>::PVT>::operand& pb_hi,
-    typename Mma<typename Shape<QT, CT, D>::PVT>::operand& pb_lo) {
+    typename Mma<typename Shape<QT, CT, D>::PVT>::operand& pb_lo,
+    float sc = 0.f) {
   typedef Shape<QT, CT, D> S;
   typedef typename S::PVT PVT;
   constexpr int PVB = S::PVB;
   const int j = lane >> 4;
   float sv[8];
+  float lvs[8];  // PT: log2 of each token's value scale
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
-    sv[e] = (t0 + slot_token(j, e) < (CAUSAL ? lim : t_end)) ? raw * qk_mul
-                                                             : -INFINITY;
+    const bool live = t0 + slot_token(j, e) < (CAUSAL ? lim : t_end);
+    float mul = qk_mul;
+    if constexpr (PT) {
+      mul *= __shfl(sc, slot_token(j, e), 64);
+      lvs[e] = __builtin_amdgcn_logf(__shfl(sc, 32 + slot_token(j, e), 64));
+    }
+    sv[e] = live ? raw * mul : -INFINITY;
   }
   float mx = sv[0];
 #pragma unroll
@@ -356,8 +404,26 @@ __device__ __forceinline__ void softmax_tile(
   }
   st.l = st.l * alpha + psum;
   st.m = m_new;
+  float orescale = alpha;
+  if constexpr (PT) {
+    float u[8];
+    float mxv = -INFINITY;
 #pragma unroll
-  for (int n = 0; n < S::NBLK; ++n) st.o[n] *= alpha;
+    for (int e = 0; e < 8; ++e) {
+      u[e] = sv[e] == -INFINITY ? -INFINITY : sv[e] + lvs[e];
+      mxv = fmaxf(mxv, u[e]);
+    }
+    mxv = xor_max(mxv, 16);
+    mxv = xor_max(mxv, 32);
+    const float mv_new = fmaxf(st.mv, mxv);
+    const float mv_use = mv_new == -INFINITY ? 0.f : mv_new;
+    orescale = fast_exp2(st.mv - mv_use);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(u[e] - mv_use);
+    st.mv = mv_new;
+  }
+#pragma unroll
+  for (int n = 0; n < S::NBLK; ++n) st.o[n] *= orescale;
 
   if constexpr (PVB == 2) {
 #pragma unroll
@@ -409,18 +475,18 @@ __device__ __forceinline__ void v_operand(
 }
 
 // One tile for one 16-column group.
-template <typename QT, typename CT, int D, bool CAUSAL = false>
+template <typename QT, typename CT, int D, bool CAUSAL = false, bool PT = false>
 __device__ __forceinline__ void compute_tile(
     const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS], const uint32_t* qw,
     WaveState<Shape<QT, CT, D>::NBLK>& st, uint8_t* vt, int t0, int t_end,
-    float qk_mul, int lane, int lim = 0) {
+    float qk_mul, int lane, int lim = 0, float sc = 0.f) {
   typedef Shape<QT, CT, D> S;
   typedef typename S::PVT PVT;
   f32x4_t sacc[2];
   qk_tile<QT, CT, D>(kw, qw, sacc);
   typename Mma<PVT>::operand pb_hi, pb_lo;
-  softmax_tile<QT, CT, D, CAUSAL>(sacc, st, t0, t_end, lim, qk_mul, lane,
-                                  pb_hi, pb_lo);
+  softmax_tile<QT, CT, D, CAUSAL, PT>(sacc, st, t0, t_end, lim, qk_mul, lane,
+                                      pb_hi, pb_lo, sc);
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) {
     typename Mma<PVT>::operand va;
@@ -432,12 +498,12 @@ __device__ __forceinline__ void compute_tile(
 
 // One tile for NG 16-column groups of query columns (causal limits per
 // group): the tile's K registers and each V^T read serve every group.
-template <typename QT, typename CT, int D, int NG>
+template <typename QT, typename CT, int D, int NG, bool PT = false>
 __device__ __forceinline__ void compute_tile_groups(
     const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS],
     const uint32_t (&qw)[NG][Shape<QT, CT, D>::QWORDS],
     WaveState<Shape<QT, CT, D>::NBLK> (&st)[NG], uint8_t* vt, int t0,
-    const int (&lim)[NG], float qk_mul, int lane) {
+    const int (&lim)[NG], float qk_mul, int lane, float sc = 0.f) {
   typedef Shape<QT, CT, D> S;
   typedef typename S::PVT PVT;
   typename Mma<PVT>::operand pb_hi[NG], pb_lo[NG];
@@ -445,8 +511,8 @@ __device__ __forceinline__ void compute_tile_groups(
   for (int g = 0; g < NG; ++g) {
     f32x4_t sacc[2];
     qk_tile<QT, CT, D>(kw, qw[g], sacc);
-    softmax_tile<QT, CT, D, true>(sacc, st[g], t0, 0, lim[g], qk_mul, lane,
-                                  pb_hi[g], pb_lo[g]);
+    softmax_tile<QT, CT, D, true, PT>(sacc, st[g], t0, 0, lim[g], qk_mul,
+                                      lane, pb_hi[g], pb_lo[g], sc);
   }
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) {
@@ -458,6 +524,15 @@ __device__ __forceinline__ void compute_tile_groups(
       if constexpr (S::PSPLIT) st[g].o[n] = Mma<PVT>::step(va, pb_lo[g], st[g].o[n]);
     }
   }
+}
+
+// With per-token value scales: O^T from units of 2^mv back to units of 2^m
+// (an empty state stays zero).
+template <int NBLK>
+__device__ __forceinline__ void fold_value_scales(WaveState<NBLK>& st) {
+  const float f = st.mv == -INFINITY ? 0.f : fast_exp2(st.mv - st.m);
+#pragma unroll
+  for (int n = 0; n < NBLK; ++n) st.o[n] *= f;
 }
 
 // ---------------------------------------------------------------------------

@@ -72,6 +72,23 @@ template <> __device__ __forceinline__ float piece_elem<BF16>(const u32x4_t* w, 
   return __uint_as_float((word >> (16 * (e & 1))) << 16);
 }
 
+// Largest magnitude of a 16-element piece (NaN elements ignored).
+template <typename ST>
+__device__ __forceinline__ float piece_amax(const u32x4_t* in) {
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(piece_elem<ST>(in, e)));
+  return m;
+}
+
+// Per-token scale of a row whose largest magnitude is amax: amax over the
+// format's largest finite value (IEEE float32 division), 1 for amax 0.
+template <typename CT>
+__device__ __forceinline__ float row_scale(float amax) {
+  const float largest = same<CT, FP8E5>::value ? 57344.f : 448.f;
+  return amax == 0.f ? 1.f : amax / largest;
+}
+
 // The 16 codes of one 16-element source piece (ST::bytes 16-byte words) in
 // the cache's fp8 format CT (FP8: E4M3, FP8E5: E5M2).
 template <typename ST, typename CT>

@@ -24,12 +24,17 @@ int dtype_bytes(int d) {
 
 // A cache dtype argument: the element type and the per-head-scale flag (only
 // for fp8 caches; any other bit is an error).  Returns false if invalid.
-bool split_cache_dtype(int arg, int* dtype, bool* per_head) {
+// A cache dtype argument: the dtype code, optionally OR-ed with one fp8
+// scale layout flag (per kv head or per token; fp8 caches only).
+bool split_cache_dtype(int arg, int* dtype, bool* per_head,
+                       bool* per_token) {
   *dtype = arg & 0xFF;
   *per_head = (arg & PKV_SCALE_PER_HEAD) != 0;
-  if ((arg & ~(0xFF | PKV_SCALE_PER_HEAD)) != 0) return false;
-  if (!valid_dtype(*dtype)) return false;
-  return !*per_head || is_fp8_dtype(*dtype);
+  *per_token = (arg & PKV_SCALE_PER_TOKEN) != 0;
+  if ((arg & ~(0xFF | PKV_SCALE_PER_HEAD | PKV_SCALE_PER_TOKEN)) != 0)
+    return false;
+  if (!valid_dtype(*dtype) || (*per_head && *per_token)) return false;
+  return !(*per_head || *per_token) || is_fp8_dtype(*dtype);
 }
 
 bool aligned(const void* p, uintptr_t n) {
@@ -94,17 +99,26 @@ const char* pkv_status_string(int status) {
   return "unknown status";
 }
 
-int cache_write_slots(const void* key, const void* value, int src_dtype,
-                      void* k_cache, void* v_cache, int cache_dtype,
-                      const int32_t* slot_mapping, int64_t num_tokens,
-                      int64_t num_blocks, int32_t block_size,
-                      int32_t num_kv_heads, int32_t head_dim,
-                      const float* k_scale, const float* v_scale,
-                      hipStream_t stream) {
-  bool per_head = false;
+namespace {
+
+// cache_write_slots (token_scales false: scales read) and
+// cache_write_slots_token_scaled (true: each row's scale written to
+// k_scales / v_scales).
+int write_common(const void* key, const void* value, int src_dtype,
+                 void* k_cache, void* v_cache, int cache_dtype,
+                 const int32_t* slot_mapping, int64_t num_tokens,
+                 int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                 int32_t head_dim, const float* k_scale, const float* v_scale,
+                 float* k_scales, float* v_scales, bool token_scales,
+                 hipStream_t stream) {
+  bool per_head = false, per_token = false;
   const int cache_arg = cache_dtype;
   if (!valid_dtype(src_dtype) ||
-      !split_cache_dtype(cache_arg, &cache_dtype, &per_head))
+      !split_cache_dtype(cache_arg, &cache_dtype, &per_head, &per_token))
+    return PKV_ERR_DTYPE;
+  // per-token scales are written by the token-scaled call only, which takes
+  // an fp8 cache code with or without the per-token flag
+  if (token_scales ? (per_head || !is_fp8_dtype(cache_dtype)) : per_token)
     return PKV_ERR_DTYPE;
   if (is_fp8_dtype(src_dtype)) return PKV_ERR_DTYPE;
   if (!is_fp8_dtype(cache_dtype) && src_dtype != cache_dtype) return PKV_ERR_DTYPE;
@@ -114,11 +128,18 @@ int cache_write_slots(const void* key, const void* value, int src_dtype,
   if (num_blocks * (int64_t)block_size > INT_MAX) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
-  if (is_fp8_dtype(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if (token_scales) {
+    if (!k_scales || !v_scales) return PKV_ERR_NULL;
+    if (!aligned(k_scales, 4) || !aligned(v_scales, 4)) return PKV_ERR_ALIGN;
+  } else if (is_fp8_dtype(cache_dtype) && (!k_scale || !v_scale)) {
+    return PKV_ERR_NULL;
+  }
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(slot_mapping, 4))
     return PKV_ERR_ALIGN;
   WriteArgs a{};
+  a.k_token_scales = token_scales ? k_scales : nullptr;
+  a.v_token_scales = token_scales ? v_scales : nullptr;
   a.scale_per_head = per_head;
   a.head_dim = head_dim;
   a.key = key;
@@ -136,6 +157,35 @@ int cache_write_slots(const void* key, const void* value, int src_dtype,
              ? PKV_OK : PKV_ERR_HIP;
 }
 
+}  // namespace
+
+int cache_write_slots(const void* key, const void* value, int src_dtype,
+                      void* k_cache, void* v_cache, int cache_dtype,
+                      const int32_t* slot_mapping, int64_t num_tokens,
+                      int64_t num_blocks, int32_t block_size,
+                      int32_t num_kv_heads, int32_t head_dim,
+                      const float* k_scale, const float* v_scale,
+                      hipStream_t stream) {
+  return write_common(key, value, src_dtype, k_cache, v_cache, cache_dtype,
+                      slot_mapping, num_tokens, num_blocks, block_size,
+                      num_kv_heads, head_dim, k_scale, v_scale, nullptr,
+                      nullptr, false, stream);
+}
+
+int cache_write_slots_token_scaled(const void* key, const void* value,
+                                   int src_dtype, void* k_cache,
+                                   void* v_cache, int cache_dtype,
+                                   float* k_scales, float* v_scales,
+                                   const int32_t* slot_mapping,
+                                   int64_t num_tokens, int64_t num_blocks,
+                                   int32_t block_size, int32_t num_kv_heads,
+                                   int32_t head_dim, hipStream_t stream) {
+  return write_common(key, value, src_dtype, k_cache, v_cache, cache_dtype,
+                      slot_mapping, num_tokens, num_blocks, block_size,
+                      num_kv_heads, head_dim, nullptr, nullptr, k_scales,
+                      v_scales, true, stream);
+}
+
 namespace {
 
 int copy_common(void* k_cache, void* v_cache, int cache_dtype,
@@ -143,9 +193,9 @@ int copy_common(void* k_cache, void* v_cache, int cache_dtype,
                 int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                 int32_t head_dim, int prefix, int32_t num_layers,
                 int64_t layer_stride, hipStream_t stream) {
-  bool per_head = false;  // (scales play no part in a copy)
+  bool per_head = false, per_token = false;  // (scales: not in a pool copy)
   const int cache_arg = cache_dtype;
-  if (!split_cache_dtype(cache_arg, &cache_dtype, &per_head))
+  if (!split_cache_dtype(cache_arg, &cache_dtype, &per_head, &per_token))
     return PKV_ERR_DTYPE;
   if (num_pairs < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1)
     return PKV_ERR_SHAPE;
@@ -173,6 +223,37 @@ int copy_common(void* k_cache, void* v_cache, int cache_dtype,
   a.block_bytes = (int64_t)block_size * a.token_bytes;
   a.block_size = block_size;
   a.prefix = prefix;
+  a.piece_bytes = 16;
+  return launch_copy_blocks(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// The per-token scale arrays [num_blocks, block_size, num_kv_heads] float32
+// through the same copies (one float per thread).
+int copy_scales_common(float* k_scales, float* v_scales,
+                       const int32_t* records, int64_t num_records,
+                       int64_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int prefix, hipStream_t stream) {
+  if (num_records < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1)
+    return PKV_ERR_SHAPE;
+  if (num_blocks * (int64_t)block_size * num_kv_heads > ((int64_t)1 << 40))
+    return PKV_ERR_SHAPE;
+  if (num_records == 0) return PKV_OK;
+  if (!k_scales || !v_scales || !records) return PKV_ERR_NULL;
+  if (!aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(records, 4))
+    return PKV_ERR_ALIGN;
+  CopyArgs a{};
+  a.num_layers = 1;
+  a.layer_stride = 0;
+  a.k_cache = k_scales;
+  a.v_cache = v_scales;
+  a.pairs = records;
+  a.num_pairs = num_records;
+  a.num_blocks = num_blocks;
+  a.token_bytes = (int64_t)num_kv_heads * 4;
+  a.block_bytes = (int64_t)block_size * a.token_bytes;
+  a.block_size = block_size;
+  a.prefix = prefix;
+  a.piece_bytes = 4;
   return launch_copy_blocks(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -185,6 +266,23 @@ int copy_blocks(void* k_cache, void* v_cache, int cache_dtype,
   return copy_common(k_cache, v_cache, cache_dtype, block_pairs, num_pairs,
                      num_blocks, block_size, num_kv_heads, head_dim, 0, 1, 0,
                      stream);
+}
+
+int copy_token_scales(float* k_scales, float* v_scales,
+                      const int32_t* block_pairs, int64_t num_pairs,
+                      int64_t num_blocks, int32_t block_size,
+                      int32_t num_kv_heads, hipStream_t stream) {
+  return copy_scales_common(k_scales, v_scales, block_pairs, num_pairs,
+                            num_blocks, block_size, num_kv_heads, 0, stream);
+}
+
+int copy_token_scale_prefixes(float* k_scales, float* v_scales,
+                              const int32_t* block_triples,
+                              int64_t num_copies, int64_t num_blocks,
+                              int32_t block_size, int32_t num_kv_heads,
+                              hipStream_t stream) {
+  return copy_scales_common(k_scales, v_scales, block_triples, num_copies,
+                            num_blocks, block_size, num_kv_heads, 1, stream);
 }
 
 int copy_blocks_layers(void* k_caches, void* v_caches, int64_t layer_stride,
@@ -254,13 +352,16 @@ int decode_common(float* out, const void* query, int q_dtype,
                   size_t workspace_bytes, const void* key, const void* value,
                   const int32_t* slot_mapping, bool fused,
                   hipStream_t stream) {
-  bool per_head = false;
+  bool per_head = false, per_token = false;
   const int cache_arg = cache_dtype;
   if (!valid_dtype(q_dtype) ||
-      !split_cache_dtype(cache_arg, &cache_dtype, &per_head))
+      !split_cache_dtype(cache_arg, &cache_dtype, &per_head, &per_token))
     return PKV_ERR_DTYPE;
   if (is_fp8_dtype(q_dtype)) return PKV_ERR_DTYPE;
   if (!is_fp8_dtype(cache_dtype) && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
+  // the fused write stores no per-token scales: write with
+  // cache_write_slots_token_scaled, then paged_attn_decode
+  if (fused && per_token) return PKV_ERR_UNSUPPORTED;
   if (num_blocks < 1 || block_size < 1 || max_blocks_per_seq < 1 ||
       max_seq_len < 0 || max_waves < 0)
     return PKV_ERR_SHAPE;
@@ -281,6 +382,8 @@ int decode_common(float* out, const void* query, int q_dtype,
     return PKV_ERR_NULL;
   if (fused && (!key || !value || !slot_mapping)) return PKV_ERR_NULL;
   if (is_fp8_dtype(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if (per_token && (!aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return PKV_ERR_ALIGN;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4))
     return PKV_ERR_ALIGN;
@@ -315,6 +418,7 @@ int decode_common(float* out, const void* query, int q_dtype,
   a.max_seq_tokens = max_seq_len;  // within the table's reach (checked)
   a.qk_scale_log2 = scale * 1.4426950408889634f;
   a.scale_per_head = per_head;
+  a.scale_per_token = per_token;
   a.new_key = key;
   a.new_value = value;
   a.slot_mapping = slot_mapping;
@@ -379,10 +483,10 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
                      int32_t head_dim, int64_t num_blocks, int32_t block_size,
                      float scale, int32_t max_waves, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
-  bool per_head = false;
+  bool per_head = false, per_token = false;
   const int cache_arg = cache_dtype;
   if (!valid_dtype(q_dtype) ||
-      !split_cache_dtype(cache_arg, &cache_dtype, &per_head))
+      !split_cache_dtype(cache_arg, &cache_dtype, &per_head, &per_token))
     return PKV_ERR_DTYPE;
   if (is_fp8_dtype(q_dtype)) return PKV_ERR_DTYPE;
   if (!is_fp8_dtype(cache_dtype) && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
@@ -412,6 +516,8 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
       !query_start)
     return PKV_ERR_NULL;
   if (is_fp8_dtype(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if (per_token && (!aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return PKV_ERR_ALIGN;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(block_tables, 4) ||
       !aligned(seq_lens, 4) || !aligned(query_start, 4))
@@ -444,6 +550,7 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
   a.max_seq_tokens = max_seq_len;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
   a.scale_per_head = per_head;
+  a.scale_per_token = per_token;
   a.query_start = query_start;
   a.num_query_tokens = num_query_tokens;
   a.max_query_len = max_query_len;

@@ -53,6 +53,8 @@ struct AttnArgs {
   int32_t num_waves;      // waves of the partition kernel's grid
   float qk_scale_log2;    // softmax scale * log2(e)
   int32_t scale_per_head; // fp8 scales: one per kv head (else one per tensor)
+  int32_t scale_per_token;  // fp8 scales: k_scale / v_scale are
+                            // [num_blocks, block_size, num_kv_heads]
   // several query tokens per sequence (paged_attn_multi) only:
   const int32_t* query_start;  // [num_seqs + 1] first query row of each
   int32_t num_query_tokens;    // rows of query / out (starts clamped to it)
@@ -89,6 +91,10 @@ struct WriteArgs {
   int32_t head_dim;
   int32_t block_size;
   int32_t row_elems;      // num_kv_heads * head_dim
+  // per-token fp8 scales: each written (token, kv head) row's own scale is
+  // stored here, [num_blocks, block_size, num_kv_heads] (null otherwise)
+  float* k_token_scales;
+  float* v_token_scales;
 };
 
 hipError_t launch_cache_write(const WriteArgs& a, int src_dtype,
@@ -106,6 +112,7 @@ struct CopyArgs {
   int32_t prefix;         // 1: copy only the first `tokens` token rows
   int32_t num_layers;     // pools of every layer, layer_stride bytes apart
   int64_t layer_stride;
+  int32_t piece_bytes;    // 16 (pools) or 4 (per-token scale arrays)
 };
 
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);

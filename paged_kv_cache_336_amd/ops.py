@@ -5,8 +5,10 @@ the current HIP stream; every step of the computation runs in the library's
 HIP kernels.  There is no fallback: if the shared library is missing the
 first call raises.
 
-Functions keep the C names: :func:`cache_write_slots`, :func:`copy_blocks`,
-:func:`copy_block_prefixes`, :func:`paged_attn_decode`,
+Functions keep the C names: :func:`cache_write_slots`,
+:func:`cache_write_slots_token_scaled`, :func:`copy_blocks`,
+:func:`copy_block_prefixes`, :func:`copy_token_scales`,
+:func:`copy_token_scale_prefixes`, :func:`paged_attn_decode`,
 :func:`paged_attn_decode_fused`,
 :func:`paged_attn_workspace_size`, :func:`paged_attn_multi`,
 :func:`paged_attn_multi_workspace_size`, :func:`pkv_status_string`.
@@ -20,11 +22,14 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E5M2 = 0, 1, 2, 3, 4
 PKV_SCALE_PER_HEAD = 0x100
+PKV_SCALE_PER_TOKEN = 0x200
 KIND_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
               "fp8_e4m3": PKV_FP8_E4M3, "fp8_e5m2": PKV_FP8_E5M2}
 
-EXPORTED = ("pkv_status_string", "cache_write_slots", "copy_blocks",
-            "copy_block_prefixes", "paged_attn_workspace_size",
+EXPORTED = ("pkv_status_string", "cache_write_slots",
+            "cache_write_slots_token_scaled", "copy_blocks",
+            "copy_block_prefixes", "copy_token_scales",
+            "copy_token_scale_prefixes", "paged_attn_workspace_size",
             "copy_blocks_layers", "copy_block_prefixes_layers",
             "paged_attn_decode", "paged_attn_decode_fused",
             "paged_attn_multi_workspace_size", "paged_attn_multi")
@@ -58,6 +63,13 @@ def load_library(path=None):
     lib.cache_write_slots.restype = ci
     lib.cache_write_slots.argtypes = [vp, vp, ci, vp, vp, ci, vp, i64, i64, i32,
                                       i32, i32, vp, vp, vp]
+    lib.cache_write_slots_token_scaled.restype = ci
+    lib.cache_write_slots_token_scaled.argtypes = [vp, vp, ci, vp, vp, ci, vp,
+                                                   vp, vp, i64, i64, i32, i32,
+                                                   i32, vp]
+    for fn in (lib.copy_token_scales, lib.copy_token_scale_prefixes):
+        fn.restype = ci
+        fn.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp]
     lib.copy_blocks.restype = ci
     lib.copy_blocks.argtypes = [vp, vp, ci, vp, i64, i64, i32, i32, i32, vp]
     lib.copy_block_prefixes.restype = ci
@@ -119,12 +131,15 @@ def dtype_code(t, kind=None):
 
 
 def cache_code(k_cache, cache_kind, k_scale):
-    """The cache dtype argument: the element type, with PKV_SCALE_PER_HEAD
-    when an fp8 cache's scales hold one value per kv head."""
+    """The cache dtype argument: the element type, with PKV_SCALE_PER_TOKEN
+    when an fp8 cache's scales are [num_blocks, block_size, Hkv] arrays, or
+    PKV_SCALE_PER_HEAD when they hold one value per kv head."""
     code = dtype_code(k_cache, cache_kind)
-    if code in (PKV_FP8_E4M3, PKV_FP8_E5M2) and k_scale is not None \
-            and k_scale.numel() > 1:
-        code |= PKV_SCALE_PER_HEAD
+    if code in (PKV_FP8_E4M3, PKV_FP8_E5M2) and k_scale is not None:
+        if k_scale.dim() == 3:
+            code |= PKV_SCALE_PER_TOKEN
+        elif k_scale.numel() > 1:
+            code |= PKV_SCALE_PER_HEAD
     return code
 
 
@@ -158,6 +173,48 @@ def cache_write_slots(key, value, k_cache, v_cache, slot_mapping,
         cache_code(k_cache, cache_kind, k_scale), _ptr(slot_mapping),
         int(slot_mapping.shape[0]), nb, bs, hkv, d, _ptr(k_scale),
         _ptr(v_scale), _stream(stream)))
+
+
+def cache_write_slots_token_scaled(key, value, k_cache, v_cache, k_scales,
+                                   v_scales, slot_mapping, cache_kind=None,
+                                   stream=None):
+    """Scatter key/value [T, Hkv, D] into an fp8 cache with a scale per
+    written row, stored in k_scales / v_scales [num_blocks, block_size,
+    Hkv] (float32, in place)."""
+    lib = load_library()
+    nb, bs, hkv, d = k_cache.shape
+    assert tuple(k_scales.shape) == (nb, bs, hkv) and \
+        tuple(v_scales.shape) == (nb, bs, hkv)
+    _check("cache_write_slots_token_scaled",
+           lib.cache_write_slots_token_scaled(
+               _ptr(key), _ptr(value), dtype_code(key), _ptr(k_cache),
+               _ptr(v_cache), dtype_code(k_cache, cache_kind) |
+               PKV_SCALE_PER_TOKEN, _ptr(k_scales), _ptr(v_scales),
+               _ptr(slot_mapping), int(slot_mapping.shape[0]), nb, bs, hkv,
+               d, _stream(stream)))
+
+
+def _scales_copy(name, k_scales, v_scales, rows, width, stream):
+    lib = load_library()
+    nb, bs, hkv = k_scales.shape
+    assert tuple(v_scales.shape) == (nb, bs, hkv)
+    assert rows.shape[1:] == (width,)
+    _check(name, getattr(lib, name)(
+        _ptr(k_scales), _ptr(v_scales), _ptr(rows), int(rows.shape[0]), nb,
+        bs, hkv, _stream(stream)))
+
+
+def copy_token_scales(k_scales, v_scales, block_pairs, stream=None):
+    """Per-token scale arrays through whole-block copies [P, 2]."""
+    _scales_copy("copy_token_scales", k_scales, v_scales, block_pairs,
+                 2, stream)
+
+
+def copy_token_scale_prefixes(k_scales, v_scales, block_triples,
+                              stream=None):
+    """Per-token scale arrays through token-prefix copies [P, 3]."""
+    _scales_copy("copy_token_scale_prefixes", k_scales, v_scales,
+                 block_triples, 3, stream)
 
 
 def copy_blocks(k_cache, v_cache, block_pairs, cache_kind=None, stream=None):

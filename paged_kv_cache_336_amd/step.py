@@ -52,7 +52,7 @@ class DeviceStep:
         self.key = _to_torch(w.key, w.src_kind, dev)
         self.value = _to_torch(w.value, w.src_kind, dev)
         self.seq_lens = torch.from_numpy(w.seq_lens.astype(np.int32)).to(dev)
-        # one scale, or one per kv head
+        # one scale, one per kv head, or per token [nb, bs, Hkv]
         self.k_scale = torch.from_numpy(np.atleast_1d(
             np.asarray(w.k_scale, dtype=np.float32)).copy()).to(dev)
         self.v_scale = torch.from_numpy(np.atleast_1d(
@@ -74,13 +74,27 @@ class DeviceStep:
         self.workspace = ops.Workspace(dev)
         self.max_seq_len = w.max_seq_len
 
+    @property
+    def token_scales(self):
+        """True when the fp8 scales are per (slot, kv head) arrays."""
+        return self.k_scale.dim() == 3
+
     def copy(self, r=0, stream=None):
         pairs = self.sets[r]["copy_pairs"]
         ops.copy_blocks(self.k_cache, self.v_cache, pairs,
                         cache_kind=self.cache_kind, stream=stream)
+        if self.token_scales:
+            ops.copy_token_scales(self.k_scale, self.v_scale, pairs,
+                                  stream=stream)
 
     def write(self, r=0, stream=None):
         kind = self.cache_kind
+        if self.token_scales:
+            ops.cache_write_slots_token_scaled(
+                self.key, self.value, self.k_cache, self.v_cache,
+                self.k_scale, self.v_scale, self.sets[r]["slot_mapping"],
+                cache_kind=kind, stream=stream)
+            return
         ops.cache_write_slots(self.key, self.value, self.k_cache, self.v_cache,
                               self.sets[r]["slot_mapping"],
                               k_scale=self.k_scale, v_scale=self.v_scale,

@@ -483,13 +483,14 @@ def prefix_sharing(block_size=32, phase="fork", groups=8, samples=8,
 
 
 def long_context_fp8(num_seqs=8, seq_len=131072, block_size=64,
-                     seed_family=4):
+                     seed_family=4, per_token_scales=False):
     """Long-context split-K decode: 8 sequences of 131072 tokens, 32/8
     heads, D 128, bs 64; K/V cached as fp8 E4M3 with per-tensor scales
-    (max|live value| / 448), Q and the new rows bf16.  Blocks are a random
-    permutation of the used blocks plus one poisoned spare for unused table
-    columns.  (How each sequence is split for the log-sum-exp merge is the
-    kernel's choice, not part of the inputs.)"""
+    (max|live value| / 448; with per_token_scales one per (slot, kv head)
+    instead), Q and the new rows bf16.  Blocks are a random permutation of
+    the used blocks plus one poisoned spare for unused table columns.  (How
+    each sequence is split for the log-sum-exp merge is the kernel's choice,
+    not part of the inputs.)"""
     rng = np.random.default_rng([SEED_BASE, seed_family])
     bs = block_size
     lens = np.full(num_seqs, seq_len, dtype=np.int64)
@@ -504,7 +505,8 @@ def long_context_fp8(num_seqs=8, seq_len=131072, block_size=64,
                   src_kind="bf16", hq=32, hkv=8, d=128, bs=bs, nb=nb,
                   block_tables=tables, seq_lens=lens, cached_lens=cached,
                   slot_mapping=slots, copy_pairs=np.zeros((0, 2)),
-                  note=f"{used} used blocks + 1 spare")
+                  note=f"{used} used blocks + 1 spare",
+                  per_token_scales=per_token_scales)
 
 
 def custom_decode(*, seed, num_seqs, lens, hq, hkv, d, bs, q_kind, kv_kind,

@@ -299,3 +299,53 @@ def test_layers_copy_validation(lib):
     assert lib.copy_blocks_layers(*args(0, 1, 0)) == OK          # one layer
     assert lib.copy_block_prefixes_layers(*args(pool, 0)) == SHAPE
     assert lib.copy_block_prefixes_layers(*args(pool, 3, 0)) == OK
+
+
+def cwt(lib, **kw):
+    a = dict(key=FAKE, value=FAKE, src=BF16, kc=FAKE, vc=FAKE, cache=FP8,
+             ks=FAKE, vs=FAKE, slots=FAKE, T=4, nb=64, bs=16, hkv=8, d=128)
+    a.update(kw)
+    return lib.cache_write_slots_token_scaled(
+        a["key"], a["value"], a["src"], a["kc"], a["vc"], a["cache"], a["ks"],
+        a["vs"], a["slots"], a["T"], a["nb"], a["bs"], a["hkv"], a["d"], None)
+
+
+def test_token_scale_validation(lib):
+    """Per-token fp8 scales (PKV_SCALE_PER_TOKEN): written only by the
+    token-scaled write, read by the attention calls, refused by the fused
+    call; the scale copies check their arguments like the pool copies."""
+    E5M2, PER_HEAD, PER_TOKEN = 4, 0x100, 0x200
+    assert cwt(lib, T=0) == OK
+    assert cwt(lib, cache=BF16) == DTYPE                 # fp8 caches only
+    assert cwt(lib, cache=FP8 | PER_HEAD) == DTYPE
+    assert cwt(lib, cache=E5M2 | PER_TOKEN, ks=None) == NULL
+    assert cwt(lib, vs=None) == NULL
+    assert cwt(lib, ks=ctypes.c_void_p(4096 + 2)) == ALIGN
+    assert cwt(lib, src=FP8) == DTYPE
+    assert cwt(lib, d=96) == UNSUP
+    assert cwt(lib, nb=0) == SHAPE
+    # the plain write does not write per-token scales
+    assert cw(lib, src=BF16, cache=FP8 | PER_TOKEN, ks=FAKE, vs=FAKE) == DTYPE
+    assert cw(lib, cache=BF16 | PER_TOKEN) == DTYPE
+    # attention reads them (4-byte aligned arrays)
+    assert pa(lib, qd=BF16, cache=FP8 | PER_TOKEN, ks=FAKE, vs=FAKE,
+              ws=None) == WS
+    assert pa(lib, qd=BF16, cache=E5M2 | PER_TOKEN, ks=FAKE,
+              vs=ctypes.c_void_p(4096 + 2), ws=None) == ALIGN
+    assert pa(lib, qd=BF16, cache=FP8 | PER_TOKEN | PER_HEAD, ks=FAKE,
+              vs=FAKE) == DTYPE
+    assert pm(lib, qd=BF16, cache=FP8 | PER_TOKEN, ks=FAKE, vs=FAKE,
+              ws=None) == WS
+    assert pf(lib, qd=BF16, cache=FP8 | PER_TOKEN, ks=FAKE, vs=FAKE) == UNSUP
+    # the pool copies accept (and ignore) the flag
+    assert lib.copy_blocks(FAKE, FAKE, FP8 | PER_TOKEN, FAKE, 0, 16, 16, 8,
+                           128, None) == OK
+    for fn in (lib.copy_token_scales, lib.copy_token_scale_prefixes):
+        assert fn(FAKE, FAKE, FAKE, 0, 16, 16, 8, None) == OK
+        assert fn(None, None, None, 0, 16, 16, 8, None) == OK
+        assert fn(FAKE, None, FAKE, 3, 16, 16, 8, None) == NULL
+        assert fn(FAKE, FAKE, None, 3, 16, 16, 8, None) == NULL
+        assert fn(FAKE, FAKE, FAKE, -1, 16, 16, 8, None) == SHAPE
+        assert fn(FAKE, FAKE, FAKE, 3, 16, 0, 8, None) == SHAPE
+        assert fn(ctypes.c_void_p(4096 + 2), FAKE, FAKE, 3, 16, 16, 8,
+                  None) == ALIGN
