@@ -53,6 +53,9 @@ def algorithmic_bytes(w):
     es = ELEM_BYTES[w.src_kind]
     T = w.num_tokens
     write = T * hkv * d * (es + e) * 2 + 4 * T
+    if np.ndim(w.k_scale) == 3:   # fp8 scales per token: 4 B per row read
+        attn += int(L.sum()) * hkv * 4 * 2                   # and written
+        write += T * hkv * 4 * 2
     copy = 2 * len(w.copy_pairs) * bs * hkv * d * e * 2
     return {"attention": attn, "cache_write": write, "copy_blocks": copy}
 
@@ -453,6 +456,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--token-scales", action="store_true",
+                    help="long_context_fp8 with fp8 scales per (slot, kv "
+                    "head) instead of per tensor")
     ap.add_argument("--unfused", action="store_true",
                     help="time the step as separate write and attention "
                     "calls even where they can go in one launch")
@@ -486,7 +492,12 @@ def main():
         return
     kw = {"replicas": args.replicas} if args.workload == "llama8b_decode" \
         else {}
+    if args.token_scales:
+        if args.workload != "long_context_fp8":
+            sys.exit("bench.py: --token-scales applies to long_context_fp8")
+        kw["per_token_scales"] = True
     w = W.workload_by_name(args.workload, **kw)
+    token_scales = np.ndim(w.k_scale) == 3
     dev = DeviceStep(w, device="cuda:0")
     R = len(dev.sets)
     nbytes = algorithmic_bytes(w)
@@ -495,7 +506,8 @@ def main():
     # the write and the attention go in one launch where the batch has one
     # new token per (non-empty) sequence and at most 16 query heads per kv
     # head; else as two calls
-    fused = (not args.unfused and w.num_tokens == w.num_seqs and
+    fused = (not args.unfused and not token_scales and
+             w.num_tokens == w.num_seqs and
              bool((w.seq_lens > 0).all()) and
              w.num_q_heads // w.num_kv_heads <= 16)
 
@@ -598,7 +610,9 @@ def main():
     attn_gbps = B / (attn_avg_ms * 1e-3) / 1e9
     tokens_per_s = w.num_seqs / (ms_step * 1e-3)
 
-    traffic = load_traffic(args.traffic_json, args.workload, DECODE_SOURCES)
+    traffic = load_traffic(args.traffic_json, args.workload +
+                           ("_token_scales" if token_scales else ""),
+                           DECODE_SOURCES)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -629,6 +643,10 @@ def main():
             "block_size": w.block_size,
             "kv_dtype": w.kv_kind,
             "q_dtype": w.q_kind,
+            "kv_scales": ("per token" if token_scales else
+                          "per kv head" if np.size(w.k_scale) > 1 else
+                          "per tensor") if w.kv_kind.startswith("fp8")
+                         else None,
             "sum_seq_len": int(w.seq_lens.sum()),
             "max_seq_len": w.max_seq_len,
             "replicas": R,

@@ -303,6 +303,17 @@ class Workspace:
 
 
 _default_ws = {}
+_NO_SIZE = (1 << 64) - 1     # (size_t)-1: the size query's "invalid"
+
+
+def _workspace_buf(workspace, need):
+    """The buffer to pass: none for a shape the size query calls invalid
+    (the call itself then reports why), else the caller's buffer or a
+    Workspace grown to the size."""
+    if need == _NO_SIZE:
+        return None
+    return workspace.get(need) if isinstance(workspace, Workspace) \
+        else workspace
 
 
 def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
@@ -313,11 +324,11 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
-    need = paged_attn_workspace_size(s, hq, hkv, d)
+    need = load_library().paged_attn_workspace_size(s, hq, hkv, d)
     if workspace is None:
         key = str(query.device)
         workspace = _default_ws.setdefault(key, Workspace(query.device))
-    buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    buf = _workspace_buf(workspace, need)
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
         _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale), _ptr(k_scale),
@@ -337,11 +348,11 @@ def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
-    need = paged_attn_workspace_size(s, hq, hkv, d)
+    need = load_library().paged_attn_workspace_size(s, hq, hkv, d)
     if workspace is None:
         key_ = str(query.device)
         workspace = _default_ws.setdefault(key_, Workspace(query.device))
-    buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    buf = _workspace_buf(workspace, need)
     _check("paged_attn_decode_fused", lib.paged_attn_decode_fused(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(key), _ptr(value),
         _ptr(k_cache), _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale),
@@ -362,11 +373,11 @@ def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
     t, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
     s = int(seq_lens.shape[0])
-    need = paged_attn_multi_workspace_size(s, hq, hkv, d)
+    need = load_library().paged_attn_multi_workspace_size(s, hq, hkv, d)
     if workspace is None:
         key = str(query.device)
         workspace = _default_ws.setdefault(key, Workspace(query.device))
-    buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    buf = _workspace_buf(workspace, need)
     _check("paged_attn_multi", lib.paged_attn_multi(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
         _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale), _ptr(k_scale),

@@ -519,7 +519,8 @@ def custom_decode(*, seed, num_seqs, lens, hq, hkv, d, bs, q_kind, kv_kind,
     rng = np.random.default_rng([SEED_BASE, 100, seed])
     src_kind = src_kind or (q_kind if kv_kind in FP8_KINDS else kv_kind)
     lens = np.asarray(lens, dtype=np.int64)
-    need = sum(blocks_for(L, bs) for L in lens)
+    need = sum(blocks_for(max(int(L), 1), bs) for L in lens)  # (an empty
+    # sequence still gets a table row laid out over one block)
     nb = need + spare_blocks
     perm = rng.permutation(nb).astype(np.int32)
     filler = int(perm[-1])
