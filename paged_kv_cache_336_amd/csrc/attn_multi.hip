@@ -396,6 +396,314 @@ void attn_multi_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Long query runs (a prompt chunk against its cached prefix), 16-bit caches
+// with block_size % 16 == 0: rows of kPrefillGroups = 16 column groups, one
+// row per workgroup at a time.  The split is over workgroups; the four waves
+// walk the same tiles in lockstep, wave w computing groups 4w .. 4w + 3, and
+// each tile's K and V rows are loaded once per workgroup: every thread
+// fetches 1/256 of the tile into registers two tiles ahead, stores it into
+// one of two LDS buffers one tile ahead, and all waves read the tile from
+// LDS (K rows XOR-swizzled by 16-byte piece for conflict-free operand
+// reads, V rows in the span-permuted layout the transposing reads use).  So
+// a sequence's K/V is read once per 16 * tpr new tokens (64 at G = 4), and a
+// tile's loads are in flight for two tile steps of the whole workgroup
+// instead of one wave's, while each wave keeps four groups' state without a
+// tile of its own in registers.
+// ---------------------------------------------------------------------------
+constexpr int kPrefillGroups = 4 * kWaves;
+
+// One thread's share of a tile's K and V rows (16-byte pieces q = tid + 256 i
+// of the tile's 32 x D/8 pieces: token q / (D/8), piece q % (D/8)).
+template <int D> struct PrefillStage {
+  static constexpr int PPR = D / 8;               // 16-byte pieces per row
+  static constexpr int CH = 32 * PPR / kThreads;  // per thread: 2 or 1
+  u32x4_t k[CH], v[CH];
+};
+
+// Issue the loads of tile t0 of segment X (rows past X.t_end read as zero
+// and are not fetched).  Every wave's pieces of one load lie in one 16-token
+// half, whose block id a readlane takes from the wave's table window.
+template <typename ET, int D>
+__device__ __forceinline__ void prefill_load(PrefillStage<D>& st,
+                                             const MSeg& X, int t0,
+                                             uint32_t ta, uint32_t tb, int wb,
+                                             const AttnArgs& a, int tid) {
+  constexpr int PPR = PrefillStage<D>::PPR;
+  constexpr int ROW = D * ET::bytes;
+  const int64_t stride = (int64_t)a.num_kv_heads * ROW;
+  const uint8_t* kbase =
+      static_cast<const uint8_t*>(a.k_cache) + (int64_t)X.h * ROW;
+  const uint8_t* vbase =
+      static_cast<const uint8_t*>(a.v_cache) + (int64_t)X.h * ROW;
+#pragma unroll
+  for (int i = 0; i < PrefillStage<D>::CH; ++i) {
+    const int q = tid + kThreads * i;
+    const int r = q / PPR;
+    const int x = q - r * PPR;
+    const int hh = __builtin_amdgcn_readfirstlane(r >> 4);
+    const int th = __builtin_amdgcn_readfirstlane(t0 + 16 * hh);
+    int nvalid = X.t_end - th;
+    nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
+    int64_t row0 = 0;
+    if (nvalid > 0) {
+      const int lb = th / a.block_size;
+      const int idx = lb - wb;  // 0 .. 127
+      int phys = idx < 64 ? __builtin_amdgcn_readlane(ta, idx)
+                          : __builtin_amdgcn_readlane(tb, idx - 64);
+      phys = (uint32_t)phys < (uint32_t)a.num_blocks ? phys : a.num_blocks - 1;
+      row0 = (int64_t)phys * a.block_size + (th - lb * a.block_size);
+    }
+    const int nrec = __builtin_amdgcn_readfirstlane(nvalid * (int)stride);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kbase + row0 * stride), (short)0, nrec,
+        kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(vbase + row0 * stride), (short)0, nrec,
+        kRawBufferFlags);
+    const int off = (r - 16 * hh) * (int)stride + x * 16;
+    st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+    st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
+  }
+}
+
+// LDS byte offset of piece x of K row r: pieces XOR-permuted by row, so the
+// 16 rows one operand read touches fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int prefill_k_at(int r, int x) {
+  constexpr int PPR = D / 8;
+  return r * (D * 2) + ((x ^ (r & (PPR - 1))) << 4);
+}
+
+template <int D>
+__device__ __forceinline__ void prefill_store(const PrefillStage<D>& st,
+                                              uint8_t* kb, uint8_t* vb,
+                                              int tid) {
+  constexpr int PPR = PrefillStage<D>::PPR;
+  constexpr int SPANS = D * 2 / 32;
+#pragma unroll
+  for (int i = 0; i < PrefillStage<D>::CH; ++i) {
+    const int q = tid + kThreads * i;
+    const int r = q / PPR;
+    const int x = q - r * PPR;
+    *reinterpret_cast<u32x4_t*>(kb + prefill_k_at<D>(r, x)) = st.k[i];
+    // the layout stage_v gives a 16-bit V row (32-byte spans permuted by
+    // token), which v_operand's transposing reads expect
+    const int span = (x >> 1) ^ (r & (SPANS - 1));
+    *reinterpret_cast<u32x4_t*>(vb + r * (D * 2) + (span << 5) +
+                                ((x & 1) << 4)) = st.v[i];
+  }
+}
+
+// The tile's K rows as this lane's MFMA A operand (token 16 hh + c, pieces
+// 4 r + j), as load_tile_uniform leaves them in registers.
+template <typename ET, int D>
+using KRegs = uint32_t[2][Shape<ET, ET, D>::KWORDS];
+
+template <typename ET, int D>
+__device__ __forceinline__ void prefill_k_operand(KRegs<ET, D>& kw,
+                                                  const uint8_t* kb, int lane) {
+  typedef Shape<ET, ET, D> S;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int r = 0; r < S::KPIECES; ++r) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+          kb + prefill_k_at<D>(16 * hh + c, 4 * r + j));
+      kw[hh][4 * r + 0] = v[0];
+      kw[hh][4 * r + 1] = v[1];
+      kw[hh][4 * r + 2] = v[2];
+      kw[hh][4 * r + 3] = v[3];
+    }
+  }
+}
+
+template <typename ET, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void attn_prefill_kernel(AttnArgs a) {
+  typedef Shape<ET, ET, D> S;
+  static_assert(ET::bytes == 2, "16-bit caches");
+  constexpr int NG = 4;  // groups per wave
+  constexpr int TILE = 32 * D * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][TILE];
+  __shared__ int sm_wsum[kWaves];
+  extern __shared__ int sm_seq[];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+  const int nS = a.num_seqs;
+  int* tex = sm_seq;
+  int* lens = tex + nS + 1;
+  int* qs0 = lens + nS;
+  int* qn = qs0 + nS;
+
+  // ---- unit counts of all sequences and their exclusive prefix (as in
+  // attn_multi_kernel) ----
+  {
+    const int per = (nS + kThreads - 1) / kThreads;
+    const int b0 = min(tid * per, nS);
+    const int b1 = min(b0 + per, nS);
+    int sum = 0;
+    for (int i = b0; i < b1; ++i) {
+      const MqSeq m = mq_seq(a, i);
+      lens[i] = m.L;
+      qs0[i] = m.q0;
+      qn[i] = m.nq;
+      sum += a.num_kv_heads * ((m.nq + a.row_tokens - 1) / a.row_tokens) *
+             ((m.L + 31) / 32);
+    }
+    const int incl = block_inclusive_scan(sum, sm_wsum);
+    int run = incl - sum;
+    for (int i = b0; i < b1; ++i) {
+      tex[i] = run;
+      run += a.num_kv_heads * ((qn[i] + a.row_tokens - 1) / a.row_tokens) *
+             ((lens[i] + 31) / 32);
+    }
+    if (tid == kThreads - 1) tex[nS] = incl;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)  // the merge kernel reads the prefix from here
+    for (int i = tid; i <= nS; i += kThreads) a.tile_prefix[i] = tex[i];
+
+  const int W = a.num_waves;  // ranges: one per workgroup
+  const int w = blockIdx.x;
+  const int gbase = wave * NG;
+  const int64_t T_all = tex[nS];
+  const int64_t tb = first_tile_of_wave(w, T_all, W);
+  const int64_t te = first_tile_of_wave(w + 1, T_all, W);
+  const int64_t n = te - tb;  // tiles of this workgroup (the same in every wave)
+  const int gmax = a.slot_heads;
+
+  // ---- the loading side: its segment, tile and table windows, and the
+  // next segment's windows ----
+  MSeg LX = mseg_at(tb, te, tex, lens, qs0, qn, a);
+  int64_t lpos_n = tb + LX.ntiles;
+  MSeg LXn = mseg_at(lpos_n, te, tex, lens, qs0, qn, a);
+  int lk = 0;
+  int lwb = LX.wb;
+  uint32_t lta = load_window(LX, 0, a, lane), ltb = load_window(LX, 1, a, lane);
+  uint32_t lta_n = load_window(LXn, 0, a, lane);
+  uint32_t ltb_n = load_window(LXn, 1, a, lane);
+  auto load_next = [&](PrefillStage<D>& st) {
+    const int t0 = LX.valid ? LX.t_begin + 32 * lk : 0;
+    if (LX.valid && t0 / a.block_size - lwb >= 64) {
+      // the window moves on by 64 blocks (at most once per tile)
+      lwb += 64;
+      lta = ltb;
+      Seg shifted = LX;
+      shifted.wb = lwb;
+      ltb = load_window(shifted, 1, a, lane);
+    }
+    prefill_load<ET, D>(st, LX, t0, lta, ltb, lwb, a, tid);
+    if (LX.valid && ++lk == LX.ntiles) {
+      LX = LXn;
+      lk = 0;
+      lwb = LX.wb;
+      lta = lta_n;
+      ltb = ltb_n;
+      lpos_n += LX.ntiles;
+      LXn = mseg_at(lpos_n, te, tex, lens, qs0, qn, a);
+      lta_n = load_window(LXn, 0, a, lane);
+      ltb_n = load_window(LXn, 1, a, lane);
+    }
+  };
+
+  // ---- the computing side ----
+  MSeg X = mseg_at(tb, te, tex, lens, qs0, qn, a);
+  int64_t pos_n = tb + X.ntiles;
+  int k = 0;  // tile within X
+  bool first_seg = true;
+  uint32_t qw[NG][S::QWORDS];
+  int lim[NG];
+  WaveState<S::NBLK> st[NG];
+  const float qk_mul = a.qk_scale_log2;
+  auto start_segment = [&]() {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      load_query_mq<ET, ET, D>(qw[g], X, a, gbase + g, lane);
+      lim[g] = mq_limit(X, a, gbase + g, lane);
+      st[g].m = -INFINITY;
+      st[g].l = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < S::NBLK; ++nb)
+        st[g].o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto finish_segment = [&]() {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float l_tot = xor_sum(st[g].l, 16);
+      l_tot = xor_sum(l_tot, 32);
+      const int tok = mq_token(X, a, gbase + g, c);
+      if (tok < 0) continue;
+      if (X.full) {
+        const int64_t row = (int64_t)(X.q0 + tok) * a.num_q_heads +
+                            X.h * a.group + c % a.group;
+        const float f = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float* dst = a.out + row * D + 4 * j;
+#pragma unroll
+        for (int nb = 0; nb < S::NBLK; ++nb)
+          *reinterpret_cast<f32x4_t*>(dst + 16 * nb) = st[g].o[nb] * f;
+      } else {
+        // slot column: the token's place in the row times G plus the head
+        const int64_t sl = slot_index(w, first_seg ? 0 : 1) * gmax +
+                           (gbase + g) * a.tpr * a.group + c;
+        float* dst = a.part_o + sl * D + 4 * j;
+#pragma unroll
+        for (int nb = 0; nb < S::NBLK; ++nb)
+          *reinterpret_cast<f32x4_t*>(dst + 16 * nb) = st[g].o[nb];
+        if (j == 0) {
+          a.part_m[sl] = st[g].m;
+          a.part_l[sl] = l_tot;
+        }
+      }
+    }
+  };
+  // tile p of the range: its loads were issued two steps back and its LDS
+  // buffer filled one step back; it fills the other buffer with tile p + 1
+  // (held in `next`), reloads `next` with tile p + 3, computes, and the
+  // barrier both publishes tile p + 1 and frees buffer b for tile p + 2
+  auto tile_step = [&](PrefillStage<D>& next, int b) {
+    prefill_store<D>(next, kbuf[b ^ 1], vbuf[b ^ 1], tid);
+    load_next(next);
+    if (k == 0) start_segment();
+    const int t0 = X.t_begin + 32 * k;
+    if (t0 < X.t_end) {  // (tiles past the row's columns hold nothing)
+      uint32_t kw[2][S::KWORDS];
+      prefill_k_operand<ET, D>(kw, kbuf[b], lane);
+      compute_tile_groups<ET, ET, D, NG, false, true>(kw, qw, st, vbuf[b],
+                                                      t0, lim, qk_mul, lane);
+    }
+    __syncthreads();
+    if (++k == X.ntiles) {
+      finish_segment();
+      first_seg = false;
+      X = mseg_at(pos_n, te, tex, lens, qs0, qn, a);
+      pos_n += X.ntiles;
+      k = 0;
+    }
+  };
+
+  if (n > 0) {
+    PrefillStage<D> A, B;
+    load_next(A);  // tile 0
+    load_next(B);  // tile 1
+    prefill_store<D>(A, kbuf[0], vbuf[0], tid);
+    load_next(A);  // tile 2
+    __syncthreads();
+    for (int64_t p = 0; p < n; p += 2) {
+      tile_step(B, 0);                  // tile p (buffer 0), B: p+1 -> p+3
+      if (p + 1 < n) tile_step(A, 1);   // tile p+1 (buffer 1), A: p+2 -> p+4
+    }
+  }
+}
+
 // Merge of a cut multi-query row: workgroup (s, h, rr) over a grid of
 // num_seqs * num_kv_heads * max_rps (rows past a sequence's count exit).
 template <int D, bool SCALED, int BATCH>
@@ -453,9 +761,36 @@ static hipError_t launch_mu(AttnArgs a, int max_waves, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename ET, int D>
+static hipError_t launch_prefill(AttnArgs a, int max_waves,
+                                 hipStream_t stream) {
+  auto kernel = attn_prefill_kernel<ET, D>;
+  const size_t dyn = ((size_t)4 * a.num_seqs + 1) * sizeof(int);
+  // ranges of 16 groups: the workspace's 1024 * 4 group slots per slot
+  // pair hold 256 of them
+  const int cap = max_waves > 0 && max_waves < kMaxWavesMulti ? max_waves
+                                                              : kMaxWavesMulti;
+  const int grid = resident_grid(kernel, dyn, cap);
+  if (grid < 0) return hipErrorInvalidValue;
+  a.num_waves = grid;  // one range per workgroup
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
+  const int64_t rows = (int64_t)a.num_seqs * a.num_kv_heads * a.max_rps;
+  if (rows > 0 && a.num_waves >= 4 * rows)
+    hipLaunchKernelGGL((attn_multi_merge_kernel<D, false, 16>),
+                       dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
+  else if (rows > 0)
+    hipLaunchKernelGGL((attn_multi_merge_kernel<D, false, 4>),
+                       dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <typename QT, typename CT, int D>
 static hipError_t launch_md(const AttnArgs& a, int max_waves, bool uniform,
                             hipStream_t stream) {
+  if constexpr (same<QT, CT>::value && QT::bytes == 2) {
+    if (a.row_tokens / a.tpr == kPrefillGroups)
+      return launch_prefill<QT, D>(a, max_waves, stream);
+  }
   if constexpr (is_fp8<CT>::value) {
     if (a.scale_per_token) {
       if constexpr (!same<QT, F32>::value) {
@@ -487,11 +822,18 @@ static hipError_t launch_mt(const AttnArgs& a, int head_dim, int max_waves,
   return launch_md<QT, CT, 128>(a, max_waves, uniform, stream);
 }
 
-int multi_groups_per_row(int q_dtype, int max_query_len, int tpr) {
+int multi_groups_per_row(int q_dtype, int cache_dtype, bool uniform,
+                         bool token_scales, int max_query_len, int tpr) {
+  const int groups = (max_query_len + tpr - 1) / tpr;
+  // workgroup rows of 16 groups for long query runs on 16-bit caches with
+  // block_size % 16 == 0
+  if (q_dtype == cache_dtype && (q_dtype == PKV_BF16 || q_dtype == PKV_F16) &&
+      uniform && !token_scales && groups >= 12)
+    return kPrefillGroups;
   // four groups once a row would hold three or more (float32 queries keep
   // one: their operands alone fill the registers)
   if (q_dtype == PKV_F32) return 1;
-  return (max_query_len + tpr - 1) / tpr >= 3 ? 4 : 1;
+  return groups >= 3 ? 4 : 1;
 }
 
 hipError_t launch_attn_multi(const AttnArgs& a, int q_dtype, int cache_dtype,

@@ -363,7 +363,18 @@ __device__ __forceinline__ void qk_tile(
 // to the PV product stay in (0, 1] whatever the scales' range, and O^T is
 // rescaled by 2^(mv_old - mv_new) as the sum l is by 2^(m_old - m_new).
 // fold_value_scales turns O^T back into units of 2^m at the end.
-template <typename QT, typename CT, int D, bool CAUSAL, bool PT = false>
+//
+// LAZY: the reference maximum moves only when a tile's maximum exceeds it by
+// more than kLazyMargin (log2 units), so weights reach at most
+// 2^kLazyMargin and O^T and l are rescaled only on those (rare) steps -- a
+// wave-uniform branch skips the multiply of the accumulators otherwise.  The
+// result is the same softmax with another reference point (m is what the
+// partials and the merge carry); the PV weights keep the hi + lo split's
+// precision relative to their size.
+constexpr float kLazyMargin = 8.f;
+
+template <typename QT, typename CT, int D, bool CAUSAL, bool PT = false,
+          bool LAZY = false>
 __device__ __forceinline__ void softmax_tile(
     const f32x4_t (&sacc)[2], WaveState<Shape<QT, CT, D>::NBLK>& st, int t0,
     int t_end, int lim, float qk_mul, int lane,
@@ -392,9 +403,13 @@ __device__ __forceinline__ void softmax_tile(
   for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
   mx = xor_max(mx, 16);
   mx = xor_max(mx, 32);
-  const float m_new = fmaxf(st.m, mx);
+  // (LAZY: keep the old reference unless the tile's maximum passes it by
+  // more than the margin; -inf + margin is -inf, so a first finite
+  // maximum always moves it)
+  const bool grow = !LAZY || mx > st.m + kLazyMargin;
+  const float m_new = LAZY ? (grow ? mx : st.m) : fmaxf(st.m, mx);
   const float m_use = CAUSAL && m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - m_use);
+  const float alpha = grow ? fast_exp2(st.m - m_use) : 1.f;
   float pv[8];
   float psum = 0.f;
 #pragma unroll
@@ -405,6 +420,7 @@ __device__ __forceinline__ void softmax_tile(
   st.l = st.l * alpha + psum;
   st.m = m_new;
   float orescale = alpha;
+  static_assert(!(PT && LAZY), "per-token scales use the eager update");
   if constexpr (PT) {
     float u[8];
     float mxv = -INFINITY;
@@ -422,8 +438,10 @@ __device__ __forceinline__ void softmax_tile(
     for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(u[e] - mv_use);
     st.mv = mv_new;
   }
+  if (!LAZY || __builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-  for (int n = 0; n < S::NBLK; ++n) st.o[n] *= orescale;
+    for (int n = 0; n < S::NBLK; ++n) st.o[n] *= orescale;
+  }
 
   if constexpr (PVB == 2) {
 #pragma unroll
@@ -498,7 +516,8 @@ __device__ __forceinline__ void compute_tile(
 
 // One tile for NG 16-column groups of query columns (causal limits per
 // group): the tile's K registers and each V^T read serve every group.
-template <typename QT, typename CT, int D, int NG, bool PT = false>
+template <typename QT, typename CT, int D, int NG, bool PT = false,
+          bool LAZY = false>
 __device__ __forceinline__ void compute_tile_groups(
     const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS],
     const uint32_t (&qw)[NG][Shape<QT, CT, D>::QWORDS],
@@ -511,8 +530,9 @@ __device__ __forceinline__ void compute_tile_groups(
   for (int g = 0; g < NG; ++g) {
     f32x4_t sacc[2];
     qk_tile<QT, CT, D>(kw, qw[g], sacc);
-    softmax_tile<QT, CT, D, true, PT>(sacc, st[g], t0, 0, lim[g], qk_mul,
-                                      lane, pb_hi[g], pb_lo[g], sc);
+    softmax_tile<QT, CT, D, true, PT, LAZY>(sacc, st[g], t0, 0, lim[g],
+                                            qk_mul, lane, pb_hi[g], pb_lo[g],
+                                            sc);
   }
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) {

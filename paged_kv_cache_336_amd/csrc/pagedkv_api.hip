@@ -504,7 +504,9 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
                          dtype_bytes(q_dtype);
   if (qbytes >= ((int64_t)1 << 31)) return PKV_ERR_SHAPE;
   const int32_t tpr = 16 / s.group;
-  const int32_t ng = multi_groups_per_row(q_dtype, max_query_len, tpr);
+  const int32_t ng =
+      multi_groups_per_row(q_dtype, cache_dtype, block_size % 16 == 0,
+                           per_token, max_query_len, tpr);
   const int32_t max_rps = (max_query_len + ng * tpr - 1) / (ng * tpr);
   // every unit index of the call, and the merge grid, fit an int32
   const int64_t rows = (int64_t)num_seqs * num_kv_heads * max_rps;

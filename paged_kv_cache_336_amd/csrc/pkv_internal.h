@@ -21,7 +21,8 @@ constexpr int kMaxWavesMulti = 1024;
 constexpr int kMaxGroupsMulti = 4;
 
 // Column groups per row of paged_attn_multi for these arguments.
-int multi_groups_per_row(int q_dtype, int max_query_len, int tpr);
+int multi_groups_per_row(int q_dtype, int cache_dtype, bool uniform,
+                         bool token_scales, int max_query_len, int tpr);
 
 // Most waves of the partition kernel (16 per CU of a 256-CU part); the
 // workspace holds two partial slots per wave.
