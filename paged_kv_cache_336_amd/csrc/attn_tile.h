@@ -62,8 +62,10 @@ template <typename QT, typename CT, int D> struct Shape {
 };
 
 // One tile's raw K and V bytes as loaded from the pool, per sub-tile; with
-// per-token fp8 scales also the tile's scales: lane i < 32 holds token i's
-// key scale, lane 32 + i its value scale.
+// per-token fp8 scales also the tile's scales, one per lane: lane c + 16 j
+// holds the key (c < 8) or value (c >= 8) scale of the token in score slot
+// c % 8 of row group j (slot_token(j, c % 8)), so each 16-lane row holds
+// exactly the 16 scales its score slots need (see softmax_tile).
 template <typename QT, typename CT, int D> struct TileRegs {
   typedef Shape<QT, CT, D> S;
   uint32_t kw[S::SUB][2][S::KWORDS];
@@ -169,13 +171,14 @@ __device__ __forceinline__ void load_tile_uniform(
           vr[hh], vofs + tin * (int)stride, 0, 0);
     }
     if constexpr (PT) {
-      // lane (i + 32 kv): token i's key (kv 0) or value (kv 1) scale
-      const int hl = (lane >> 4) & 1;
-      const int tin = lane & 15;
-      const int64_t slot = (hl ? first_slot[1] : first_slot[0]) + tin;
+      // score slot c % 8: token 4 j + c % 4 of half (c / 4) % 2 (0 past
+      // the half's live rows)
+      const int hl = (c >> 2) & 1;
+      const int t = 4 * j + (c & 3);
       tr.sc[sb] = 0.f;
-      if (tin < (hl ? live[1] : live[0]))
-        tr.sc[sb] = (lane < 32 ? tsc.k : tsc.v)[slot * tsc.hkv];
+      if (t < (hl ? live[1] : live[0]))
+        tr.sc[sb] = (c < 8 ? tsc.k : tsc.v)[
+            ((hl ? first_slot[1] : first_slot[0]) + t) * tsc.hkv];
     }
   }
 }
@@ -225,10 +228,12 @@ __device__ __forceinline__ void load_tile_any(
         tr.vraw[sb][v] = *reinterpret_cast<const u32x4_t*>(
             vbase + (int64_t)vs * stride + (lane % S::PPR) * 16);
     }
-    if constexpr (PT) {  // lane (i + 32 kv): token i's key / value scale
+    if constexpr (PT) {  // score slot c % 8's token (see TileRegs)
+      const int t = slot_token(j, c & 7);
+      const int st = __shfl(myslot, t, 64);
       tr.sc[sb] = 0.f;
-      if (tok < t_end)
-        tr.sc[sb] = (lane < 32 ? tsc.k : tsc.v)[(int64_t)myslot * tsc.hkv];
+      if (ts + t < t_end)
+        tr.sc[sb] = (c < 8 ? tsc.k : tsc.v)[(int64_t)st * tsc.hkv];
     }
   }
 }
@@ -387,14 +392,17 @@ __device__ __forceinline__ void softmax_tile(
   const int j = lane >> 4;
   float sv[8];
   float lvs[8];  // PT: log2 of each token's value scale
+  // PT: lanes 8..15 of each row hold value scales: their log2, then lane e
+  // (key scale) and 8 + e (log2 value scale) of the row serve slot e
+  const float own = PT && (lane & 8) ? __builtin_amdgcn_logf(sc) : sc;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
     const bool live = t0 + slot_token(j, e) < (CAUSAL ? lim : t_end);
     float mul = qk_mul;
     if constexpr (PT) {
-      mul *= __shfl(sc, slot_token(j, e), 64);
-      lvs[e] = __builtin_amdgcn_logf(__shfl(sc, 32 + slot_token(j, e), 64));
+      mul *= row_broadcast(own, e);
+      lvs[e] = row_broadcast(own, 8 + e);
     }
     sv[e] = live ? raw * mul : -INFINITY;
   }

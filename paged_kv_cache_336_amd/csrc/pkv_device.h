@@ -177,6 +177,25 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// The value of lane n (0..15) of this lane's 16-lane row: a DPP
+// row_newbcast move (the control must be a constant; unrolled callers fold
+// the switch).
+__device__ __forceinline__ float row_broadcast(float v, int n) {
+  const int x = __float_as_int(v);
+  int r;
+#define PKV_ROW_BCAST(k) \
+  case k: r = __builtin_amdgcn_update_dpp(0, x, 0x150 + k, 0xF, 0xF, false); break;
+  switch (n) {
+    PKV_ROW_BCAST(0) PKV_ROW_BCAST(1) PKV_ROW_BCAST(2) PKV_ROW_BCAST(3)
+    PKV_ROW_BCAST(4) PKV_ROW_BCAST(5) PKV_ROW_BCAST(6) PKV_ROW_BCAST(7)
+    PKV_ROW_BCAST(8) PKV_ROW_BCAST(9) PKV_ROW_BCAST(10) PKV_ROW_BCAST(11)
+    PKV_ROW_BCAST(12) PKV_ROW_BCAST(13) PKV_ROW_BCAST(14)
+    default: r = __builtin_amdgcn_update_dpp(0, x, 0x15F, 0xF, 0xF, false); break;
+  }
+#undef PKV_ROW_BCAST
+  return __int_as_float(r);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }

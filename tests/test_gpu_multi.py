@@ -189,3 +189,28 @@ def test_multi_per_head_scales(kv_kind):
     _, out = run_multi(mq)
     err = max_abs_err(out, oracle_multi(mq, oracle_pools(mq.w)))
     assert err <= TOL[kv_kind], f"{err:.3g}"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+def test_long_runs_with_growing_scores(kv):
+    """Long query runs (the workgroup rows of 16 groups) over keys whose
+    size grows with their position, so the running maximum keeps moving
+    past the lazy-rescale margin tile after tile: every rescale step is
+    taken, and the result still matches the oracle."""
+    lens, qlens = [700, 1200, 300], [200, 64, 300]
+    mq = W.custom_multi(seed=88, lens=lens, qlens=qlens, hq=16, hkv=4,
+                        d=128, bs=16, q_kind=kv, kv_kind=kv)
+    w = mq.w
+    k = oracle.to_float64(w.k_pool, kv).astype(np.float32)
+    for s, L in enumerate(lens):
+        for t in range(L):
+            b, o = int(w.block_tables[s, t // 16]), t % 16
+            k[b, o] *= np.float32(1 + t / 6)
+    w.k_pool[...] = W._cast_from_f32(k, kv)
+    say(f"multi growing scores {kv}")
+    for waves in (0, 8):
+        _, out = run_multi(mq, max_waves=waves)
+        ref = oracle_multi(mq, oracle_pools(mq.w))
+        err = max_abs_err(out, ref)
+        say(f"  waves {waves}: max abs err {err:.3g}")
+        assert err <= TOL[kv], f"waves {waves}: {err:.3g}"
