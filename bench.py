@@ -341,6 +341,13 @@ def bench_multi(args):
 
     mq = W.MULTI_WORKLOADS[args.workload](replicas=args.replicas)
     w = mq.w
+    # the library's choice of partition kernel: workgroup rows of 16
+    # column groups for 12 or more groups of new tokens on a 16-bit cache
+    # the queries share, block_size % 16 == 0
+    G = w.num_q_heads // w.num_kv_heads
+    long_rows = (w.q_kind == w.kv_kind and w.kv_kind in ("bf16", "f16") and
+                 w.block_size % 16 == 0 and
+                 -(-mq.max_query_len // (16 // G)) >= 12)
     dev = MultiStep(mq, device="cuda:0")
     R = len(dev.sets)
     cost = multi_algorithmic(mq)
@@ -380,8 +387,9 @@ def bench_multi(args):
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(attn_gbps / HBM_PEAK_GBPS, 4)}
     roof.update({
-        "kernel": "paged_attn_multi (attn_multi_kernel + "
-                  "attn_multi_merge_kernel)",
+        "kernel": "paged_attn_multi (" + (
+            "attn_prefill_kernel" if long_rows else "attn_multi_kernel") +
+            " + attn_multi_merge_kernel)",
         "traffic": load_traffic(args.traffic_json, args.workload,
                                 MULTI_SOURCES),
         "algorithmic_bytes_per_launch": B,
