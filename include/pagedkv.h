@@ -387,13 +387,18 @@ size_t paged_attn_multi_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * per sequence (query_start[s] = s) the result is paged_attn_decode's, bit
  * for bit.
  *
- * Work split: the 16 query columns of an MFMA tile hold 16 / G new tokens of
- * all G = num_q_heads / num_kv_heads heads of one kv head, so the keys and
- * values of a sequence are read once per 16 / G new tokens; all 32-token
- * tiles of all such rows are divided evenly among the waves and split rows
- * are merged by log-sum-exp, as in paged_attn_decode.  At most 4096 sequences
- * and G <= 16 (PKV_ERR_UNSUPPORTED beyond); the query tensor below 2 GiB and
- * num_seqs * num_kv_heads * ceil(max_query_len / (16 / G)) *
+ * Work split: the 16 query columns of an MFMA tile (a group) hold 16 / G new
+ * tokens of all G = num_q_heads / num_kv_heads heads of one kv head, and a
+ * row of NG groups reads a sequence's keys and values once for its
+ * NG * 16 / G new tokens: NG = 1 for short runs (drafted tokens), 4 for
+ * longer ones, and 16 -- a row per workgroup, the tiles staged through LDS
+ * -- when max_query_len fills 12 or more groups on a 16-bit cache that the
+ * queries share, with block_size % 16 == 0 and no per-token scales.  All
+ * 32-token tiles of all rows are divided evenly among the waves (or
+ * workgroups) and split rows are merged by log-sum-exp, as in
+ * paged_attn_decode.  At most 4096 sequences and G <= 16
+ * (PKV_ERR_UNSUPPORTED beyond); the query tensor below 2 GiB and
+ * num_seqs * num_kv_heads * ceil(max_query_len / (NG * 16 / G)) *
  * ceil(max_seq_len / 32) < 2^31 (PKV_ERR_SHAPE beyond).  A call with no query
  * token launches nothing.
  */
