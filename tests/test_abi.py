@@ -204,9 +204,13 @@ def test_multi_validation(lib):
     assert pm(lib, maxq=4097) == SHAPE                  # above max_seq_len
     assert pm(lib, T=1 << 17, hq=64, hkv=8) == SHAPE    # query of 2 GiB
     assert pm(lib, mb=255) == SHAPE                     # table too short
-    # unit indices beyond int32: 4096 seqs x 16 kv heads x 4096 rows x 2^10
-    assert pm(lib, S=4096, hq=16, hkv=16, maxq=4096, maxlen=32768,
-              mb=2048) == SHAPE
+    # unit indices beyond int32 with rows of one group (float32): 4096 seqs
+    # x 16 kv heads x 256 rows x 2^10 tiles; with the 16-group rows of a
+    # 16-bit cache the same call fits, and 2^12 tiles do not
+    assert pm(lib, qd=F32, cache=F32, S=4096, hq=16, hkv=16, maxq=4096,
+              maxlen=32768, mb=2048) == SHAPE
+    assert pm(lib, S=4096, hq=16, hkv=16, maxq=4096, maxlen=131072,
+              mb=8192) == SHAPE
     assert pm(lib, out=None) == NULL
     assert pm(lib, qs=None) == NULL
     assert pm(lib, qs=ctypes.c_void_p(4096 + 2)) == ALIGN
