@@ -391,7 +391,7 @@ size_t paged_attn_multi_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * tokens of all G = num_q_heads / num_kv_heads heads of one kv head, and a
  * row of NG groups reads a sequence's keys and values once for its
  * NG * 16 / G new tokens: NG = 1 for short runs (drafted tokens), 4 for
- * longer ones, and 16 -- a row per workgroup, the tiles staged through LDS
+ * longer ones, and 8 -- a row per workgroup, the tiles staged through LDS
  * -- when max_query_len fills 12 or more groups on a 16-bit cache that the
  * queries share, with block_size % 16 == 0 and no per-token scales.  All
  * 32-token tiles of all rows are divided evenly among the waves (or

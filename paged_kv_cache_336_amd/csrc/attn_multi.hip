@@ -398,20 +398,24 @@ void attn_multi_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Long query runs (a prompt chunk against its cached prefix), 16-bit caches
-// with block_size % 16 == 0: rows of kPrefillGroups = 16 column groups, one
+// with block_size % 16 == 0: rows of kPrefillGroups = 8 column groups, one
 // row per workgroup at a time.  The split is over workgroups; the four waves
-// walk the same tiles in lockstep, wave w computing groups 4w .. 4w + 3, and
+// walk the same tiles in lockstep, wave w computing groups 2w, 2w + 1, and
 // each tile's K and V rows are loaded once per workgroup: every thread
 // fetches 1/256 of the tile into registers two tiles ahead, stores it into
 // one of two LDS buffers one tile ahead, and all waves read the tile from
 // LDS (K rows XOR-swizzled by 16-byte piece for conflict-free operand
 // reads, V rows in the span-permuted layout the transposing reads use).  So
-// a sequence's K/V is read once per 16 * tpr new tokens (64 at G = 4), and a
-// tile's loads are in flight for two tile steps of the whole workgroup
-// instead of one wave's, while each wave keeps four groups' state without a
-// tile of its own in registers.
+// a sequence's K/V is read once per 8 * tpr new tokens (32 at G = 4), and a
+// tile's loads are in flight for two tile steps of the whole workgroup.
+// Two groups per wave keep a wave under 256 registers, so two workgroups
+// share each CU and one wave's softmax overlaps the other's MFMAs (one
+// wave per SIMD with four groups each left the matrix cores idle during
+// every softmax).
 // ---------------------------------------------------------------------------
-constexpr int kPrefillGroups = 4 * kWaves;
+constexpr int kPrefillGPW = 2;                  // groups per wave
+constexpr int kPrefillGroups = kPrefillGPW * kWaves;
+constexpr int kPrefillWGsPerCU = 2;             // two waves per SIMD
 
 // One thread's share of a tile's K and V rows (16-byte pieces q = tid + 256 i
 // of the tile's 32 x D/8 pieces: token q / (D/8), piece q % (D/8)).
@@ -521,11 +525,12 @@ __device__ __forceinline__ void prefill_k_operand(KRegs<ET, D>& kw,
 }
 
 template <typename ET, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kPrefillWGsPerCU)))
 void attn_prefill_kernel(AttnArgs a) {
   typedef Shape<ET, ET, D> S;
   static_assert(ET::bytes == 2, "16-bit caches");
-  constexpr int NG = 4;  // groups per wave
+  constexpr int NG = kPrefillGPW;  // groups per wave
   constexpr int TILE = 32 * D * 2;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][TILE];
@@ -766,11 +771,12 @@ static hipError_t launch_prefill(AttnArgs a, int max_waves,
                                  hipStream_t stream) {
   auto kernel = attn_prefill_kernel<ET, D>;
   const size_t dyn = ((size_t)4 * a.num_seqs + 1) * sizeof(int);
-  // ranges of 16 groups: the workspace's 1024 * 4 group slots per slot
-  // pair hold 256 of them
-  const int cap = max_waves > 0 && max_waves < kMaxWavesMulti ? max_waves
-                                                              : kMaxWavesMulti;
-  const int grid = resident_grid(kernel, dyn, cap);
+  // ranges of kPrefillGroups groups: the workspace's 1024 * 4 group slots
+  // per slot pair hold 4096 / kPrefillGroups of them
+  constexpr int kMaxRanges = kMaxWavesMulti * kMaxGroupsMulti / kPrefillGroups;
+  const int cap = max_waves > 0 && max_waves < kMaxRanges * kWaves
+                      ? max_waves : kMaxRanges * kWaves;
+  const int grid = resident_grid(kernel, dyn, cap, kPrefillWGsPerCU);
   if (grid < 0) return hipErrorInvalidValue;
   a.num_waves = grid;  // one range per workgroup
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
@@ -788,7 +794,7 @@ template <typename QT, typename CT, int D>
 static hipError_t launch_md(const AttnArgs& a, int max_waves, bool uniform,
                             hipStream_t stream) {
   if constexpr (same<QT, CT>::value && QT::bytes == 2) {
-    if (a.row_tokens / a.tpr == kPrefillGroups)
+    if (uniform && a.row_tokens / a.tpr == kPrefillGroups)
       return launch_prefill<QT, D>(a, max_waves, stream);
   }
   if constexpr (is_fp8<CT>::value) {
@@ -825,8 +831,8 @@ static hipError_t launch_mt(const AttnArgs& a, int head_dim, int max_waves,
 int multi_groups_per_row(int q_dtype, int cache_dtype, bool uniform,
                          bool token_scales, int max_query_len, int tpr) {
   const int groups = (max_query_len + tpr - 1) / tpr;
-  // workgroup rows of 16 groups for long query runs on 16-bit caches with
-  // block_size % 16 == 0
+  // workgroup rows of kPrefillGroups groups for long query runs on 16-bit
+  // caches with block_size % 16 == 0
   if (q_dtype == cache_dtype && (q_dtype == PKV_BF16 || q_dtype == PKV_F16) &&
       uniform && !token_scales && groups >= 12)
     return kPrefillGroups;

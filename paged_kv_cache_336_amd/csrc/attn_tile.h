@@ -750,7 +750,8 @@ __device__ __forceinline__ uint32_t load_window(const Seg& g, int half,
 // Workgroups of the partition kernel: as many as can be resident at once
 // (occupancy x CUs), capped by the caller's wave limit and kMaxWaves.
 template <typename K>
-static int resident_grid(K kernel, size_t dyn_lds, int max_waves) {
+static int resident_grid(K kernel, size_t dyn_lds, int max_waves,
+                         int per_cu_cap = kWorkgroupsPerCU) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
@@ -762,7 +763,7 @@ static int resident_grid(K kernel, size_t dyn_lds, int max_waves) {
   // One workgroup (one wave per SIMD) per CU measured fastest for the
   // streaming loop: more resident waves deepen the memory queues without
   // adding bandwidth.
-  int64_t g = (int64_t)(per_cu < kWorkgroupsPerCU ? per_cu : kWorkgroupsPerCU) * cus;
+  int64_t g = (int64_t)(per_cu < per_cu_cap ? per_cu : per_cu_cap) * cus;
   if (g < cus) g = cus;
   int64_t cap = kMaxWaves / kWaves;
   if (max_waves > 0 && max_waves / kWaves < cap) cap = max_waves / kWaves;
