@@ -586,7 +586,8 @@ def main():
                                       k_scale=dev.k_scale, v_scale=dev.v_scale,
                                       max_waves=args.max_waves,
                                       workspace=dev.workspace,
-                                      cache_kind=dev.cache_kind)
+                                      cache_kind=dev.cache_kind,
+                                      kv_stream=dev.sets[0]["kv_stream"])
         run_contig()
         contig_total, _ = timed_region(torch, clock, run_contig,
                                        host_step_ms * K)
@@ -659,6 +660,8 @@ def main():
             "max_seq_len": w.max_seq_len,
             "replicas": R,
             "max_waves": args.max_waves,
+            # PKV_KV_STREAM: passed when no block is read by two sequences
+            "kv_stream_hint": bool(dev.sets[0]["kv_stream"]),
         },
         "step": ("copy_blocks + paged_attn_decode_fused (write and "
                  "attention in one launch)" if fused else

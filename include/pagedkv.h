@@ -90,6 +90,19 @@ typedef enum pkv_dtype {
 #define PKV_SCALE_PER_HEAD 0x100
 #define PKV_SCALE_PER_TOKEN 0x200
 
+/* Cache-policy hint, OR-ed into any call's cache dtype argument: the caller
+ * states that no physical block is read by more than one sequence of the
+ * call (no shared prefix, no forked samples).  paged_attn_decode and
+ * paged_attn_decode_fused then fetch K/V rows of 256 bytes or more
+ * (head_dim * element size) with non-temporal loads, which measured faster
+ * on such batches; without the hint the rows go through the caches, so a
+ * block shared by several sequences is served from them after its first
+ * read (the pages' copy-on-write sharing: "PagedAttention",
+ * shubhamtatvamasi.com, section "Sharing and copy-on-write").  The hint
+ * changes no result, only speed, and is wrong-but-harmless if untrue (shared
+ * blocks are then re-read from HBM).  The other calls accept and ignore it. */
+#define PKV_KV_STREAM 0x400
+
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_NULL = 1,        /* a required pointer is NULL                   */

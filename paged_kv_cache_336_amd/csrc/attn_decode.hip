@@ -216,7 +216,7 @@ __device__ __forceinline__ void wait_stores() {
 // PT: per-token fp8 scales (a.k_scale / a.v_scale are [num_blocks,
 // block_size, num_kv_heads] arrays read beside the rows).
 template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE,
-          bool PT = false>
+          bool PT = false, int AUX = 0>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_decode_kernel(AttnArgs a) {
   typedef Shape<QT, CT, D> S;
@@ -323,7 +323,7 @@ void attn_decode_kernel(AttnArgs a) {
   };
   TileRegs<QT, CT, D> cur;
   if constexpr (PREFETCH)
-    load_tile_uniform<QT, CT, D, PT>(cur, a.block_size, a.num_blocks, ta, tbw,
+    load_tile_uniform<QT, CT, D, PT, AUX>(cur, a.block_size, a.num_blocks, ta, tbw,
                                      X.wb, kpool + (int64_t)X.h * S::ROW_BYTES,
                                      vpool + (int64_t)X.h * S::ROW_BYTES,
                                      stride, X.t_begin, X.t_end, lane,
@@ -376,7 +376,7 @@ void attn_decode_kernel(AttnArgs a) {
           tbw = load_window(shifted, 1, a, lane);
         }
         TileRegs<QT, CT, D> nxt;
-        load_tile_uniform<QT, CT, D, PT>(
+        load_tile_uniform<QT, CT, D, PT, AUX>(
             nxt, a.block_size, a.num_blocks, same_seg ? ta : ta_n, same_seg ? tbw : tb_n,
             same_seg ? wb : Xn.wb, same_seg ? kbase : kbase_n,
             same_seg ? vbase : vbase_n, stride,
@@ -406,7 +406,7 @@ void attn_decode_kernel(AttnArgs a) {
           shifted.wb = wb;
           const uint32_t wa = load_window(shifted, 0, a, lane);
           const uint32_t wbb = load_window(shifted, 1, a, lane);
-          load_tile_uniform<QT, CT, D, PT>(cur, a.block_size, a.num_blocks,
+          load_tile_uniform<QT, CT, D, PT, AUX>(cur, a.block_size, a.num_blocks,
                                            wa, wbb, wb, kbase, vbase, stride,
                                            t0, X.t_end, lane, tsc);
         } else {
@@ -488,9 +488,9 @@ template <> struct DtypeCode<FP8> { static constexpr int value = PKV_FP8_E4M3; }
 template <> struct DtypeCode<FP8E5> { static constexpr int value = PKV_FP8_E5M2; };
 
 template <typename QT, typename CT, int D, bool UNIFORM, bool WRITE,
-          bool PT = false>
+          bool PT = false, int AUX = 0>
 static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
-  auto kernel = attn_decode_kernel<QT, CT, D, UNIFORM, WRITE, PT>;
+  auto kernel = attn_decode_kernel<QT, CT, D, UNIFORM, WRITE, PT, AUX>;
   constexpr bool SCALED = is_fp8<CT>::value && !PT;  // merge: output scale
   const size_t dyn = ((size_t)2 * a.num_seqs + 1) * sizeof(int);
   const int grid = resident_grid(kernel, dyn, max_waves);
@@ -518,7 +518,8 @@ static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
       const hipError_t e = launch_cache_write(w, DtypeCode<QT>::value,
                                               DtypeCode<CT>::value, stream);
       if (e != hipSuccess) return e;
-      return launch_u<QT, CT, D, UNIFORM, false>(a, max_waves, stream);
+      return launch_u<QT, CT, D, UNIFORM, false, false, AUX>(a, max_waves,
+                                                             stream);
     }
   }
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
@@ -545,6 +546,19 @@ static hipError_t launch_d(const AttnArgs& a, int max_waves, bool uniform,
       if (uniform)
         return launch_u<QT, CT, D, true, false, true>(a, max_waves, stream);
       return launch_u<QT, CT, D, false, false, true>(a, max_waves, stream);
+    }
+  }
+  // Rows of 256 bytes or more of a batch whose blocks no two sequences share
+  // stream with non-temporal loads (measured faster on unshared 16-bit
+  // batches; shared prefixes need the caches, and 128-byte fp8 rows measured
+  // slower with the streaming policy).
+  if constexpr (D * CT::bytes >= 256) {
+    if (uniform && a.kv_stream) {
+      if (fused)
+        return launch_u<QT, CT, D, true, true, false, kLoadNT>(a, max_waves,
+                                                               stream);
+      return launch_u<QT, CT, D, true, false, false, kLoadNT>(a, max_waves,
+                                                              stream);
     }
   }
   if (fused) {

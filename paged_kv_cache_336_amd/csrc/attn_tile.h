@@ -15,6 +15,10 @@ constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWorkgroupsPerCU = 1;       // default grid: one workgroup per CU
 constexpr uint32_t kRawBufferFlags = 0x00020000;  // dword3: 32-bit data format
+// Cache-policy operand of a buffer load: 0 = the default policy; kLoadNT
+// sets the non-temporal (streaming) bit, for K/V rows that no other wave of
+// the call reads again.
+constexpr int kLoadNT = 2;
 
 template <typename QT, typename CT> struct PvOperand { typedef CT type; };
 template <> struct PvOperand<BF16, FP8> { typedef F16 type; };
@@ -100,7 +104,7 @@ template <int NBLK> struct WaveState {
 // two VGPRs: lane i of tab_a / tab_b holds the entry of logical block
 // wb + i / wb + 64 + i, and a wave-uniform readlane turns it into a scalar.
 // ---------------------------------------------------------------------------
-template <typename QT, typename CT, int D, bool PT = false>
+template <typename QT, typename CT, int D, bool PT = false, int AUX = 0>
 __device__ __forceinline__ void load_tile_uniform(
     TileRegs<QT, CT, D>& tr, int bs, int nblocks, uint32_t tab_a,
     uint32_t tab_b, int wb, const uint8_t* kbase, const uint8_t* vbase,
@@ -155,7 +159,7 @@ __device__ __forceinline__ void load_tile_uniform(
 #pragma unroll
       for (int r = 0; r < S::KPIECES; ++r) {
         const u32x4_t v =
-            __builtin_amdgcn_raw_buffer_load_b128(kr[hh], kofs + r * 64, 0, 0);
+            __builtin_amdgcn_raw_buffer_load_b128(kr[hh], kofs + r * 64, 0, AUX);
         tr.kw[sb][hh][4 * r + 0] = v[0];
         tr.kw[sb][hh][4 * r + 1] = v[1];
         tr.kw[sb][hh][4 * r + 2] = v[2];
@@ -168,7 +172,7 @@ __device__ __forceinline__ void load_tile_uniform(
       const int tin = (v * S::TOK_PER_V) & 15;
       // the whole offset goes in the per-lane operand: the range check covers it
       tr.vraw[sb][v] = __builtin_amdgcn_raw_buffer_load_b128(
-          vr[hh], vofs + tin * (int)stride, 0, 0);
+          vr[hh], vofs + tin * (int)stride, 0, AUX);
     }
     if constexpr (PT) {
       // score slot c % 8: token 4 j + c % 4 of half (c / 4) % 2 (0 past

@@ -22,16 +22,18 @@ int dtype_bytes(int d) {
   return d == PKV_F32 ? 4 : (is_fp8_dtype(d) ? 1 : 2);
 }
 
-// A cache dtype argument: the element type and the per-head-scale flag (only
-// for fp8 caches; any other bit is an error).  Returns false if invalid.
 // A cache dtype argument: the dtype code, optionally OR-ed with one fp8
-// scale layout flag (per kv head or per token; fp8 caches only).
-bool split_cache_dtype(int arg, int* dtype, bool* per_head,
-                       bool* per_token) {
+// scale layout flag (per kv head or per token; fp8 caches only) and with the
+// PKV_KV_STREAM hint (any cache; *kv_stream, when asked for).  Any other bit
+// is an error.  Returns false if invalid.
+bool split_cache_dtype(int arg, int* dtype, bool* per_head, bool* per_token,
+                       bool* kv_stream = nullptr) {
   *dtype = arg & 0xFF;
   *per_head = (arg & PKV_SCALE_PER_HEAD) != 0;
   *per_token = (arg & PKV_SCALE_PER_TOKEN) != 0;
-  if ((arg & ~(0xFF | PKV_SCALE_PER_HEAD | PKV_SCALE_PER_TOKEN)) != 0)
+  if (kv_stream) *kv_stream = (arg & PKV_KV_STREAM) != 0;
+  if ((arg & ~(0xFF | PKV_SCALE_PER_HEAD | PKV_SCALE_PER_TOKEN |
+               PKV_KV_STREAM)) != 0)
     return false;
   if (!valid_dtype(*dtype) || (*per_head && *per_token)) return false;
   return !(*per_head || *per_token) || is_fp8_dtype(*dtype);
@@ -352,10 +354,11 @@ int decode_common(float* out, const void* query, int q_dtype,
                   size_t workspace_bytes, const void* key, const void* value,
                   const int32_t* slot_mapping, bool fused,
                   hipStream_t stream) {
-  bool per_head = false, per_token = false;
+  bool per_head = false, per_token = false, kv_stream = false;
   const int cache_arg = cache_dtype;
   if (!valid_dtype(q_dtype) ||
-      !split_cache_dtype(cache_arg, &cache_dtype, &per_head, &per_token))
+      !split_cache_dtype(cache_arg, &cache_dtype, &per_head, &per_token,
+                         &kv_stream))
     return PKV_ERR_DTYPE;
   if (is_fp8_dtype(q_dtype)) return PKV_ERR_DTYPE;
   if (!is_fp8_dtype(cache_dtype) && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
@@ -419,6 +422,7 @@ int decode_common(float* out, const void* query, int q_dtype,
   a.qk_scale_log2 = scale * 1.4426950408889634f;
   a.scale_per_head = per_head;
   a.scale_per_token = per_token;
+  a.kv_stream = kv_stream;
   a.new_key = key;
   a.new_value = value;
   a.slot_mapping = slot_mapping;

@@ -56,6 +56,7 @@ struct AttnArgs {
   int32_t scale_per_head; // fp8 scales: one per kv head (else one per tensor)
   int32_t scale_per_token;  // fp8 scales: k_scale / v_scale are
                             // [num_blocks, block_size, num_kv_heads]
+  int32_t kv_stream;      // no block is read by two sequences: streaming loads
   // several query tokens per sequence (paged_attn_multi) only:
   const int32_t* query_start;  // [num_seqs + 1] first query row of each
   int32_t num_query_tokens;    // rows of query / out (starts clamped to it)

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E5M2 = 0, 1, 2, 3, 4
 PKV_SCALE_PER_HEAD = 0x100
 PKV_SCALE_PER_TOKEN = 0x200
+PKV_KV_STREAM = 0x400       # hint: no block is read by two sequences
 KIND_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
               "fp8_e4m3": PKV_FP8_E4M3, "fp8_e5m2": PKV_FP8_E5M2}
 
@@ -130,16 +131,19 @@ def dtype_code(t, kind=None):
     raise TypeError(f"no pkv dtype for {t.dtype}; pass kind=")
 
 
-def cache_code(k_cache, cache_kind, k_scale):
+def cache_code(k_cache, cache_kind, k_scale, kv_stream=False):
     """The cache dtype argument: the element type, with PKV_SCALE_PER_TOKEN
     when an fp8 cache's scales are [num_blocks, block_size, Hkv] arrays, or
-    PKV_SCALE_PER_HEAD when they hold one value per kv head."""
+    PKV_SCALE_PER_HEAD when they hold one value per kv head; PKV_KV_STREAM
+    when kv_stream is true."""
     code = dtype_code(k_cache, cache_kind)
     if code in (PKV_FP8_E4M3, PKV_FP8_E5M2) and k_scale is not None:
         if k_scale.dim() == 3:
             code |= PKV_SCALE_PER_TOKEN
         elif k_scale.numel() > 1:
             code |= PKV_SCALE_PER_HEAD
+    if kv_stream:
+        code |= PKV_KV_STREAM
     return code
 
 
@@ -319,8 +323,9 @@ def _workspace_buf(workspace, need):
 def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
                       max_seq_len, scale, k_scale=None, v_scale=None,
                       max_waves=0, workspace=None, cache_kind=None,
-                      stream=None):
-    """out[S, Hq, D] (float32) = paged decode attention; see pagedkv.h."""
+                      stream=None, kv_stream=False):
+    """out[S, Hq, D] (float32) = paged decode attention; see pagedkv.h.
+    kv_stream=True passes PKV_KV_STREAM (no block read by two sequences)."""
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
@@ -331,8 +336,9 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
     buf = _workspace_buf(workspace, need)
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
-        _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale), _ptr(k_scale),
-        _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale, kv_stream),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]),
         _ptr(seq_lens), int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
         int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
@@ -342,9 +348,10 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
 def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
                             slot_mapping, block_tables, seq_lens, max_seq_len,
                             scale, k_scale=None, v_scale=None, max_waves=0,
-                            workspace=None, cache_kind=None, stream=None):
+                            workspace=None, cache_kind=None, stream=None,
+                            kv_stream=False):
     """cache_write_slots of one new token per sequence fused into
-    paged_attn_decode; see pagedkv.h."""
+    paged_attn_decode; see pagedkv.h (kv_stream as for paged_attn_decode)."""
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
@@ -355,7 +362,8 @@ def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
     buf = _workspace_buf(workspace, need)
     _check("paged_attn_decode_fused", lib.paged_attn_decode_fused(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(key), _ptr(value),
-        _ptr(k_cache), _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale),
+        _ptr(k_cache), _ptr(v_cache),
+        cache_code(k_cache, cache_kind, k_scale, kv_stream),
         _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), s, hq,
         hkv, d, nb, bs, float(scale), int(max_waves), _ptr(buf),

@@ -40,6 +40,17 @@ def to_host_storage(t, kind):
     return t.numpy()
 
 
+def blocks_unshared(block_tables, seq_lens, block_size):
+    """True when no physical block is read by two sequences: the live table
+    entries (the first ceil(L / block_size) of each row) are all distinct.
+    Such a batch may pass the PKV_KV_STREAM hint to the attention calls."""
+    tables = np.asarray(block_tables)
+    used = [tables[i, :(int(n) + block_size - 1) // block_size]
+            for i, n in enumerate(np.asarray(seq_lens))]
+    ids = np.concatenate(used) if used else np.zeros(0, np.int64)
+    return np.unique(ids).size == ids.size
+
+
 class DeviceStep:
     def __init__(self, w, device="cuda", replicas=True):
         import torch
@@ -62,6 +73,8 @@ class DeviceStep:
         if replicas:
             sets += list(w.replicas)
         self.sets = [{
+            "kv_stream": blocks_unshared(r["block_tables"], w.seq_lens,
+                                         w.block_size),
             "block_tables": torch.from_numpy(
                 np.ascontiguousarray(r["block_tables"], dtype=np.int32)).to(dev),
             "slot_mapping": torch.from_numpy(
@@ -106,7 +119,8 @@ class DeviceStep:
                               self.max_seq_len, self.w.scale,
                               k_scale=self.k_scale, v_scale=self.v_scale,
                               max_waves=max_waves, workspace=self.workspace,
-                              cache_kind=self.cache_kind, stream=stream)
+                              cache_kind=self.cache_kind, stream=stream,
+                              kv_stream=self.sets[r]["kv_stream"])
 
     def attend_fused(self, r=0, stream=None, max_waves=0):
         """Write and attention in one launch (one new token per sequence)."""
@@ -116,7 +130,8 @@ class DeviceStep:
             self.sets[r]["block_tables"], self.seq_lens, self.max_seq_len,
             self.w.scale, k_scale=self.k_scale, v_scale=self.v_scale,
             max_waves=max_waves, workspace=self.workspace,
-            cache_kind=self.cache_kind, stream=stream)
+            cache_kind=self.cache_kind, stream=stream,
+            kv_stream=self.sets[r]["kv_stream"])
 
     def run(self, r=0, stream=None):
         self.copy(r, stream)

@@ -290,6 +290,22 @@ def test_cache_dtype_argument(lib):
 
 
 
+def test_stream_hint_argument(lib):
+    """PKV_KV_STREAM (0x400) is accepted by every call, with any cache dtype
+    and beside the fp8 scale flags; the bit above it is not."""
+    E5M2, PER_HEAD, STREAM = 4, 0x100, 0x400
+    for cache, ks in ((BF16 | STREAM, None), (F16 | STREAM, None),
+                      (FP8 | STREAM, FAKE), (E5M2 | PER_HEAD | STREAM, FAKE)):
+        qd = F16 if cache & 0xFF == F16 else BF16
+        assert pa(lib, qd=qd, cache=cache, ks=ks, vs=ks, ws=None) == WS
+        assert pf(lib, qd=qd, cache=cache, ks=ks, vs=ks, ws=None) == WS
+        assert pm(lib, qd=qd, cache=cache, ks=ks, vs=ks, ws=None) == WS
+    assert pa(lib, qd=BF16, cache=BF16 | 0x800) == DTYPE
+    assert cw(lib, src=BF16, cache=BF16 | STREAM, T=0) == OK
+    assert lib.copy_blocks(FAKE, FAKE, BF16 | STREAM, FAKE, 0, 16, 16, 8,
+                           128, None) == OK
+
+
 def test_layers_copy_validation(lib):
     # bf16 pool of 16 blocks x 16 tokens x 8 heads x 128 = 512 KiB per layer
     pool = 16 * 16 * 8 * 128 * 2

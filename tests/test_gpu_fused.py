@@ -61,8 +61,11 @@ def run_pair(w, max_waves=0, drop=()):
 def assert_same(sep, fus):
     a = sep.out.cpu().numpy()
     b = fus.out.cpu().numpy()
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), \
-        "fused output differs from write + decode"
+    bad = np.argwhere(a.view(np.uint32) != b.view(np.uint32))
+    assert bad.size == 0, (
+        f"fused output differs from write + decode at {len(bad)} elements, "
+        f"(sequence, head) pairs {sorted(set(map(tuple, bad[:, :2].tolist())))[:16]}, "
+        f"max abs difference {np.max(np.abs(a.astype(np.float64) - b)):.3g}")
     ka, va = sep.pools_host()
     assert_pools_bitwise(fus, (ka, va))
 
@@ -135,6 +138,7 @@ def test_fused_per_head_scales(kv):
                         hkv=4, d=128, bs=16, q_kind="bf16", kv_kind=kv,
                         per_head_scales=True)
     for wv in (0, 4):
+        say(f"per-head scales {kv}: waves {wv or 'all'}")
         sep, fus = run_pair(w, max_waves=wv)
         assert_same(sep, fus)
         assert_pools_bitwise(fus, oracle_pools(w))
