@@ -92,9 +92,11 @@ typedef enum pkv_dtype {
 
 /* Cache-policy hint, OR-ed into any call's cache dtype argument: the caller
  * states that no physical block is read by more than one sequence of the
- * call (no shared prefix, no forked samples).  paged_attn_decode and
- * paged_attn_decode_fused then fetch K/V rows of 256 bytes or more
- * (head_dim * element size) with non-temporal loads, which measured faster
+ * call (no shared prefix, no forked samples).  paged_attn_decode,
+ * paged_attn_decode_fused and paged_attn_multi (its per-wave rows; the
+ * workgroup rows of long query runs share tiles through LDS and ignore it)
+ * then fetch K/V rows of 256 bytes or more (head_dim * element size) with
+ * non-temporal loads, which measured faster
  * on such batches; without the hint the rows go through the caches, so a
  * block shared by several sequences is served from them after its first
  * read (the pages' copy-on-write sharing: "PagedAttention",

@@ -162,7 +162,7 @@ template <> struct MultiOccupancy<4> { static constexpr int waves = 1; };
 // PT: per-token fp8 scales (a.k_scale / a.v_scale are [num_blocks,
 // block_size, num_kv_heads] arrays read beside the rows).
 template <typename QT, typename CT, int D, bool UNIFORM, int NG,
-          bool PT = false>
+          bool PT = false, int AUX = 0>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(MultiOccupancy<NG>::waves)))
 void attn_multi_kernel(AttnArgs a) {
@@ -251,7 +251,7 @@ void attn_multi_kernel(AttnArgs a) {
   };
   TileRegs<QT, CT, D> cur;
   if constexpr (PREFETCH)
-    load_tile_uniform<QT, CT, D, PT>(cur, a.block_size, a.num_blocks, ta, tbw,
+    load_tile_uniform<QT, CT, D, PT, AUX>(cur, a.block_size, a.num_blocks, ta, tbw,
                                      X.wb, kpool + (int64_t)X.h * S::ROW_BYTES,
                                      vpool + (int64_t)X.h * S::ROW_BYTES,
                                      stride, X.t_begin, X.t_end, lane,
@@ -300,7 +300,7 @@ void attn_multi_kernel(AttnArgs a) {
           tbw = load_window(shifted, 1, a, lane);
         }
         TileRegs<QT, CT, D> nxt;
-        load_tile_uniform<QT, CT, D, PT>(
+        load_tile_uniform<QT, CT, D, PT, AUX>(
             nxt, a.block_size, a.num_blocks, same_seg ? ta : ta_n,
             same_seg ? tbw : tb_n, same_seg ? wb : Xn.wb,
             same_seg ? kbase : kbase_n, same_seg ? vbase : vbase_n, stride,
@@ -323,7 +323,7 @@ void attn_multi_kernel(AttnArgs a) {
           shifted.wb = wb;
           const uint32_t wa = load_window(shifted, 0, a, lane);
           const uint32_t wbb = load_window(shifted, 1, a, lane);
-          load_tile_uniform<QT, CT, D, PT>(cur, a.block_size, a.num_blocks,
+          load_tile_uniform<QT, CT, D, PT, AUX>(cur, a.block_size, a.num_blocks,
                                            wa, wbb, wb, kbase, vbase, stride,
                                            t0, X.t_end, lane, tsc);
         } else {
@@ -745,9 +745,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_multi_merge_kernel(
 }
 
 template <typename QT, typename CT, int D, bool UNIFORM, int NG,
-          bool PT = false>
+          bool PT = false, int AUX = 0>
 static hipError_t launch_mu(AttnArgs a, int max_waves, hipStream_t stream) {
-  auto kernel = attn_multi_kernel<QT, CT, D, UNIFORM, NG, PT>;
+  auto kernel = attn_multi_kernel<QT, CT, D, UNIFORM, NG, PT, AUX>;
   constexpr bool SCALED = is_fp8<CT>::value && !PT;  // merge: output scale
   const size_t dyn = ((size_t)4 * a.num_seqs + 1) * sizeof(int);
   const int cap = max_waves > 0 && max_waves < kMaxWavesMulti ? max_waves
@@ -809,6 +809,18 @@ static hipError_t launch_md(const AttnArgs& a, int max_waves, bool uniform,
       if (uniform)
         return launch_mu<QT, CT, D, true, 1, true>(a, max_waves, stream);
       return launch_mu<QT, CT, D, false, 1, true>(a, max_waves, stream);
+    }
+  }
+  // unshared batches stream 16-bit rows of 256 bytes with non-temporal
+  // loads, as the decode kernel does
+  if constexpr (same<QT, CT>::value && QT::bytes == 2 &&
+                D * CT::bytes >= 256) {
+    if (uniform && a.kv_stream) {
+      if (a.row_tokens / a.tpr == 4)
+        return launch_mu<QT, CT, D, true, 4, false, kLoadNT>(a, max_waves,
+                                                             stream);
+      return launch_mu<QT, CT, D, true, 1, false, kLoadNT>(a, max_waves,
+                                                           stream);
     }
   }
   if constexpr (!same<QT, F32>::value) {

@@ -487,10 +487,11 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
                      int32_t head_dim, int64_t num_blocks, int32_t block_size,
                      float scale, int32_t max_waves, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
-  bool per_head = false, per_token = false;
+  bool per_head = false, per_token = false, kv_stream = false;
   const int cache_arg = cache_dtype;
   if (!valid_dtype(q_dtype) ||
-      !split_cache_dtype(cache_arg, &cache_dtype, &per_head, &per_token))
+      !split_cache_dtype(cache_arg, &cache_dtype, &per_head, &per_token,
+                         &kv_stream))
     return PKV_ERR_DTYPE;
   if (is_fp8_dtype(q_dtype)) return PKV_ERR_DTYPE;
   if (!is_fp8_dtype(cache_dtype) && q_dtype != cache_dtype) return PKV_ERR_DTYPE;
@@ -557,6 +558,7 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
   a.qk_scale_log2 = scale * 1.4426950408889634f;
   a.scale_per_head = per_head;
   a.scale_per_token = per_token;
+  a.kv_stream = kv_stream;
   a.query_start = query_start;
   a.num_query_tokens = num_query_tokens;
   a.max_query_len = max_query_len;

@@ -374,9 +374,10 @@ def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
 def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
                      query_start, max_query_len, max_seq_len, scale,
                      k_scale=None, v_scale=None, max_waves=0, workspace=None,
-                     cache_kind=None, stream=None):
+                     cache_kind=None, stream=None, kv_stream=False):
     """out[T, Hq, D] (float32) = paged attention of T new query tokens,
-    causal among each sequence's new tokens; see pagedkv.h."""
+    causal among each sequence's new tokens; see pagedkv.h (kv_stream as
+    for paged_attn_decode)."""
     lib = load_library()
     t, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
@@ -388,8 +389,9 @@ def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
     buf = _workspace_buf(workspace, need)
     _check("paged_attn_multi", lib.paged_attn_multi(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
-        _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale), _ptr(k_scale),
-        _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale, kv_stream),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]),
         _ptr(seq_lens), _ptr(query_start), t, int(max_query_len),
         int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
         int(max_waves), _ptr(buf),

@@ -168,4 +168,5 @@ class MultiStep(DeviceStep):
                              self.max_seq_len, self.w.scale,
                              k_scale=self.k_scale, v_scale=self.v_scale,
                              max_waves=max_waves, workspace=self.workspace,
-                             cache_kind=self.cache_kind, stream=stream)
+                             cache_kind=self.cache_kind, stream=stream,
+                             kv_stream=self.sets[r]["kv_stream"])
