@@ -95,7 +95,7 @@ typedef enum pkv_dtype {
  * call (no shared prefix, no forked samples).  paged_attn_decode,
  * paged_attn_decode_fused and paged_attn_multi (its per-wave rows; the
  * workgroup rows of long query runs share tiles through LDS and ignore it)
- * then fetch K/V rows of 256 bytes or more (head_dim * element size) with
+ * then fetch V rows of 128 bytes or more (head_dim * element size) with
  * non-temporal loads, which measured faster
  * on such batches; without the hint the rows go through the caches, so a
  * block shared by several sequences is served from them after its first

@@ -540,19 +540,22 @@ static hipError_t launch_u(AttnArgs a, int max_waves, hipStream_t stream) {
 template <typename QT, typename CT, int D>
 static hipError_t launch_d(const AttnArgs& a, int max_waves, bool uniform,
                            bool fused, hipStream_t stream) {
+  // A batch whose blocks no two sequences share fetches its V rows (of 128
+  // bytes or more: whole lines) with non-temporal loads, measured faster;
+  // shared prefixes need the caches.
+  constexpr bool kLines = D * CT::bytes >= 128;
   if constexpr (is_fp8<CT>::value) {
     if (a.scale_per_token) {  // (never fused: the host rejects it)
       if (fused) return hipErrorInvalidValue;
+      if (uniform && a.kv_stream && kLines)
+        return launch_u<QT, CT, D, true, false, true, kLoadNT>(a, max_waves,
+                                                               stream);
       if (uniform)
         return launch_u<QT, CT, D, true, false, true>(a, max_waves, stream);
       return launch_u<QT, CT, D, false, false, true>(a, max_waves, stream);
     }
   }
-  // Rows of 256 bytes or more of a batch whose blocks no two sequences share
-  // stream with non-temporal loads (measured faster on unshared 16-bit
-  // batches; shared prefixes need the caches, and 128-byte fp8 rows measured
-  // slower with the streaming policy).
-  if constexpr (D * CT::bytes >= 256) {
+  if constexpr (kLines) {
     if (uniform && a.kv_stream) {
       if (fused)
         return launch_u<QT, CT, D, true, true, false, kLoadNT>(a, max_waves,

@@ -811,11 +811,10 @@ static hipError_t launch_md(const AttnArgs& a, int max_waves, bool uniform,
       return launch_mu<QT, CT, D, false, 1, true>(a, max_waves, stream);
     }
   }
-  // unshared batches stream 16-bit rows of 256 bytes with non-temporal
-  // loads, as the decode kernel does
-  if constexpr (same<QT, CT>::value && QT::bytes == 2 &&
-                D * CT::bytes >= 256) {
-    if (uniform && a.kv_stream) {
+  // unshared batches fetch V rows of 128 bytes or more with non-temporal
+  // loads, as the decode kernel does (per-token scales excepted)
+  if constexpr (!same<QT, F32>::value && D * CT::bytes >= 128) {
+    if (uniform && a.kv_stream && !a.scale_per_token) {
       if (a.row_tokens / a.tpr == 4)
         return launch_mu<QT, CT, D, true, 4, false, kLoadNT>(a, max_waves,
                                                              stream);

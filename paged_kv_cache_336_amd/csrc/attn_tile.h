@@ -16,8 +16,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWorkgroupsPerCU = 1;       // default grid: one workgroup per CU
 constexpr uint32_t kRawBufferFlags = 0x00020000;  // dword3: 32-bit data format
 // Cache-policy operand of a buffer load: 0 = the default policy; kLoadNT
-// sets the non-temporal (streaming) bit, for K/V rows that no other wave of
-// the call reads again.
+// sets the non-temporal (streaming) bit.  The tile loaders apply it to the V
+// rows only, whose loads cover whole 128-byte lines: each K load instruction
+// reads 64 bytes of each of 16 rows, so a line is requested by two
+// instructions, and streaming K measured slower.
 constexpr int kLoadNT = 2;
 
 template <typename QT, typename CT> struct PvOperand { typedef CT type; };
@@ -159,7 +161,7 @@ __device__ __forceinline__ void load_tile_uniform(
 #pragma unroll
       for (int r = 0; r < S::KPIECES; ++r) {
         const u32x4_t v =
-            __builtin_amdgcn_raw_buffer_load_b128(kr[hh], kofs + r * 64, 0, AUX);
+            __builtin_amdgcn_raw_buffer_load_b128(kr[hh], kofs + r * 64, 0, 0);
         tr.kw[sb][hh][4 * r + 0] = v[0];
         tr.kw[sb][hh][4 * r + 1] = v[1];
         tr.kw[sb][hh][4 * r + 2] = v[2];

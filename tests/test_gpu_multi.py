@@ -103,19 +103,20 @@ def test_one_token_is_decode_bit_for_bit(kv_kind, q_kind, hq, hkv, d, bs):
                               dec.cpu().numpy().view(np.uint32)), waves
 
 
-@pytest.mark.parametrize("q,qlens", [("bf16", [4, 4, 1, 3]),
-                                     ("f16", [12, 20, 9, 4])])
-def test_stream_hint_changes_no_bit(q, qlens):
+@pytest.mark.parametrize("q,kv,qlens", [("bf16", "bf16", [4, 4, 1, 3]),
+                                        ("f16", "f16", [12, 20, 9, 4]),
+                                        ("bf16", "fp8_e4m3", [12, 20, 9, 4])])
+def test_stream_hint_changes_no_bit(q, kv, qlens):
     """PKV_KV_STREAM changes only the K/V loads' cache policy: one- and
     four-group rows give the same bits with and without it."""
     import torch
     lens = [600, 2100, 40, 333]
     mq = W.custom_multi(seed=13, lens=lens, qlens=qlens, hq=16, hkv=4,
-                        d=128, bs=16, q_kind=q, kv_kind=q)
-    say(f"multi stream hint: {q} qlens {qlens}")
+                        d=128, bs=16, q_kind=q, kv_kind=kv)
+    say(f"multi stream hint: {q} {kv} qlens {qlens}")
     dev, out = run_multi(mq, max_waves=20)
     assert dev.sets[0]["kv_stream"]
-    assert max_abs_err(out, oracle_multi(mq, oracle_pools(mq.w))) <= TOL[q]
+    assert max_abs_err(out, oracle_multi(mq, oracle_pools(mq.w))) <= TOL[kv]
     dev.sets[0]["kv_stream"] = False
     dev.attend(max_waves=20)
     torch.cuda.synchronize()

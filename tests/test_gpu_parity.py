@@ -300,19 +300,26 @@ def test_repeated_calls_are_bitwise_identical():
         assert np.max(np.abs(outs[0] - first)) < 1e-5
 
 
-@pytest.mark.parametrize("q,d,fused", [("bf16", 128, False),
-                                       ("f16", 128, True),
-                                       ("f32", 64, False),
-                                       ("f32", 128, True),
-                                       ("bf16", 64, False)])
-def test_stream_hint_changes_no_bit(q, d, fused):
+@pytest.mark.parametrize("q,kv,d,fused", [("bf16", "bf16", 128, False),
+                                          ("f16", "f16", 128, True),
+                                          ("f32", "f32", 64, False),
+                                          ("f32", "f32", 128, True),
+                                          ("bf16", "bf16", 64, False),
+                                          ("bf16", "fp8_e4m3", 128, False),
+                                          ("f16", "fp8_e5m2", 128, True),
+                                          ("bf16", "fp8_e4m3", 64, False)])
+def test_stream_hint_changes_no_bit(q, kv, d, fused):
     """PKV_KV_STREAM changes only the cache policy of the K/V loads: the
     output, and with the fused write the pools, are bit for bit those of the
     call without it; the hinted call is within tolerance of the oracle."""
     import torch
     w = W.custom_decode(seed=40 + d, num_seqs=5, lens=[1, 31, 300, 1200, 77],
-                        hq=16, hkv=4, d=d, bs=16, q_kind=q, kv_kind=q)
-    say(f"stream hint: {q} D{d} fused={fused}")
+                        hq=16, hkv=4, d=d, bs=16, q_kind=q, kv_kind=kv)
+    if kv == "fp8_e4m3":
+        w = replace(w, k_scale=0.0123, v_scale=0.0217)
+    elif kv == "fp8_e5m2":
+        w = replace(w, k_scale=0.0123 / 128, v_scale=0.0217 / 128)
+    say(f"stream hint: {q} {kv} D{d} fused={fused}")
     dev = DeviceStep(w, replicas=False)
     assert dev.sets[0]["kv_stream"]
     pools = oracle_pools(w)
@@ -336,7 +343,7 @@ def test_stream_hint_changes_no_bit(q, d, fused):
     if fused:
         assert_pools_bitwise(dev, pools)
         ref = oracle_out(w, pools)
-        assert max_abs_err(res[0][0], ref) <= TOL[q]
+        assert max_abs_err(res[0][0], ref) <= TOL[kv]
 
 
 def test_workspace_reuse_across_shapes():
