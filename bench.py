@@ -104,8 +104,21 @@ def cpu_baseline(w, budget_s):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
 
+    # fp8 scales per (slot, kv head) travel with the pools: the copy and the
+    # token-scaled write update them, and attention reads the updated ones
+    token_scales = np.ndim(w.k_scale) == 3
+    scales = {}
+
     def prepare():
         kp, vp = oracle.copy_blocks(w.k_pool, w.v_pool, w.copy_pairs)
+        if token_scales:
+            ks, vs = oracle.copy_token_scales(w.k_scale, w.v_scale,
+                                              w.copy_pairs)
+            kp, vp, scales["k"], scales["v"] = oracle.cache_write_token_scales(
+                kp, vp, ks, vs, w.kv_kind, w.key, w.value, w.src_kind,
+                w.slot_mapping, w.block_size)
+            return kp, vp
+        scales["k"], scales["v"] = w.k_scale, w.v_scale
         return oracle.cache_write(kp, vp, w.kv_kind, w.key, w.value,
                                   w.src_kind, w.slot_mapping, w.block_size,
                                   w.k_scale, w.v_scale)
@@ -113,7 +126,7 @@ def cpu_baseline(w, budget_s):
     def attend(kp, vp, lo, hi):
         oracle.paged_attention(w.query[lo:hi], w.q_kind, kp, vp, w.kv_kind,
                                w.block_tables[lo:hi], w.seq_lens[lo:hi],
-                               w.block_size, w.scale, w.k_scale, w.v_scale)
+                               w.block_size, w.scale, scales["k"], scales["v"])
 
     t0 = time.perf_counter()
     kp, vp = prepare()
@@ -454,7 +467,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_decode",
                     help="llama8b_decode (default), llama70b_decode, "
-                    "prefix_sharing_{prompt,divergent}_bs{32,544}, "
+                    "prefix_sharing_{fork,divergent}_bs{32,544}, "
                     "long_context_fp8, worked_example; several new tokens "
                     "per sequence: spec_verify_llama8b, "
                     "chunked_prefill_llama8b")
