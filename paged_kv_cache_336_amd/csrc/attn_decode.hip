@@ -358,12 +358,12 @@ void attn_decode_kernel(AttnArgs a) {
       int wb = X.wb;
       for (int k = 0; k < X.ntiles; ++k) {
         const int t0 = X.t_begin + S::TT * k;
-        stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
         // the next tile of this wave's stream: tile k + 1 of X, else the
         // first tile of the next segment (an empty range past the end);
-        // requested before this tile is computed, which the scheduling
-        // barrier keeps (the compiler would otherwise sink the loads to
-        // shorten register lifetimes)
+        // requested before this tile's V rows are waited for and staged, so
+        // that two tiles are in flight during that wait, and kept there by
+        // the scheduling barrier (the compiler would otherwise sink the loads
+        // to shorten register lifetimes)
         const bool same_seg = k + 1 < X.ntiles;
         const int t_next = t0 + S::TT;
         if (same_seg && t_next / a.block_size - wb >= 64) {
@@ -383,6 +383,7 @@ void attn_decode_kernel(AttnArgs a) {
             same_seg ? t_next : Xn.t_begin, same_seg ? X.t_end : Xn.t_end,
             lane, same_seg ? tsc : token_scales(Xn));
         __builtin_amdgcn_sched_barrier(0);
+        stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
         compute_tile<QT, CT, D, false, PT>(cur.kw[0], qw, st, vt, t0, X.t_end,
                                            qk_mul, lane, 0, cur.sc[0]);
 #pragma unroll
