@@ -384,13 +384,13 @@ void attn_decode_kernel(AttnArgs a) {
             lane, same_seg ? tsc : token_scales(Xn));
         __builtin_amdgcn_sched_barrier(0);
         stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
-        compute_tile<QT, CT, D, false, PT>(cur.kw[0], qw, st, vt, t0, X.t_end,
+        compute_tile<QT, CT, D, false, PT, !PT>(cur.kw[0], qw, st, vt, t0, X.t_end,
                                            qk_mul, lane, 0, cur.sc[0]);
 #pragma unroll
         for (int sb = 1; sb < S::SUB; ++sb) {
           if (t0 + 32 * sb < X.t_end) {  // (only the last tile has empty ones)
             stage_v<QT, CT, D>(cur.vraw[sb], vt, lane);
-            compute_tile<QT, CT, D, false, PT>(cur.kw[sb], qw, st, vt,
+            compute_tile<QT, CT, D, false, PT, !PT>(cur.kw[sb], qw, st, vt,
                                                t0 + 32 * sb, X.t_end, qk_mul,
                                                lane, 0, cur.sc[sb]);
           }
@@ -419,7 +419,7 @@ void attn_decode_kernel(AttnArgs a) {
         for (int sb = 0; sb < S::SUB; ++sb) {
           if (t0 + 32 * sb < X.t_end) {
             stage_v<QT, CT, D>(cur.vraw[sb], vt, lane);
-            compute_tile<QT, CT, D, false, PT>(cur.kw[sb], qw, st, vt,
+            compute_tile<QT, CT, D, false, PT, !PT>(cur.kw[sb], qw, st, vt,
                                                t0 + 32 * sb, X.t_end, qk_mul,
                                                lane, 0, cur.sc[sb]);
           }

@@ -506,8 +506,9 @@ __device__ __forceinline__ void v_operand(
   }
 }
 
-// One tile for one 16-column group.
-template <typename QT, typename CT, int D, bool CAUSAL = false, bool PT = false>
+// One tile for one 16-column group (LAZY: see softmax_tile).
+template <typename QT, typename CT, int D, bool CAUSAL = false, bool PT = false,
+          bool LAZY = false>
 __device__ __forceinline__ void compute_tile(
     const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS], const uint32_t* qw,
     WaveState<Shape<QT, CT, D>::NBLK>& st, uint8_t* vt, int t0, int t_end,
@@ -517,8 +518,8 @@ __device__ __forceinline__ void compute_tile(
   f32x4_t sacc[2];
   qk_tile<QT, CT, D>(kw, qw, sacc);
   typename Mma<PVT>::operand pb_hi, pb_lo;
-  softmax_tile<QT, CT, D, CAUSAL, PT>(sacc, st, t0, t_end, lim, qk_mul, lane,
-                                      pb_hi, pb_lo, sc);
+  softmax_tile<QT, CT, D, CAUSAL, PT, LAZY>(sacc, st, t0, t_end, lim, qk_mul,
+                                            lane, pb_hi, pb_lo, sc);
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) {
     typename Mma<PVT>::operand va;

@@ -346,6 +346,50 @@ def test_stream_hint_changes_no_bit(q, kv, d, fused):
         assert max_abs_err(res[0][0], ref) <= TOL[kv]
 
 
+@pytest.mark.parametrize("kv,q", [("bf16", "bf16"), ("f16", "f16"),
+                                  ("fp8_e4m3", "bf16")])
+def test_growing_scores_take_every_rescale(kv, q):
+    """Keys whose size grows with their position move the running maximum
+    past the lazy-rescale margin tile after tile (and keys shrinking after
+    position 1800 leave it in place): every branch of the decode update is
+    taken, and the result still matches the oracle at any split; one new
+    token per sequence through paged_attn_multi gives the same bits."""
+    import torch
+    from paged_kv_cache_336_amd.step import MultiStep
+    lens = [900, 2100, 64, 333]
+    w = W.custom_decode(seed=61, num_seqs=len(lens), lens=lens, hq=16,
+                        hkv=4, d=128, bs=16, q_kind=q, kv_kind=kv)
+    if kv == "fp8_e4m3":
+        w = replace(w, k_scale=0.05, v_scale=0.0217)
+    # stored values (fp8: codes), grown by position, stored back.  (The
+    # update is one template for every cache type; float32 caches are left
+    # out because keys grown this far put the float32 rounding of the
+    # scores at the 1e-5 bound, which is one for scores of unit size: the
+    # eager update measured the same 1.05e-5 there.)
+    k = oracle.to_float64(w.k_pool, kv).astype(np.float32)
+    for s, L in enumerate(lens):
+        for t in range(L):
+            b, o = int(w.block_tables[s, t // 16]), t % 16
+            k[b, o] *= np.float32(min(1 + t / 8, 120.0) if t < 1800 else 0.5)
+    w.k_pool[...] = (W._fp8_codes_from_f32(k, 1.0, kv) if kv == "fp8_e4m3"
+                     else W._cast_from_f32(k, kv))
+    say(f"decode growing scores {q}/{kv}")
+    outs = []
+    for waves in (0, 8, 40):
+        _, _, out = run_full(w, max_waves=waves)
+        outs.append(out)
+    # one new token per sequence: paged_attn_multi's rows, bit for bit
+    mq = W.MultiQuery(w=w, query=w.query,
+                      query_start=np.arange(len(lens) + 1, dtype=np.int32))
+    mdev = MultiStep(mq, replicas=False)
+    mdev.copy()
+    mdev.write()
+    mdev.attend(max_waves=8)
+    torch.cuda.synchronize()
+    assert np.array_equal(mdev.out.cpu().numpy().view(np.uint32),
+                          outs[1].view(np.uint32))
+
+
 def test_workspace_reuse_across_shapes():
     import torch
     from paged_kv_cache_336_amd import ops
