@@ -265,7 +265,8 @@ void attn_decode_kernel(AttnArgs a) {
     for (int i = tid; i <= nS; i += kThreads) a.tile_prefix[i] = tex[i];
 
   const int W = a.num_waves;
-  const int w = blockIdx.x * kWaves + wave;
+  const int w = split_workgroup(blockIdx.x, gridDim.x, !a.kv_stream) * kWaves +
+                wave;
   const int64_t T = (int64_t)U * tex[nS];
   const int64_t tb = first_tile_of_wave(w, T, W);
   const int64_t te = first_tile_of_wave(w + 1, T, W);

@@ -217,7 +217,8 @@ void attn_multi_kernel(AttnArgs a) {
     for (int i = tid; i <= nS; i += kThreads) a.tile_prefix[i] = tex[i];
 
   const int W = a.num_waves;
-  const int w = blockIdx.x * kWaves + wave;
+  const int w = split_workgroup(blockIdx.x, gridDim.x, !a.kv_stream) * kWaves +
+                wave;
   const int64_t T = tex[nS];
   const int64_t tb = first_tile_of_wave(w, T, W);
   const int64_t te = first_tile_of_wave(w + 1, T, W);
@@ -577,7 +578,7 @@ void attn_prefill_kernel(AttnArgs a) {
     for (int i = tid; i <= nS; i += kThreads) a.tile_prefix[i] = tex[i];
 
   const int W = a.num_waves;  // ranges: one per workgroup
-  const int w = blockIdx.x;
+  const int w = split_workgroup(blockIdx.x, gridDim.x, !a.kv_stream);
   const int gbase = wave * NG;
   const int64_t T_all = tex[nS];
   const int64_t tb = first_tile_of_wave(w, T_all, W);

@@ -14,6 +14,21 @@ namespace pkv {
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWorkgroupsPerCU = 1;       // default grid: one workgroup per CU
+constexpr int kXcds = 8;                  // dies a grid is dispatched over
+
+// The workgroup number the split uses for workgroup `b` of a grid of `n`.
+// Workgroups are handed to the XCDs in turn (b to XCD b % 8), and each XCD
+// has its own L2.  When blocks may be shared between sequences (no
+// PKV_KV_STREAM hint), the split numbers the workgroups XCD by XCD, so that
+// the ranges of one XCD are neighbours in the tile order: sequences that
+// share a prompt sit next to each other there, and their shared blocks are
+// then served by that XCD's L2 after the first read.  Without sharing the
+// dispatch order is kept.  Either way every range is processed exactly
+// once, so the result does not depend on it.
+__device__ __forceinline__ int split_workgroup(int b, int n, bool shared) {
+  if (!shared || n % kXcds != 0) return b;
+  return (b % kXcds) * (n / kXcds) + b / kXcds;
+}
 constexpr uint32_t kRawBufferFlags = 0x00020000;  // dword3: 32-bit data format
 // Cache-policy operand of a buffer load: 0 = the default policy; kLoadNT
 // sets the non-temporal (streaming) bit.  The tile loaders apply it to the V
