@@ -133,6 +133,15 @@ int pkv_bm_tables(const pkv_block_manager* bm, const int32_t* seqs, int32_t n,
                   int32_t* tables, int32_t row_stride, int32_t fill,
                   int32_t* lens);
 
+/* Whether an attention call over the n live sequences seqs[] may carry the
+ * PKV_KV_STREAM hint (pagedkv.h): *unshared = 1 when no physical block
+ * appears in two of their tables (a forked or prefix-cached prompt block
+ * shows up in every sequence that holds it), else 0.  Blocks shared only
+ * with sequences outside the call do not count: the hint is about reads
+ * within one call. */
+int pkv_bm_blocks_unshared(const pkv_block_manager* bm, const int32_t* seqs,
+                           int32_t n, int32_t* unshared);
+
 typedef struct pkv_bm_stats {
   int64_t free_blocks;     /* blocks with no reference (the free list, and
                               with prefix caching the evictable blocks)     */

@@ -70,6 +70,9 @@ def _lib():
         lib.pkv_bm_free.argtypes = [vp, i32]
         lib.pkv_bm_tables.restype = ci
         lib.pkv_bm_tables.argtypes = [vp, vp, i32, vp, i32, i32, vp]
+        lib.pkv_bm_blocks_unshared.restype = ci
+        lib.pkv_bm_blocks_unshared.argtypes = [vp, vp, i32,
+                                               ctypes.POINTER(i32)]
         lib.pkv_bm_get_stats.restype = ci
         lib.pkv_bm_get_stats.argtypes = [vp, ctypes.POINTER(_Stats)]
         lib.pkv_bm_refcount.restype = i32
@@ -187,6 +190,16 @@ class BlockManager:
                                       _ptr(tab), stride, fill, _ptr(lens)),
                "tables")
         return tab, lens
+
+    def blocks_unshared(self, seqs):
+        """True when no physical block appears in two of these sequences'
+        tables: an attention call over them may pass PKV_KV_STREAM."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        out = ctypes.c_int32(-1)
+        _check(self.lib.pkv_bm_blocks_unshared(self.h, _ptr(seqs), len(seqs),
+                                               ctypes.byref(out)),
+               "blocks_unshared")
+        return bool(out.value)
 
     def stats(self):
         st = _Stats()

@@ -377,6 +377,29 @@ int pkv_bm_tables(const pkv_block_manager* bm, const int32_t* seqs, int32_t n,
   return PKV_OK;
 }
 
+int pkv_bm_blocks_unshared(const pkv_block_manager* bm, const int32_t* seqs,
+                           int32_t n, int32_t* unshared) {
+  if (!bm || !unshared) return PKV_ERR_NULL;
+  if (n < 0) return PKV_ERR_SHAPE;
+  if (n > 0 && !seqs) return PKV_ERR_NULL;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!bm->seq_ok(seqs[i])) return PKV_ERR_SHAPE;
+    if (!bm->live[seqs[i]]) return PKV_ERR_SEQ;
+  }
+  std::vector<uint8_t> seen(bm->num_blocks, 0);
+  *unshared = 1;
+  for (int32_t i = 0; i < n && *unshared; ++i) {
+    for (const int32_t b : bm->table[seqs[i]]) {
+      if (seen[b]) {
+        *unshared = 0;
+        break;
+      }
+      seen[b] = 1;
+    }
+  }
+  return PKV_OK;
+}
+
 int pkv_bm_get_stats(const pkv_block_manager* bm, pkv_bm_stats* out) {
   if (!bm || !out) return PKV_ERR_NULL;
   pkv_bm_stats st{};

@@ -37,6 +37,11 @@ def assert_same(bm, ob, nblocks, max_seqs):
         assert bm.seq_len(s) == ob.lengths.get(s, -1)
     assert [bm.refcount(b) for b in range(nblocks)] == ob.refs
     assert bm.stats() == ob.stats()
+    # the streaming hint's condition: no block in two of the tables, over
+    # all live sequences and over every other one of them
+    for subset in (live, live[::2]):
+        ids = [b for s in subset for b in ob.table(s)]
+        assert bm.blocks_unshared(subset) == (len(set(ids)) == len(ids))
 
 
 @pytest.mark.parametrize("seed,nblocks,bs", [(1, 64, 4), (2, 40, 16),
@@ -84,6 +89,21 @@ def test_matches_oracle_on_random_operations(seed, nblocks, bs):
             bm.free(s)
             live.discard(s)
         assert_same(bm, ob, nblocks, max_seqs)
+
+
+def test_blocks_unshared_after_fork_and_copy_on_write():
+    bm = blocks.BlockManager(64, 4, 8, 16)
+    bm.add_sequence(0, 10)            # blocks for 10 tokens (3 blocks)
+    bm.add_sequence(1, 4)
+    assert bm.blocks_unshared([0, 1])
+    bm.fork(0, 2)                     # child shares all three blocks
+    assert not bm.blocks_unshared([0, 2])
+    assert bm.blocks_unshared([0, 1]) and bm.blocks_unshared([2, 1])
+    bm.append([0, 2])                 # the shared partial block is copied
+    assert not bm.blocks_unshared([0, 2])   # the two full blocks stay shared
+    assert bm.blocks_unshared([])
+    with pytest.raises(BlockError):
+        bm.blocks_unshared([5])       # not live
 
 
 def test_status_codes():
