@@ -17,6 +17,7 @@ EXPORTED = ("pkv_bm_create", "pkv_bm_create_prefix_cached",
             "pkv_bm_add_sequence_tokens", "pkv_bm_prefix_stats",
             "pkv_bm_destroy", "pkv_bm_add_sequence",
             "pkv_bm_fork", "pkv_bm_append", "pkv_bm_free", "pkv_bm_tables",
+            "pkv_bm_blocks_unshared",
             "pkv_bm_get_stats", "pkv_bm_refcount", "pkv_bm_seq_len",
             "pkv_ca_create", "pkv_ca_destroy", "pkv_ca_reserve",
             "pkv_ca_release", "pkv_ca_get_stats")
