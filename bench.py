@@ -493,9 +493,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for "
-              f"{args.gpus}); the multi-GPU split is a design note, not a "
-              "measured path", file=sys.stderr)
+        print(f"bench.py: the hot path runs on one GPU (asked for "
+              f"{args.gpus}); splitting it across GPUs is described, not "
+              "measured", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_calibration:

@@ -110,7 +110,7 @@ typedef enum pkv_status {
   PKV_ERR_NULL = 1,        /* a required pointer is NULL                   */
   PKV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent       */
   PKV_ERR_DTYPE = 3,       /* unknown dtype or unsupported dtype pairing   */
-  PKV_ERR_UNSUPPORTED = 4, /* valid request this build does not implement  */
+  PKV_ERR_UNSUPPORTED = 4, /* valid request the library does not implement */
   PKV_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned             */
   PKV_ERR_WORKSPACE = 6,   /* attention workspace missing or too small     */
   PKV_ERR_HIP = 8,         /* the HIP runtime reported an error            */
