@@ -46,15 +46,6 @@ def gather_sequence(pool, table_row, seq_len, block_size, head):
     return rows[:seq_len]
 
 
-def kv_scales(kv_kind, k_scale, v_scale, num_kv_heads):
-    """Per-kv-head float64 scales of the stored values (ones unless fp8)."""
-    if kv_kind in FP8_KINDS:
-        return (head_scales(k_scale, num_kv_heads),
-                head_scales(v_scale, num_kv_heads))
-    one = np.ones(num_kv_heads)
-    return one, one
-
-
 def is_token_scales(scale):
     """True for per-token scales: a [num_blocks, block_size, kv_heads]
     array (one float32 per slot and kv head)."""
@@ -126,22 +117,33 @@ def paged_attention(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
 def paged_attention_rows(query, q_kind, k_pool, v_pool, kv_kind, block_tables,
                          seq_lens, block_size, scale, rows, k_scale=1.0,
                          v_scale=1.0):
-    """Same as :func:`paged_attention`, but only for the (seq, q_head) pairs
-    in ``rows``; returns float64 [len(rows), D].  Used to check sampled
-    outputs of full-size workloads one by one."""
+    """:func:`paged_attention` for the (seq, q_head) pairs in ``rows`` only;
+    returns float64 [len(rows), D], row i being ``paged_attention(...)[s,
+    hq]`` of ``rows[i] = (s, hq)`` bit for bit.  The pairs are grouped by
+    (sequence, kv head): each group's rows are gathered once, and all G
+    query heads of that kv head go through the same float64 computation as
+    in :func:`paged_attention`, of which the asked-for heads are kept.  Used
+    to check full-size workloads, whose whole output would not fit the
+    oracle's time, sequence by sequence or on sampled pairs."""
     S, Hq, D = query.shape
     Hkv = k_pool.shape[2]
+    assert Hq % Hkv == 0
+    assert k_pool.shape[1] == block_size
     G = Hq // Hkv
     out = np.zeros((len(rows), D), dtype=np.float64)
+    groups = {}
     for i, (s, hq) in enumerate(rows):
+        groups.setdefault((int(s), int(hq) // G), []).append((i, int(hq)))
+    for (s, h), members in groups.items():
         L = int(seq_lens[s])
         if L == 0:
             continue
-        h = hq // G
         k = stored_rows(k_pool, kv_kind, block_tables[s], L, block_size, h,
                         k_scale)
         v = stored_rows(v_pool, kv_kind, block_tables[s], L, block_size, h,
                         v_scale)
-        q = to_float64(query[s, hq:hq + 1], q_kind)
-        out[i] = attention_one_head(q, k, v, scale)[0]
+        q = to_float64(query[s, h * G:(h + 1) * G], q_kind)
+        o = attention_one_head(q, k, v, scale)
+        for i, hq in members:
+            out[i] = o[hq - h * G]
     return out

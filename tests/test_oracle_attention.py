@@ -245,3 +245,109 @@ def test_poisoned_slots_are_never_read():
     assert np.isnan(kp.astype(np.float32)).any()
     out = run_oracle(w, (kp, vp))
     assert np.isfinite(out).all()
+
+
+# ----------------------------------------------------------------------------
+# paged_attention_rows: the oracle for full-size workloads, checked row by
+# row.  It must give exactly paged_attention's rows whatever order and
+# subset the pairs come in, for every scale layout, and it is also checked
+# against SDPA on its own (one row, token-by-token dequantisation).
+# ----------------------------------------------------------------------------
+
+ROW_CASES = [
+    dict(q_kind="bf16", kv_kind="bf16"),
+    dict(q_kind="f32", kv_kind="fp8_e4m3"),
+    dict(q_kind="bf16", kv_kind="fp8_e4m3", per_head_scales=True),
+    dict(q_kind="f16", kv_kind="fp8_e5m2", per_head_scales=True),
+    dict(q_kind="bf16", kv_kind="fp8_e4m3", per_token_scales=True),
+    dict(q_kind="f32", kv_kind="fp8_e5m2", per_token_scales=True),
+]
+
+
+@pytest.mark.parametrize("bs", [3, 16])
+@pytest.mark.parametrize("case", ROW_CASES,
+                         ids=lambda c: "-".join(
+                             [c["q_kind"], c["kv_kind"]] +
+                             (["head"] if c.get("per_head_scales") else []) +
+                             (["token"] if c.get("per_token_scales") else [])))
+def test_rows_equal_full_oracle(case, bs):
+    """Every (s, hq) pair, asked for in a shuffled order (so a slip in the
+    kv head h = hq // G, in the grouping or in the output order shows), and
+    a strided subset of them: the rows are paged_attention's bit for bit.
+    A length-0 sequence gives zero rows."""
+    # (no pending new token: every slot of every sequence holds a live row)
+    w = W.custom_decode(seed=40 + bs, num_seqs=5, lens=[7, 0, 33, 1, 50],
+                        hq=12, hkv=3, d=16, bs=bs, num_new_per_seq=0, **case)
+    full = run_oracle(w)
+    assert np.isfinite(full).all()
+    S, Hq, _ = full.shape
+    pairs = [(s, h) for s in range(S) for h in range(Hq)]
+    rng = np.random.default_rng(bs)
+    order = rng.permutation(len(pairs))
+    rows = [pairs[i] for i in order]
+    got = oracle.paged_attention_rows(
+        w.query, w.q_kind, w.k_pool, w.v_pool, w.kv_kind, w.block_tables,
+        w.seq_lens, w.block_size, w.scale, rows, w.k_scale, w.v_scale)
+    want = np.stack([full[s, h] for s, h in rows])
+    assert got.tobytes() == want.tobytes()
+    assert not np.any(full[1])                   # the empty sequence
+    sub = rows[::7]
+    got_sub = oracle.paged_attention_rows(
+        w.query, w.q_kind, w.k_pool, w.v_pool, w.kv_kind, w.block_tables,
+        w.seq_lens, w.block_size, w.scale, sub, w.k_scale, w.v_scale)
+    assert got_sub.tobytes() == np.stack([full[s, h] for s, h in sub]).tobytes()
+    # the same pair twice gives the same row twice
+    twice = oracle.paged_attention_rows(
+        w.query, w.q_kind, w.k_pool, w.v_pool, w.kv_kind, w.block_tables,
+        w.seq_lens, w.block_size, w.scale, [(2, 5), (2, 5)], w.k_scale,
+        w.v_scale)
+    assert twice[0].tobytes() == twice[1].tobytes() == full[2, 5].tobytes()
+
+
+TORCH_FP8_KINDS = {"fp8_e4m3": torch.float8_e4m3fn,
+                   "fp8_e5m2": torch.float8_e5m2}
+
+
+@pytest.mark.parametrize("case", [ROW_CASES[0], ROW_CASES[3], ROW_CASES[4]],
+                         ids=["bf16", "e5m2-head", "e4m3-token"])
+def test_rows_match_sdpa(case):
+    """One pair against torch SDPA in float64 on rows gathered token by
+    token through the table (slot = table[j // bs] * bs + j % bs), decoded
+    by torch's float8 types and multiplied by the scale that applies to the
+    slot (per tensor, per kv head, or the slot's own)."""
+    w = W.custom_decode(seed=77, num_seqs=3, lens=[21, 45, 9], hq=8, hkv=2,
+                        d=32, bs=4, num_new_per_seq=0, **case)
+    s, hq = 1, 6
+    G = w.num_q_heads // w.num_kv_heads
+    h = hq // G
+    L = int(w.seq_lens[s])
+    bs = w.block_size
+
+    def rows_of(pool, scale):
+        out = []
+        for j in range(L):
+            b = int(w.block_tables[s, j // bs])
+            o = j % bs
+            raw = pool[b, o, h]
+            if w.kv_kind in TORCH_FP8_KINDS:
+                x = torch.from_numpy(np.ascontiguousarray(raw)).view(
+                    TORCH_FP8_KINDS[w.kv_kind]).to(torch.float64)
+                sc = np.asarray(scale, dtype=np.float32)
+                f = sc[b, o, h] if sc.ndim == 3 else (
+                    sc[h] if sc.size > 1 else sc.reshape(()))
+                out.append(x * float(f))
+            else:
+                out.append(torch.from_numpy(to_float64(raw, w.kv_kind)))
+        return torch.stack(out)
+
+    k = rows_of(w.k_pool, w.k_scale)
+    v = rows_of(w.v_pool, w.v_scale)
+    q = torch.from_numpy(to_float64(w.query[s, hq], w.q_kind))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.view(1, 1, -1), k.unsqueeze(0), v.unsqueeze(0), scale=w.scale)
+    got = oracle.paged_attention_rows(
+        w.query, w.q_kind, w.k_pool, w.v_pool, w.kv_kind, w.block_tables,
+        w.seq_lens, w.block_size, w.scale, [(s, hq)], w.k_scale, w.v_scale)
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got[0], ref.numpy().reshape(-1), rtol=0,
+                               atol=1e-12)
