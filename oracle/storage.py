@@ -14,6 +14,21 @@ from .fp8_e5m2 import e5m2_decode
 
 KINDS = ("f32", "f16", "bf16", "fp8_e4m3", "fp8_e5m2")
 FP8_KINDS = ("fp8_e4m3", "fp8_e5m2")
+_FP8_DECODERS = {"fp8_e4m3": e4m3_decode, "fp8_e5m2": e5m2_decode}
+_FP8_TABLES = {}
+
+
+def fp8_table(kind):
+    """float64 [256]: the decoder's value of every code, in code order.
+    Large arrays are widened by looking their codes up here, which gives
+    the decoder's own values (each code is decoded by the same elementwise
+    formula) without running the formula once per element."""
+    t = _FP8_TABLES.get(kind)
+    if t is None:
+        t = _FP8_DECODERS[kind](np.arange(256, dtype=np.uint8))
+        t.setflags(write=False)
+        _FP8_TABLES[kind] = t
+    return t
 
 
 def to_float64(arr, kind):
@@ -28,12 +43,9 @@ def to_float64(arr, kind):
         assert a.dtype == np.uint16, a.dtype
         bits32 = a.astype(np.uint32) << np.uint32(16)
         return bits32.view(np.float32).astype(np.float64)
-    if kind == "fp8_e4m3":
+    if kind in FP8_KINDS:
         assert a.dtype == np.uint8, a.dtype
-        return e4m3_decode(a)
-    if kind == "fp8_e5m2":
-        assert a.dtype == np.uint8, a.dtype
-        return e5m2_decode(a)
+        return fp8_table(kind)[a]
     raise ValueError(f"unknown storage kind {kind!r}")
 
 

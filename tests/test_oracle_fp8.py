@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from oracle import e4m3_decode, e4m3_encode
 
 
@@ -97,3 +98,18 @@ def test_encode_is_monotone():
     spacing = np.where(np.abs(x) < 2.0 ** -6, 2.0 ** -9,
                        2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 1e-30))) - 3))
     assert np.all(err[fin] <= spacing[fin] / 2 + 1e-12)
+
+
+def test_widening_table_is_the_decoder():
+    """to_float64 widens fp8 codes through a table of the decoders' values;
+    on every code and on a random array (with NaN codes) it gives the
+    decoders' float64 values bit for bit."""
+    from oracle.storage import to_float64
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 256, (37, 64), dtype=np.uint8)
+    for kind, dec in (("fp8_e4m3", oracle.e4m3_decode),
+                      ("fp8_e5m2", oracle.e5m2_decode)):
+        every = np.arange(256, dtype=np.uint8)
+        assert to_float64(every, kind).tobytes() == dec(every).tobytes()
+        assert to_float64(codes, kind).tobytes() == dec(codes).tobytes()
+        assert to_float64(codes, kind).shape == codes.shape
