@@ -42,13 +42,15 @@
  * contents of device buffers (table entries in range, slots in range,
  * lengths within the table's reach, no duplicate slots, copy pairs with
  * distinct destinations that are not also sources) are the caller's
- * contract.  Breaking it gives unspecified results but never an access
- * outside the buffers: table entries outside [0, num_blocks) are clamped
- * into the pool, slots and copy pairs outside it are skipped, lengths are
- * cut to max_seq_len, and query extents (paged_attn_multi) to the query rows
- * there are.  A failed launch returns
+ * contract, verified only in debug mode (pkv_set_debug_checks,
+ * PAGEDKV_DEBUG=1: PKV_ERR_RANGE).  Breaking it gives unspecified results
+ * but never an access outside the buffers: table entries outside
+ * [0, num_blocks) are clamped into the pool, slots and copy pairs outside it
+ * are skipped, lengths are cut to max_seq_len, and query extents
+ * (paged_attn_multi) to the query rows there are.  A failed launch returns
  * PKV_ERR_HIP.  The library allocates no memory, never synchronises
- * and keeps no state: calls are thread-safe, and two calls that share an
+ * (outside debug mode) and keeps no state beyond cached launch sizes and
+ * the debug setting: calls are thread-safe, and two calls that share an
  * attention workspace must not overlap in time.
  */
 #ifndef PAGEDKV_H
@@ -113,6 +115,8 @@ typedef enum pkv_status {
   PKV_ERR_UNSUPPORTED = 4, /* valid request the library does not implement */
   PKV_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned             */
   PKV_ERR_WORKSPACE = 6,   /* attention workspace missing or too small     */
+  PKV_ERR_RANGE = 7,       /* debug checks: device contents break the call's
+                              contract (see pkv_set_debug_checks)          */
   PKV_ERR_HIP = 8,         /* the HIP runtime reported an error            */
   PKV_ERR_NO_BLOCKS = 9,   /* block manager: too few free blocks or slots  */
   PKV_ERR_SEQ = 10         /* block manager: sequence not live / in use    */
@@ -120,6 +124,39 @@ typedef enum pkv_status {
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* pkv_status_string(int status);
+
+/*
+ * pkv_set_debug_checks -- turn the checks of device contents on (non-zero)
+ * or off (0) for every later call in the process; returns the previous
+ * setting.  The initial setting is read once, at the first call that needs
+ * it, from the environment: PAGEDKV_DEBUG set to anything but "" or "0"
+ * turns the checks on.
+ *
+ * With the checks on, every device call first copies the small index
+ * arrays it was given (block tables, lengths, query starts, slots, copy
+ * pairs) to the host on its stream, waits for the copy (so the call is no
+ * longer asynchronous), and verifies the contract stated for the call:
+ *   lengths         0 <= seq_lens[s] <= max_seq_len;
+ *   block tables    the first ceil(seq_lens[s] / block_size) entries of row
+ *                   s lie in [0, num_blocks);
+ *   slots           every slot >= 0 is below num_blocks * block_size, and
+ *                   no slot >= 0 appears twice (a slot names one token's
+ *                   place: "How PagedAttention Works in vLLM ...",
+ *                   instagit.com, section "write_to_paged_cache");
+ *   fused slots     additionally, slot s >= 0 is that of position
+ *                   seq_lens[s] - 1 through row s of the table;
+ *   copy pairs      src and dst in [0, num_blocks), destinations distinct,
+ *                   no destination also a source (a copy-on-write copies a
+ *                   shared block into a fresh one before the write:
+ *                   "PagedAttention", shubhamtatvamasi.com, FAQ entry on
+ *                   copy-on-write);
+ *   query starts    non-decreasing from >= 0 to <= num_query_tokens, each
+ *                   sequence's count <= max_query_len and <= its length.
+ * A violation returns PKV_ERR_RANGE and launches nothing; a failed copy
+ * returns PKV_ERR_HIP.  With the checks off (the default) nothing is copied
+ * and the calls are as fast as without this facility.
+ */
+int pkv_set_debug_checks(int enable);
 
 /*
  * cache_write_slots -- write new K/V rows into the pools in place.

@@ -6,6 +6,10 @@
 #ifndef PKV_ATTN_TILE_H
 #define PKV_ATTN_TILE_H
 
+#include <mutex>
+#include <unordered_map>
+#include <utility>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -769,19 +773,51 @@ __device__ __forceinline__ uint32_t load_window(const Seg& g, int half,
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+// Compute units of the current device and the workgroups of `kernel` one CU
+// holds at once with dyn_lds bytes of dynamic LDS.  The answers depend only
+// on the device, the kernel and the LDS size, so they are asked of the
+// runtime once per (kernel instance, device, LDS size) and kept: later calls
+// cost one hipGetDevice and a lookup under a lock.  (The LDS size follows
+// the number of sequences, so a serving loop meets a bounded set of them.)
+template <typename K>
+static bool device_occupancy(K kernel, size_t dyn_lds, int* cus, int* per_cu) {
+  static std::mutex mu;
+  static std::unordered_map<uint64_t, std::pair<int, int>> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const uint64_t key = ((uint64_t)(uint32_t)dev << 32) | (uint32_t)dyn_lds;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) {
+      *cus = it->second.first;
+      *per_cu = it->second.second;
+      return true;
+    }
+  }
+  int c = 0, p = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &p, reinterpret_cast<const void*>(kernel), kThreads, dyn_lds) !=
+          hipSuccess)
+    return false;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = {c, p};
+  }
+  *cus = c;
+  *per_cu = p;
+  return true;
+}
+
 // Workgroups of the partition kernel: as many as can be resident at once
 // (occupancy x CUs), capped by the caller's wave limit and kMaxWaves.
 template <typename K>
 static int resident_grid(K kernel, size_t dyn_lds, int max_waves,
                          int per_cu_cap = kWorkgroupsPerCU) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-          hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(kernel), kThreads, dyn_lds) !=
-          hipSuccess)
-    return -1;
+  int cus = 0, per_cu = 0;
+  if (!device_occupancy(kernel, dyn_lds, &cus, &per_cu)) return -1;
   // One workgroup (one wave per SIMD) per CU measured fastest for the
   // streaming loop: more resident waves deepen the memory queues without
   // adding bandwidth.

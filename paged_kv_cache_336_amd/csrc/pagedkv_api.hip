@@ -4,6 +4,12 @@
 // cache_ops.hip.
 
 #include <limits.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <unordered_set>
+#include <vector>
 
 #include "pkv_internal.h"
 
@@ -60,7 +66,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // 16 / group tokens times the group's heads (group <= 16), for at most
 // kMaxWavesMulti waves.
 int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-               int32_t head_dim, bool multi, AttnShape* out) {
+               int32_t head_dim, bool multi, AttnShape* out,
+               int waves_cap = kMaxWaves) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1) return PKV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (num_seqs > (multi ? kMaxSeqsMulti : kMaxSeqs)) return PKV_ERR_UNSUPPORTED;
@@ -72,7 +79,7 @@ int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   s.slot_heads = multi ? 16 / s.group * s.group : (s.group < 16 ? s.group : 16);
   const size_t slots =
       multi ? (size_t)kMaxWavesMulti * 2 * kMaxGroupsMulti * s.slot_heads
-            : (size_t)kMaxWaves * 2 * s.slot_heads;
+            : (size_t)waves_cap * 2 * s.slot_heads;
   s.off_m = align_up((size_t)(num_seqs + 1) * 4, 256);
   s.off_l = align_up(s.off_m + slots * 4, 256);
   s.off_o = align_up(s.off_l + slots * 4, 256);
@@ -81,9 +88,97 @@ int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   return PKV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Debug checks of device contents (pkv_set_debug_checks, PAGEDKV_DEBUG): the
+// index arrays a call was given are copied to the host on the call's stream
+// and verified against the call's contract before anything is launched.
+// ---------------------------------------------------------------------------
+std::atomic<int> g_debug{-1};  // -1: not read from the environment yet
+
+bool debug_checks() {
+  int v = g_debug.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = getenv("PAGEDKV_DEBUG");
+    int want = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+    int expected = -1;
+    g_debug.compare_exchange_strong(expected, want);
+    v = g_debug.load(std::memory_order_relaxed);
+  }
+  return v > 0;
+}
+
+// n int32 values of a device array, on the host (stream-ordered, waited for).
+bool fetch_i32(const int32_t* dev, int64_t n, hipStream_t stream,
+               std::vector<int32_t>* out) {
+  out->assign((size_t)(n > 0 ? n : 0), 0);
+  if (n <= 0) return true;
+  if (hipMemcpyAsync(out->data(), dev, (size_t)n * sizeof(int32_t),
+                     hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return false;
+  return hipStreamSynchronize(stream) == hipSuccess;
+}
+
+// Slots: each one >= 0 below num_slots, and none >= 0 twice.
+int check_slots(const std::vector<int32_t>& slots, int64_t num_slots) {
+  std::unordered_set<int32_t> seen;
+  seen.reserve(slots.size() * 2);
+  for (int32_t v : slots) {
+    if (v < 0) continue;
+    if ((int64_t)v >= num_slots || !seen.insert(v).second) return PKV_ERR_RANGE;
+  }
+  return PKV_OK;
+}
+
+// Copy records {src, dst[, tokens]}: blocks inside the pool, destinations
+// distinct, no destination also a source.
+int check_copies(const int32_t* records, int64_t n, int width,
+                 int64_t num_blocks, hipStream_t stream) {
+  std::vector<int32_t> r;
+  if (!fetch_i32(records, n * width, stream, &r)) return PKV_ERR_HIP;
+  std::unordered_set<int32_t> srcs, dsts;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t src = r[(size_t)(i * width)], dst = r[(size_t)(i * width + 1)];
+    if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks)
+      return PKV_ERR_RANGE;
+    if (!dsts.insert(dst).second) return PKV_ERR_RANGE;
+    srcs.insert(src);
+  }
+  for (int32_t d : dsts)
+    if (srcs.count(d)) return PKV_ERR_RANGE;
+  return PKV_OK;
+}
+
+// Lengths in [0, max_seq_len] and the live table entries inside the pool;
+// the host copies of both are returned for further checks.
+int check_tables(const int32_t* block_tables, int32_t max_blocks,
+                 const int32_t* seq_lens, int32_t num_seqs,
+                 int32_t max_seq_len, int64_t num_blocks, int32_t block_size,
+                 hipStream_t stream, std::vector<int32_t>* lens,
+                 std::vector<int32_t>* tables) {
+  if (!fetch_i32(seq_lens, num_seqs, stream, lens) ||
+      !fetch_i32(block_tables, (int64_t)num_seqs * max_blocks, stream, tables))
+    return PKV_ERR_HIP;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = (*lens)[s];
+    if (L < 0 || L > max_seq_len) return PKV_ERR_RANGE;
+    const int64_t nblk = ((int64_t)L + block_size - 1) / block_size;
+    for (int64_t i = 0; i < nblk; ++i) {
+      const int32_t b = (*tables)[(size_t)((int64_t)s * max_blocks + i)];
+      if (b < 0 || b >= num_blocks) return PKV_ERR_RANGE;
+    }
+  }
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int pkv_set_debug_checks(int enable) {
+  const int prev = debug_checks() ? 1 : 0;
+  g_debug.store(enable ? 1 : 0);
+  return prev;
+}
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -94,6 +189,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_RANGE:
+      return "device contents break the call's contract (debug checks)";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_NO_BLOCKS: return "not enough free blocks";
     case PKV_ERR_SEQ: return "sequence not live, or already live";
@@ -139,6 +236,12 @@ int write_common(const void* key, const void* value, int src_dtype,
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(slot_mapping, 4))
     return PKV_ERR_ALIGN;
+  if (debug_checks()) {
+    std::vector<int32_t> slots;
+    if (!fetch_i32(slot_mapping, num_tokens, stream, &slots)) return PKV_ERR_HIP;
+    const int rc = check_slots(slots, num_blocks * (int64_t)block_size);
+    if (rc != PKV_OK) return rc;
+  }
   WriteArgs a{};
   a.k_token_scales = token_scales ? k_scales : nullptr;
   a.v_token_scales = token_scales ? v_scales : nullptr;
@@ -213,6 +316,11 @@ int copy_common(void* k_cache, void* v_cache, int cache_dtype,
   if (!k_cache || !v_cache || !block_pairs) return PKV_ERR_NULL;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 4))
     return PKV_ERR_ALIGN;
+  if (debug_checks()) {
+    const int rc = check_copies(block_pairs, num_pairs, prefix ? 3 : 2,
+                                num_blocks, stream);
+    if (rc != PKV_OK) return rc;
+  }
   CopyArgs a{};
   a.num_layers = num_layers;
   a.layer_stride = num_layers > 1 ? layer_stride : 0;
@@ -243,6 +351,11 @@ int copy_scales_common(float* k_scales, float* v_scales,
   if (!k_scales || !v_scales || !records) return PKV_ERR_NULL;
   if (!aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(records, 4))
     return PKV_ERR_ALIGN;
+  if (debug_checks()) {
+    const int rc = check_copies(records, num_records, prefix ? 3 : 2,
+                                num_blocks, stream);
+    if (rc != PKV_OK) return rc;
+  }
   CopyArgs a{};
   a.num_layers = 1;
   a.layer_stride = 0;
@@ -395,6 +508,29 @@ int decode_common(float* out, const void* query, int q_dtype,
     return PKV_ERR_ALIGN;
   if (!workspace || workspace_bytes < s.ws_bytes) return PKV_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return PKV_ERR_ALIGN;
+  if (debug_checks()) {
+    std::vector<int32_t> lens, tables, slots;
+    int rc = check_tables(block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                          max_seq_len, num_blocks, block_size, stream, &lens,
+                          &tables);
+    if (rc != PKV_OK) return rc;
+    if (fused) {
+      if (!fetch_i32(slot_mapping, num_seqs, stream, &slots)) return PKV_ERR_HIP;
+      rc = check_slots(slots, num_blocks * (int64_t)block_size);
+      if (rc != PKV_OK) return rc;
+      // a slot >= 0 is that of the sequence's last position
+      for (int32_t q = 0; q < num_seqs; ++q) {
+        if (slots[q] < 0) continue;
+        const int32_t L = lens[q];
+        if (L < 1) return PKV_ERR_RANGE;
+        const int64_t phys =
+            tables[(size_t)((int64_t)q * max_blocks_per_seq +
+                            (L - 1) / block_size)];
+        if ((int64_t)slots[q] != phys * block_size + (L - 1) % block_size)
+          return PKV_ERR_RANGE;
+      }
+    }
+  }
   AttnArgs a{};
   a.out = out;
   a.query = query;
@@ -531,6 +667,20 @@ int paged_attn_multi(float* out, const void* query, int q_dtype,
     return PKV_ERR_ALIGN;
   if (!workspace || workspace_bytes < s.ws_bytes) return PKV_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return PKV_ERR_ALIGN;
+  if (debug_checks()) {
+    std::vector<int32_t> lens, tables, qs;
+    const int rc = check_tables(block_tables, max_blocks_per_seq, seq_lens,
+                                num_seqs, max_seq_len, num_blocks, block_size,
+                                stream, &lens, &tables);
+    if (rc != PKV_OK) return rc;
+    if (!fetch_i32(query_start, (int64_t)num_seqs + 1, stream, &qs))
+      return PKV_ERR_HIP;
+    if (qs[0] < 0 || qs[num_seqs] > num_query_tokens) return PKV_ERR_RANGE;
+    for (int32_t q = 0; q < num_seqs; ++q) {
+      const int64_t n = (int64_t)qs[q + 1] - qs[q];
+      if (n < 0 || n > max_query_len || n > lens[q]) return PKV_ERR_RANGE;
+    }
+  }
   AttnArgs a{};
   a.out = out;
   a.query = query;

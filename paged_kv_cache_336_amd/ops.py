@@ -11,7 +11,8 @@ Functions keep the C names: :func:`cache_write_slots`,
 :func:`copy_token_scale_prefixes`, :func:`paged_attn_decode`,
 :func:`paged_attn_decode_fused`,
 :func:`paged_attn_workspace_size`, :func:`paged_attn_multi`,
-:func:`paged_attn_multi_workspace_size`, :func:`pkv_status_string`.
+:func:`paged_attn_multi_workspace_size`, :func:`pkv_status_string`,
+:func:`pkv_set_debug_checks`.
 """
 
 import ctypes
@@ -27,7 +28,7 @@ PKV_KV_STREAM = 0x400       # hint: no block is read by two sequences
 KIND_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
               "fp8_e4m3": PKV_FP8_E4M3, "fp8_e5m2": PKV_FP8_E5M2}
 
-EXPORTED = ("pkv_status_string", "cache_write_slots",
+EXPORTED = ("pkv_status_string", "pkv_set_debug_checks", "cache_write_slots",
             "cache_write_slots_token_scaled", "copy_blocks",
             "copy_block_prefixes", "copy_token_scales",
             "copy_token_scale_prefixes", "paged_attn_workspace_size",
@@ -61,6 +62,8 @@ def load_library(path=None):
     ci = ctypes.c_int
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [ci]
+    lib.pkv_set_debug_checks.restype = ci
+    lib.pkv_set_debug_checks.argtypes = [ci]
     lib.cache_write_slots.restype = ci
     lib.cache_write_slots.argtypes = [vp, vp, ci, vp, vp, ci, vp, i64, i64, i32,
                                       i32, i32, vp, vp, vp]
@@ -103,6 +106,12 @@ def load_library(path=None):
 
 def pkv_status_string(status):
     return load_library().pkv_status_string(int(status)).decode()
+
+
+def pkv_set_debug_checks(enable):
+    """Turn the library's checks of device contents on or off (see
+    pagedkv.h); returns the previous setting as a bool."""
+    return bool(load_library().pkv_set_debug_checks(1 if enable else 0))
 
 
 # ----------------------------------------------------------------------------
@@ -290,10 +299,18 @@ def paged_attn_multi_workspace_size(num_seqs, num_q_heads, num_kv_heads,
 
 class Workspace:
     """A device workspace for the attention calls, grown (never shrunk) to
-    the largest size asked for; it needs no initialisation."""
+    the largest size asked for; it needs no initialisation.
 
-    def __init__(self, device="cuda"):
+    A workspace serves one stream: two calls that share it must not
+    overlap in time, which calls on one stream never do.  It is allocated
+    while ``stream`` is current, so torch's caching allocator ties the
+    memory to the stream the kernels use it on, and a buffer dropped when
+    the workspace grows is reused only after the work queued on that stream
+    before the drop (torch's stream-ordered reuse)."""
+
+    def __init__(self, device="cuda", stream=None):
         self.device = device
+        self.stream = stream
         self.buf = None
 
     def get(self, nbytes):
@@ -301,13 +318,34 @@ class Workspace:
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.empty(int(nbytes), dtype=torch.uint8,
-                                   device=self.device)
+            self.buf = None
+            if self.stream is not None:
+                with torch.cuda.stream(self.stream):
+                    self.buf = torch.empty(int(nbytes), dtype=torch.uint8,
+                                           device=self.device)
+            else:
+                self.buf = torch.empty(int(nbytes), dtype=torch.uint8,
+                                       device=self.device)
         return self.buf
 
 
+# default workspaces, one per (device, stream): calls on different streams
+# never share one (they could overlap in time)
 _default_ws = {}
 _NO_SIZE = (1 << 64) - 1     # (size_t)-1: the size query's "invalid"
+
+
+def _resolve_stream(device, stream):
+    torch = _torch()
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _default_workspace(device, stream):
+    key = (str(device), int(stream.cuda_stream))
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = _default_ws[key] = Workspace(device, stream)
+    return ws
 
 
 def _workspace_buf(workspace, need):
@@ -329,10 +367,10 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
-    need = load_library().paged_attn_workspace_size(s, hq, hkv, d)
+    need = lib.paged_attn_workspace_size(s, hq, hkv, d)
+    stream = _resolve_stream(query.device, stream)
     if workspace is None:
-        key = str(query.device)
-        workspace = _default_ws.setdefault(key, Workspace(query.device))
+        workspace = _default_workspace(query.device, stream)
     buf = _workspace_buf(workspace, need)
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
@@ -355,10 +393,10 @@ def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
-    need = load_library().paged_attn_workspace_size(s, hq, hkv, d)
+    need = lib.paged_attn_workspace_size(s, hq, hkv, d)
+    stream = _resolve_stream(query.device, stream)
     if workspace is None:
-        key_ = str(query.device)
-        workspace = _default_ws.setdefault(key_, Workspace(query.device))
+        workspace = _default_workspace(query.device, stream)
     buf = _workspace_buf(workspace, need)
     _check("paged_attn_decode_fused", lib.paged_attn_decode_fused(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(key), _ptr(value),
@@ -382,10 +420,10 @@ def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
     t, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
     s = int(seq_lens.shape[0])
-    need = load_library().paged_attn_multi_workspace_size(s, hq, hkv, d)
+    need = lib.paged_attn_multi_workspace_size(s, hq, hkv, d)
+    stream = _resolve_stream(query.device, stream)
     if workspace is None:
-        key = str(query.device)
-        workspace = _default_ws.setdefault(key, Workspace(query.device))
+        workspace = _default_workspace(query.device, stream)
     buf = _workspace_buf(workspace, need)
     _check("paged_attn_multi", lib.paged_attn_multi(
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),

@@ -52,10 +52,26 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, 1, 2, 3, 4, 5, 6, 8, 9, 10):
+    for code in (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10):
         assert ops.pkv_status_string(code) != "unknown status"
     assert ops.pkv_status_string(0) == "ok"
     assert ops.pkv_status_string(99) == "unknown status"
+
+
+def test_debug_setting_toggles_and_reports_the_previous_one(lib):
+    """pkv_set_debug_checks returns the setting it replaces (the initial one
+    comes from PAGEDKV_DEBUG, unset here); host-side rejections come before
+    any device copy, so they are unchanged with the checks on."""
+    assert os.environ.get("PAGEDKV_DEBUG", "") in ("", "0")
+    first = lib.pkv_set_debug_checks(1)
+    try:
+        assert first == 0
+        assert lib.pkv_set_debug_checks(1) == 1
+        assert cw(lib, key=None) == NULL
+        assert cw(lib, d=96) == UNSUP
+    finally:
+        assert lib.pkv_set_debug_checks(0) == 1
+    assert lib.pkv_set_debug_checks(0) == 0
 
 
 FAKE = ctypes.c_void_p(4096)      # aligned, never dereferenced by host checks
