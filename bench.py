@@ -460,17 +460,63 @@ def bench_multi(args):
     print(json.dumps(line), flush=True)
 
 
+def workload_kwargs(name, replicas):
+    """Generator arguments: the 8B-shaped batch is small (101 MB of K/V), so
+    it rotates over disjoint replicas that together exceed the 256 MB
+    Infinity Cache; the larger batches (1.7 GB, 2.1 GB) need none."""
+    return {"replicas": replicas} if name == "llama8b_decode" else {}
+
+
+def attention_only(args, name):
+    """The attention call of another decode workload: K calls back to back
+    between one event pair, rotating over its replicas, with its algorithmic
+    bytes and roofline fraction (reported beside the main line)."""
+    import torch
+    from paged_kv_cache_336_amd import workloads as W
+    from paged_kv_cache_336_amd.step import DeviceStep
+    w = W.workload_by_name(name, **workload_kwargs(name, args.replicas))
+    dev = DeviceStep(w, device="cuda:0")
+    R = len(dev.sets)
+    K = args.steps
+
+    def run_attn():
+        for i in range(K):
+            dev.attend(i % R, max_waves=args.max_waves)
+    host_ms = warm_and_estimate(torch, lambda i: dev.attend(
+        i % R, max_waves=args.max_waves), args.warmup)
+    clock = GpuClock(torch)
+    total, enqueue_ms = timed_region(torch, clock, run_attn, host_ms * K)
+    ms = total / K
+    B = algorithmic_bytes(w)["attention"]
+    gbps = B / (ms * 1e-3) / 1e9
+    rec = {"workload": w.name, "attention_us": round(ms * 1e3, 3),
+           "algorithmic_bytes_per_launch": B, "achieved_gbps": round(gbps, 2),
+           "frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "host_us_per_attention_call": round(enqueue_ms * 1e3 / K, 2),
+           "kv_stream_hint": bool(dev.sets[0]["kv_stream"]),
+           "replicas": R}
+    del dev, w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b_decode",
-                    help="llama8b_decode (default), llama70b_decode, "
+    ap.add_argument("--workload", default="llama70b_decode",
+                    help="llama70b_decode (default: the largest single-GPU "
+                    "decode batch at 16-bit precision), llama8b_decode, "
                     "prefix_sharing_{fork,divergent}_bs{32,544}, "
                     "long_context_fp8, worked_example; several new tokens "
                     "per sequence: spec_verify_llama8b, "
                     "chunked_prefill_llama8b")
+    ap.add_argument("--also", default="llama8b_decode,long_context_fp8",
+                    help="comma-separated decode workloads whose attention "
+                    "call is also timed and reported beside the main line "
+                    "(\"\" for none)")
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--max-waves", type=int, default=0,
                     help="cap on the attention kernel's waves (0 = all)")
@@ -511,8 +557,7 @@ def main():
     if args.workload in W.MULTI_WORKLOADS:
         bench_multi(args)
         return
-    kw = {"replicas": args.replicas} if args.workload == "llama8b_decode" \
-        else {}
+    kw = workload_kwargs(args.workload, args.replicas)
     if args.token_scales:
         if args.workload != "long_context_fp8":
             sys.exit("bench.py: --token-scales applies to long_context_fp8")
@@ -579,7 +624,8 @@ def main():
     def run_attn():
         for i in range(K):
             dev.attend(i % R, max_waves=args.max_waves)
-    attn_total, _ = timed_region(torch, clock, run_attn, host_step_ms * K)
+    attn_total, attn_host_ms = timed_region(torch, clock, run_attn,
+                                           host_step_ms * K)
     attn_avg_ms = attn_total / K
 
     # ---- paging overhead: the same calls with contiguous block tables ----
@@ -690,6 +736,8 @@ def main():
         "copy_blocks_gbps": (round(nbytes["copy_blocks"] / (copy_ms * 1e-3)
                                    / 1e9, 2) if copy_ms > 0 else None),
         "host_enqueue_ms": round(host_ms, 3),
+        "host_us_per_step": round(host_ms * 1e3 / K, 2),
+        "host_us_per_attention_call": round(attn_host_ms * 1e3 / K, 2),
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_attn_decode (attn_decode_kernel + attn_merge_kernel)",
@@ -703,6 +751,13 @@ def main():
         "cpu_baseline": cpu,
         "paging_overhead": paging,
     }
+    others = [n for n in args.also.split(",") if n and n != args.workload
+              and n in W.DECODE_WORKLOADS] if not args.token_scales else []
+    if others:
+        del dev
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        line["other_workloads"] = [attention_only(args, n) for n in others]
     print(json.dumps(line), flush=True)
 
 

@@ -701,3 +701,10 @@ def workload_by_name(name, **kw):
     if name == "long_context_fp8":
         return long_context_fp8(**kw)
     raise KeyError(name)
+
+
+# decode workloads workload_by_name knows (one new token per sequence)
+DECODE_WORKLOADS = ("worked_example", "llama8b_decode", "llama70b_decode",
+                    "prefix_sharing_fork_bs32", "prefix_sharing_fork_bs544",
+                    "prefix_sharing_divergent_bs32",
+                    "prefix_sharing_divergent_bs544", "long_context_fp8")

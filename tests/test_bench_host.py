@@ -29,3 +29,20 @@ def test_attention_bytes_count_each_live_row_once():
     q_out = w.num_seqs * w.num_q_heads * w.head_dim * (2 + 4)
     tables = int(np.sum((w.seq_lens + 15) // 16)) * 4 + 4 * w.num_seqs
     assert B == kv + q_out + tables
+
+
+def test_default_line_runs_the_largest_16bit_decode_batch():
+    """With no flags the line measures the 70B-shaped batch (256 sequences,
+    1.7 GB of K/V per call); the other decode workloads it also times are
+    names the generator knows."""
+    import subprocess
+    import sys
+    src = open(bench.__file__).read()
+    assert 'ap.add_argument("--workload", default="llama70b_decode"' in src
+    start = src.index('ap.add_argument("--also", default="') + \
+        len('ap.add_argument("--also", default="')
+    also = src[start:src.index('"', start)].split(",")
+    assert also and all(n in W.DECODE_WORKLOADS for n in also)
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
