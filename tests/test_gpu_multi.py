@@ -186,16 +186,16 @@ def test_spec_verify_full():
     assert err <= TOL["bf16"]
 
 
-def test_chunked_prefill_full_sampled():
+def test_chunked_prefill_full():
     """The chunked-prefill batch at full size (8 x (4096 cached + 512 new)),
-    in the launch configuration the benchmark times; sequences 0 and 5
-    against the oracle (all their 512 rows), every row finite."""
+    in the launch configuration the benchmark times; every output row of
+    every sequence against the oracle."""
     mq = W.chunked_prefill_llama8b()
     say("multi chunked_prefill_llama8b full")
     _, out = run_multi(mq)
     assert np.isfinite(out).all()
-    rows, ref = oracle_multi(mq, oracle_pools(mq.w), seqs=[0, 5])
-    err = max_abs_err(out[rows], ref)
+    ref = oracle_multi(mq, oracle_pools(mq.w))
+    err = max_abs_err(out, ref)
     say(f"multi chunked_prefill_llama8b: max abs err {err:.3g}")
     assert err <= TOL["bf16"]
 
