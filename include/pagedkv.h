@@ -361,6 +361,42 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
                       hipStream_t stream);
 
 /*
+ * paged_attn_decode_noalloc -- paged_attn_decode without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * call allocates nothing; the partial results that paged_attn_decode keeps
+ * in the caller's workspace live in a device array of the library instead
+ * (16.3 MiB per GPU the library runs on, held until the process ends; its
+ * device address is looked up once per device, at the first call there).
+ *
+ * Arguments, results and rules are paged_attn_decode's, with these limits:
+ * the split uses at most 1024 waves (max_waves 0 means every wave the GPU
+ * holds at once, up to 1024; max_waves above 1024 returns
+ * PKV_ERR_UNSUPPORTED), and the debug checks of pkv_set_debug_checks are
+ * not run (they copy and wait).  On a GPU whose resident waves number 1024
+ * or fewer (an MI355X holds 1024 in this kernel's launch shape) the output
+ * is that of paged_attn_decode with the same max_waves, bit for bit.
+ *
+ * Every call on one GPU shares that GPU's array and needs nothing in it
+ * from an earlier call (no part of it must start at zero).  Calls that
+ * overlap in time on one GPU (on different streams, or from different
+ * threads without ordering) race on it and give unspecified results;
+ * calls on one stream never overlap.
+ */
+int paged_attn_decode_noalloc(float* out, const void* query, int q_dtype,
+                              const void* k_cache, const void* v_cache,
+                              int cache_dtype, const float* k_scale,
+                              const float* v_scale,
+                              const int32_t* block_tables,
+                              int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t max_seq_len,
+                              int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              int64_t num_blocks, int32_t block_size,
+                              float scale, int32_t max_waves,
+                              hipStream_t stream);
+
+/*
  * paged_attn_decode_fused -- cache_write_slots of one new token per sequence
  * and paged_attn_decode in one launch: the result (out and both pools) is
  * that of cache_write_slots(key, value, ..., slot_mapping, num_seqs, ...)

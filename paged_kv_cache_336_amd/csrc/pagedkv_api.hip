@@ -8,6 +8,8 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -85,6 +87,47 @@ int attn_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   s.off_o = align_up(s.off_l + slots * 4, 256);
   s.ws_bytes = s.off_o + slots * (size_t)head_dim * 4;
   *out = s;
+  return PKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of paged_attn_decode_noalloc: the attention workspace of a call
+// with at most kScratchWaves waves, held in a device array of this library
+// (one per GPU, alive until the process ends) instead of a buffer the
+// caller allocates.  Its size is the workspace layout's largest case:
+// kMaxSeqs + 1 tile-prefix words, then running maxima and sums and partial
+// outputs of 16 query heads per slot at head_dim 128 (16.3 MiB).
+// ---------------------------------------------------------------------------
+constexpr int kScratchWaves = 1024;
+constexpr size_t kScratchSlots = (size_t)kScratchWaves * 2 * 16;
+constexpr size_t kScratchOffM = ((size_t)(kMaxSeqs + 1) * 4 + 255) / 256 * 256;
+constexpr size_t kScratchOffL = (kScratchOffM + kScratchSlots * 4 + 255) / 256 * 256;
+constexpr size_t kScratchOffO = (kScratchOffL + kScratchSlots * 4 + 255) / 256 * 256;
+constexpr size_t kScratchBytes = kScratchOffO + kScratchSlots * 128 * 4;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The scratch array's device address on the current device, looked up once
+// per device (with that device current) and kept.  The array's name is a
+// host-side stand-in in host code: only this address may be handed to
+// kernels.
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  const auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return PKV_OK;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+    return PKV_ERR_HIP;
+  g_scratch_ptr[dev] = ptr;
+  *out = ptr;
   return PKV_OK;
 }
 
@@ -466,7 +509,7 @@ int decode_common(float* out, const void* query, int q_dtype,
                   float scale, int32_t max_waves, void* workspace,
                   size_t workspace_bytes, const void* key, const void* value,
                   const int32_t* slot_mapping, bool fused,
-                  hipStream_t stream) {
+                  hipStream_t stream, bool noalloc = false) {
   bool per_head = false, per_token = false, kv_stream = false;
   const int cache_arg = cache_dtype;
   if (!valid_dtype(q_dtype) ||
@@ -483,9 +526,12 @@ int decode_common(float* out, const void* query, int q_dtype,
     return PKV_ERR_SHAPE;
   if (num_blocks * (int64_t)block_size > INT_MAX) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKV_ERR_SHAPE;
+  // the scratch holds the partials of at most kScratchWaves waves
+  if (noalloc && max_waves > kScratchWaves) return PKV_ERR_UNSUPPORTED;
   AttnShape s;
   const int rc =
-      attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, false, &s);
+      attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, false, &s,
+                 noalloc ? kScratchWaves : kMaxWaves);
   if (rc != PKV_OK) return rc;
   // the fused write relies on one query-head chunk per kv head
   if (fused && s.group > 16) return PKV_ERR_UNSUPPORTED;
@@ -506,9 +552,18 @@ int decode_common(float* out, const void* query, int q_dtype,
   if (fused && (!aligned(key, 16) || !aligned(value, 16) ||
                 !aligned(slot_mapping, 4)))
     return PKV_ERR_ALIGN;
+  if (noalloc) {
+    if (s.ws_bytes > kScratchBytes) return PKV_ERR_WORKSPACE;
+    const int src = scratch_address(&workspace);
+    if (src != PKV_OK) return src;
+    workspace_bytes = kScratchBytes;
+    if (max_waves == 0) max_waves = kScratchWaves;
+  }
   if (!workspace || workspace_bytes < s.ws_bytes) return PKV_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return PKV_ERR_ALIGN;
-  if (debug_checks()) {
+  // (debug checks copy and wait, which a call that must stay capturable
+  // cannot do: the no-alloc entry skips them)
+  if (!noalloc && debug_checks()) {
     std::vector<int32_t> lens, tables, slots;
     int rc = check_tables(block_tables, max_blocks_per_seq, seq_lens, num_seqs,
                           max_seq_len, num_blocks, block_size, stream, &lens,
@@ -589,6 +644,26 @@ int paged_attn_decode(float* out, const void* query, int q_dtype,
                        num_kv_heads, head_dim, num_blocks, block_size, scale,
                        max_waves, workspace, workspace_bytes, nullptr, nullptr,
                        nullptr, false, stream);
+}
+
+int paged_attn_decode_noalloc(float* out, const void* query, int q_dtype,
+                              const void* k_cache, const void* v_cache,
+                              int cache_dtype, const float* k_scale,
+                              const float* v_scale,
+                              const int32_t* block_tables,
+                              int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t max_seq_len,
+                              int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              int64_t num_blocks, int32_t block_size,
+                              float scale, int32_t max_waves,
+                              hipStream_t stream) {
+  return decode_common(out, query, q_dtype, k_cache, v_cache, cache_dtype,
+                       k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       seq_lens, max_seq_len, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, num_blocks, block_size, scale,
+                       max_waves, nullptr, 0, nullptr, nullptr, nullptr,
+                       false, stream, true);
 }
 
 int paged_attn_decode_fused(float* out, const void* query, int q_dtype,

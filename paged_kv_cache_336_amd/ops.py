@@ -9,7 +9,7 @@ Functions keep the C names: :func:`cache_write_slots`,
 :func:`cache_write_slots_token_scaled`, :func:`copy_blocks`,
 :func:`copy_block_prefixes`, :func:`copy_token_scales`,
 :func:`copy_token_scale_prefixes`, :func:`paged_attn_decode`,
-:func:`paged_attn_decode_fused`,
+:func:`paged_attn_decode_noalloc`, :func:`paged_attn_decode_fused`,
 :func:`paged_attn_workspace_size`, :func:`paged_attn_multi`,
 :func:`paged_attn_multi_workspace_size`, :func:`pkv_status_string`,
 :func:`pkv_set_debug_checks`.
@@ -33,7 +33,8 @@ EXPORTED = ("pkv_status_string", "pkv_set_debug_checks", "cache_write_slots",
             "copy_block_prefixes", "copy_token_scales",
             "copy_token_scale_prefixes", "paged_attn_workspace_size",
             "copy_blocks_layers", "copy_block_prefixes_layers",
-            "paged_attn_decode", "paged_attn_decode_fused",
+            "paged_attn_decode", "paged_attn_decode_noalloc",
+            "paged_attn_decode_fused",
             "paged_attn_multi_workspace_size", "paged_attn_multi")
 
 _lib = None
@@ -88,6 +89,10 @@ def load_library(path=None):
     lib.paged_attn_decode.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp, vp, i32,
                                       vp, i32, i32, i32, i32, i32, i64, i32,
                                       f32, i32, vp, sz, vp]
+    lib.paged_attn_decode_noalloc.restype = ci
+    lib.paged_attn_decode_noalloc.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp,
+                                              vp, i32, vp, i32, i32, i32, i32,
+                                              i32, i64, i32, f32, i32, vp]
     lib.paged_attn_decode_fused.restype = ci
     lib.paged_attn_decode_fused.argtypes = [vp, vp, ci, vp, vp, vp, vp, ci,
                                             vp, vp, vp, vp, i32, vp, i32, i32,
@@ -381,6 +386,23 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
         int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
         _stream(stream)))
+
+
+def paged_attn_decode_noalloc(out, query, k_cache, v_cache, block_tables,
+                              seq_lens, max_seq_len, scale, k_scale=None,
+                              v_scale=None, max_waves=0, cache_kind=None,
+                              stream=None, kv_stream=False):
+    """paged_attn_decode with the library's own scratch instead of a
+    workspace: allocates nothing (see pagedkv.h)."""
+    lib = load_library()
+    s, hq, d = query.shape
+    nb, bs, hkv, _ = k_cache.shape
+    _check("paged_attn_decode_noalloc", lib.paged_attn_decode_noalloc(
+        _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
+        _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale, kv_stream),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), s, hq,
+        hkv, d, nb, bs, float(scale), int(max_waves), _stream(stream)))
 
 
 def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
