@@ -23,8 +23,11 @@
 //     buffer resource whose size covers exactly the live rows, so rows past
 //     the end of the sequence are neither fetched nor need a branch, and the
 //     next tile's rows are requested before the current one is computed.
-//   * K rows go straight from HBM into MFMA A-operand registers as 16-byte
-//     loads (lane = token row + 16 * piece group), Q sits in the B operand;
+//   * K rows go from HBM into MFMA A-operand registers as 16-byte loads
+//     (lane = token row + 16 * piece group) -- or, with the streaming hint,
+//     are loaded as whole 128-byte lines like the V rows (so they can
+//     stream), staged in the wave's LDS and read back in that layout --; Q
+//     sits in the B operand;
 //     S = K . Q^T on v_mfma_f32_16x16x32 (bf16/f16; fp8 keys are decoded to
 //     the query's type first) or eight 16x16x4 f32 steps.
 //   * Scores are scaled into the log2 domain; the running max uses xor
@@ -222,10 +225,15 @@ void attn_decode_kernel(AttnArgs a) {
   typedef Shape<QT, CT, D> S;
   constexpr int NBLK = S::NBLK;
   constexpr bool PREFETCH = UNIFORM && CT::bytes <= 2;
+  // K rows through LDS where they stream (AUX: the batch's hint): loaded as
+  // whole lines like the V rows, then read back as the MFMA operand
+  constexpr bool KL = PREFETCH && AUX != 0;
+  constexpr int KST = KL ? S::KSTAGE_BYTES : 0;
   static_assert(!PT || (is_fp8<CT>::value && !WRITE),
                 "per-token scales: fp8 caches, separate write");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * S::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16)))
+  uint8_t smem[kWaves * (S::STAGE_BYTES + KST)];
   __shared__ int sm_wsum[kWaves];
   extern __shared__ int sm_seq[];  // tex[num_seqs + 1] | lens[num_seqs]
 
@@ -298,6 +306,7 @@ void attn_decode_kernel(AttnArgs a) {
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_cache);
   uint8_t* vt = smem + wave * S::STAGE_BYTES;
+  uint8_t* kt = smem + kWaves * S::STAGE_BYTES + wave * KST;
   const int gmax = a.slot_heads;
 
   Seg X = segment_at<S::TT>(tb, te, U, tex, lens, a);
@@ -324,7 +333,7 @@ void attn_decode_kernel(AttnArgs a) {
   };
   TileRegs<QT, CT, D> cur;
   if constexpr (PREFETCH)
-    load_tile_uniform<QT, CT, D, PT, AUX>(cur, a.block_size, a.num_blocks, ta, tbw,
+    load_tile_uniform<QT, CT, D, PT, AUX, KL>(cur, a.block_size, a.num_blocks, ta, tbw,
                                      X.wb, kpool + (int64_t)X.h * S::ROW_BYTES,
                                      vpool + (int64_t)X.h * S::ROW_BYTES,
                                      stride, X.t_begin, X.t_end, lane,
@@ -377,7 +386,7 @@ void attn_decode_kernel(AttnArgs a) {
           tbw = load_window(shifted, 1, a, lane);
         }
         TileRegs<QT, CT, D> nxt;
-        load_tile_uniform<QT, CT, D, PT, AUX>(
+        load_tile_uniform<QT, CT, D, PT, AUX, KL>(
             nxt, a.block_size, a.num_blocks, same_seg ? ta : ta_n, same_seg ? tbw : tb_n,
             same_seg ? wb : Xn.wb, same_seg ? kbase : kbase_n,
             same_seg ? vbase : vbase_n, stride,
@@ -385,16 +394,16 @@ void attn_decode_kernel(AttnArgs a) {
             lane, same_seg ? tsc : token_scales(Xn));
         __builtin_amdgcn_sched_barrier(0);
         stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
-        compute_tile<QT, CT, D, false, PT, !PT>(cur.kw[0], qw, st, vt, t0, X.t_end,
-                                           qk_mul, lane, 0, cur.sc[0]);
-#pragma unroll
-        for (int sb = 1; sb < S::SUB; ++sb) {
-          if (t0 + 32 * sb < X.t_end) {  // (only the last tile has empty ones)
-            stage_v<QT, CT, D>(cur.vraw[sb], vt, lane);
-            compute_tile<QT, CT, D, false, PT, !PT>(cur.kw[sb], qw, st, vt,
-                                               t0 + 32 * sb, X.t_end, qk_mul,
-                                               lane, 0, cur.sc[sb]);
-          }
+        if constexpr (KL) {
+          stage_k<QT, CT, D>(cur.kraw[0], kt, lane);
+          uint32_t kw[2][S::KWORDS];
+          k_from_lds<QT, CT, D>(kw, kt, lane);
+          compute_tile<QT, CT, D, false, PT, !PT>(kw, qw, st, vt, t0, X.t_end,
+                                             qk_mul, lane, 0, cur.sc[0]);
+        } else {
+          compute_tile<QT, CT, D, false, PT, !PT>(cur.kw[0], qw, st, vt, t0,
+                                             X.t_end, qk_mul, lane, 0,
+                                             cur.sc[0]);
         }
         cur = nxt;
       }

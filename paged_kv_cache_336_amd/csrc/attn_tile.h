@@ -36,9 +36,11 @@ __device__ __forceinline__ int split_workgroup(int b, int n, bool shared) {
 constexpr uint32_t kRawBufferFlags = 0x00020000;  // dword3: 32-bit data format
 // Cache-policy operand of a buffer load: 0 = the default policy; kLoadNT
 // sets the non-temporal (streaming) bit.  The tile loaders apply it to the V
-// rows only, whose loads cover whole 128-byte lines: each K load instruction
-// reads 64 bytes of each of 16 rows, so a line is requested by two
-// instructions, and streaming K measured slower.
+// rows, whose loads cover whole 128-byte lines, and to K rows loaded the
+// same way for staging through LDS (load_tile_uniform's KL); loaded straight
+// into the MFMA operand layout, each K load instruction reads 64 bytes of
+// each of 16 rows, so a line is requested by two instructions, and
+// streaming those measured slower.
 constexpr int kLoadNT = 2;
 
 template <typename QT, typename CT> struct PvOperand { typedef CT type; };
@@ -74,6 +76,7 @@ template <typename QT, typename CT, int D> struct Shape {
   static constexpr int QWORDS = D / 4 * QT::bytes / 4;
   static constexpr int NBLK = D / 16;                 // 16-wide output blocks
   static constexpr int STAGE_BYTES = 32 * LDS_ROW;    // V sub-tile, one wave
+  static constexpr int KSTAGE_BYTES = 32 * ROW_BYTES;
   static constexpr int SPANS = LDS_ROW / 32;          // 32-byte spans per row
   // A tile -- the unit of the split and of each load request -- is SUB
   // 32-token sub-tiles (the MFMA tile).  One sub-tile per request measured
@@ -94,6 +97,7 @@ template <typename QT, typename CT, int D> struct Shape {
 template <typename QT, typename CT, int D> struct TileRegs {
   typedef Shape<QT, CT, D> S;
   uint32_t kw[S::SUB][2][S::KWORDS];
+  u32x4_t kraw[S::SUB][S::NV];
   u32x4_t vraw[S::SUB][S::NV];
   float sc[S::SUB];
 };
@@ -125,7 +129,8 @@ template <int NBLK> struct WaveState {
 // two VGPRs: lane i of tab_a / tab_b holds the entry of logical block
 // wb + i / wb + 64 + i, and a wave-uniform readlane turns it into a scalar.
 // ---------------------------------------------------------------------------
-template <typename QT, typename CT, int D, bool PT = false, int AUX = 0>
+template <typename QT, typename CT, int D, bool PT = false, int AUX = 0,
+          bool KL = false>
 __device__ __forceinline__ void load_tile_uniform(
     TileRegs<QT, CT, D>& tr, int bs, int nblocks, uint32_t tab_a,
     uint32_t tab_b, int wb, const uint8_t* kbase, const uint8_t* vbase,
@@ -175,16 +180,26 @@ __device__ __forceinline__ void load_tile_uniform(
           const_cast<uint8_t*>(vbase + row0 * stride), (short)0, nrec,
           kRawBufferFlags);
     }
+    if constexpr (KL) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+      for (int v = 0; v < S::NV; ++v) {
+        const int hh = (v * S::TOK_PER_V) >> 4;
+        const int tin = (v * S::TOK_PER_V) & 15;
+        tr.kraw[sb][v] = __builtin_amdgcn_raw_buffer_load_b128(
+            kr[hh], vofs + tin * (int)stride, 0, AUX);
+      }
+    } else {
 #pragma unroll
-      for (int r = 0; r < S::KPIECES; ++r) {
-        const u32x4_t v =
-            __builtin_amdgcn_raw_buffer_load_b128(kr[hh], kofs + r * 64, 0, 0);
-        tr.kw[sb][hh][4 * r + 0] = v[0];
-        tr.kw[sb][hh][4 * r + 1] = v[1];
-        tr.kw[sb][hh][4 * r + 2] = v[2];
-        tr.kw[sb][hh][4 * r + 3] = v[3];
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int r = 0; r < S::KPIECES; ++r) {
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+              kr[hh], kofs + r * 64, 0, 0);
+          tr.kw[sb][hh][4 * r + 0] = v[0];
+          tr.kw[sb][hh][4 * r + 1] = v[1];
+          tr.kw[sb][hh][4 * r + 2] = v[2];
+          tr.kw[sb][hh][4 * r + 3] = v[3];
+        }
       }
     }
 #pragma unroll
@@ -315,6 +330,49 @@ __device__ __forceinline__ void stage_v(const u32x4_t (&vraw)[Shape<QT, CT, D>::
     }
   }
 
+}
+
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ int k_lds_at(int t, int x) {
+  typedef Shape<QT, CT, D> S;
+  constexpr int RPB = S::ROW_BYTES >= 256 ? 1 : 256 / S::ROW_BYTES;
+  constexpr int NSW = S::PPR < 16 ? S::PPR : 16;
+  return t * S::ROW_BYTES + ((x ^ ((t / RPB) & (NSW - 1))) << 4);
+}
+
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void stage_k(
+    const u32x4_t (&kraw)[Shape<QT, CT, D>::NV], uint8_t* kt, int lane) {
+  typedef Shape<QT, CT, D> S;
+#pragma unroll
+  for (int v = 0; v < S::NV; ++v) {
+    const int tv = lane / S::PPR + v * S::TOK_PER_V;
+    *reinterpret_cast<u32x4_t*>(kt + k_lds_at<QT, CT, D>(tv, lane % S::PPR)) =
+        kraw[v];
+  }
+}
+
+template <typename QT, typename CT, int D>
+using KWords = uint32_t[2][Shape<QT, CT, D>::KWORDS];
+
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void k_from_lds(KWords<QT, CT, D>& kw,
+                                           const uint8_t* kt, int lane) {
+  typedef Shape<QT, CT, D> S;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int r = 0; r < S::KPIECES; ++r) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+          kt + k_lds_at<QT, CT, D>(16 * hh + c, 4 * r + j));
+      kw[hh][4 * r + 0] = v[0];
+      kw[hh][4 * r + 1] = v[1];
+      kw[hh][4 * r + 2] = v[2];
+      kw[hh][4 * r + 3] = v[3];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
