@@ -619,6 +619,17 @@ def main():
             host_step_ms * K)
         unfused_ms = unfused_total / K
 
+    # ---- the same steps through prepared calls: arguments marshalled once,
+    # as a serving loop whose tensors stay in place issues them ----
+    dev.prepare(fused=fused, max_waves=args.max_waves)
+    for i in range(max(args.warmup, 1)):
+        dev.step_prepared(i % R)
+    torch.cuda.synchronize()
+    prep_total, prep_host_ms = timed_region(
+        torch, clock, lambda: [dev.step_prepared(i % R) for i in range(K)],
+        host_step_ms * K)
+    prep_ms = prep_total / K
+
     # ---- the attention call alone: K calls back to back between one event
     # pair on the stream the kernels run on (torch's current stream) ----
     def run_attn():
@@ -627,6 +638,11 @@ def main():
     attn_total, attn_host_ms = timed_region(torch, clock, run_attn,
                                            host_step_ms * K)
     attn_avg_ms = attn_total / K
+    attn_calls = [dev.attend(r, max_waves=args.max_waves, prepare=True)
+                  for r in range(R)]
+    _, attn_prep_host_ms = timed_region(
+        torch, clock, lambda: [attn_calls[i % R]() for i in range(K)],
+        host_step_ms * K)
 
     # ---- paging overhead: the same calls with contiguous block tables ----
     paging = None
@@ -738,6 +754,12 @@ def main():
         "host_enqueue_ms": round(host_ms, 3),
         "host_us_per_step": round(host_ms * 1e3 / K, 2),
         "host_us_per_attention_call": round(attn_host_ms * 1e3 / K, 2),
+        "prepared": {"ms_per_step": round(prep_ms, 5),
+                     "host_us_per_step": round(prep_host_ms * 1e3 / K, 2),
+                     "host_us_per_attention_call":
+                         round(attn_prep_host_ms * 1e3 / K, 2),
+                     "note": "the same calls with their arguments "
+                             "marshalled once (ops prepare=True)"},
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_attn_decode (attn_decode_kernel + attn_merge_kernel)",

@@ -13,6 +13,11 @@ Functions keep the C names: :func:`cache_write_slots`,
 :func:`paged_attn_workspace_size`, :func:`paged_attn_multi`,
 :func:`paged_attn_multi_workspace_size`, :func:`pkv_status_string`,
 :func:`pkv_set_debug_checks`.
+
+Each operation also takes ``prepare=True``, which returns the call with its
+arguments marshalled (a :class:`PreparedCall`) instead of making it: a
+serving loop whose tensors stay in place issues each step's calls again
+without any per-call lookups.
 """
 
 import ctypes
@@ -165,15 +170,58 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _stream_handle(stream, t):
+    """The HIP stream a call is queued on, as an integer handle: ``stream``
+    if given, else the current stream of tensor t's device (read without
+    building a torch Stream object, which costs microseconds per call)."""
+    if stream is not None:
+        return int(stream.cuda_stream)
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    idx = t.device.index
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None and idx is not None:
+        return raw(idx)
+    return int(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _stream(stream, t):
+    return ctypes.c_void_p(_stream_handle(stream, t))
 
 
 def _check(fn, status):
     if status != 0:
         raise PagedKVError(fn, status)
+
+
+class PreparedCall:
+    """One library call with its arguments marshalled once: pointers,
+    sizes, dtype codes, the stream and, for attention, the workspace.
+    Calling it issues the same call again, which is the cheapest way to
+    queue a step whose buffers stay in place (a serving loop's persistent
+    tensors): no shape, dtype or stream lookups per call.  The tensors it
+    was made from must stay alive and in place; their contents may change
+    between calls.  The ``prepare=True`` argument of the operations below
+    returns one instead of making the call."""
+
+    __slots__ = ("name", "fn", "args")
+
+    def __init__(self, name, fn, args):
+        self.name = name
+        self.fn = fn
+        self.args = args
+
+    def __call__(self):
+        status = self.fn(*self.args)
+        if status != 0:
+            raise PagedKVError(self.name, status)
+
+
+def _run(name, fn, args, prepare):
+    """Make the call, or with prepare return it as a PreparedCall."""
+    if prepare:
+        return PreparedCall(name, fn, args)
+    _check(name, fn(*args))
+    return None
 
 
 # ----------------------------------------------------------------------------
@@ -182,20 +230,21 @@ def _check(fn, status):
 
 def cache_write_slots(key, value, k_cache, v_cache, slot_mapping,
                       k_scale=None, v_scale=None, cache_kind=None,
-                      stream=None):
-    """Scatter key/value [T, Hkv, D] into the pools at slot_mapping (in place)."""
+                      stream=None, prepare=False):
+    """Scatter key/value [T, Hkv, D] into the pools at slot_mapping (in
+    place)."""
     lib = load_library()
     nb, bs, hkv, d = k_cache.shape
-    _check("cache_write_slots", lib.cache_write_slots(
+    return _run("cache_write_slots", lib.cache_write_slots, (
         _ptr(key), _ptr(value), dtype_code(key), _ptr(k_cache), _ptr(v_cache),
         cache_code(k_cache, cache_kind, k_scale), _ptr(slot_mapping),
         int(slot_mapping.shape[0]), nb, bs, hkv, d, _ptr(k_scale),
-        _ptr(v_scale), _stream(stream)))
+        _ptr(v_scale), _stream(stream, k_cache)), prepare)
 
 
 def cache_write_slots_token_scaled(key, value, k_cache, v_cache, k_scales,
                                    v_scales, slot_mapping, cache_kind=None,
-                                   stream=None):
+                                   stream=None, prepare=False):
     """Scatter key/value [T, Hkv, D] into an fp8 cache with a scale per
     written row, stored in k_scales / v_scales [num_blocks, block_size,
     Hkv] (float32, in place)."""
@@ -203,61 +252,65 @@ def cache_write_slots_token_scaled(key, value, k_cache, v_cache, k_scales,
     nb, bs, hkv, d = k_cache.shape
     assert tuple(k_scales.shape) == (nb, bs, hkv) and \
         tuple(v_scales.shape) == (nb, bs, hkv)
-    _check("cache_write_slots_token_scaled",
-           lib.cache_write_slots_token_scaled(
-               _ptr(key), _ptr(value), dtype_code(key), _ptr(k_cache),
-               _ptr(v_cache), dtype_code(k_cache, cache_kind) |
-               PKV_SCALE_PER_TOKEN, _ptr(k_scales), _ptr(v_scales),
-               _ptr(slot_mapping), int(slot_mapping.shape[0]), nb, bs, hkv,
-               d, _stream(stream)))
+    return _run("cache_write_slots_token_scaled",
+                lib.cache_write_slots_token_scaled, (
+                    _ptr(key), _ptr(value), dtype_code(key), _ptr(k_cache),
+                    _ptr(v_cache), dtype_code(k_cache, cache_kind) |
+                    PKV_SCALE_PER_TOKEN, _ptr(k_scales), _ptr(v_scales),
+                    _ptr(slot_mapping), int(slot_mapping.shape[0]), nb, bs,
+                    hkv, d, _stream(stream, k_cache)), prepare)
 
 
-def _scales_copy(name, k_scales, v_scales, rows, width, stream):
+def _scales_copy(name, k_scales, v_scales, rows, width, stream,
+                 prepare=False):
     lib = load_library()
     nb, bs, hkv = k_scales.shape
     assert tuple(v_scales.shape) == (nb, bs, hkv)
     assert rows.shape[1:] == (width,)
-    _check(name, getattr(lib, name)(
+    return _run(name, getattr(lib, name), (
         _ptr(k_scales), _ptr(v_scales), _ptr(rows), int(rows.shape[0]), nb,
-        bs, hkv, _stream(stream)))
+        bs, hkv, _stream(stream, k_scales)), prepare)
 
 
-def copy_token_scales(k_scales, v_scales, block_pairs, stream=None):
+def copy_token_scales(k_scales, v_scales, block_pairs, stream=None,
+                      prepare=False):
     """Per-token scale arrays through whole-block copies [P, 2]."""
-    _scales_copy("copy_token_scales", k_scales, v_scales, block_pairs,
-                 2, stream)
+    return _scales_copy("copy_token_scales", k_scales, v_scales,
+                        block_pairs, 2, stream, prepare)
 
 
 def copy_token_scale_prefixes(k_scales, v_scales, block_triples,
-                              stream=None):
+                              stream=None, prepare=False):
     """Per-token scale arrays through token-prefix copies [P, 3]."""
-    _scales_copy("copy_token_scale_prefixes", k_scales, v_scales,
-                 block_triples, 3, stream)
+    return _scales_copy("copy_token_scale_prefixes", k_scales, v_scales,
+                        block_triples, 3, stream, prepare)
 
 
-def copy_blocks(k_cache, v_cache, block_pairs, cache_kind=None, stream=None):
+def copy_blocks(k_cache, v_cache, block_pairs, cache_kind=None, stream=None,
+                prepare=False):
     """Copy whole blocks src -> dst for every row of block_pairs [P, 2]."""
     lib = load_library()
     nb, bs, hkv, d = k_cache.shape
-    _check("copy_blocks", lib.copy_blocks(
+    return _run("copy_blocks", lib.copy_blocks, (
         _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache, cache_kind),
         _ptr(block_pairs), int(block_pairs.shape[0]), nb, bs, hkv, d,
-        _stream(stream)))
+        _stream(stream, k_cache)), prepare)
 
 
 def copy_block_prefixes(k_cache, v_cache, block_triples, cache_kind=None,
-                        stream=None):
+                        stream=None, prepare=False):
     """Copy the first `tokens` slots of block src to block dst for every
     row {src, dst, tokens} of block_triples [P, 3]."""
     lib = load_library()
     nb, bs, hkv, d = k_cache.shape
-    _check("copy_block_prefixes", lib.copy_block_prefixes(
+    return _run("copy_block_prefixes", lib.copy_block_prefixes, (
         _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache, cache_kind),
         _ptr(block_triples), int(block_triples.shape[0]), nb, bs, hkv, d,
-        _stream(stream)))
+        _stream(stream, k_cache)), prepare)
 
 
-def _layers_copy(fn, k_caches, v_caches, rows, cache_kind, stream, width):
+def _layers_copy(fn, k_caches, v_caches, rows, cache_kind, stream, width,
+                 prepare=False):
     """k_caches, v_caches: [num_layers, num_blocks, block_size, Hkv, D]."""
     lib = load_library()
     nl, nb, bs, hkv, d = k_caches.shape
@@ -265,24 +318,25 @@ def _layers_copy(fn, k_caches, v_caches, rows, cache_kind, stream, width):
     assert v_caches.shape == k_caches.shape and \
         v_caches.stride(0) == k_caches.stride(0)
     assert rows.shape[1:] == (width,)
-    _check(fn.__name__, fn(
+    return _run(fn.__name__, fn, (
         _ptr(k_caches), _ptr(v_caches), stride, nl,
         dtype_code(k_caches, cache_kind), _ptr(rows), int(rows.shape[0]), nb,
-        bs, hkv, d, _stream(stream)))
+        bs, hkv, d, _stream(stream, k_caches)), prepare)
 
 
 def copy_blocks_layers(k_caches, v_caches, block_pairs, cache_kind=None,
-                       stream=None):
+                       stream=None, prepare=False):
     """Whole-block copies src -> dst in every layer's pools (one launch)."""
-    _layers_copy(load_library().copy_blocks_layers, k_caches, v_caches,
-                 block_pairs, cache_kind, stream, 2)
+    return _layers_copy(load_library().copy_blocks_layers, k_caches,
+                        v_caches, block_pairs, cache_kind, stream, 2, prepare)
 
 
 def copy_block_prefixes_layers(k_caches, v_caches, block_triples,
-                               cache_kind=None, stream=None):
+                               cache_kind=None, stream=None, prepare=False):
     """copy_block_prefixes in every layer's pools (one launch)."""
-    _layers_copy(load_library().copy_block_prefixes_layers, k_caches,
-                 v_caches, block_triples, cache_kind, stream, 3)
+    return _layers_copy(load_library().copy_block_prefixes_layers, k_caches,
+                        v_caches, block_triples, cache_kind, stream, 3,
+                        prepare)
 
 
 def paged_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim):
@@ -340,13 +394,10 @@ _default_ws = {}
 _NO_SIZE = (1 << 64) - 1     # (size_t)-1: the size query's "invalid"
 
 
-def _resolve_stream(device, stream):
-    torch = _torch()
-    return stream if stream is not None else torch.cuda.current_stream(device)
-
-
-def _default_workspace(device, stream):
-    key = (str(device), int(stream.cuda_stream))
+def _default_workspace(device, stream, handle):
+    """The default workspace of (device, stream handle); created while that
+    stream is current (``stream`` None: it is the current stream)."""
+    key = (device.index, handle)
     ws = _default_ws.get(key)
     if ws is None:
         ws = _default_ws[key] = Workspace(device, stream)
@@ -366,18 +417,18 @@ def _workspace_buf(workspace, need):
 def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
                       max_seq_len, scale, k_scale=None, v_scale=None,
                       max_waves=0, workspace=None, cache_kind=None,
-                      stream=None, kv_stream=False):
+                      stream=None, kv_stream=False, prepare=False):
     """out[S, Hq, D] (float32) = paged decode attention; see pagedkv.h.
     kv_stream=True passes PKV_KV_STREAM (no block read by two sequences)."""
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
     need = lib.paged_attn_workspace_size(s, hq, hkv, d)
-    stream = _resolve_stream(query.device, stream)
+    handle = _stream_handle(stream, query)
     if workspace is None:
-        workspace = _default_workspace(query.device, stream)
+        workspace = _default_workspace(query.device, stream, handle)
     buf = _workspace_buf(workspace, need)
-    _check("paged_attn_decode", lib.paged_attn_decode(
+    return _run("paged_attn_decode", lib.paged_attn_decode, (
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
         _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale, kv_stream),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
@@ -385,42 +436,43 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
         _ptr(seq_lens), int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
         int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
-        _stream(stream)))
+        ctypes.c_void_p(handle)), prepare)
 
 
 def paged_attn_decode_noalloc(out, query, k_cache, v_cache, block_tables,
                               seq_lens, max_seq_len, scale, k_scale=None,
                               v_scale=None, max_waves=0, cache_kind=None,
-                              stream=None, kv_stream=False):
+                              stream=None, kv_stream=False, prepare=False):
     """paged_attn_decode with the library's own scratch instead of a
     workspace: allocates nothing (see pagedkv.h)."""
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
-    _check("paged_attn_decode_noalloc", lib.paged_attn_decode_noalloc(
+    return _run("paged_attn_decode_noalloc", lib.paged_attn_decode_noalloc, (
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
         _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale, kv_stream),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), s, hq,
-        hkv, d, nb, bs, float(scale), int(max_waves), _stream(stream)))
+        hkv, d, nb, bs, float(scale), int(max_waves),
+        _stream(stream, query)), prepare)
 
 
 def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
                             slot_mapping, block_tables, seq_lens, max_seq_len,
                             scale, k_scale=None, v_scale=None, max_waves=0,
                             workspace=None, cache_kind=None, stream=None,
-                            kv_stream=False):
+                            kv_stream=False, prepare=False):
     """cache_write_slots of one new token per sequence fused into
     paged_attn_decode; see pagedkv.h (kv_stream as for paged_attn_decode)."""
     lib = load_library()
     s, hq, d = query.shape
     nb, bs, hkv, _ = k_cache.shape
     need = lib.paged_attn_workspace_size(s, hq, hkv, d)
-    stream = _resolve_stream(query.device, stream)
+    handle = _stream_handle(stream, query)
     if workspace is None:
-        workspace = _default_workspace(query.device, stream)
+        workspace = _default_workspace(query.device, stream, handle)
     buf = _workspace_buf(workspace, need)
-    _check("paged_attn_decode_fused", lib.paged_attn_decode_fused(
+    return _run("paged_attn_decode_fused", lib.paged_attn_decode_fused, (
         _ptr(out), _ptr(query), dtype_code(query), _ptr(key), _ptr(value),
         _ptr(k_cache), _ptr(v_cache),
         cache_code(k_cache, cache_kind, k_scale, kv_stream),
@@ -428,13 +480,14 @@ def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), s, hq,
         hkv, d, nb, bs, float(scale), int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
-        _stream(stream)))
+        ctypes.c_void_p(handle)), prepare)
 
 
 def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
                      query_start, max_query_len, max_seq_len, scale,
                      k_scale=None, v_scale=None, max_waves=0, workspace=None,
-                     cache_kind=None, stream=None, kv_stream=False):
+                     cache_kind=None, stream=None, kv_stream=False,
+                     prepare=False):
     """out[T, Hq, D] (float32) = paged attention of T new query tokens,
     causal among each sequence's new tokens; see pagedkv.h (kv_stream as
     for paged_attn_decode)."""
@@ -443,11 +496,11 @@ def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
     nb, bs, hkv, _ = k_cache.shape
     s = int(seq_lens.shape[0])
     need = lib.paged_attn_multi_workspace_size(s, hq, hkv, d)
-    stream = _resolve_stream(query.device, stream)
+    handle = _stream_handle(stream, query)
     if workspace is None:
-        workspace = _default_workspace(query.device, stream)
+        workspace = _default_workspace(query.device, stream, handle)
     buf = _workspace_buf(workspace, need)
-    _check("paged_attn_multi", lib.paged_attn_multi(
+    return _run("paged_attn_multi", lib.paged_attn_multi, (
         _ptr(out), _ptr(query), dtype_code(query), _ptr(k_cache),
         _ptr(v_cache), cache_code(k_cache, cache_kind, k_scale, kv_stream),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
@@ -456,4 +509,4 @@ def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
         int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
         int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
-        _stream(stream)))
+        ctypes.c_void_p(handle)), prepare)

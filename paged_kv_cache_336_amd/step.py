@@ -92,51 +92,114 @@ class DeviceStep:
         """True when the fp8 scales are per (slot, kv head) arrays."""
         return self.k_scale.dim() == 3
 
-    def copy(self, r=0, stream=None):
-        pairs = self.sets[r]["copy_pairs"]
-        ops.copy_blocks(self.k_cache, self.v_cache, pairs,
-                        cache_kind=self.cache_kind, stream=stream)
-        if self.token_scales:
-            ops.copy_token_scales(self.k_scale, self.v_scale, pairs,
-                                  stream=stream)
+    # (each call below takes prepare=True to return the library call(s) as
+    # ops.PreparedCall objects instead of making them)
 
-    def write(self, r=0, stream=None):
+    def copy(self, r=0, stream=None, prepare=False):
+        pairs = self.sets[r]["copy_pairs"]
+        calls = [ops.copy_blocks(self.k_cache, self.v_cache, pairs,
+                                 cache_kind=self.cache_kind, stream=stream,
+                                 prepare=prepare)]
+        if self.token_scales:
+            calls.append(ops.copy_token_scales(self.k_scale, self.v_scale,
+                                               pairs, stream=stream,
+                                               prepare=prepare))
+        return calls
+
+    def write(self, r=0, stream=None, prepare=False):
         kind = self.cache_kind
         if self.token_scales:
-            ops.cache_write_slots_token_scaled(
+            return ops.cache_write_slots_token_scaled(
                 self.key, self.value, self.k_cache, self.v_cache,
                 self.k_scale, self.v_scale, self.sets[r]["slot_mapping"],
-                cache_kind=kind, stream=stream)
-            return
-        ops.cache_write_slots(self.key, self.value, self.k_cache, self.v_cache,
-                              self.sets[r]["slot_mapping"],
-                              k_scale=self.k_scale, v_scale=self.v_scale,
-                              cache_kind=kind, stream=stream)
+                cache_kind=kind, stream=stream, prepare=prepare)
+        return ops.cache_write_slots(
+            self.key, self.value, self.k_cache, self.v_cache,
+            self.sets[r]["slot_mapping"], k_scale=self.k_scale,
+            v_scale=self.v_scale, cache_kind=kind, stream=stream,
+            prepare=prepare)
 
-    def attend(self, r=0, stream=None, max_waves=0):
-        ops.paged_attn_decode(self.out, self.query, self.k_cache, self.v_cache,
-                              self.sets[r]["block_tables"], self.seq_lens,
-                              self.max_seq_len, self.w.scale,
-                              k_scale=self.k_scale, v_scale=self.v_scale,
-                              max_waves=max_waves, workspace=self.workspace,
-                              cache_kind=self.cache_kind, stream=stream,
-                              kv_stream=self.sets[r]["kv_stream"])
+    def attend(self, r=0, stream=None, max_waves=0, prepare=False):
+        return ops.paged_attn_decode(
+            self.out, self.query, self.k_cache, self.v_cache,
+            self.sets[r]["block_tables"], self.seq_lens, self.max_seq_len,
+            self.w.scale, k_scale=self.k_scale, v_scale=self.v_scale,
+            max_waves=max_waves, workspace=self.workspace,
+            cache_kind=self.cache_kind, stream=stream,
+            kv_stream=self.sets[r]["kv_stream"], prepare=prepare)
 
-    def attend_fused(self, r=0, stream=None, max_waves=0):
+    def attend_fused(self, r=0, stream=None, max_waves=0, prepare=False):
         """Write and attention in one launch (one new token per sequence)."""
-        ops.paged_attn_decode_fused(
+        return ops.paged_attn_decode_fused(
             self.out, self.query, self.key, self.value, self.k_cache,
             self.v_cache, self.sets[r]["slot_mapping"],
             self.sets[r]["block_tables"], self.seq_lens, self.max_seq_len,
             self.w.scale, k_scale=self.k_scale, v_scale=self.v_scale,
             max_waves=max_waves, workspace=self.workspace,
             cache_kind=self.cache_kind, stream=stream,
-            kv_stream=self.sets[r]["kv_stream"])
+            kv_stream=self.sets[r]["kv_stream"], prepare=prepare)
+
+    def prepare(self, fused=False, max_waves=0, stream=None):
+        """Every replica set's step as prepared library calls: copy_blocks
+        (and the per-token scales' copies), then cache_write_slots and
+        paged_attn_decode, or paged_attn_decode_fused.  step_prepared(r)
+        then issues them with no per-call shape, dtype or stream lookups
+        (a serving loop's steady state: the same tensors every step)."""
+        self.prepared = []
+        for r in range(len(self.sets)):
+            calls = self.copy(r, stream, prepare=True)
+            if fused:
+                calls.append(self.attend_fused(r, stream, max_waves, True))
+            else:
+                calls.append(self.write(r, stream, prepare=True))
+                calls.append(self.attend(r, stream, max_waves, True))
+            self.prepared.append(tuple(calls))
+        return self.prepared
+
+    def step_prepared(self, r=0):
+        """One step of replica set r through the prepared calls."""
+        for call in self.prepared[r]:
+            call()
+        return self.out
 
     def run(self, r=0, stream=None):
         self.copy(r, stream)
         self.write(r, stream)
         self.attend(r, stream)
+        return self.out
+
+    def capture(self, fused=False, max_waves=0):
+        """Record the whole step of every replica set -- copy_blocks, then
+        cache_write_slots and paged_attn_decode, or paged_attn_decode_fused
+        -- as one HIP graph each (torch.cuda.CUDAGraph), on a side stream of
+        default priority.  replay(r) then queues a step with a single launch
+        call instead of one library call per operation.  The workspace is
+        grown to its size first, so nothing is allocated while recording;
+        none of the calls records a memset."""
+        import torch
+        s, hq, d = self.query.shape
+        self.workspace.get(ops.paged_attn_workspace_size(
+            s, hq, self.k_cache.shape[2], d))
+        side = torch.cuda.Stream(device=self.device)
+        cur = torch.cuda.current_stream(self.device)
+        side.wait_stream(cur)
+        self.graphs = []
+        for r in range(len(self.sets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                self.copy(r)
+                if fused:
+                    self.attend_fused(r, max_waves=max_waves)
+                else:
+                    self.write(r)
+                    self.attend(r, max_waves=max_waves)
+            self.graphs.append(g)
+        cur.wait_stream(side)
+        return self.graphs
+
+    def replay(self, r=0):
+        """One recorded step (capture() first) on the current stream."""
+        self.graphs[r].replay()
         return self.out
 
     def pools_host(self):

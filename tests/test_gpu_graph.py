@@ -1,0 +1,80 @@
+"""The decode step recorded as HIP graphs (DeviceStep.capture: copy_blocks,
+cache_write_slots and paged_attn_decode, or the fused call, one graph per
+replica set) against the same calls made one by one, through the C ABI on
+the GPU.  Every replay -- several rounds, with other eager work queued and
+synchronised between them -- must give the eager output bit for bit and
+leave the pools as the eager steps left them."""
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_336_amd import workloads as W
+from paged_kv_cache_336_amd.step import DeviceStep
+
+from parity_helpers import TOL, max_abs_err, oracle_out, oracle_pools, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("8B-shaped, 3 replicas, separate write",
+     lambda: W.llama8b_decode(num_seqs=12, median=300, cap=1500,
+                              num_blocks=4096, replicas=3), False),
+    ("8B-shaped, 2 replicas, fused write",
+     lambda: W.llama8b_decode(num_seqs=12, median=300, cap=1500,
+                              num_blocks=4096, replicas=2), True),
+    ("fp8 long context, small",
+     lambda: W.long_context_fp8(num_seqs=2, seq_len=6000), False),
+    ("prefix sharing fork (copy-on-write copies)",
+     lambda: W.prefix_sharing(block_size=32, phase="fork", groups=2,
+                              samples=3, prompt_len=500, max_tail=100)[0],
+     False),
+]
+
+
+@pytest.mark.parametrize("label,make,fused", CASES,
+                         ids=[c[0] for c in CASES])
+def test_graph_replays_equal_eager_steps(label, make, fused):
+    import torch
+    say(f"graph step: {label}")
+    w = make()
+    dev = DeviceStep(w, device="cuda:0")
+    R = len(dev.sets)
+
+    def eager(r):
+        dev.copy(r)
+        if fused:
+            dev.attend_fused(r)
+        else:
+            dev.write(r)
+            dev.attend(r)
+
+    refs = []
+    for r in range(R):
+        eager(r)
+        torch.cuda.synchronize()
+        refs.append(dev.out.clone())
+    if R == 1 or not fused:
+        # the first set's eager output against the oracle (its own tables;
+        # the pools then hold every set's writes, which set 0 never reads)
+        pools = oracle_pools(w)
+        assert max_abs_err(refs[0].cpu().numpy(),
+                           oracle_out(w, pools)) <= TOL[w.kv_kind]
+    k_ref, v_ref = dev.k_cache.clone(), dev.v_cache.clone()
+
+    dev.capture(fused=fused)
+    for rnd in range(3):
+        for r in range(R):
+            dev.out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            dev.replay(r)
+            torch.cuda.synchronize()
+            assert torch.equal(dev.out.view(torch.int32),
+                               refs[r].view(torch.int32)), (rnd, r)
+            # other eager work between replays
+            dev.attend((r + 1) % R)
+            torch.cuda.synchronize()
+            assert torch.equal(dev.out.view(torch.int32),
+                               refs[(r + 1) % R].view(torch.int32))
+    assert torch.equal(dev.k_cache.view(torch.uint8), k_ref.view(torch.uint8))
+    assert torch.equal(dev.v_cache.view(torch.uint8), v_ref.view(torch.uint8))
+    assert np.isfinite(refs[0].cpu().numpy()).all()
