@@ -153,6 +153,18 @@ __device__ __forceinline__ int mq_limit(const MSeg& g, const AttnArgs& a,
   return tok >= 0 ? min(g.t_end, g.L - g.nq + tok + 1) : 0;
 }
 
+// The smallest key limit among the columns of group grp that hold a token
+// (INT_MAX when none does), the same in every lane: a tile whose keys all
+// lie below it needs no causal mask.
+__device__ __forceinline__ int mq_limit_lo(int lim, const MSeg& g,
+                                           const AttnArgs& a, int grp,
+                                           int lane) {
+  int v = mq_token(g, a, grp, lane & 15) >= 0 ? lim : INT_MAX;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = min(v, __shfl_xor(v, m, 64));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 // NG = 1 keeps the one-token kernel's register budget (two waves per SIMD
 // possible); NG = 4 needs up to 512 registers per lane (one wave per SIMD,
 // which is what the grid runs anyway).
@@ -267,13 +279,14 @@ void attn_multi_kernel(AttnArgs a) {
     const float qk_mul = a.qk_scale_log2 * kscale;
     const TokenScales tsc = token_scales(X);
     uint32_t qn_w[QPREFETCH ? NG : 1][S::QWORDS];
-    int lim[NG];
+    int lim[NG], lim_lo[NG];
     WaveState<NBLK> st[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if constexpr (QPREFETCH)
         load_query_mq<QT, CT, D>(qn_w[g], Xn, a, g, lane);
       lim[g] = mq_limit(X, a, g, lane);
+      lim_lo[g] = mq_limit_lo(lim[g], X, a, g, lane);
       st[g].m = -INFINITY;
       st[g].mv = -INFINITY;
       st[g].l = 0.f;
@@ -310,7 +323,8 @@ void attn_multi_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (live)
           compute_tile_groups<QT, CT, D, NG, PT, !PT>(cur.kw[0], qw, st, vt, t0,
-                                                 lim, qk_mul, lane, cur.sc[0]);
+                                                 lim, lim_lo, qk_mul, lane,
+                                                 cur.sc[0]);
         cur = nxt;
       }
     } else {
@@ -334,7 +348,7 @@ void attn_multi_kernel(AttnArgs a) {
         }
         stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
         compute_tile_groups<QT, CT, D, NG, PT, !PT>(cur.kw[0], qw, st, vt, t0, lim,
-                                               qk_mul, lane, cur.sc[0]);
+                                               lim_lo, qk_mul, lane, cur.sc[0]);
       }
     }
     if constexpr (PT) {
@@ -626,7 +640,7 @@ void attn_prefill_kernel(AttnArgs a) {
   int k = 0;  // tile within X
   bool first_seg = true;
   uint32_t qw[NG][S::QWORDS];
-  int lim[NG];
+  int lim[NG], lim_lo[NG];
   WaveState<S::NBLK> st[NG];
   const float qk_mul = a.qk_scale_log2;
   auto start_segment = [&]() {
@@ -634,6 +648,7 @@ void attn_prefill_kernel(AttnArgs a) {
     for (int g = 0; g < NG; ++g) {
       load_query_mq<ET, ET, D>(qw[g], X, a, gbase + g, lane);
       lim[g] = mq_limit(X, a, gbase + g, lane);
+      lim_lo[g] = mq_limit_lo(lim[g], X, a, gbase + g, lane);
       st[g].m = -INFINITY;
       st[g].l = 0.f;
 #pragma unroll
@@ -684,7 +699,8 @@ void attn_prefill_kernel(AttnArgs a) {
       uint32_t kw[2][S::KWORDS];
       prefill_k_operand<ET, D>(kw, kbuf[b], lane);
       compute_tile_groups<ET, ET, D, NG, false, true>(kw, qw, st, vbuf[b],
-                                                      t0, lim, qk_mul, lane);
+                                                      t0, lim, lim_lo, qk_mul,
+                                                      lane);
     }
     __syncthreads();
     if (++k == X.ntiles) {

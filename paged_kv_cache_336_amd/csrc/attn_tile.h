@@ -6,6 +6,8 @@
 #ifndef PKV_ATTN_TILE_H
 #define PKV_ATTN_TILE_H
 
+#include <limits.h>
+
 #include <mutex>
 #include <unordered_map>
 #include <utility>
@@ -465,7 +467,7 @@ template <typename QT, typename CT, int D, bool CAUSAL, bool PT = false,
           bool LAZY = false>
 __device__ __forceinline__ void softmax_tile(
     const f32x4_t (&sacc)[2], WaveState<Shape<QT, CT, D>::NBLK>& st, int t0,
-    int t_end, int lim, float qk_mul, int lane,
+    int t_end, int lim, int full_to, float qk_mul, int lane,
     typename Mma<typename Shape<QT, CT, D>::PVT>::operand& pb_hi,
     typename Mma<typename Shape<QT, CT, D>::PVT>::operand& pb_lo,
     float sc = 0.f) {
@@ -478,16 +480,30 @@ __device__ __forceinline__ void softmax_tile(
   // PT: lanes 8..15 of each row hold value scales: their log2, then lane e
   // (key scale) and 8 + e (log2 value scale) of the row serve slot e
   const float own = PT && (lane & 8) ? __builtin_amdgcn_logf(sc) : sc;
+  float mul[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
-    const bool live = t0 + slot_token(j, e) < (CAUSAL ? lim : t_end);
-    float mul = qk_mul;
+    mul[e] = qk_mul;
     if constexpr (PT) {
-      mul *= row_broadcast(own, e);
+      mul[e] *= row_broadcast(own, e);
       lvs[e] = row_broadcast(own, 8 + e);
     }
-    sv[e] = live ? raw * mul : -INFINITY;
+  }
+  // full_to (wave-uniform): every key of a tile below it is live for every
+  // column whose output is kept, so such a tile -- most of them -- skips
+  // the per-slot mask (columns holding no token compute unmasked scores
+  // that are never stored)
+  if (t0 + 32 <= full_to) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      sv[e] = (e < 4 ? sacc[0][e] : sacc[1][e - 4]) * mul[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
+      const bool live = t0 + slot_token(j, e) < (CAUSAL ? lim : t_end);
+      sv[e] = live ? raw * mul[e] : -INFINITY;
+    }
   }
   float mx = sv[0];
 #pragma unroll
@@ -535,16 +551,16 @@ __device__ __forceinline__ void softmax_tile(
   }
 
   if constexpr (PVB == 2) {
+    // pairs of weights rounded to the 16-bit type in one packed conversion;
+    // with the split, the residual of each (exact in float32) rounded again
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t h0 = f32_to_bits(pv[2 * w], PVT{});
-      const uint32_t h1 = f32_to_bits(pv[2 * w + 1], PVT{});
-      pb_hi[w] = h0 | (h1 << 16);
-      if constexpr (S::PSPLIT) {
-        const uint32_t l0 = f32_to_bits(pv[2 * w] - bits_to_f32(h0, PVT{}), PVT{});
-        const uint32_t l1 = f32_to_bits(pv[2 * w + 1] - bits_to_f32(h1, PVT{}), PVT{});
-        pb_lo[w] = l0 | (l1 << 16);
-      }
+      const uint32_t h = f32x2_to_bits(pv[2 * w], pv[2 * w + 1], PVT{});
+      pb_hi[w] = h;
+      if constexpr (S::PSPLIT)
+        pb_lo[w] = f32x2_to_bits(pv[2 * w] - lo_bits_to_f32(h, PVT{}),
+                                 pv[2 * w + 1] - hi_bits_to_f32(h, PVT{}),
+                                 PVT{});
     }
   } else {
 #pragma unroll
@@ -595,7 +611,8 @@ __device__ __forceinline__ void compute_tile(
   f32x4_t sacc[2];
   qk_tile<QT, CT, D>(kw, qw, sacc);
   typename Mma<PVT>::operand pb_hi, pb_lo;
-  softmax_tile<QT, CT, D, CAUSAL, PT, LAZY>(sacc, st, t0, t_end, lim, qk_mul,
+  softmax_tile<QT, CT, D, CAUSAL, PT, LAZY>(sacc, st, t0, t_end, lim,
+                                            CAUSAL ? INT_MIN : t_end, qk_mul,
                                             lane, pb_hi, pb_lo, sc);
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) {
@@ -607,14 +624,16 @@ __device__ __forceinline__ void compute_tile(
 }
 
 // One tile for NG 16-column groups of query columns (causal limits per
-// group): the tile's K registers and each V^T read serve every group.
+// group, lim_lo[g] the smallest limit among the group's token columns,
+// wave-uniform): the tile's K registers and each V^T read serve every group.
 template <typename QT, typename CT, int D, int NG, bool PT = false,
           bool LAZY = false>
 __device__ __forceinline__ void compute_tile_groups(
     const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS],
     const uint32_t (&qw)[NG][Shape<QT, CT, D>::QWORDS],
     WaveState<Shape<QT, CT, D>::NBLK> (&st)[NG], uint8_t* vt, int t0,
-    const int (&lim)[NG], float qk_mul, int lane, float sc = 0.f) {
+    const int (&lim)[NG], const int (&lim_lo)[NG], float qk_mul, int lane,
+    float sc = 0.f) {
   typedef Shape<QT, CT, D> S;
   typedef typename S::PVT PVT;
   typename Mma<PVT>::operand pb_hi[NG], pb_lo[NG];
@@ -623,8 +642,8 @@ __device__ __forceinline__ void compute_tile_groups(
     f32x4_t sacc[2];
     qk_tile<QT, CT, D>(kw, qw[g], sacc);
     softmax_tile<QT, CT, D, true, PT, LAZY>(sacc, st[g], t0, 0, lim[g],
-                                            qk_mul, lane, pb_hi[g], pb_lo[g],
-                                            sc);
+                                            lim_lo[g], qk_mul, lane, pb_hi[g],
+                                            pb_lo[g], sc);
   }
 #pragma unroll
   for (int n = 0; n < S::NBLK; ++n) {

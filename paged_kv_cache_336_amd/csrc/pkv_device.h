@@ -157,6 +157,31 @@ __device__ __forceinline__ float bits_to_f32(uint16_t b, F16) {
   return static_cast<float>(bitcast<_Float16>(b));
 }
 
+// Two floats rounded (to nearest even, as f32_to_bits) into one word, x0 in
+// the low half: one packed conversion (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bits(float x0, float x1, BF16) {
+  typedef __bf16 v2_t __attribute__((ext_vector_type(2)));
+  return bitcast<uint32_t>(__builtin_convertvector(f32x2v_t{x0, x1}, v2_t));
+}
+__device__ __forceinline__ uint32_t f32x2_to_bits(float x0, float x1, F16) {
+  typedef _Float16 v2_t __attribute__((ext_vector_type(2)));
+  return bitcast<uint32_t>(__builtin_convertvector(f32x2v_t{x0, x1}, v2_t));
+}
+// The low / high 16-bit element of a packed word as a float.
+__device__ __forceinline__ float lo_bits_to_f32(uint32_t w, BF16) {
+  return bitcast<float>(w << 16);
+}
+__device__ __forceinline__ float hi_bits_to_f32(uint32_t w, BF16) {
+  return bitcast<float>(w & 0xFFFF0000u);
+}
+__device__ __forceinline__ float lo_bits_to_f32(uint32_t w, F16) {
+  return static_cast<float>(bitcast<_Float16>(static_cast<uint16_t>(w)));
+}
+__device__ __forceinline__ float hi_bits_to_f32(uint32_t w, F16) {
+  return static_cast<float>(bitcast<_Float16>(static_cast<uint16_t>(w >> 16)));
+}
+
 // ---------------------------------------------------------------------------
 // Wave-wide helpers (wave64).
 // ---------------------------------------------------------------------------
