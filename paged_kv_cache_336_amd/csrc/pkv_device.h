@@ -185,11 +185,37 @@ __device__ __forceinline__ float hi_bits_to_f32(uint32_t w, F16) {
 // ---------------------------------------------------------------------------
 // Wave-wide helpers (wave64).
 // ---------------------------------------------------------------------------
+// This lane's value and that of lane ^ mask.  Masks 16 and 32 use gfx950's
+// row / half swaps (v_permlane16_swap_b32, v_permlane32_swap_b32: VALU
+// operations with no LDS round trip); swapping a value with itself leaves
+// each lane holding its own value and its partner's, in some order.  Other
+// masks go through an LDS permute.
+__device__ __forceinline__ void xor_pair(float v, int mask, float& a,
+                                         float& b) {
+  if (mask == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(
+        __float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else if (mask == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(
+        __float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    a = v;
+    b = __shfl_xor(v, mask, 64);
+  }
+}
 __device__ __forceinline__ float xor_max(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
+  float a, b;
+  xor_pair(v, mask, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float xor_sum(float v, int mask) {
-  return v + __shfl_xor(v, mask, 64);
+  float a, b;
+  xor_pair(v, mask, a, b);
+  return a + b;  // (addition commutes exactly: the same sum in both lanes)
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
