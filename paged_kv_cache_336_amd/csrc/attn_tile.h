@@ -391,11 +391,15 @@ __device__ __forceinline__ void qk_tile(
     const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS], const uint32_t* qw,
     f32x4_t (&sacc)[2]) {
   typedef Shape<QT, CT, D> S;
+  sacc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the two halves' accumulations are independent: step over D with both
+  // in turn, so each MFMA's latency is covered by the other half's
+  // (the same order of additions per accumulator)
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    sacc[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < S::QSTEPS; ++q) {
 #pragma unroll
-    for (int q = 0; q < S::QSTEPS; ++q) {
+    for (int hh = 0; hh < 2; ++hh) {
       typename Mma<QT>::operand ka, qb;
       if constexpr (same<QT, CT>::value && QT::bytes == 2) {
 #pragma unroll
@@ -614,12 +618,20 @@ __device__ __forceinline__ void compute_tile(
   softmax_tile<QT, CT, D, CAUSAL, PT, LAZY>(sacc, st, t0, t_end, lim,
                                             CAUSAL ? INT_MIN : t_end, qk_mul,
                                             lane, pb_hi, pb_lo, sc);
+  // output blocks two at a time, so that a block's lo step does not wait
+  // right behind its own hi step (same order per accumulator)
+  static_assert(S::NBLK % 2 == 0, "pairs of output blocks");
 #pragma unroll
-  for (int n = 0; n < S::NBLK; ++n) {
-    typename Mma<PVT>::operand va;
-    v_operand<QT, CT, D>(vt, n, lane, va);
-    st.o[n] = Mma<PVT>::step(va, pb_hi, st.o[n]);
-    if constexpr (S::PSPLIT) st.o[n] = Mma<PVT>::step(va, pb_lo, st.o[n]);
+  for (int n = 0; n < S::NBLK; n += 2) {
+    typename Mma<PVT>::operand va0, va1;
+    v_operand<QT, CT, D>(vt, n, lane, va0);
+    v_operand<QT, CT, D>(vt, n + 1, lane, va1);
+    st.o[n] = Mma<PVT>::step(va0, pb_hi, st.o[n]);
+    st.o[n + 1] = Mma<PVT>::step(va1, pb_hi, st.o[n + 1]);
+    if constexpr (S::PSPLIT) {
+      st.o[n] = Mma<PVT>::step(va0, pb_lo, st.o[n]);
+      st.o[n + 1] = Mma<PVT>::step(va1, pb_lo, st.o[n + 1]);
+    }
   }
 }
 
@@ -645,14 +657,31 @@ __device__ __forceinline__ void compute_tile_groups(
                                             lim_lo[g], qk_mul, lane, pb_hi[g],
                                             pb_lo[g], sc);
   }
+  if constexpr (NG == 1) {
+    // (one group: output blocks two at a time, as compute_tile)
 #pragma unroll
-  for (int n = 0; n < S::NBLK; ++n) {
-    typename Mma<PVT>::operand va;
-    v_operand<QT, CT, D>(vt, n, lane, va);
+    for (int n = 0; n < S::NBLK; n += 2) {
+      typename Mma<PVT>::operand va0, va1;
+      v_operand<QT, CT, D>(vt, n, lane, va0);
+      v_operand<QT, CT, D>(vt, n + 1, lane, va1);
+      st[0].o[n] = Mma<PVT>::step(va0, pb_hi[0], st[0].o[n]);
+      st[0].o[n + 1] = Mma<PVT>::step(va1, pb_hi[0], st[0].o[n + 1]);
+      if constexpr (S::PSPLIT) {
+        st[0].o[n] = Mma<PVT>::step(va0, pb_lo[0], st[0].o[n]);
+        st[0].o[n + 1] = Mma<PVT>::step(va1, pb_lo[0], st[0].o[n + 1]);
+      }
+    }
+  } else {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      st[g].o[n] = Mma<PVT>::step(va, pb_hi[g], st[g].o[n]);
-      if constexpr (S::PSPLIT) st[g].o[n] = Mma<PVT>::step(va, pb_lo[g], st[g].o[n]);
+    for (int n = 0; n < S::NBLK; ++n) {
+      typename Mma<PVT>::operand va;
+      v_operand<QT, CT, D>(vt, n, lane, va);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        st[g].o[n] = Mma<PVT>::step(va, pb_hi[g], st[g].o[n]);
+        if constexpr (S::PSPLIT)
+          st[g].o[n] = Mma<PVT>::step(va, pb_lo[g], st[g].o[n]);
+      }
     }
   }
 }
