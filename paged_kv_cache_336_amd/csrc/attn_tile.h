@@ -649,6 +649,11 @@ __device__ __forceinline__ void compute_tile_groups(
   typedef Shape<QT, CT, D> S;
   typedef typename S::PVT PVT;
   typename Mma<PVT>::operand pb_hi[NG], pb_lo[NG];
+  // (several groups: the QK products and softmax steps run at a raised wave
+  // priority, so that while one wave works through them the SIMD's other
+  // wave's PV MFMAs fill the matrix unit -- measured 647 -> 632 us on chunked
+  // prefill; raising it around the PV MFMAs instead changed nothing)
+  if constexpr (NG > 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     f32x4_t sacc[2];
@@ -657,6 +662,7 @@ __device__ __forceinline__ void compute_tile_groups(
                                             lim_lo[g], qk_mul, lane, pb_hi[g],
                                             pb_lo[g], sc);
   }
+  if constexpr (NG > 1) __builtin_amdgcn_s_setprio(0);
   if constexpr (NG == 1) {
     // (one group: output blocks two at a time, as compute_tile)
 #pragma unroll
