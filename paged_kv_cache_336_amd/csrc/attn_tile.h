@@ -499,13 +499,17 @@ __device__ __forceinline__ void softmax_tile(
   // that are never stored)
   if (t0 + 32 <= full_to) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      sv[e] = (e < 4 ? sacc[0][e] : sacc[1][e - 4]) * mul[e];
+    for (int e = 0; e < 8; ++e) {
+      const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
+      sv[e] = raw * mul[e];
+    }
   } else {
+    // slot e of lane group j is key t0 + 4 j + (e < 4 ? e : 12 + e)
+    const int bound = (CAUSAL ? lim : t_end) - t0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
-      const bool live = t0 + slot_token(j, e) < (CAUSAL ? lim : t_end);
+      const bool live = 4 * j < bound - (e < 4 ? e : 12 + e);
       sv[e] = live ? raw * mul[e] : -INFINITY;
     }
   }
