@@ -203,12 +203,16 @@ class PreparedCall:
     between calls.  The ``prepare=True`` argument of the operations below
     returns one instead of making the call."""
 
-    __slots__ = ("name", "fn", "args")
+    __slots__ = ("name", "fn", "args", "keep")
 
-    def __init__(self, name, fn, args):
+    def __init__(self, name, fn, args, keep=()):
         self.name = name
         self.fn = fn
         self.args = args
+        # the workspace buffer it points at (a default workspace may be
+        # replaced by a larger one later; this reference keeps the buffer
+        # this call uses alive)
+        self.keep = keep
 
     def __call__(self):
         status = self.fn(*self.args)
@@ -216,10 +220,11 @@ class PreparedCall:
             raise PagedKVError(self.name, status)
 
 
-def _run(name, fn, args, prepare):
-    """Make the call, or with prepare return it as a PreparedCall."""
+def _run(name, fn, args, prepare, keep=()):
+    """Make the call, or with prepare return it as a PreparedCall (holding
+    `keep`, the buffers the library owns that the call points at)."""
     if prepare:
-        return PreparedCall(name, fn, args)
+        return PreparedCall(name, fn, args, keep)
     _check(name, fn(*args))
     return None
 
@@ -436,7 +441,7 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens,
         _ptr(seq_lens), int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
         int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
-        ctypes.c_void_p(handle)), prepare)
+        ctypes.c_void_p(handle)), prepare, (buf,))
 
 
 def paged_attn_decode_noalloc(out, query, k_cache, v_cache, block_tables,
@@ -480,7 +485,7 @@ def paged_attn_decode_fused(out, query, key, value, k_cache, v_cache,
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), s, hq,
         hkv, d, nb, bs, float(scale), int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
-        ctypes.c_void_p(handle)), prepare)
+        ctypes.c_void_p(handle)), prepare, (buf,))
 
 
 def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
@@ -509,4 +514,4 @@ def paged_attn_multi(out, query, k_cache, v_cache, block_tables, seq_lens,
         int(max_seq_len), s, hq, hkv, d, nb, bs, float(scale),
         int(max_waves), _ptr(buf),
         0 if buf is None else buf.numel() * buf.element_size(),
-        ctypes.c_void_p(handle)), prepare)
+        ctypes.c_void_p(handle)), prepare, (buf,))

@@ -1,6 +1,7 @@
 """The Python binding on the host (CPU only, no compute call): a prepared
 call holds the marshalled arguments and makes the library call only when it
-is called, reporting the status the same way as a direct call."""
+is called, reporting the status the same way as a direct call, and keeps
+the workspace buffer it points at alive."""
 
 import ctypes
 
@@ -51,3 +52,20 @@ def test_prepared_copy_with_nothing_to_copy_succeeds():
     assert isinstance(call, ops.PreparedCall)
     call()                                         # zero pairs: status 0
     assert isinstance(call.args[-1], ctypes.c_void_p)
+
+
+def test_prepared_call_keeps_its_workspace_buffer():
+    # a Workspace replaces its buffer when it grows; the prepared call keeps
+    # the buffer its marshalled pointer names alive
+    out, q, kc, bt, sl = _decode_args()
+    ws = ops.Workspace("cpu")
+    call = ops.paged_attn_decode(out, q, kc, kc, bt, sl, 64, 0.1,
+                                 workspace=ws, stream=_FakeStream(),
+                                 prepare=True)
+    (held,) = call.keep
+    first = held.data_ptr()
+    ws.get(held.numel() * 4)                     # grows: a new buffer
+    assert ws.buf is not held
+    assert call.keep[0] is held and held.data_ptr() == first
+    ptr = call.args[-3]
+    assert (ptr.value if isinstance(ptr, ctypes.c_void_p) else ptr) == first
