@@ -782,6 +782,57 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
   const int tid = threadIdx.x;
   const int gmax = a.slot_heads;
   const int items = gcount * D4;
+  if (items > kMergeThreads) {
+    // More than one item per thread: thread tid folds items it and
+    // it + kMergeThreads together (it = tid, tid + 2 kMergeThreads, ...), so
+    // the loads of both are in flight at once.  Each item folds its pieces
+    // in order, as below.
+    constexpr int HB = BATCH / 2 > 0 ? BATCH / 2 : 1;
+    const uint32_t step = 2u * (uint32_t)gmax;
+    for (int it = tid; it < items; it += 2 * kMergeThreads) {
+      const int itb = it + kMergeThreads;
+      const bool has_b = itb < items;
+      const int ga = it / D4, da = it - ga * D4;
+      const int gb = has_b ? itb / D4 : ga, db = has_b ? itb - gb * D4 : da;
+      const uint32_t sla = (uint32_t)(slot_index(wf, 0) * gmax + ga);
+      const uint32_t slb = (uint32_t)(slot_index(wf, 0) * gmax + gb);
+      float ma = -INFINITY, la = 0.f, mb = -INFINITY, lb = 0.f;
+      f32x4_t acca = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
+      for (int i0 = 0; i0 < npieces; i0 += HB) {
+        float mi[2][HB], li[2][HB];
+        f32x4_t oi[2][HB];
+#pragma unroll
+        for (int k = 0; k < HB; ++k) {
+          const int i = i0 + k;
+          const uint32_t q = i == 0 ? (uint32_t)(q_first * gmax) : 0u;
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            mi[x][k] = -INFINITY;
+            li[x][k] = 0.f;
+            oi[x][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (i < npieces && (x == 0 || has_b)) {
+              const uint32_t sl = (x ? slb : sla) + step * (uint32_t)i + q;
+              mi[x][k] = load_at<float>(a.part_m, sl * 4u);
+              li[x][k] = load_at<float>(a.part_l, sl * 4u);
+              oi[x][k] = load_at<f32x4_t>(
+                  a.part_o, (sl * (uint32_t)D + 4u * (x ? db : da)) * 4u);
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < HB; ++k) {
+          lse_fold(ma, la, acca, mi[0][k], li[0][k], oi[0][k]);
+          lse_fold(mb, lb, accb, mi[1][k], li[1][k], oi[1][k]);
+        }
+      }
+      *reinterpret_cast<f32x4_t*>(a.out + row_of(ga) * D + 4 * da) =
+          acca * (vscale / la);
+      if (has_b)
+        *reinterpret_cast<f32x4_t*>(a.out + row_of(gb) * D + 4 * db) =
+            accb * (vscale / lb);
+    }
+    return;
+  }
   const int nsub = items >= kMergeThreads ? 1 : kMergeThreads / items;
   for (int it = tid; it < items * nsub; it += kMergeThreads) {
     const int item = it % items;
