@@ -8,8 +8,9 @@
 
 #include <limits.h>
 
+#include <map>
 #include <mutex>
-#include <unordered_map>
+#include <tuple>
 #include <utility>
 
 #include "pkv_device.h"
@@ -946,13 +947,17 @@ __device__ __forceinline__ uint32_t load_window(const Seg& g, int half,
 // runtime once per (kernel instance, device, LDS size) and kept: later calls
 // cost one hipGetDevice and a lookup under a lock.  (The LDS size follows
 // the number of sequences, so a serving loop meets a bounded set of them.)
+// (Every kernel here has the same type, so the kernel's address is part of
+// the key: instances differ in registers and so in occupancy.)
 template <typename K>
 static bool device_occupancy(K kernel, size_t dyn_lds, int* cus, int* per_cu) {
   static std::mutex mu;
-  static std::unordered_map<uint64_t, std::pair<int, int>> cache;
+  static std::map<std::tuple<int, const void*, size_t>, std::pair<int, int>>
+      cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
-  const uint64_t key = ((uint64_t)(uint32_t)dev << 32) | (uint32_t)dyn_lds;
+  const auto key =
+      std::make_tuple(dev, reinterpret_cast<const void*>(kernel), dyn_lds);
   {
     std::lock_guard<std::mutex> lock(mu);
     const auto it = cache.find(key);
