@@ -20,6 +20,7 @@ serving loop whose tensors stay in place issues each step's calls again
 without any per-call lookups.
 """
 
+import collections
 import ctypes
 import os
 
@@ -394,8 +395,12 @@ class Workspace:
 
 
 # default workspaces, one per (device, stream): calls on different streams
-# never share one (they could overlap in time)
-_default_ws = {}
+# never share one (they could overlap in time).  The most recently used
+# _DEFAULT_WS_KEEP are kept; dropping one is safe, as its buffer was
+# allocated on its own stream and torch reuses it only in that stream's order
+# (and a prepared call holds the buffer it was made with).
+_default_ws = collections.OrderedDict()
+_DEFAULT_WS_KEEP = 16
 _NO_SIZE = (1 << 64) - 1     # (size_t)-1: the size query's "invalid"
 
 
@@ -406,6 +411,10 @@ def _default_workspace(device, stream, handle):
     ws = _default_ws.get(key)
     if ws is None:
         ws = _default_ws[key] = Workspace(device, stream)
+        while len(_default_ws) > _DEFAULT_WS_KEEP:
+            _default_ws.popitem(last=False)
+    else:
+        _default_ws.move_to_end(key)
     return ws
 
 

@@ -1,7 +1,8 @@
 """The Python binding on the host (CPU only, no compute call): a prepared
 call holds the marshalled arguments and makes the library call only when it
 is called, reporting the status the same way as a direct call, and keeps
-the workspace buffer it points at alive."""
+the workspace buffer it points at alive; the default workspaces (one per
+device and stream) are bounded to the most recently used."""
 
 import ctypes
 
@@ -69,3 +70,21 @@ def test_prepared_call_keeps_its_workspace_buffer():
     assert call.keep[0] is held and held.data_ptr() == first
     ptr = call.args[-3]
     assert (ptr.value if isinstance(ptr, ctypes.c_void_p) else ptr) == first
+
+
+def test_default_workspaces_are_bounded():
+    # one default workspace per (device, stream) in use, the most recently
+    # used kept
+    ops._default_ws.clear()
+    dev = torch.device("cpu")
+    first = ops._default_workspace(dev, None, 1000)
+    for h in range(1001, 1001 + ops._DEFAULT_WS_KEEP + 5):
+        ops._default_workspace(dev, None, h)
+    assert len(ops._default_ws) == ops._DEFAULT_WS_KEEP
+    assert (None, 1000) not in ops._default_ws
+    again = ops._default_workspace(dev, None, 1000)
+    assert again is not first
+    last = ops._default_workspace(dev, None, 1001 + ops._DEFAULT_WS_KEEP + 4)
+    assert ops._default_workspace(dev, None,
+                                  1001 + ops._DEFAULT_WS_KEEP + 4) is last
+    ops._default_ws.clear()
