@@ -235,3 +235,35 @@ def test_long_runs_with_growing_scores(kv):
         err = max_abs_err(out, ref)
         say(f"  waves {waves}: max abs err {err:.3g}")
         assert err <= TOL[kv], f"waves {waves}: {err:.3g}"
+
+
+PREFILL_CASES = [
+    # name, lens, qlens, hq, hkv, d, bs, kind: every case has a run of at
+    # least 12 column groups (16 / G tokens each), so the workgroup-row
+    # prefill kernel takes the call
+    ("g1_d64_f16_bs32", [400, 260, 33], [200, 260, 33], 4, 4, 64, 32, "f16"),
+    ("g2_d128_bf16_bs64", [500, 130, 97], [100, 130, 1], 4, 2, 128, 64,
+     "bf16"),
+    ("g3_d64_bf16_bs16", [300, 75, 640], [75, 75, 64], 6, 2, 64, 16, "bf16"),
+    ("g8_d64_f16_bs16", [90, 513, 1], [90, 40, 1], 16, 2, 64, 16, "f16"),
+    ("g8_d128_f16_bs32", [700, 30], [48, 30], 8, 1, 128, 32, "f16"),
+    ("g1_d128_bf16_bs16", [260, 1000], [200, 13], 2, 2, 128, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_rows_every_group_shape(case):
+    """The workgroup-row prefill kernel over group shapes G = 1, 2, 3, 8 (16,
+    8, 5 and 2 new tokens per 16-column group), head_dim 64 and 128, both
+    16-bit types, whole prompts and single new tokens beside long runs, at
+    the default split and a 24-range one, against the multi-query oracle."""
+    name, lens, qlens, hq, hkv, d, bs, kind = case
+    mq = W.custom_multi(seed=sum(map(ord, name)), lens=lens, qlens=qlens,
+                        hq=hq, hkv=hkv, d=d, bs=bs, q_kind=kind, kv_kind=kind)
+    ref = oracle_multi(mq, oracle_pools(mq.w))
+    for waves in (0, 24):
+        say(f"prefill rows {name}: waves {waves or 'all'}")
+        _, out = run_multi(mq, max_waves=waves)
+        err = max_abs_err(out, ref)
+        say(f"  max abs err {err:.3g}")
+        assert err <= TOL[kind], f"{name} waves {waves}: {err:.3g}"
