@@ -1,8 +1,7 @@
 """Score multipliers of either sign, and zero, through every attention kernel
-against the oracle on the GPU.  The kernels fold the multiplier into each
-weight's exponent (one fma), which needs it positive: a negative one becomes
-its magnitude by negating the query operand, and zero is raised to the
-smallest normal float.  The oracle takes the scale as given."""
+against the oracle on the GPU: a negative multiplier turns the order of the
+scores around (the running maximum and the lazy reference must follow it),
+and zero makes every weight equal.  The oracle takes the scale as given."""
 
 import numpy as np
 import pytest
