@@ -642,11 +642,19 @@ void attn_prefill_kernel(AttnArgs a) {
   uint32_t qw[NG][S::QWORDS];
   int lim[NG], lim_lo[NG];
   WaveState<S::NBLK> st[NG];
-  const float qk_mul = a.qk_scale_log2;
+  // the score multiplier goes into each weight's exponent (softmax_tile's
+  // FOLD), which needs it positive: a negative one becomes its magnitude
+  // with the query negated, and zero the smallest normal float (every
+  // weight then still rounds to 1)
+  const float qk_mul = a.qk_scale_log2 == 0.f ? 1.17549435e-38f
+                                              : fabsf(a.qk_scale_log2);
+  const uint32_t qflip = a.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
   auto start_segment = [&]() {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       load_query_mq<ET, ET, D>(qw[g], X, a, gbase + g, lane);
+#pragma unroll
+      for (int q = 0; q < S::QWORDS; ++q) qw[g][q] ^= qflip;
       lim[g] = mq_limit(X, a, gbase + g, lane);
       lim_lo[g] = mq_limit_lo(lim[g], X, a, gbase + g, lane);
       st[g].m = -INFINITY;
@@ -698,7 +706,7 @@ void attn_prefill_kernel(AttnArgs a) {
     if (t0 < X.t_end) {  // (tiles past the row's columns hold nothing)
       uint32_t kw[2][S::KWORDS];
       prefill_k_operand<ET, D>(kw, kbuf[b], lane);
-      compute_tile_groups<ET, ET, D, NG, false, true>(kw, qw, st, vbuf[b],
+      compute_tile_groups<ET, ET, D, NG, false, true, true>(kw, qw, st, vbuf[b],
                                                       t0, lim, lim_lo, qk_mul,
                                                       lane);
     }

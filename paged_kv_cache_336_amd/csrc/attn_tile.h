@@ -468,8 +468,14 @@ __device__ __forceinline__ void qk_tile(
 // precision relative to their size.
 constexpr float kLazyMargin = 8.f;
 
+// FOLD (no per-token scales; qk_mul > 0): the multiplier is applied inside
+// each weight's exponent, 2^fma(s, qk_mul, -m), and to the tile's maximum,
+// instead of to every score first -- one fused operation per score instead
+// of two.  The maximum's own weight is then 2^(its rounding residual), not
+// exactly 1, so only callers that promise no bit-exact one-token results
+// use it.
 template <typename QT, typename CT, int D, bool CAUSAL, bool PT = false,
-          bool LAZY = false>
+          bool LAZY = false, bool FOLD = false>
 __device__ __forceinline__ void softmax_tile(
     const f32x4_t (&sacc)[2], WaveState<Shape<QT, CT, D>::NBLK>& st, int t0,
     int t_end, int lim, int full_to, float qk_mul, int lane,
@@ -485,10 +491,11 @@ __device__ __forceinline__ void softmax_tile(
   // PT: lanes 8..15 of each row hold value scales: their log2, then lane e
   // (key scale) and 8 + e (log2 value scale) of the row serve slot e
   const float own = PT && (lane & 8) ? __builtin_amdgcn_logf(sc) : sc;
+  static_assert(!(FOLD && PT), "folded multiplier: no per-token scales");
   float mul[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    mul[e] = qk_mul;
+    mul[e] = FOLD ? 1.f : qk_mul;
     if constexpr (PT) {
       mul[e] *= row_broadcast(own, e);
       lvs[e] = row_broadcast(own, 8 + e);
@@ -502,7 +509,7 @@ __device__ __forceinline__ void softmax_tile(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
-      sv[e] = raw * mul[e];
+      sv[e] = FOLD ? raw : raw * mul[e];
     }
   } else {
     // slot e of lane group j is key t0 + 4 j + (e < 4 ? e : 12 + e)
@@ -511,7 +518,7 @@ __device__ __forceinline__ void softmax_tile(
     for (int e = 0; e < 8; ++e) {
       const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
       const bool live = 4 * j < bound - (e < 4 ? e : 12 + e);
-      sv[e] = live ? raw * mul[e] : -INFINITY;
+      sv[e] = live ? (FOLD ? raw : raw * mul[e]) : -INFINITY;
     }
   }
   float mx = sv[0];
@@ -519,6 +526,7 @@ __device__ __forceinline__ void softmax_tile(
   for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
   mx = xor_max(mx, 16);
   mx = xor_max(mx, 32);
+  if constexpr (FOLD) mx *= qk_mul;  // (-inf stays -inf: qk_mul > 0)
   // (LAZY: keep the old reference unless the tile's maximum passes it by
   // more than the margin; -inf + margin is -inf, so a first finite
   // maximum always moves it)
@@ -530,7 +538,8 @@ __device__ __forceinline__ void softmax_tile(
   float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    pv[e] = fast_exp2(sv[e] - m_use);
+    pv[e] = FOLD ? fast_exp2(__builtin_fmaf(sv[e], qk_mul, -m_use))
+                 : fast_exp2(sv[e] - m_use);
     psum += pv[e];
   }
   st.l = st.l * alpha + psum;
@@ -644,7 +653,7 @@ __device__ __forceinline__ void compute_tile(
 // group, lim_lo[g] the smallest limit among the group's token columns,
 // wave-uniform): the tile's K registers and each V^T read serve every group.
 template <typename QT, typename CT, int D, int NG, bool PT = false,
-          bool LAZY = false>
+          bool LAZY = false, bool FOLD = false>
 __device__ __forceinline__ void compute_tile_groups(
     const uint32_t (&kw)[2][Shape<QT, CT, D>::KWORDS],
     const uint32_t (&qw)[NG][Shape<QT, CT, D>::QWORDS],
@@ -663,9 +672,9 @@ __device__ __forceinline__ void compute_tile_groups(
   for (int g = 0; g < NG; ++g) {
     f32x4_t sacc[2];
     qk_tile<QT, CT, D>(kw, qw[g], sacc);
-    softmax_tile<QT, CT, D, true, PT, LAZY>(sacc, st[g], t0, 0, lim[g],
-                                            lim_lo[g], qk_mul, lane, pb_hi[g],
-                                            pb_lo[g], sc);
+    softmax_tile<QT, CT, D, true, PT, LAZY, FOLD>(sacc, st[g], t0, 0, lim[g],
+                                                  lim_lo[g], qk_mul, lane,
+                                                  pb_hi[g], pb_lo[g], sc);
   }
   if constexpr (NG > 1) __builtin_amdgcn_s_setprio(0);
   if constexpr (NG == 1) {
