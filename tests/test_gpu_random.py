@@ -1,0 +1,130 @@
+"""Seeded random shapes through the decode and multi-query calls, through the
+C ABI on the GPU, against the float64 oracle.  Each case draws its cache and
+query types, the heads and their grouping (G up to 20 for decode, where rows
+of more than 16 query heads are cut into chunks), head_dim, block size
+(multiples of 16 and not), the lengths (empty sequences, lengths on and off
+block and tile boundaries), fp8 scales per tensor or per kv head, and the
+wave cap, so the combinations the hand-picked cases do not name are run too.
+The step's copy and write go first, as in every parity test.  An fp8 cache's
+scales get 4x headroom over the generated pool's (the stored codes stay as
+they are): a scale set from a small pool's largest value can be exceeded by
+the step's freshly drawn new tokens, which E5M2 then stores as infinities
+(kernel and oracle alike), and attention over an infinite key is NaN."""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_336_amd import workloads as W
+from paged_kv_cache_336_amd.step import DeviceStep, MultiStep
+
+from parity_helpers import TOL, check_attention, max_abs_err, oracle_pools, say
+
+pytestmark = pytest.mark.gpu
+
+KINDS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
+         ("bf16", "fp8_e4m3"), ("f16", "fp8_e5m2"), ("f32", "fp8_e4m3"),
+         ("bf16", "fp8_e5m2")]
+
+
+def _lengths(rng, n, bs, cap):
+    lens = rng.integers(1, cap, size=n)
+    for i in range(n):
+        r = rng.random()
+        if r < 0.12:
+            lens[i] = 0                        # an empty sequence
+        elif r < 0.24:
+            lens[i] = bs * int(rng.integers(1, max(2, cap // bs)))  # on a block
+        elif r < 0.36:
+            lens[i] = 32 * int(rng.integers(1, max(2, cap // 32))) + 1
+    return [int(x) for x in lens]
+
+
+def draw_decode(seed):
+    rng = np.random.default_rng([336, 900, seed])
+    q, kv = KINDS[int(rng.integers(len(KINDS)))]
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 20]))
+    while hkv * g > 64:
+        hkv //= 2
+    hkv = max(hkv, 1)
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([1, 3, 7, 16, 32, 48, 64]))
+    n = int(rng.integers(1, 13))
+    lens = _lengths(rng, n, bs, 1500)
+    waves = int(rng.choice([0, 4, 8, 24, 100]))
+    per_head = kv.startswith("fp8") and bool(rng.random() < 0.5)
+    return dict(q=q, kv=kv, hq=hkv * g, hkv=hkv, d=d, bs=bs, lens=lens,
+                waves=waves, per_head=per_head)
+
+
+def draw_multi(seed):
+    rng = np.random.default_rng([336, 901, seed])
+    q, kv = KINDS[int(rng.integers(len(KINDS)))]
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([3, 16, 32, 48]))
+    n = int(rng.integers(1, 7))
+    lens = [max(1, L) for L in _lengths(rng, n, bs, 900)]
+    qlens = []
+    for L in lens:
+        r = rng.random()
+        qlens.append(L if r < 0.15 else (0 if r < 0.25 else
+                                          int(rng.integers(1, min(L, 260) + 1))))
+    waves = int(rng.choice([0, 8, 40]))
+    per_head = kv.startswith("fp8") and bool(rng.random() < 0.5)
+    return dict(q=q, kv=kv, hq=hkv * g, hkv=hkv, d=d, bs=bs, lens=lens,
+                qlens=qlens, waves=waves, per_head=per_head)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_decode(seed):
+    c = draw_decode(seed)
+    say(f"random decode {seed}: {c}")
+    w = W.custom_decode(seed=1000 + seed, num_seqs=len(c["lens"]),
+                        lens=c["lens"], hq=c["hq"], hkv=c["hkv"], d=c["d"],
+                        bs=c["bs"], q_kind=c["q"], kv_kind=c["kv"],
+                        per_head_scales=c["per_head"])
+    if c["kv"].startswith("fp8"):
+        w = replace(w, k_scale=np.float32(4) * w.k_scale,
+                    v_scale=np.float32(4) * w.v_scale)
+    dev = DeviceStep(w, replicas=False)
+    dev.copy()
+    dev.write()
+    err, out = check_attention(dev, w, oracle_pools(w), max_waves=c["waves"])
+    say(f"  max abs err {err:.3g}")
+    # rows of empty sequences are zeros
+    for s, L in enumerate(c["lens"]):
+        if L == 0:
+            assert not out[s].any()
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_multi(seed):
+    import torch
+    c = draw_multi(seed)
+    say(f"random multi {seed}: {c}")
+    mq = W.custom_multi(seed=2000 + seed, lens=c["lens"], qlens=c["qlens"],
+                        hq=c["hq"], hkv=c["hkv"], d=c["d"], bs=c["bs"],
+                        q_kind=c["q"], kv_kind=c["kv"],
+                        per_head_scales=c["per_head"])
+    if c["kv"].startswith("fp8"):
+        mq = replace(mq, w=replace(mq.w, k_scale=np.float32(4) * mq.w.k_scale,
+                                   v_scale=np.float32(4) * mq.w.v_scale))
+    dev = MultiStep(mq)
+    dev.copy()
+    dev.write()
+    dev.attend(max_waves=c["waves"])
+    torch.cuda.synchronize()
+    w = mq.w
+    kp, vp = oracle_pools(w)
+    ref = oracle.paged_attention_multi(
+        mq.query, w.q_kind, kp, vp, w.kv_kind, w.block_tables, w.seq_lens,
+        mq.query_start, w.block_size, w.scale, w.k_scale, w.v_scale)
+    assert np.isfinite(ref).all(), "the inputs overflow the cache type"
+    err = max_abs_err(dev.out.cpu().numpy(), ref)
+    say(f"  max abs err {err:.3g}")
+    assert err <= TOL[c["kv"]], f"{err:.3g}"
