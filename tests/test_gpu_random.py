@@ -20,7 +20,8 @@ import oracle
 from paged_kv_cache_336_amd import workloads as W
 from paged_kv_cache_336_amd.step import DeviceStep, MultiStep
 
-from parity_helpers import TOL, check_attention, max_abs_err, oracle_pools, say
+from parity_helpers import (TOL, check_attention, max_abs_err, oracle_out,
+                            oracle_pools, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -128,3 +129,59 @@ def test_random_multi(seed):
     err = max_abs_err(dev.out.cpu().numpy(), ref)
     say(f"  max abs err {err:.3g}")
     assert err <= TOL[c["kv"]], f"{err:.3g}"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_fused_equals_separate(seed):
+    """The fused write + attention on random shapes (G up to 16, uniform and
+    other block sizes) against the separate write and decode: the same
+    output and pools bit for bit; the separate pair against the oracle."""
+    from test_gpu_fused import assert_same, run_pair
+    c = draw_decode(100 + seed)
+    while c["hq"] // c["hkv"] > 16:
+        c["hq"] //= 2
+        c["hq"] = max(c["hq"], c["hkv"]) // c["hkv"] * c["hkv"]
+    say(f"random fused {seed}: {c}")
+    w = W.custom_decode(seed=3000 + seed, num_seqs=len(c["lens"]),
+                        lens=c["lens"], hq=c["hq"], hkv=c["hkv"], d=c["d"],
+                        bs=c["bs"], q_kind=c["q"], kv_kind=c["kv"],
+                        per_head_scales=c["per_head"])
+    if c["kv"].startswith("fp8"):
+        w = replace(w, k_scale=np.float32(4) * w.k_scale,
+                    v_scale=np.float32(4) * w.v_scale)
+    sep, fus = run_pair(w, max_waves=c["waves"])
+    assert_same(sep, fus)
+    err = max_abs_err(sep.out.cpu().numpy(), oracle_out(w, oracle_pools(w)))
+    say(f"  max abs err {err:.3g}")
+    assert err <= TOL[c["kv"]], f"{err:.3g}"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_token_scales(seed):
+    """Per-token fp8 scales on random shapes: the token-scaled write, then
+    decode, against the oracle's token-scaled write and attention."""
+    import torch
+    c = draw_decode(200 + seed)
+    kv = "fp8_e4m3" if seed % 2 == 0 else "fp8_e5m2"
+    q = ("bf16", "f16", "f32")[seed % 3]
+    say(f"random token scales {seed}: {q}/{kv} {c}")
+    w = W.custom_decode(seed=4000 + seed, num_seqs=len(c["lens"]),
+                        lens=c["lens"], hq=c["hq"], hkv=c["hkv"], d=c["d"],
+                        bs=c["bs"], q_kind=q, kv_kind=kv,
+                        per_token_scales=True)
+    dev = DeviceStep(w, replicas=False)
+    dev.copy()
+    dev.write()
+    dev.attend(max_waves=c["waves"])
+    torch.cuda.synchronize()
+    kp, vp = oracle.copy_blocks(w.k_pool, w.v_pool, w.copy_pairs)
+    ks, vs = oracle.copy_token_scales(w.k_scale, w.v_scale, w.copy_pairs)
+    kp, vp, ks, vs = oracle.cache_write_token_scales(
+        kp, vp, ks, vs, w.kv_kind, w.key, w.value, w.src_kind,
+        w.slot_mapping, w.block_size)
+    ref = oracle.paged_attention(w.query, q, kp, vp, kv, w.block_tables,
+                                 w.seq_lens, w.block_size, w.scale, ks, vs)
+    assert np.isfinite(ref).all()
+    err = max_abs_err(dev.out.cpu().numpy(), ref)
+    say(f"  max abs err {err:.3g}")
+    assert err <= TOL[kv], f"{err:.3g}"
