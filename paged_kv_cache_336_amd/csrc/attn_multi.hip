@@ -442,11 +442,15 @@ template <int D> struct PrefillStage {
 
 // Issue the loads of tile t0 of segment X (rows past X.t_end read as zero
 // and are not fetched).  Every wave's pieces of one load lie in one 16-token
-// half, whose block id a readlane takes from the wave's table window.
+// half, whose block id a readlane takes from the wave's table window.  The
+// tile's first token is token off0 of logical block lb0 (the caller advances
+// the pair tile by tile, so no division by block_size is needed here;
+// block_size is a multiple of 16, so a half never straddles two blocks).
 template <typename ET, int D>
 __device__ __forceinline__ void prefill_load(PrefillStage<D>& st,
-                                             const MSeg& X, int t0,
-                                             uint32_t ta, uint32_t tb, int wb,
+                                             const MSeg& X, int t0, int lb0,
+                                             int off0, uint32_t ta,
+                                             uint32_t tb, int wb,
                                              const AttnArgs& a, int tid) {
   constexpr int PPR = PrefillStage<D>::PPR;
   constexpr int ROW = D * ET::bytes;
@@ -466,12 +470,16 @@ __device__ __forceinline__ void prefill_load(PrefillStage<D>& st,
     nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
     int64_t row0 = 0;
     if (nvalid > 0) {
-      const int lb = th / a.block_size;
+      int lb = lb0, off = off0 + 16 * hh;  // token th of the sequence
+      if (off >= a.block_size) {
+        off -= a.block_size;
+        ++lb;
+      }
       const int idx = lb - wb;  // 0 .. 127
       int phys = idx < 64 ? __builtin_amdgcn_readlane(ta, idx)
                           : __builtin_amdgcn_readlane(tb, idx - 64);
       phys = (uint32_t)phys < (uint32_t)a.num_blocks ? phys : a.num_blocks - 1;
-      row0 = (int64_t)phys * a.block_size + (th - lb * a.block_size);
+      row0 = (int64_t)phys * a.block_size + off;
     }
     const int nrec = __builtin_amdgcn_readfirstlane(nvalid * (int)stride);
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
@@ -607,12 +615,14 @@ void attn_prefill_kernel(AttnArgs a) {
   MSeg LXn = mseg_at(lpos_n, te, tex, lens, qs0, qn, a);
   int lk = 0;
   int lwb = LX.wb;
+  // the next tile's first token: token loff of logical block lblk
+  int lblk = LX.wb, loff = LX.t_begin - LX.wb * a.block_size;
   uint32_t lta = load_window(LX, 0, a, lane), ltb = load_window(LX, 1, a, lane);
   uint32_t lta_n = load_window(LXn, 0, a, lane);
   uint32_t ltb_n = load_window(LXn, 1, a, lane);
   auto load_next = [&](PrefillStage<D>& st) {
     const int t0 = LX.valid ? LX.t_begin + 32 * lk : 0;
-    if (LX.valid && t0 / a.block_size - lwb >= 64) {
+    if (LX.valid && lblk - lwb >= 64) {
       // the window moves on by 64 blocks (at most once per tile)
       lwb += 64;
       lta = ltb;
@@ -620,11 +630,22 @@ void attn_prefill_kernel(AttnArgs a) {
       shifted.wb = lwb;
       ltb = load_window(shifted, 1, a, lane);
     }
-    prefill_load<ET, D>(st, LX, t0, lta, ltb, lwb, a, tid);
+    prefill_load<ET, D>(st, LX, t0, lblk, loff, lta, ltb, lwb, a, tid);
+    loff += 32;  // (block_size 16 crosses two blocks per tile)
+    if (loff >= a.block_size) {
+      loff -= a.block_size;
+      ++lblk;
+      if (loff >= a.block_size) {
+        loff -= a.block_size;
+        ++lblk;
+      }
+    }
     if (LX.valid && ++lk == LX.ntiles) {
       LX = LXn;
       lk = 0;
       lwb = LX.wb;
+      lblk = LX.wb;
+      loff = LX.t_begin - LX.wb * a.block_size;
       lta = lta_n;
       ltb = ltb_n;
       lpos_n += LX.ntiles;
