@@ -575,7 +575,11 @@ __device__ __forceinline__ void softmax_tile(
     for (int w = 0; w < 4; ++w) {
       const uint32_t h = f32x2_to_bits(pv[2 * w], pv[2 * w + 1], PVT{});
       pb_hi[w] = h;
-      if constexpr (S::PSPLIT)
+      if constexpr (S::PSPLIT && FOLD)
+        pb_lo[w] = f32x2_to_bits(minus_element<false>(pv[2 * w], h, PVT{}),
+                                 minus_element<true>(pv[2 * w + 1], h, PVT{}),
+                                 PVT{});
+      else if constexpr (S::PSPLIT)
         pb_lo[w] = f32x2_to_bits(pv[2 * w] - lo_bits_to_f32(h, PVT{}),
                                  pv[2 * w + 1] - hi_bits_to_f32(h, PVT{}),
                                  PVT{});

@@ -182,6 +182,30 @@ __device__ __forceinline__ float hi_bits_to_f32(uint32_t w, F16) {
   return static_cast<float>(bitcast<_Float16>(static_cast<uint16_t>(w >> 16)));
 }
 
+// x minus the low (or high) 16-bit element of the packed word w, in one
+// dot2 instruction: the products with -1 and 0 are exact, and so is the
+// difference whenever the element is x rounded to the 16-bit type (the
+// residual a split into hi + lo parts needs).
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+// (The pair of factors is passed in a scalar register: left to the compiler,
+// (-1, 0) becomes the inline constant -1.0, and the residuals came out wrong
+// on gfx950.)
+template <bool HI>
+__device__ __forceinline__ float minus_element(float x, uint32_t w, BF16) {
+  uint32_t m = HI ? 0xBF800000u : 0x0000BF80u;  // (0, -1) or (-1, 0)
+  asm("" : "+s"(m));
+  return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2v_t>(w),
+                                         bitcast<bf16x2v_t>(m), x, false);
+}
+template <bool HI>
+__device__ __forceinline__ float minus_element(float x, uint32_t w, F16) {
+  uint32_t m = HI ? 0xBC000000u : 0x0000BC00u;
+  asm("" : "+s"(m));
+  return __builtin_amdgcn_fdot2(bitcast<f16x2v_t>(w), bitcast<f16x2v_t>(m), x,
+                                false);
+}
+
 // ---------------------------------------------------------------------------
 // Wave-wide helpers (wave64).
 // ---------------------------------------------------------------------------
