@@ -533,7 +533,19 @@ __device__ __forceinline__ void softmax_tile(
   const bool grow = !LAZY || mx > st.m + kLazyMargin;
   const float m_new = LAZY ? (grow ? mx : st.m) : fmaxf(st.m, mx);
   const float m_use = CAUSAL && m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = grow ? fast_exp2(st.m - m_use) : 1.f;
+  // (LAZY: the old sums' factor is needed only in the rare tiles where some
+  // column's reference moves; its exponential and the rescale of the
+  // accumulators are taken there, in one branch)
+  float alpha = 1.f;
+  if constexpr (LAZY) {
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      alpha = grow ? fast_exp2(st.m - m_use) : 1.f;
+#pragma unroll
+      for (int n = 0; n < S::NBLK; ++n) st.o[n] *= alpha;
+    }
+  } else {
+    alpha = fast_exp2(st.m - m_use);
+  }
   float pv[8];
   float psum = 0.f;
 #pragma unroll
@@ -563,7 +575,7 @@ __device__ __forceinline__ void softmax_tile(
     for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(u[e] - mv_use);
     st.mv = mv_new;
   }
-  if (!LAZY || __builtin_amdgcn_ballot_w64(grow) != 0) {
+  if constexpr (!LAZY) {
 #pragma unroll
     for (int n = 0; n < S::NBLK; ++n) st.o[n] *= orescale;
   }
