@@ -398,10 +398,10 @@ void attn_decode_kernel(AttnArgs a) {
           stage_k<QT, CT, D>(cur.kraw[0], kt, lane);
           uint32_t kw[2][S::KWORDS];
           k_from_lds<QT, CT, D>(kw, kt, lane);
-          compute_tile<QT, CT, D, false, PT, !PT>(kw, qw, st, vt, t0, X.t_end,
+          compute_tile<QT, CT, D, false, PT, true>(kw, qw, st, vt, t0, X.t_end,
                                              qk_mul, lane, 0, cur.sc[0]);
         } else {
-          compute_tile<QT, CT, D, false, PT, !PT>(cur.kw[0], qw, st, vt, t0,
+          compute_tile<QT, CT, D, false, PT, true>(cur.kw[0], qw, st, vt, t0,
                                              X.t_end, qk_mul, lane, 0,
                                              cur.sc[0]);
         }
@@ -429,7 +429,7 @@ void attn_decode_kernel(AttnArgs a) {
         for (int sb = 0; sb < S::SUB; ++sb) {
           if (t0 + 32 * sb < X.t_end) {
             stage_v<QT, CT, D>(cur.vraw[sb], vt, lane);
-            compute_tile<QT, CT, D, false, PT, !PT>(cur.kw[sb], qw, st, vt,
+            compute_tile<QT, CT, D, false, PT, true>(cur.kw[sb], qw, st, vt,
                                                t0 + 32 * sb, X.t_end, qk_mul,
                                                lane, 0, cur.sc[sb]);
           }

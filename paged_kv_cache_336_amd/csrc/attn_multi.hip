@@ -322,7 +322,7 @@ void attn_multi_kernel(AttnArgs a) {
             lane, same_seg ? tsc : token_scales(Xn));
         __builtin_amdgcn_sched_barrier(0);
         if (live)
-          compute_tile_groups<QT, CT, D, NG, PT, !PT>(cur.kw[0], qw, st, vt, t0,
+          compute_tile_groups<QT, CT, D, NG, PT, true>(cur.kw[0], qw, st, vt, t0,
                                                  lim, lim_lo, qk_mul, lane,
                                                  cur.sc[0]);
         cur = nxt;
@@ -347,7 +347,7 @@ void attn_multi_kernel(AttnArgs a) {
                                        lane, tsc);
         }
         stage_v<QT, CT, D>(cur.vraw[0], vt, lane);
-        compute_tile_groups<QT, CT, D, NG, PT, !PT>(cur.kw[0], qw, st, vt, t0, lim,
+        compute_tile_groups<QT, CT, D, NG, PT, true>(cur.kw[0], qw, st, vt, t0, lim,
                                                lim_lo, qk_mul, lane, cur.sc[0]);
       }
     }

@@ -455,14 +455,16 @@ __device__ __forceinline__ void qk_tile(
 // factored out of the sum.  The PV weight of token t is then 2^(s_t - m)
 // vs_t = 2^(u_t - m) with u_t = s_t + log2 vs_t; it is formed as
 // 2^(u_t - mv) against a second running maximum mv of u, so the weights fed
-// to the PV product stay in (0, 1] whatever the scales' range, and O^T is
-// rescaled by 2^(mv_old - mv_new) as the sum l is by 2^(m_old - m_new).
+// to the PV product stay bounded (by 1, or 2^kLazyMargin under LAZY) whatever
+// the scales' range, and O^T is rescaled by 2^(mv_old - mv_new) as the sum l
+// is by 2^(m_old - m_new).
 // fold_value_scales turns O^T back into units of 2^m at the end.
 //
 // LAZY: the reference maximum moves only when a tile's maximum exceeds it by
 // more than kLazyMargin (log2 units), so weights reach at most
 // 2^kLazyMargin and O^T and l are rescaled only on those (rare) steps -- a
-// wave-uniform branch skips the multiply of the accumulators otherwise.  The
+// wave-uniform branch skips the multiply of the accumulators otherwise
+// (with per-token scales, each of the two maxima follows this rule).  The
 // result is the same softmax with another reference point (m is what the
 // partials and the merge carry); the PV weights keep the hi + lo split's
 // precision relative to their size.
@@ -540,8 +542,10 @@ __device__ __forceinline__ void softmax_tile(
   if constexpr (LAZY) {
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       alpha = grow ? fast_exp2(st.m - m_use) : 1.f;
+      if constexpr (!PT) {  // (PT: the accumulators have their own reference)
 #pragma unroll
-      for (int n = 0; n < S::NBLK; ++n) st.o[n] *= alpha;
+        for (int n = 0; n < S::NBLK; ++n) st.o[n] *= alpha;
+      }
     }
   } else {
     alpha = fast_exp2(st.m - m_use);
@@ -557,7 +561,6 @@ __device__ __forceinline__ void softmax_tile(
   st.l = st.l * alpha + psum;
   st.m = m_new;
   float orescale = alpha;
-  static_assert(!(PT && LAZY), "per-token scales use the eager update");
   if constexpr (PT) {
     float u[8];
     float mxv = -INFINITY;
@@ -568,9 +571,20 @@ __device__ __forceinline__ void softmax_tile(
     }
     mxv = xor_max(mxv, 16);
     mxv = xor_max(mxv, 32);
-    const float mv_new = fmaxf(st.mv, mxv);
+    // the accumulators' reference, lazy as the scores' one: the weights fed
+    // to the PV product stay below 2^8
+    const bool grow_v = !LAZY || mxv > st.mv + kLazyMargin;
+    const float mv_new = LAZY ? (grow_v ? mxv : st.mv) : fmaxf(st.mv, mxv);
     const float mv_use = mv_new == -INFINITY ? 0.f : mv_new;
-    orescale = fast_exp2(st.mv - mv_use);
+    if constexpr (LAZY) {
+      if (__builtin_amdgcn_ballot_w64(grow_v) != 0) {
+        const float f = grow_v ? fast_exp2(st.mv - mv_use) : 1.f;
+#pragma unroll
+        for (int n = 0; n < S::NBLK; ++n) st.o[n] *= f;
+      }
+    } else {
+      orescale = fast_exp2(st.mv - mv_use);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(u[e] - mv_use);
     st.mv = mv_new;
