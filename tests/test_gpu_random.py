@@ -5,7 +5,8 @@ of more than 16 query heads are cut into chunks), head_dim, block size
 (multiples of 16 and not), the lengths (empty sequences, lengths on and off
 block and tile boundaries), fp8 scales per tensor or per kv head, and the
 wave cap, so the combinations the hand-picked cases do not name are run too.
-The step's copy and write go first, as in every parity test.  An fp8 cache's
+The step's copy and write go first, as in every parity test, and the pools
+they leave must equal the oracle's bit for bit.  An fp8 cache's
 scales get 4x headroom over the generated pool's (the stored codes stay as
 they are): a scale set from a small pool's largest value can be exceeded by
 the step's freshly drawn new tokens, which E5M2 then stores as infinities
@@ -20,8 +21,8 @@ import oracle
 from paged_kv_cache_336_amd import workloads as W
 from paged_kv_cache_336_amd.step import DeviceStep, MultiStep
 
-from parity_helpers import (TOL, check_attention, max_abs_err, oracle_out,
-                            oracle_pools, say)
+from parity_helpers import (TOL, assert_pools_bitwise, check_attention,
+                            max_abs_err, oracle_out, oracle_pools, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -95,7 +96,9 @@ def test_random_decode(seed):
     dev = DeviceStep(w, replicas=False)
     dev.copy()
     dev.write()
-    err, out = check_attention(dev, w, oracle_pools(w), max_waves=c["waves"])
+    pools = oracle_pools(w)
+    assert_pools_bitwise(dev, pools)  # the step's copies and writes
+    err, out = check_attention(dev, w, pools, max_waves=c["waves"])
     say(f"  max abs err {err:.3g}")
     # rows of empty sequences are zeros
     for s, L in enumerate(c["lens"]):
@@ -122,6 +125,7 @@ def test_random_multi(seed):
     torch.cuda.synchronize()
     w = mq.w
     kp, vp = oracle_pools(w)
+    assert_pools_bitwise(dev, (kp, vp))  # the step's copies and writes
     ref = oracle.paged_attention_multi(
         mq.query, w.q_kind, kp, vp, w.kv_kind, w.block_tables, w.seq_lens,
         mq.query_start, w.block_size, w.scale, w.k_scale, w.v_scale)
@@ -135,7 +139,8 @@ def test_random_multi(seed):
 def test_random_fused_equals_separate(seed):
     """The fused write + attention on random shapes (G up to 16, uniform and
     other block sizes) against the separate write and decode: the same
-    output and pools bit for bit; the separate pair against the oracle."""
+    output and pools bit for bit; the separate pair against the oracle
+    (pools bit for bit, output within tolerance)."""
     from test_gpu_fused import assert_same, run_pair
     c = draw_decode(100 + seed)
     while c["hq"] // c["hkv"] > 16:
@@ -151,16 +156,20 @@ def test_random_fused_equals_separate(seed):
                     v_scale=np.float32(4) * w.v_scale)
     sep, fus = run_pair(w, max_waves=c["waves"])
     assert_same(sep, fus)
-    err = max_abs_err(sep.out.cpu().numpy(), oracle_out(w, oracle_pools(w)))
+    pools = oracle_pools(w)
+    assert_pools_bitwise(sep, pools)
+    err = max_abs_err(sep.out.cpu().numpy(), oracle_out(w, pools))
     say(f"  max abs err {err:.3g}")
     assert err <= TOL[c["kv"]], f"{err:.3g}"
 
 
 @pytest.mark.parametrize("seed", range(8))
 def test_random_token_scales(seed):
-    """Per-token fp8 scales on random shapes: the token-scaled write, then
-    decode, against the oracle's token-scaled write and attention."""
+    """Per-token fp8 scales on random shapes: the token-scaled write (codes
+    and scales bit for bit), then decode, against the oracle's token-scaled
+    write and attention."""
     import torch
+    from test_gpu_token_scales import assert_scales_bitwise
     c = draw_decode(200 + seed)
     kv = "fp8_e4m3" if seed % 2 == 0 else "fp8_e5m2"
     q = ("bf16", "f16", "f32")[seed % 3]
@@ -179,6 +188,8 @@ def test_random_token_scales(seed):
     kp, vp, ks, vs = oracle.cache_write_token_scales(
         kp, vp, ks, vs, w.kv_kind, w.key, w.value, w.src_kind,
         w.slot_mapping, w.block_size)
+    assert_pools_bitwise(dev, (kp, vp))  # codes and each row's scale
+    assert_scales_bitwise(dev, ks, vs)
     ref = oracle.paged_attention(w.query, q, kp, vp, kv, w.block_tables,
                                  w.seq_lens, w.block_size, w.scale, ks, vs)
     assert np.isfinite(ref).all()
