@@ -757,11 +757,11 @@ void attn_prefill_kernel(AttnArgs a) {
 
 // Merge of a cut multi-query row: workgroup (s, h, rr) over a grid of
 // num_seqs * num_kv_heads * max_rps (rows past a sequence's count exit).
-template <int D, bool SCALED, int BATCH>
-__global__ __launch_bounds__(kMergeThreads) void attn_multi_merge_kernel(
+template <int D, bool SCALED, int BATCH, int THREADS = kMergeThreads>
+__global__ __launch_bounds__(THREADS) void attn_multi_merge_kernel(
     AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) f32x4_t red_o[kMergeThreads];
-  __shared__ float red_m[kMergeThreads], red_l[kMergeThreads];
+  __shared__ __attribute__((aligned(16))) f32x4_t red_o[THREADS];
+  __shared__ float red_m[THREADS], red_l[THREADS];
   const int rr = (int)(blockIdx.x % (unsigned)a.max_rps);
   const int sh = (int)(blockIdx.x / (unsigned)a.max_rps);
   const int h = sh % a.num_kv_heads;
@@ -782,11 +782,11 @@ __global__ __launch_bounds__(kMergeThreads) void attn_multi_merge_kernel(
   const int G = a.group;
   const int gcount = min(a.row_tokens, m.nq - rr * a.row_tokens) * G;
   const int64_t tok0 = (int64_t)m.q0 + rr * a.row_tokens;
-  merge_row<D, BATCH>(
-      a, wf, npieces, q_first, gcount,
-      [&](int g) {
-        return (tok0 + g / G) * a.num_q_heads + h * G + g % G;
-      },
+  auto row_of = [&](int g) {
+    return (tok0 + g / G) * a.num_q_heads + h * G + g % G;
+  };
+  merge_row<D, BATCH, decltype(row_of), THREADS>(
+      a, wf, npieces, q_first, gcount, row_of,
       SCALED ? head_scale(a.v_scale, a, h) : 1.f, red_o, red_m, red_l);
 }
 
@@ -803,7 +803,11 @@ static hipError_t launch_mu(AttnArgs a, int max_waves, hipStream_t stream) {
   a.num_waves = grid * kWaves;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), dyn, stream, a);
   const int64_t rows = (int64_t)a.num_seqs * a.num_kv_heads * a.max_rps;
-  if (rows > 0 && a.num_waves >= 4 * rows)
+  if (rows > 0 && a.num_waves >= 4 * rows && a.slot_heads * D / 4 >= 512)
+    // (rows of 512 column quads or more: one quad per thread)
+    hipLaunchKernelGGL((attn_multi_merge_kernel<D, SCALED, 16, 512>),
+                       dim3((unsigned)rows), dim3(512), 0, stream, a);
+  else if (rows > 0 && a.num_waves >= 4 * rows)
     hipLaunchKernelGGL((attn_multi_merge_kernel<D, SCALED, 16>),
                        dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
   else if (rows > 0)

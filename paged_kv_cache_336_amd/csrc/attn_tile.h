@@ -812,7 +812,7 @@ __device__ __forceinline__ void lse_fold(float& m, float& l, f32x4_t& acc,
 // its first piece in that wave; output column g goes to row row_of(g) of
 // ``out`` (head_dim floats each), times vscale (an fp8 cache's value scale
 // for the row's kv head, else 1).
-template <int D, int BATCH, typename RowOf>
+template <int D, int BATCH, typename RowOf, int THREADS = kMergeThreads>
 __device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
                                           int npieces, int q_first,
                                           int gcount, RowOf row_of,
@@ -822,15 +822,15 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
   const int tid = threadIdx.x;
   const int gmax = a.slot_heads;
   const int items = gcount * D4;
-  if (items > kMergeThreads) {
+  if (items > THREADS) {
     // More than one item per thread: thread tid folds items it and
-    // it + kMergeThreads together (it = tid, tid + 2 kMergeThreads, ...), so
+    // it + THREADS together (it = tid, tid + 2 THREADS, ...), so
     // the loads of both are in flight at once.  Each item folds its pieces
     // in order, as below.
     constexpr int HB = BATCH / 2 > 0 ? BATCH / 2 : 1;
     const uint32_t step = 2u * (uint32_t)gmax;
-    for (int it = tid; it < items; it += 2 * kMergeThreads) {
-      const int itb = it + kMergeThreads;
+    for (int it = tid; it < items; it += 2 * THREADS) {
+      const int itb = it + THREADS;
       const bool has_b = itb < items;
       const int ga = it / D4, da = it - ga * D4;
       const int gb = has_b ? itb / D4 : ga, db = has_b ? itb - gb * D4 : da;
@@ -873,8 +873,10 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
     }
     return;
   }
+  // (sub-sums as with kMergeThreads threads whatever THREADS is, so that the
+  // fold order, and with it every bit, does not depend on the launch)
   const int nsub = items >= kMergeThreads ? 1 : kMergeThreads / items;
-  for (int it = tid; it < items * nsub; it += kMergeThreads) {
+  for (int it = tid; it < items * nsub; it += THREADS) {
     const int item = it % items;
     const int sub = it / items;
     const int g = item / D4;
@@ -916,7 +918,7 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
   }
   if (nsub > 1) {
     __syncthreads();
-    for (int item = tid; item < items; item += kMergeThreads) {
+    for (int item = tid; item < items; item += THREADS) {
       const int g = item / D4;
       const int d4 = item - g * D4;
       float m = red_m[item], l = red_l[item];
