@@ -811,7 +811,9 @@ __device__ __forceinline__ void lse_fold(float& m, float& l, f32x4_t& acc,
 // wf is the row's first wave, npieces its piece count, q_first the slot of
 // its first piece in that wave; output column g goes to row row_of(g) of
 // ``out`` (head_dim floats each), times vscale (an fp8 cache's value scale
-// for the row's kv head, else 1).
+// for the row's kv head, else 1).  THREADS is the workgroup's size (red_*
+// hold THREADS entries); each item folds its pieces in the same order
+// whatever it is.
 template <int D, int BATCH, typename RowOf, int THREADS = kMergeThreads>
 __device__ __forceinline__ void merge_row(const AttnArgs& a, int wf,
                                           int npieces, int q_first,
