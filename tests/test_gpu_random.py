@@ -10,8 +10,12 @@ they leave must equal the oracle's bit for bit.  An fp8 cache's
 scales get 4x headroom over the generated pool's (the stored codes stay as
 they are): a scale set from a small pool's largest value can be exceeded by
 the step's freshly drawn new tokens, which E5M2 then stores as infinities
-(kernel and oracle alike), and attention over an infinite key is NaN."""
+(kernel and oracle alike), and attention over an infinite key is NaN.
 
+PKV_RANDOM_SEEDS=N runs each test on N seeds instead of its default count
+(for long sweeps; the draws are the same functions of the seed)."""
+
+import os
 from dataclasses import replace
 
 import numpy as np
@@ -25,6 +29,12 @@ from parity_helpers import (TOL, assert_pools_bitwise, check_attention,
                             max_abs_err, oracle_out, oracle_pools, say)
 
 pytestmark = pytest.mark.gpu
+
+_SEEDS = int(os.environ.get("PKV_RANDOM_SEEDS", "0"))
+
+
+def seeds(default):
+    return range(_SEEDS if _SEEDS > 0 else default)
 
 KINDS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
          ("bf16", "fp8_e4m3"), ("f16", "fp8_e5m2"), ("f32", "fp8_e4m3"),
@@ -82,7 +92,7 @@ def draw_multi(seed):
                 qlens=qlens, waves=waves, per_head=per_head)
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", seeds(32))
 def test_random_decode(seed):
     c = draw_decode(seed)
     say(f"random decode {seed}: {c}")
@@ -106,7 +116,7 @@ def test_random_decode(seed):
             assert not out[s].any()
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", seeds(16))
 def test_random_multi(seed):
     import torch
     c = draw_multi(seed)
@@ -135,7 +145,7 @@ def test_random_multi(seed):
     assert err <= TOL[c["kv"]], f"{err:.3g}"
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", seeds(12))
 def test_random_fused_equals_separate(seed):
     """The fused write + attention on random shapes (G up to 16, uniform and
     other block sizes) against the separate write and decode: the same
@@ -163,7 +173,7 @@ def test_random_fused_equals_separate(seed):
     assert err <= TOL[c["kv"]], f"{err:.3g}"
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", seeds(8))
 def test_random_token_scales(seed):
     """Per-token fp8 scales on random shapes: the token-scaled write (codes
     and scales bit for bit), then decode, against the oracle's token-scaled
