@@ -402,3 +402,39 @@ def test_random_token_writes(seed):
     assert to_host_storage(vc, kind).tobytes() == ev.tobytes(), "v codes"
     assert kst.cpu().numpy().tobytes() == eks.tobytes(), "k scales"
     assert vst.cpu().numpy().tobytes() == evs.tobytes(), "v scales"
+
+
+@pytest.mark.parametrize("seed", seeds(8))
+def test_random_multi_token_scales(seed):
+    """Several new tokens per sequence over per-token-scaled fp8 caches on
+    random shapes: the token-scaled write (codes and scales bit for bit),
+    then the multi-query call, against the oracle."""
+    import torch
+    from test_gpu_token_scales import assert_scales_bitwise
+    c = draw_multi(300 + seed)
+    kv = "fp8_e4m3" if seed % 2 == 0 else "fp8_e5m2"
+    q = ("bf16", "f16", "f32")[seed % 3]
+    say(f"random multi token scales {seed}: {q}/{kv} {c}")
+    mq = W.custom_multi(seed=2500 + seed, lens=c["lens"], qlens=c["qlens"],
+                        hq=c["hq"], hkv=c["hkv"], d=c["d"], bs=c["bs"],
+                        q_kind=q, kv_kind=kv, per_token_scales=True)
+    dev = MultiStep(mq, replicas=False)
+    dev.copy()
+    dev.write()
+    dev.attend(max_waves=c["waves"])
+    torch.cuda.synchronize()
+    w = mq.w
+    kp, vp = oracle.copy_blocks(w.k_pool, w.v_pool, w.copy_pairs)
+    ks, vs = oracle.copy_token_scales(w.k_scale, w.v_scale, w.copy_pairs)
+    kp, vp, ks, vs = oracle.cache_write_token_scales(
+        kp, vp, ks, vs, w.kv_kind, w.key, w.value, w.src_kind,
+        w.slot_mapping, w.block_size)
+    assert_pools_bitwise(dev, (kp, vp))
+    assert_scales_bitwise(dev, ks, vs)
+    ref = oracle.paged_attention_multi(
+        mq.query, q, kp, vp, kv, w.block_tables, w.seq_lens, mq.query_start,
+        w.block_size, w.scale, ks, vs)
+    assert np.isfinite(ref).all()
+    err = max_abs_err(dev.out.cpu().numpy(), ref)
+    say(f"  max abs err {err:.3g}")
+    assert err <= TOL[kv], f"{err:.3g}"
