@@ -74,3 +74,24 @@ def test_noalloc_fp8_and_limits():
             max_waves=1028, cache_kind=dev.cache_kind)
     assert e.value.status == 4
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_noalloc_random_shapes(seed):
+    """The random decode shapes (every cache and query type pairing, G up
+    to 20, both head_dims, any block size, empty sequences, per-tensor and
+    per-head fp8 scales, several wave caps), one after another on the same
+    scratch: bit for bit against the workspace call."""
+    from dataclasses import replace
+    from test_gpu_random import draw_decode
+    c = draw_decode(400 + seed)
+    say(f"no-alloc random {seed}: {c}")
+    w = W.custom_decode(seed=4400 + seed, num_seqs=len(c["lens"]),
+                        lens=c["lens"], hq=c["hq"], hkv=c["hkv"], d=c["d"],
+                        bs=c["bs"], q_kind=c["q"], kv_kind=c["kv"],
+                        per_head_scales=c["per_head"])
+    if c["kv"].startswith("fp8"):
+        w = replace(w, k_scale=np.float32(4) * w.k_scale,
+                    v_scale=np.float32(4) * w.v_scale)
+    ref, got = decode_both(w, c["waves"])
+    assert np.array_equal(ref.view(np.uint32), got.view(np.uint32))
